@@ -1,0 +1,364 @@
+"""CPU oracle for UltraQuant 4-bit paged-KV decode attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module; the library never calls it and it
+imports nothing from the library.
+
+Plain, slow numpy float64. Every function cites the passage it follows on the
+pages (vLLM API docs):
+  [UQ-impl]  "vllm/v1/attention/backends/ultraquant_attn", class
+             UltraQuantAttentionImpl: _ensure_on_device, _store_kv,
+             _decode_attention, _ultraquant_continuation_prefill.
+  [UQ-fly]   "vllm/v1/attention/ops/flydsl_ultraquant_decode": module text,
+             _SegmBufPool, _fp4_value_lut, flydsl_ultraquant_decode_attention.
+  [TQ-v2]    "vllm/v1/attention/ops/turboquant_soa/triton_turboquant_decode_v2":
+             triton_turboquant_decode_attention_v2 (split-KV stage 1 / 2).
+The pages name the formats (FP4 E2M1, UE8M0, E4M3) but print neither the value
+tables, the scale rule nor the byte layout of a slot. Those are taken from the
+OCP Microscaling Formats (MX) v1.0 and OCP 8-bit Floating Point specs, as
+stated at each function.
+
+Parity pins: the Hadamard, the rotation, E2M1 values and rounding, UE8M0 and
+E4M3 decoding, and the attention are pinned by closed forms, library routines
+and brute force in tests/. Parity unpinned (no passage of the pages fixes
+them; they are pinned by their own definitions only): the 32-element block
+partition, the UE8M0 scale-selection rule, the nibble packing order and the
+272-byte slot layout.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+D = 256
+MX_BLOCK = 32                       # elements per UE8M0 scale
+SLOT_BYTES = 272                    # 128 K codes + 128 V codes + 8 + 8 scales
+K_CODE_OFF, V_CODE_OFF = 0, 128
+K_SCALE_OFF, V_SCALE_OFF = 256, 264
+
+# OCP MX v1.0, FP4 E2M1: magnitudes of the eight non-negative codes
+# (exponent bias 1, one mantissa bit, code 0b001 is the subnormal 0.5).
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+E2M1_EMAX = 2                       # exponent of the largest normal, 6 = 1.5 * 2**2
+
+
+# --------------------------------------------------------------------------
+# bf16 plumbing
+# --------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 (nearest, ties to even) via float32.
+
+    Only used to state what a bf16 output of an exact value is; values passed
+    here are exactly representable in float32 or the double rounding is
+    irrelevant to the caller.
+    """
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# Rotation ([UQ-impl] _ensure_on_device: the rotation is a pure Hadamard,
+# orthonormal and symmetric, so PiT = Pi = H; _store_kv rotates K by it;
+# continuation prefill rotates with x @ PiT)
+# --------------------------------------------------------------------------
+def hadamard(n: int = D) -> np.ndarray:
+    """Normalised Sylvester Hadamard: H[i, j] = (-1)**popcount(i & j) / sqrt(n).
+
+    Symmetric and orthonormal, as [UQ-impl] _ensure_on_device requires. The
+    pages do not fix the row order; the Sylvester (natural) order is the one a
+    radix-2 butterfly produces.
+    """
+    assert n > 0 and n & (n - 1) == 0
+    i = np.arange(n)
+    parity = np.zeros((n, n), dtype=np.int64)
+    x = i[:, None] & i[None, :]
+    while np.any(x):
+        parity ^= x & 1
+        x = x >> 1
+    return np.where(parity == 1, -1.0, 1.0) / np.sqrt(n)
+
+
+_H = hadamard(D)
+
+# A +-subset sum of 256 bf16 values (8 significant bits each) fits in float64's
+# 53 bits when the exponents of the non-zero inputs span at most 36 binades:
+# 53 >= span + 8 (significand) + 9 (carry of 256 terms). Then x @ H is exact
+# in any summation order and the GPU butterfly sees the same value.
+MAX_EXACT_SPAN = 36
+
+
+def exact_span_ok(x: np.ndarray) -> np.ndarray:
+    """Per vector (last axis): True when x @ H is exact in float64."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    nz = a > 0
+    e = np.where(nz, np.frexp(np.where(nz, a, 1.0))[1], 0)
+    emax = np.where(nz, e, np.iinfo(np.int64).min).max(axis=-1)
+    emin = np.where(nz, e, np.iinfo(np.int64).max).min(axis=-1)
+    return (~nz.any(axis=-1)) | (emax - emin <= MAX_EXACT_SPAN)
+
+
+def rotate(x: np.ndarray) -> np.ndarray:
+    """y = x @ H over the last axis ([UQ-impl] _store_kv; key_chunk @ PiT)."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(exact_span_ok(x)):
+        raise ValueError("input spans more than 36 binades: x @ H would not be exact")
+    return x @ _H
+
+
+# --------------------------------------------------------------------------
+# Block scale and FP4 E2M1 code ([UQ-impl] class docstring: "FP4 E2M1 + UE8M0,
+# rotated K"; [UQ-fly] _fp4_value_lut: lut[nibble] is the dequant value)
+# --------------------------------------------------------------------------
+def ue8m0_exponent(amax: np.ndarray) -> np.ndarray:
+    """Shared block exponent, OCP MX v1.0 rule: floor(log2 amax) - emax_elem.
+
+    emax_elem = 2 for E2M1. Clamped to the UE8M0 range [-127, 127]; an
+    all-zero block takes -127. floor(log2) is read from the float64 exponent
+    field, which is exact.
+    """
+    a = np.asarray(amax, dtype=np.float64)
+    pos = a > 0
+    _, ex = np.frexp(np.where(pos, a, 1.0))       # a = m * 2**ex, m in [0.5, 1)
+    e = (ex - 1) - E2M1_EMAX
+    e = np.where(pos, e, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def e2m1_round(r: np.ndarray) -> np.ndarray:
+    """Magnitude code (0..7) of r >= 0: nearest E2M1 magnitude, ties to the
+    even code, saturating at 6 (code 7)."""
+    r = np.asarray(r, dtype=np.float64)
+    dist = np.abs(r[..., None] - E2M1_MAGNITUDES)
+    best = dist.min(axis=-1, keepdims=True)
+    tie = dist == best
+    # among the nearest candidates, prefer the even code (even mantissa bit)
+    codes = np.arange(8)
+    pref = np.where(tie, np.where(codes % 2 == 0, 0, 1) * 8 + codes, 99)
+    code = pref.argmin(axis=-1)
+    return np.where(r > 6.0, 7, code).astype(np.uint8)
+
+
+def e2m1_encode(x: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """4-bit codes of x under block exponent e: sign bit 3 = signbit(x),
+    magnitude code of |x| / 2**e."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.ldexp(np.abs(x), -np.asarray(e))
+    mag = e2m1_round(r)
+    sign = np.signbit(x).astype(np.uint8) << 3
+    return (sign | mag).astype(np.uint8)
+
+
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    """Value of 4-bit E2M1 codes (the 16-entry table [UQ-fly] _fp4_value_lut)."""
+    c = np.asarray(code, dtype=np.int64)
+    v = E2M1_MAGNITUDES[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def quantize_blocks(x: np.ndarray):
+    """Split the last axis (256) into 8 blocks of 32 consecutive elements.
+
+    Returns (codes (..., 256) uint8 in 0..15, scale bytes (..., 8) uint8).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    xb = x.reshape(*x.shape[:-1], D // MX_BLOCK, MX_BLOCK)
+    e = ue8m0_exponent(np.abs(xb).max(axis=-1))
+    codes = e2m1_encode(xb, e[..., None]).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Two codes per byte, element 2i in bits 0-3 and 2i+1 in bits 4-7."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+# --------------------------------------------------------------------------
+# Store ([UQ-impl] _store_kv: key, value (N, Hk, D); kv_cache
+# (num_blocks, block_size, Hk, slot_size); slot_mapping; "Rotate K by the
+# Hadamard and pack K+V into FP4/UE8M0 slots")
+# --------------------------------------------------------------------------
+def encode_slots(key_bits: np.ndarray, value_bits: np.ndarray) -> np.ndarray:
+    """Slot bytes (..., 272) of bf16 key/value vectors (..., 256).
+
+    Slot layout: [0,128) K codes, [128,256) V codes, [256,264) K scale bytes,
+    [264,272) V scale bytes. K is rotated before quantisation, V is not
+    ([UQ-impl] continuation prefill copies V unrotated).
+    """
+    k = rotate(bf16_to_f64(key_bits))
+    v = bf16_to_f64(value_bits)
+    kc, ks = quantize_blocks(k)
+    vc, vs = quantize_blocks(v)
+    out = np.empty(k.shape[:-1] + (SLOT_BYTES,), dtype=np.uint8)
+    out[..., K_CODE_OFF:K_CODE_OFF + 128] = pack_nibbles(kc)
+    out[..., V_CODE_OFF:V_CODE_OFF + 128] = pack_nibbles(vc)
+    out[..., K_SCALE_OFF:K_SCALE_OFF + 8] = ks
+    out[..., V_SCALE_OFF:V_SCALE_OFF + 8] = vs
+    return out
+
+
+def store(key_bits, value_bits, kv_cache: np.ndarray, slot_mapping) -> None:
+    """Write token n of (N, Hk, D) key/value into flat slot slot_mapping[n]
+    of kv_cache (num_blocks, block_size, Hk, 272); negative slots are
+    skipped."""
+    key_bits = np.asarray(key_bits)
+    value_bits = np.asarray(value_bits)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    nb, bs, hk, ss = kv_cache.shape
+    assert ss == SLOT_BYTES and key_bits.shape[1] == hk
+    flat = kv_cache.reshape(nb * bs, hk, ss)
+    keep = slots >= 0
+    if not np.any(keep):
+        return
+    flat[slots[keep]] = encode_slots(key_bits[keep], value_bits[keep])
+
+
+def decode_slots(slot_bytes: np.ndarray):
+    """Dequantised (K, V) float64 (..., 256) of slot bytes (..., 272).
+
+    K stays in the rotated basis. value = E2M1(code) * 2**(byte - 127).
+    """
+    s = np.asarray(slot_bytes, dtype=np.uint8)
+
+    def part(code_off, scale_off):
+        codes = unpack_nibbles(s[..., code_off:code_off + 128])
+        e = s[..., scale_off:scale_off + 8].astype(np.int64) - 127
+        vals = e2m1_value(codes).reshape(*codes.shape[:-1], 8, MX_BLOCK)
+        return np.ldexp(vals, e[..., None]).reshape(codes.shape)
+
+    return part(K_CODE_OFF, K_SCALE_OFF), part(V_CODE_OFF, V_SCALE_OFF)
+
+
+# --------------------------------------------------------------------------
+# Query haircut ([UQ-fly] _SegmBufPool docstring: q_rot_fp32 -> fp8_e4m3 ->
+# bf16; launcher: "Always apply the E4M3 haircut: scaled QK consumes Q as
+# E4M3"; the four-op prologue copies q to fp32, multiplies by PiT, casts to
+# float8_e4m3fn and back)
+# --------------------------------------------------------------------------
+def _e4m3_grid() -> np.ndarray:
+    """All non-negative finite OCP E4M3 (fn) values, indexed by code 0..126."""
+    vals = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+E4M3_GRID = _e4m3_grid()            # last entry is 448, the largest finite value
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP E4M3 (fn) value, ties to the even code; signed zero kept.
+
+    Magnitudes above 448 saturate to 448. The pages' cast is not specified
+    beyond the format; above 464 round-to-nearest would produce NaN in this
+    format, so saturation is this build's reading.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    idx = np.searchsorted(E4M3_GRID, a)           # first grid value >= a
+    idx = np.clip(idx, 1, len(E4M3_GRID) - 1)
+    lo, hi = E4M3_GRID[idx - 1], E4M3_GRID[idx]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (idx % 2 == 0))
+    mag = np.where(pick_hi, hi, lo)
+    mag = np.where(a >= 448.0, 448.0, mag)
+    mag = np.where(a == 0, 0.0, mag)
+    return np.copysign(mag, x)
+
+
+def query_haircut(query_bits: np.ndarray) -> np.ndarray:
+    """q8 = E4M3(q @ H) per query head, float64 values."""
+    return e4m3_round(rotate(bf16_to_f64(query_bits)))
+
+
+# --------------------------------------------------------------------------
+# Decode ([UQ-impl] _decode_attention / [UQ-fly] launcher: query (B, Hq, D),
+# kv_cache, block_table, seq_lens, scale -> output (B, Hq, D) in the query
+# dtype; query head hq reads KV head hq // (Hq // Hk))
+# --------------------------------------------------------------------------
+def gather_sequence(kv_cache: np.ndarray, block_row: np.ndarray, L: int, h: int):
+    """Dequantised (K, V) (L, 256) of KV head h for the first L tokens of a
+    sequence whose logical block j lives in physical block block_row[j]."""
+    nb, bs, hk, ss = kv_cache.shape
+    t = np.arange(L)
+    phys = np.asarray(block_row, dtype=np.int64)[t // bs]
+    return decode_slots(kv_cache[phys, t % bs, h])
+
+
+def attention(q8: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(scale * q8 K^T) V over all tokens, float64; q8 (G, 256).
+
+    The decode query is the last position and seq_lens counts it, so no mask.
+    Scores use the rotated K directly: (qH).(kH) = q.k because H is orthonormal
+    ([UQ-impl] continuation prefill: rotating both sides leaves scores
+    unchanged).
+    """
+    s = scale * (q8 @ K.T)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=-1, keepdims=True)
+    return p @ V
+
+
+def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None) -> np.ndarray:
+    """Reference output (B, Hq, 256) float64, single softmax per query head.
+
+    ``pairs`` optionally restricts the work to a list of (b, kv_head); other
+    rows are left NaN.
+    """
+    query_bits = np.asarray(query_bits)
+    B, Hq, _ = query_bits.shape
+    hk = kv_cache.shape[2]
+    qg = Hq // hk
+    out = np.full((B, Hq, D), np.nan)
+    todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(hk)]
+    for b, h in todo:
+        L = int(seq_lens[b])
+        K, V = gather_sequence(kv_cache, block_table[b], L, h)
+        q8 = query_haircut(query_bits[b, h * qg:(h + 1) * qg])
+        out[b, h * qg:(h + 1) * qg] = attention(q8, K, V, scale)
+    return out
+
+
+def partial_attention(q8, K, V, scale):
+    """One split of [TQ-v2] stage 1: normalised partial output, running max
+    and sum of exponentials (m = -inf, l = 0 for an empty range)."""
+    if K.shape[0] == 0:
+        return np.zeros((q8.shape[0], D)), np.full(q8.shape[0], -np.inf), np.zeros(q8.shape[0])
+    s = scale * (q8 @ K.T)
+    m = s.max(axis=-1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=-1)
+    return (p @ V) / l[:, None], m, l
+
+
+def merge_partials(o, m, l):
+    """[TQ-v2] stage 2 log-sum-exp merge of split partials (S, G, 256)."""
+    M = m.max(axis=0)
+    w = np.where(l > 0, l * np.exp(m - M[None, :]), 0.0)
+    return (w[..., None] * o).sum(axis=0) / w.sum(axis=0)[:, None]
+
+
+def attention_split(q8, K, V, scale, bounds) -> np.ndarray:
+    """Split-KV attention over token ranges [bounds[i], bounds[i+1])."""
+    parts = [partial_attention(q8, K[a:b], V[a:b], scale) for a, b in zip(bounds[:-1], bounds[1:])]
+    o = np.stack([p[0] for p in parts])
+    m = np.stack([p[1] for p in parts])
+    l = np.stack([p[2] for p in parts])
+    return merge_partials(o, m, l)

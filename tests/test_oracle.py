@@ -1,0 +1,323 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test checks the oracle against a closed form, a library routine, a
+hand-derived fixture (tests/golden/) or brute force, so that a dropped term,
+a wrong sign or index, or a transposed operand fails at least one of them.
+"""
+import fractions
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import golden_io
+from decode_attention_bit_amd import inputs
+from oracle import uq_oracle as O
+
+
+def bf16(x):
+    return inputs.bf16_bits(inputs.to_bf16(np.asarray(x, dtype=np.float32)))
+
+
+# ---------------------------------------------------------------- Hadamard
+def test_hadamard_closed_form_matches_scipy():
+    H = O.hadamard(256)
+    assert np.array_equal(H, scipy.linalg.hadamard(256) / 16.0)
+
+
+def test_hadamard_symmetric_orthonormal_exact():
+    H = O.hadamard(256)
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H @ H.T, np.eye(256))
+
+
+def _textbook_fwht(x):
+    """Iterative radix-2 Walsh-Hadamard butterfly, unnormalised."""
+    x = np.array(x, dtype=np.float64)
+    h = 1
+    n = x.shape[-1]
+    while h < n:
+        for i in range(0, n, 2 * h):
+            a = x[..., i:i + h].copy()
+            b = x[..., i + h:i + 2 * h].copy()
+            x[..., i:i + h] = a + b
+            x[..., i + h:i + 2 * h] = a - b
+        h *= 2
+    return x
+
+
+def test_rotation_equals_butterfly():
+    rng = np.random.default_rng(7)
+    x = O.bf16_to_f64(bf16(rng.standard_normal((64, 256))))
+    assert np.array_equal(O.rotate(x), _textbook_fwht(x) / 16.0)
+
+
+def test_rotation_invariance_of_dot_products():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((32, 256))
+    k = rng.standard_normal((32, 256))
+    H = O.hadamard(256)
+    lhs = np.einsum("nd,nd->n", q, k)
+    rhs = np.einsum("nd,nd->n", q @ H, k @ H)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_rotation_exact_against_fractions():
+    rng = np.random.default_rng(9)
+    mant = rng.uniform(0.5, 2.0, (3, 256)) * rng.choice([-1.0, 1.0], (3, 256))
+    x = O.bf16_to_f64(bf16(np.ldexp(mant, rng.integers(-14, 15, (3, 256)))))
+    y = O.rotate(x)
+    n = 256
+    for r in range(3):
+        xf = [fractions.Fraction(v) for v in x[r]]
+        for j in (0, 1, 77, 128, 255):
+            s = sum((xf[i] if bin(i & j).count("1") % 2 == 0 else -xf[i]) for i in range(n))
+            assert fractions.Fraction(y[r, j]) == s / 16
+
+
+def test_rotation_rejects_inexact_span():
+    x = np.zeros(256)
+    x[0], x[1] = 1.0, 2.0 ** -60
+    assert not O.exact_span_ok(x)
+    with pytest.raises(ValueError):
+        O.rotate(x)
+
+
+# ------------------------------------------------------- E2M1 and UE8M0
+def test_e2m1_value_table_matches_ocp_table():
+    table = golden_io.e2m1_table()
+    got = O.e2m1_value(np.arange(16))
+    for c, v in table.items():
+        assert got[c] == v and math.copysign(1, got[c]) == math.copysign(1, v)
+
+
+def test_e2m1_rounding_fixture():
+    for r, code in golden_io.e2m1_rounding():
+        assert int(O.e2m1_round(np.array([r]))[0]) == code, r
+
+
+def test_e2m1_roundtrip_every_value_every_exponent():
+    mags = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    for e in range(-127, 126):
+        blk = np.zeros(32)
+        blk[: len(mags)] = mags
+        blk[7: 7 + len(mags)] = -mags
+        blk[-1] = 4.0  # block max code 6 reproduces e
+        x = np.ldexp(blk, e)
+        codes, sb = O.quantize_blocks(np.tile(x, 8))
+        assert np.all(sb == e + 127)
+        dq = np.ldexp(O.e2m1_value(codes), e)
+        assert np.array_equal(dq, np.tile(x, 8))
+
+
+def test_mx_blocks_fixture():
+    for blk in golden_io.mx_blocks():
+        codes, sb = O.quantize_blocks(np.tile(blk["x"], 8))
+        assert np.all(sb == blk["byte"]), blk["name"]
+        assert np.array_equal(codes[:32], blk["codes"]), blk["name"]
+
+
+def test_ue8m0_decode_matches_torch():
+    b = torch.arange(0, 255, dtype=torch.uint8)
+    ref = b.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    # the oracle decodes byte -> 2**(byte - 127) inside decode_slots
+    slot = np.zeros((255, 272), dtype=np.uint8)
+    slot[:, 0] = 0x2           # element 0 = code 2 = 1.0
+    slot[:, 128] = 0x2
+    slot[:, 256] = np.arange(255)
+    slot[:, 264] = np.arange(255)
+    K, V = O.decode_slots(slot)
+    assert np.array_equal(K[:, 0], ref)
+    assert np.array_equal(V[:, 0], ref)
+
+
+def test_scale_rule_max_code():
+    """After scaling, the block maximum lands in [4, 8): code 6 or 7."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((1000, 256)) * np.exp(rng.uniform(-30, 30, (1000, 1)))
+    codes, sb = O.quantize_blocks(x)
+    amax = np.abs(x.reshape(1000, 8, 32)).max(-1)
+    r = amax / np.ldexp(1.0, sb.astype(int) - 127)
+    assert np.all((r >= 4) & (r < 8))
+    assert np.all((codes.reshape(1000, 8, 32) & 7).max(-1) >= 6)
+
+
+def test_quantisation_error_bound():
+    """|x - q(x)| <= half a step of the E2M1 grid, saturation aside."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((500, 256))
+    codes, sb = O.quantize_blocks(x)
+    e = np.repeat(sb.astype(int) - 127, 32, axis=-1)
+    dq = np.ldexp(O.e2m1_value(codes), e)
+    r = np.abs(x) / np.ldexp(1.0, e)
+    step = np.where(r < 2, 0.5, np.where(r < 4, 1.0, 2.0))
+    err = np.abs(x - dq) / np.ldexp(1.0, e)
+    inside = r <= 6
+    assert np.all(err[inside] <= step[inside] / 2 + 1e-12)
+    assert np.all((codes[~inside] & 7) == 7)
+
+
+def test_pack_order_fixture_slots():
+    for case in golden_io.slot_cases():
+        got = O.encode_slots(bf16(case["key"]), bf16(case["value"]))
+        assert np.array_equal(got, case["bytes"]), case["name"]
+
+
+# -------------------------------------------------------------- E4M3 haircut
+def test_e4m3_matches_torch_cast():
+    rng = np.random.default_rng(12)
+    x = np.concatenate([
+        rng.standard_normal(200000) * np.exp(rng.uniform(-14, 6, 200000)),
+        O.E4M3_GRID, -O.E4M3_GRID,
+        (O.E4M3_GRID[1:] + O.E4M3_GRID[:-1]) / 2,          # every midpoint
+        -(O.E4M3_GRID[1:] + O.E4M3_GRID[:-1]) / 2,
+        [0.0, -0.0, 448.0, 447.0, 464.0, -464.0],
+    ])
+    x = x[np.abs(x) <= 464]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_round(x)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_e4m3_saturates():
+    assert np.array_equal(O.e4m3_round(np.array([465.0, 1e4, -1e30])), [448.0, 448.0, -448.0])
+
+
+# ----------------------------------------------------------------- attention
+def _tiny_case(seed, L, Hk=1, qg=8, scale=1 / 16):
+    rng = np.random.default_rng(seed)
+    q = bf16(rng.standard_normal((1, Hk * qg, 256)))
+    k = bf16(rng.standard_normal((L, Hk, 256)))
+    v = bf16(rng.standard_normal((L, Hk, 256)))
+    nblk = (L + 15) // 16
+    cache = np.zeros((nblk + 3, 16, Hk, 272), dtype=np.uint8)
+    table = rng.permutation(nblk + 3)[None, :nblk].astype(np.int32)
+    t = np.arange(L)
+    O.store(k, v, cache, table[0, t // 16].astype(np.int64) * 16 + t % 16)
+    return q, k, v, cache, table, np.array([L], dtype=np.int32), scale
+
+
+def test_decode_matches_sdpa_fp64():
+    q, k, v, cache, table, lens, scale = _tiny_case(13, 77, Hk=2, qg=8)
+    out = O.decode(q, cache, table, lens, scale)
+    for h in range(2):
+        K, V = O.gather_sequence(cache, table[0], 77, h)
+        q8 = O.query_haircut(q[0, h * 8:(h + 1) * 8])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q8)[None, :, None, :],
+            torch.from_numpy(K)[None, None].expand(1, 8, 77, 256),
+            torch.from_numpy(V)[None, None].expand(1, 8, 77, 256),
+            scale=scale)[0, :, 0].numpy()
+        assert np.allclose(out[0, h * 8:(h + 1) * 8], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_brute_force_loops():
+    q, k, v, cache, table, lens, scale = _tiny_case(14, 21, Hk=1, qg=6)
+    out = O.decode(q, cache, table, lens, scale)
+    H = O.hadamard(256)
+    for g in range(6):
+        qf = O.bf16_to_f64(q[0, g])
+        q8 = O.e4m3_round(np.array([sum(qf[i] * H[i, j] for i in range(256)) for j in range(256)]))
+        # read every token's slot by hand through the block table
+        scores, vals = [], []
+        for t in range(21):
+            slot = cache[table[0, t // 16], t % 16, 0]
+            kq, vq = O.decode_slots(slot)
+            scores.append(scale * sum(q8[d] * kq[d] for d in range(256)))
+            vals.append(vq)
+        mx = max(scores)
+        w = [math.exp(s - mx) for s in scores]
+        ref = sum(wi * vi for wi, vi in zip(w, vals)) / sum(w)
+        assert np.allclose(out[0, g], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_two_token_fixture():
+    d = golden_io.decode_two_token()
+    L = d["seq_len"]
+    k = bf16(np.stack([d["key"][t] for t in range(L)])[:, None, :])
+    v = bf16(np.stack([d["value"][t] for t in range(L)])[:, None, :])
+    q = bf16(d["query"][None, None, :])
+    cache = np.zeros((1, 16, 1, 272), dtype=np.uint8)
+    O.store(k, v, cache, np.arange(L))
+    out = O.decode(q, cache, np.zeros((1, 1), np.int32), np.array([L]), d["scale"])
+    want = np.zeros(256)
+    for i, x in d["out"].items():
+        want[i] = x
+    assert np.allclose(out[0, 0], want, rtol=1e-15, atol=1e-15)
+
+
+def test_single_token_returns_dequantised_value():
+    q, k, v, cache, table, lens, scale = _tiny_case(15, 1)
+    out = O.decode(q, cache, table, lens, scale)
+    _, V = O.gather_sequence(cache, table[0], 1, 0)
+    assert np.array_equal(out[0], np.broadcast_to(V[0], out[0].shape))
+
+
+def test_zero_query_gives_mean_of_values():
+    q, k, v, cache, table, lens, scale = _tiny_case(16, 50)
+    q[:] = 0
+    out = O.decode(q, cache, table, lens, scale)
+    _, V = O.gather_sequence(cache, table[0], 50, 0)
+    assert np.allclose(out[0], V.mean(0), rtol=1e-13, atol=1e-14)
+
+
+def test_dominant_key_selects_its_value():
+    q, k, v, cache, table, lens, scale = _tiny_case(17, 40)
+    K, V = O.gather_sequence(cache, table[0], 40, 0)
+    # query = the (un-rotated) key of token 11 -> its score dominates with a big scale
+    qv = O.bf16_to_f64(k[11, 0])
+    q[0, :] = bf16(qv * 4)
+    out = O.decode(q, cache, table, lens, 8.0)
+    assert np.allclose(out[0, 0], V[11], atol=1e-6)
+
+
+def test_split_merge_equals_single_softmax():
+    q, k, v, cache, table, lens, scale = _tiny_case(18, 203)
+    K, V = O.gather_sequence(cache, table[0], 203, 0)
+    q8 = O.query_haircut(q[0])
+    ref = O.attention(q8, K, V, scale)
+    for bounds in ([0, 203], [0, 64, 128, 192, 203], [0, 0, 50, 50, 203, 203], list(range(0, 203, 16)) + [203]):
+        got = O.attention_split(q8, K, V, scale, bounds)
+        assert np.allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- the cache
+def test_store_order_and_batching_invariant():
+    rng = np.random.default_rng(19)
+    k = bf16(rng.standard_normal((40, 2, 256)))
+    v = bf16(rng.standard_normal((40, 2, 256)))
+    slots = rng.permutation(64)[:40]
+    a = np.zeros((4, 16, 2, 272), dtype=np.uint8)
+    O.store(k, v, a, slots)
+    b = np.zeros_like(a)
+    perm = rng.permutation(40)
+    for chunk in np.array_split(perm, 5):
+        O.store(k[chunk], v[chunk], b, slots[chunk])
+    assert np.array_equal(a, b)
+
+
+def test_store_leaves_other_slots_and_skips_negative():
+    rng = np.random.default_rng(20)
+    k = bf16(rng.standard_normal((10, 1, 256)))
+    v = bf16(rng.standard_normal((10, 1, 256)))
+    cache = np.full((2, 16, 1, 272), 0xA5, dtype=np.uint8)
+    slots = np.array([3, -1, 7, 8, -1, 30, 0, 1, 2, 31])
+    O.store(k, v, cache, slots)
+    flat = cache.reshape(32, 272)
+    untouched = sorted(set(range(32)) - set(slots[slots >= 0].tolist()))
+    assert np.all(flat[untouched] == 0xA5)
+    assert not np.all(flat[3] == 0xA5)
+
+
+def test_block_permutation_leaves_output_unchanged():
+    q, k, v, cache, table, lens, scale = _tiny_case(21, 90)
+    ref = O.decode(q, cache, table, lens, scale)
+    rng = np.random.default_rng(22)
+    perm = rng.permutation(cache.shape[0])        # new home of physical block p
+    moved = np.empty_like(cache)
+    moved[perm] = cache
+    got = O.decode(q, moved, perm[table].astype(np.int32), lens, scale)
+    assert np.array_equal(got, ref)
