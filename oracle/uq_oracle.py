@@ -201,7 +201,10 @@ def encode_slots(key_bits: np.ndarray, value_bits: np.ndarray) -> np.ndarray:
     [264,272) V scale bytes. K is rotated before quantisation, V is not
     ([UQ-impl] continuation prefill copies V unrotated).
     """
-    k = rotate(bf16_to_f64(key_bits))
+    # A rotated coordinate that is exactly zero has no sign of its own (its
+    # float sign would depend on the summation order); it is encoded as +0.
+    # V is copied as-is and keeps the sign of a -0 input.
+    k = rotate(bf16_to_f64(key_bits)) + 0.0
     v = bf16_to_f64(value_bits)
     kc, ks = quantize_blocks(k)
     vc, vs = quantize_blocks(v)

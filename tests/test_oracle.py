@@ -159,6 +159,20 @@ def test_quantisation_error_bound():
     assert np.all((codes[~inside] & 7) == 7)
 
 
+def test_zero_rotated_key_encodes_positive_zero():
+    k = np.zeros((2, 256))
+    k[0, 0], k[0, 1] = 1.0, 1.0          # rotated: 1/8 on even d, exactly 0 on odd d
+    k[1, :] = -0.0                        # all -0 -> every rotated coordinate is 0
+    v = np.zeros((2, 256))
+    v[1, 3] = -0.0
+    s = O.encode_slots(bf16(k), bf16(v))
+    kc = O.unpack_nibbles(s[:, :128])
+    assert np.all(kc[0, 1::2] == 0) and np.all(kc[0, 0::2] == 6)
+    assert np.all(kc[1] == 0)
+    vc = O.unpack_nibbles(s[:, 128:256])
+    assert vc[1, 3] == 8 and vc[1, 2] == 0
+
+
 def test_pack_order_fixture_slots():
     for case in golden_io.slot_cases():
         got = O.encode_slots(bf16(case["key"]), bf16(case["value"]))
