@@ -333,6 +333,11 @@ def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None) -> np
     todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(hk)]
     for b, h in todo:
         L = int(seq_lens[b])
+        if L <= 0:
+            # no key to attend to: the empty weighted sum, zero (this build's
+            # reading; the pages only decode sequences holding the new token)
+            out[b, h * qg:(h + 1) * qg] = 0.0
+            continue
         K, V = gather_sequence(kv_cache, block_table[b], L, h)
         q8 = query_haircut(query_bits[b, h * qg:(h + 1) * qg])
         out[b, h * qg:(h + 1) * qg] = attention(q8, K, V, scale)

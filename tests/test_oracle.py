@@ -288,6 +288,12 @@ def test_dominant_key_selects_its_value():
     assert np.allclose(out[0, 0], V[11], atol=1e-6)
 
 
+def test_empty_sequence_gives_zeros():
+    q, k, v, cache, table, lens, scale = _tiny_case(23, 30)
+    out = O.decode(q, cache, table, np.array([0]), scale)
+    assert np.array_equal(out, np.zeros_like(out))
+
+
 def test_split_merge_equals_single_softmax():
     q, k, v, cache, table, lens, scale = _tiny_case(18, 203)
     K, V = O.gather_sequence(cache, table[0], 203, 0)
