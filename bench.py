@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Decode throughput of the 4-bit paged-KV attention on one MI355X.
+
+Workload: B=32 sequences of 4096 tokens, Hq=32, Hk=4 (GQA-8), D=256,
+block_size 16 with a shuffled block table, 32 KV splits, bf16 q/k/v ~ N(0,1)
+(seeded, synthetic). One step = one full uq_decode (query prologue, split-KV
+stage 1, stage-2 merge) over the resident cache.
+
+Metric: cache bytes streamed per step (sum_b L_b * Hk * 272) / step time, in
+GB/s, with the fraction of the 8 TB/s HBM peak and tokens/s (B per step).
+The 142.6 MB cache would fit the 256 MB Infinity Cache, so steps rotate over
+enough stored copies of the cache that each step reads one untouched for the
+last >= 768 MB of traffic.
+
+Timing: HIP events on the stream the kernels run on. The host first queues a
+spin kernel, then all timed steps, so the GPU runs them back to back without
+waiting on Python. A second pass brackets stage 1 alone with events to give
+the dominant kernel's duration for the roofline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode KV-bytes GB/s (% of HBM peak) + decode tokens/s, B=32 GQA-8 D=256 4K ctx"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def setup(w, dev):
+    import numpy as np
+    import torch
+
+    import decode_attention_bit_amd as uq
+    from decode_attention_bit_amd import inputs
+
+    lay = inputs.make_layout(w)
+    q = inputs.make_query(w).to(dev)
+    cache = torch.zeros((lay.num_blocks, w.block_size, w.Hk, inputs.SLOT_BYTES), dtype=torch.uint8, device=dev)
+    for b in range(w.B):
+        k, v = inputs.make_kv(w, lay, b)
+        slots = inputs.slots_for(lay, b, 0, int(lay.seq_lens[b]))
+        uq.store(k.to(dev), v.to(dev), cache, torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    nbytes = cache.numel()
+    reps = max(2, math.ceil(768e6 / nbytes) + 1)
+    caches = [cache] + [cache.clone() for _ in range(reps - 1)]
+    bt = torch.from_numpy(lay.block_table).to(dev)
+    sl = torch.from_numpy(lay.seq_lens).to(dev)
+    torch.cuda.synchronize()
+    return lay, q, caches, bt, sl
+
+
+def busy():
+    """A bounded spin kernel so that the queued steps start back to back."""
+    import torch
+    torch.cuda._sleep(20_000_000)
+
+
+def gpu_time(w, lay, q, caches, bt, sl, steps, warmup):
+    import torch
+
+    import decode_attention_bit_amd as uq
+
+    dev = q.device
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(uq.decode_workspace_bytes(w.B, w.Hq, w.Hk, w.num_kv_splits), dtype=torch.uint8, device=dev)
+    R = len(caches)
+    args = lambda i: (q, caches[i % R], bt, sl, w.scale, w.num_kv_splits)
+
+    for i in range(warmup):
+        uq.decode(*args(i), out=out, workspace=ws)
+    torch.cuda.synchronize()
+
+    # pass 1: whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    busy()                                   # keep the GPU busy while the host queues the steps
+    e0.record()
+    for i in range(steps):
+        uq.decode(*args(i), out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+
+    # pass 2: stage 1 bracketed by events, prologue and merge outside
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    busy()
+    for i in range(steps):
+        a, b, c, d = ev[i]
+        a.record()
+        uq.decode(*args(i), out=out, workspace=ws, stages=uq.STAGE_PROLOGUE)
+        b.record()
+        uq.decode(*args(i), out=out, workspace=ws, stages=uq.STAGE_SPLIT)
+        c.record()
+        uq.decode(*args(i), out=out, workspace=ws, stages=uq.STAGE_MERGE)
+        d.record()
+    torch.cuda.synchronize()
+    pro = sum(x[0].elapsed_time(x[1]) for x in ev) / steps
+    st1 = sum(x[1].elapsed_time(x[2]) for x in ev) / steps
+    st2 = sum(x[2].elapsed_time(x[3]) for x in ev) / steps
+    return step_ms, pro, st1, st2
+
+
+def cpu_baseline(w, lay, seconds):
+    """The oracle, untuned, on a bounded sample: whole (sequence, KV head)
+    decodes of this workload, one BLAS thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from decode_attention_bit_amd import inputs
+    from oracle import uq_oracle as O
+
+    q_bits = inputs.bf16_bits(inputs.make_query(w))
+    rng = np.random.default_rng(0)
+    with threadpool_limits(limits=1):
+        pairs, done_bytes, elapsed = [], 0, 0.0
+        while elapsed < seconds and len(pairs) < w.B * w.Hk:
+            b, h = int(rng.integers(w.B)), int(rng.integers(w.Hk))
+            L = int(lay.seq_lens[b])
+            cache = np.zeros((lay.num_blocks, w.block_size, w.Hk, 272), dtype=np.uint8)
+            k, v = inputs.make_kv(w, lay, b)
+            O.store(inputs.bf16_bits(k), inputs.bf16_bits(v), cache, inputs.slots_for(lay, b, 0, L))
+            t = time.perf_counter()
+            O.decode(q_bits, cache, lay.block_table, lay.seq_lens, w.scale, pairs=[(b, h)])
+            elapsed += time.perf_counter() - t
+            done_bytes += L * 272
+            pairs.append((b, h))
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(pairs)} whole (sequence, KV head) decodes of this workload "
+                      f"({done_bytes / 1e6:.1f} MB of cache), {elapsed:.1f} s, cache encoding untimed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not "
+                                   "part of this build (see DESIGN.md for how the path would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from decode_attention_bit_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"setup {w.name}")
+    lay, q, caches, bt, sl = setup(w, dev)
+    kv_bytes = inputs.kv_bytes(w, lay)
+    log(f"timing {args.steps} steps ({len(caches)} cache copies)")
+    step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup)
+    gbs = kv_bytes / (step_ms * 1e-3) / 1e9
+    st1_gbs = kv_bytes / (st1_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4xe4m3-mfma+bf16-mfma",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hk={w.Hk} D={w.D} "
+                               f"seq_len={int(lay.seq_lens.max())} block_size={w.block_size} "
+                               f"num_kv_splits={w.num_kv_splits}",
+                   "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "block_size": w.block_size,
+                   "num_kv_splits": w.num_kv_splits, "kv_bytes_per_step": kv_bytes},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.B / (step_ms * 1e-3), 1),
+        "stage_ms": {"prologue": round(pro_ms, 5), "split_kv": round(st1_ms, 5), "merge": round(st2_ms, 5)},
+        "cache_copies": len(caches),
+        "roofline": {"bound": "hbm", "achieved": round(st1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(st1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "stage1_kernel (split-KV)", "bytes_per_launch": kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        res["cpu_baseline"] = cpu_baseline(w, lay, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+// C ABI of libuq: host-side argument checks, then kernel launches. Every
+// check runs before the first HIP call, so a rejected call touches no device
+// state and can be exercised without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/uq.h"
+#include "uq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return UQ_OK;
+}
+
+bool pow2_in(long v, long lo, long hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(UQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int uq_build_hadamard(int D, float* H, void* stream) {
+  if (!H) return fail(UQ_EINVAL, "uq_build_hadamard: H is null");
+  if (!pow2_in(D, 1, 256)) return fail(UQ_EINVAL, "uq_build_hadamard: D=%d is not a power of two in [1, 256]", D);
+  return hip_status(uq::launch_hadamard(D, H, (hipStream_t)stream), "uq_build_hadamard launch");
+}
+
+int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
+             const int64_t* slot_mapping, int64_t N, int Hk, int D, int64_t num_blocks,
+             int block_size, int slot_size, int64_t key_stride_n, int64_t key_stride_h,
+             int64_t val_stride_n, int64_t val_stride_h, void* stream) {
+  if (N < 0) return fail(UQ_EINVAL, "uq_store: N=%lld < 0", (long long)N);
+  if (Hk < 1) return fail(UQ_EINVAL, "uq_store: Hk=%d < 1", Hk);
+  if (num_blocks < 1) return fail(UQ_EINVAL, "uq_store: num_blocks=%lld < 1", (long long)num_blocks);
+  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_store: head_dim %d unsupported (only 256)", D);
+  if (slot_size != UQ_SLOT_BYTES) return fail(UQ_EUNSUPPORTED, "uq_store: slot_size %d unsupported (only 272)", slot_size);
+  if (!pow2_in(block_size, 16, 256))
+    return fail(UQ_EUNSUPPORTED, "uq_store: block_size %d unsupported (16, 32, 64, 128, 256)", block_size);
+  if (N == 0) return ok();
+  if (!key || !value || !kv_cache || !slot_mapping) return fail(UQ_EINVAL, "uq_store: null pointer argument");
+  if (key_stride_n < 0 || key_stride_h < 0 || val_stride_n < 0 || val_stride_h < 0 ||
+      key_stride_n % 4 || key_stride_h % 4 || val_stride_n % 4 || val_stride_h % 4)
+    return fail(UQ_EINVAL, "uq_store: strides must be non-negative multiples of 4 elements");
+  if (!aligned(key, 8) || !aligned(value, 8) || !aligned(kv_cache, 16) || !aligned(slot_mapping, 8))
+    return fail(UQ_EINVAL, "uq_store: misaligned pointer (key/value 8 B, kv_cache 16 B, slot_mapping 8 B)");
+  if ((N * Hk + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "uq_store: N*Hk too large for one launch");
+  uq::StoreArgs a{key, value, kv_cache, slot_mapping, N, Hk, num_blocks, block_size,
+                  key_stride_n, key_stride_h, val_stride_n, val_stride_h};
+  return hip_status(uq::launch_store(a, (hipStream_t)stream), "uq_store launch");
+}
+
+size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits) {
+  if (B < 1 || Hk < 1 || Hq < Hk || Hq % Hk || D != UQ_HEAD_DIM || num_kv_splits < 1 ||
+      num_kv_splits > UQ_MAX_SPLITS)
+    return 0;
+  return uq::plan_decode(B, Hq, Hk, num_kv_splits).total;
+}
+
+int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_cache,
+                     const int32_t* block_table, const int32_t* seq_lens, float scale,
+                     int num_kv_splits, uint16_t* out, int B, int Hq, int Hk, int D,
+                     int64_t num_blocks, int block_size, int max_blocks_per_seq,
+                     int64_t q_stride_b, int64_t q_stride_h, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (stage_mask <= 0 || (stage_mask & ~7))
+    return fail(UQ_EINVAL, "uq_decode: stage_mask %d is not a non-empty subset of 1|2|4", stage_mask);
+  if (B < 1 || Hq < 1 || Hk < 1) return fail(UQ_EINVAL, "uq_decode: B=%d Hq=%d Hk=%d must be >= 1", B, Hq, Hk);
+  if (num_blocks < 1 || max_blocks_per_seq < 1)
+    return fail(UQ_EINVAL, "uq_decode: num_blocks and max_blocks_per_seq must be >= 1");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(UQ_EINVAL, "uq_decode: scale must be finite and > 0");
+  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_decode: head_dim %d unsupported (only 256)", D);
+  if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "uq_decode: Hq=%d is not a multiple of Hk=%d", Hq, Hk);
+  const int qg = Hq / Hk;
+  if (qg != 6 && qg != 8 && qg != 16)
+    return fail(UQ_EUNSUPPORTED, "uq_decode: GQA group %d unsupported (6, 8, 16)", qg);
+  if (!pow2_in(block_size, 16, 256))
+    return fail(UQ_EUNSUPPORTED, "uq_decode: block_size %d unsupported (16, 32, 64, 128, 256)", block_size);
+  if (num_kv_splits < 1 || num_kv_splits > UQ_MAX_SPLITS)
+    return fail(UQ_EUNSUPPORTED, "uq_decode: num_kv_splits %d outside [1, %d]", num_kv_splits, UQ_MAX_SPLITS);
+  if ((long long)max_blocks_per_seq * block_size > 0x7FFFFFFFLL)
+    return fail(UQ_EUNSUPPORTED, "uq_decode: max_blocks_per_seq * block_size exceeds 2^31");
+  if (!query || !kv_cache || !block_table || !seq_lens || !out || !workspace)
+    return fail(UQ_EINVAL, "uq_decode: null pointer argument");
+  if (q_stride_b < 0 || q_stride_h < 0 || q_stride_b % 4 || q_stride_h % 4)
+    return fail(UQ_EINVAL, "uq_decode: query strides must be non-negative multiples of 4 elements");
+  if (!aligned(query, 8) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return fail(UQ_EINVAL, "uq_decode: misaligned pointer (query 8 B, kv_cache/out 16 B, workspace 256 B)");
+  const uq::DecodePlan plan = uq::plan_decode(B, Hq, Hk, num_kv_splits);
+  if (workspace_bytes < plan.total)
+    return fail(UQ_EWORKSPACE, "uq_decode: workspace %zu bytes < required %zu", workspace_bytes, plan.total);
+  if ((long long)B * num_kv_splits * plan.nsub * Hk > 0x7FFFFFFFLL)
+    return fail(UQ_EUNSUPPORTED, "uq_decode: grid too large");
+  uq::DecodeArgs a{query, kv_cache, block_table, seq_lens, scale, out, num_blocks, block_size,
+                   max_blocks_per_seq, q_stride_b, q_stride_h,
+                   reinterpret_cast<uint8_t*>(workspace)};
+  return hip_status(uq::launch_decode(a, plan, stage_mask, (hipStream_t)stream),
+                    "uq_decode launch");
+}
+
+int uq_decode(const uint16_t* query, const uint8_t* kv_cache, const int32_t* block_table,
+              const int32_t* seq_lens, float scale, int num_kv_splits, uint16_t* out, int B,
+              int Hq, int Hk, int D, int64_t num_blocks, int block_size, int max_blocks_per_seq,
+              int64_t q_stride_b, int64_t q_stride_h, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  return uq_decode_stages(UQ_STAGE_PROLOGUE | UQ_STAGE_SPLIT | UQ_STAGE_MERGE, query, kv_cache,
+                          block_table, seq_lens, scale, num_kv_splits, out, B, Hq, Hk, D,
+                          num_blocks, block_size, max_blocks_per_seq, q_stride_b, q_stride_h,
+                          workspace, workspace_bytes, stream);
+}
+
+const char* uq_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

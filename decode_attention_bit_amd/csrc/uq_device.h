@@ -1,0 +1,94 @@
+// Device helpers shared by the store and decode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uq {
+
+constexpr int kHeadDim = 256;
+constexpr int kSlotBytes = 272;
+constexpr int kKCodeOff = 0, kVCodeOff = 128, kKScaleOff = 256, kVScaleOff = 264;
+constexpr int kTile = 16;        // tokens per decode tile
+
+typedef int   v8i  __attribute__((ext_vector_type(8)));
+typedef float v4f  __attribute__((ext_vector_type(4)));
+typedef short v4s  __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double bf16_to_f64(uint32_t h16) {
+  return (double)__uint_as_float(h16 << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// 2**k as a double for |k| <= 1022, built from its exponent field.
+__device__ __forceinline__ double pow2(int k) {
+  return __longlong_as_double((long long)(k + 1023) << 52);
+}
+
+// floor(log2(a)) of a normal, positive double, read from the exponent field.
+__device__ __forceinline__ int floor_log2(double a) {
+  return (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;
+}
+
+// 256-point Walsh-Hadamard butterfly (unnormalised) over one wave: lane l
+// holds x[4l .. 4l+3] in v[0..3]. Index bits 0-1 live inside a lane, bits 2-7
+// are lane bits 0-5. Each stage maps (a, b) -> (a + b, a - b). In float64 the
+// result is exact whenever every +-sum of the inputs fits 53 bits, which
+// holds for bf16 inputs whose non-zero magnitudes span at most 36 binades.
+__device__ __forceinline__ void fwht256_wave(double v[4], int lane) {
+  const double a0 = v[0] + v[1], a1 = v[0] - v[1];
+  const double a2 = v[2] + v[3], a3 = v[2] - v[3];
+  v[0] = a0 + a2; v[1] = a1 + a3; v[2] = a0 - a2; v[3] = a1 - a3;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double o = __shfl_xor(v[i], m);
+      v[i] = upper ? (o - v[i]) : (v[i] + o);
+    }
+  }
+}
+
+// UE8M0 block exponent: clamp(floor(log2 amax) - 2, -127, 127); -127 for an
+// all-zero block (2 is the exponent of E2M1's largest magnitude, 6 = 1.5*2^2).
+__device__ __forceinline__ int mx_block_exponent(double amax) {
+  if (!(amax > 0.0)) return -127;
+  int e = floor_log2(amax) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 4-bit E2M1 code of x under block exponent e: magnitude |x| * 2**-e rounded
+// to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,
+// saturating at 6; bit 3 carries the sign of x.
+__device__ __forceinline__ uint32_t e2m1_code(double x, double inv_scale) {
+  const double r = fabs(x) * inv_scale;
+  uint32_t c = (uint32_t)(r > 0.25) + (uint32_t)(r >= 0.75) + (uint32_t)(r > 1.25) +
+               (uint32_t)(r >= 1.75) + (uint32_t)(r > 2.5) + (uint32_t)(r >= 3.5) +
+               (uint32_t)(r > 5.0);
+  return c | (signbit(x) ? 8u : 0u);
+}
+
+// OCP FP8 E4M3 (fn) code of x, round to nearest even, magnitudes above 448
+// saturate to 448. Exact: every step is a power-of-two scaling and one
+// rint() of a value below 2**5.
+__device__ __forceinline__ uint32_t e4m3_code(double x) {
+  const double a = fabs(x);
+  uint32_t c;
+  if (a >= 448.0) {
+    c = 0x7E;
+  } else if (a < 0.015625) {                       // below 2**-6: grid k * 2**-9
+    c = (uint32_t)rint(a * 512.0);                 // k = 8 is the first normal, code 8
+  } else {
+    const int E = floor_log2(a);                   // -6 .. 8
+    const uint32_t m = (uint32_t)rint(a * pow2(3 - E));   // 8 .. 16
+    c = ((uint32_t)(E + 7) << 3) + (m - 8);        // m = 16 carries into the exponent
+    if (c > 0x7E) c = 0x7E;
+  }
+  return c | (signbit(x) ? 0x80u : 0u);
+}
+
+}  // namespace uq

@@ -13,9 +13,11 @@ Recipe (every workload):
     random), the permutation of physical blocks, then outlier channels
     (ragged only).
   * ``default_rng([seed, 1])`` draws the query ``(B, Hq, D)``.
-  * ``default_rng([seed, 2, b])`` draws the keys of sequence ``b`` and
-    ``default_rng([seed, 3, b])`` its values, each ``(L_b, Hk, D)``; one
-    stream per sequence lets a single sequence be regenerated on its own.
+  * Keys of sequence ``b``, tokens ``[4096 c, 4096 (c + 1))``, come from
+    ``default_rng([seed, 2, b, c])`` and values from
+    ``default_rng([seed, 3, b, c])``, each ``(n, Hk, D)``: one stream per
+    4096-token chunk lets any part of a sequence be regenerated on its own,
+    and lets chunks be drawn in parallel threads.
   * Normal draws are float32, then rounded to bf16 by torch's CPU cast
     (round to nearest even). Student-t draws are float64, cast to float32
     first.
@@ -27,6 +29,7 @@ Recipe (every workload):
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -144,16 +147,21 @@ def make_query(w: Workload) -> torch.Tensor:
     return to_bf16(rng.standard_normal((w.B, w.Hq, w.D), dtype=np.float32))
 
 
-def make_kv(w: Workload, layout: Layout, b: int, n_tokens: int | None = None):
-    """Keys and values of sequence ``b``: two (n, Hk, D) bf16 CPU tensors.
+KV_CHUNK = 4096
+_POOL = None
 
-    ``n_tokens`` defaults to ``seq_lens[b]``; a shorter count returns the
-    leading tokens of the same draw.
-    """
-    L = int(layout.seq_lens[b])
-    n = L if n_tokens is None else int(n_tokens)
-    shape = (L, w.Hk, w.D)
-    rk = np.random.default_rng([w.seed, 2, b])
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
+
+
+def _kv_chunk(w: Workload, layout: Layout, b: int, c: int, n: int):
+    shape = (n, w.Hk, w.D)
+    rk = np.random.default_rng([w.seed, 2, b, c])
     if w.k_kind == "student_t":
         k = rk.standard_t(w.extra["student_t_dof"], size=shape).astype(np.float32)
     else:
@@ -162,9 +170,44 @@ def make_kv(w: Workload, layout: Layout, b: int, n_tokens: int | None = None):
             gain = np.float32(w.extra["outlier_gain"])
             for h in range(w.Hk):
                 k[:, h, layout.outlier_idx[h]] *= gain
-    rv = np.random.default_rng([w.seed, 3, b])
+    rv = np.random.default_rng([w.seed, 3, b, c])
     v = rv.standard_normal(shape, dtype=np.float32)
-    return to_bf16(k[:n]), to_bf16(v[:n])
+    return k, v
+
+
+def make_kv(w: Workload, layout: Layout, b: int, t0: int = 0, t1: int | None = None):
+    """Keys and values of tokens [t0, t1) of sequence b: two (n, Hk, D) bf16
+    CPU tensors (t1 defaults to seq_lens[b])."""
+    L = int(layout.seq_lens[b])
+    t1 = L if t1 is None else int(t1)
+    assert 0 <= t0 <= t1 <= L
+    k_out = torch.empty((t1 - t0, w.Hk, w.D), dtype=torch.bfloat16)
+    v_out = torch.empty((t1 - t0, w.Hk, w.D), dtype=torch.bfloat16)
+
+    def fill(c):
+        lo = c * KV_CHUNK
+        k, v = _kv_chunk(w, layout, b, c, min(KV_CHUNK, L - lo))
+        a, e = max(t0, lo), min(t1, lo + KV_CHUNK)
+        k_out[a - t0:e - t0].copy_(torch.from_numpy(k[a - lo:e - lo]))
+        v_out[a - t0:e - t0].copy_(torch.from_numpy(v[a - lo:e - lo]))
+
+    list(_pool().map(fill, range(t0 // KV_CHUNK, (t1 + KV_CHUNK - 1) // KV_CHUNK)))
+    return k_out, v_out
+
+
+def make_kv_tokens(w: Workload, layout: Layout, b: int, tokens: np.ndarray):
+    """Keys and values of an arbitrary sorted token subset of sequence b,
+    generating only the chunks that hold them."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    L = int(layout.seq_lens[b])
+    cs = np.unique(tokens // KV_CHUNK)
+    parts = dict(zip(cs.tolist(), _pool().map(
+        lambda c: _kv_chunk(w, layout, b, c, min(KV_CHUNK, L - c * KV_CHUNK)), cs.tolist())))
+    k = np.stack([parts[t // KV_CHUNK][0][t % KV_CHUNK] for t in tokens.tolist()]) if len(tokens) else \
+        np.zeros((0, w.Hk, w.D), np.float32)
+    v = np.stack([parts[t // KV_CHUNK][1][t % KV_CHUNK] for t in tokens.tolist()]) if len(tokens) else \
+        np.zeros((0, w.Hk, w.D), np.float32)
+    return to_bf16(k), to_bf16(v)
 
 
 def slots_for(layout: Layout, b: int, t0: int, t1: int, block_size: int = BLOCK_SIZE) -> np.ndarray:

@@ -1,0 +1,169 @@
+/*
+ * uq.h - C ABI of libuq: UltraQuant-style 4-bit paged-KV decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method (vLLM API docs, "vllm/v1/attention/backends/ultraquant_attn",
+ * UltraQuantAttentionImpl, and "vllm/v1/attention/ops/flydsl_ultraquant_decode"):
+ * keys are rotated by the orthonormal, symmetric 256-point Hadamard matrix and
+ * stored, with the values, as FP4 E2M1 codes with one UE8M0 power-of-two scale
+ * per 32 elements in a block-table-indexed (paged) cache. Decode rotates the
+ * query by the same matrix, rounds it to FP8 E4M3 (the "haircut"), and runs
+ * split-KV attention: stage 1 writes a partial output, running max and sum of
+ * exponentials per split; stage 2 merges the splits by log-sum-exp.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are device memory on the current HIP device;
+ *     the caller owns every buffer. The library allocates nothing, keeps no
+ *     device state between calls and never synchronises the stream.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Results are visible once the stream has been synchronised.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Return value: UQ_OK (0) or a negative UQ_E* code. All argument checks
+ *     run on the host before any HIP call, so a rejected call enqueues
+ *     nothing; uq_last_error() returns a message for the calling thread.
+ *
+ * Cache slot (one token, one KV head), 272 bytes:
+ *   [0,128)   K codes: byte i holds element 2i in bits 0-3, 2i+1 in bits 4-7;
+ *             K is in the rotated basis
+ *   [128,256) V codes, same packing, not rotated
+ *   [256,264) K scale bytes, one per 32 consecutive elements (UE8M0: 2**(b-127))
+ *   [264,272) V scale bytes
+ *   A 4-bit code is sign (bit 3) plus E2M1 magnitude {0,.5,1,1.5,2,3,4,6}.
+ *   The scale byte of a block with maximum magnitude a is
+ *   clamp(floor(log2 a) - 2, -127, 127) + 127 (0 for an all-zero block), the
+ *   OCP MX shared-exponent rule; codes are rounded to nearest, ties to even,
+ *   saturating at 6.
+ * The cache is (num_blocks, block_size, Hk, 272) bytes, contiguous: slot s of
+ * KV head h starts at byte (s * Hk + h) * 272.
+ */
+#ifndef UQ_H
+#define UQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define UQ_OK            0
+#define UQ_EINVAL       -1   /* null pointer, non-positive size, bad stride */
+#define UQ_EUNSUPPORTED -2   /* a shape or option the kernels do not cover  */
+#define UQ_EWORKSPACE   -3   /* workspace smaller than uq_decode_workspace_bytes() */
+#define UQ_EHIP         -4   /* a HIP launch failed                          */
+
+#define UQ_HEAD_DIM   256
+#define UQ_SLOT_BYTES 272
+#define UQ_MAX_SPLITS 512
+
+/*
+ * Build the normalised Sylvester Hadamard matrix
+ * H[i][j] = (-1)**popcount(i & j) / sqrt(D) as D x D float32, row-major.
+ * Follows _ensure_on_device on the UltraQuantAttentionImpl page: one matrix
+ * serves as both Pi and PiT because it is orthonormal and symmetric.
+ *   D: power of two, 1 <= D <= 256.
+ *   H: (device) D*D floats, written.
+ * Errors: UQ_EINVAL for a null H or D not a power of two in range.
+ */
+int uq_build_hadamard(int D, float* H, void* stream);
+
+/*
+ * Store N tokens: rotate each key vector by H (exactly, in float64), quantise
+ * keys and values to FP4 E2M1 + UE8M0 per 32 elements, and write slot
+ * slot_mapping[n] of every KV head. Follows _store_kv on the
+ * UltraQuantAttentionImpl page (key, value (N, Hk, D); kv_cache
+ * (num_blocks, block_size, Hk, slot_size); slot_mapping).
+ *   key, value:   (device) bf16, element (n, h, d) at n*stride_n + h*stride_h + d
+ *                 (strides in elements; d is contiguous).
+ *   kv_cache:     (device) uint8, (num_blocks, block_size, Hk, 272), in/out;
+ *                 only the written slots change.
+ *   slot_mapping: (device) int64, (N,). A slot outside
+ *                 [0, num_blocks * block_size) - for instance -1 for padding -
+ *                 is skipped.
+ *   D must be 256, slot_size 272, block_size a power of two in [16, 256].
+ *   N == 0 is a no-op.
+ * Exactness: the rotation is exact when the non-zero magnitudes of a key
+ * vector span at most 36 binades (always true for bf16 data of ordinary
+ * range); the cache bytes are then a function of the inputs alone.
+ * Errors: UQ_EINVAL, UQ_EUNSUPPORTED, UQ_EHIP.
+ */
+int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
+             const int64_t* slot_mapping, int64_t N, int Hk, int D,
+             int64_t num_blocks, int block_size, int slot_size,
+             int64_t key_stride_n, int64_t key_stride_h,
+             int64_t val_stride_n, int64_t val_stride_h, void* stream);
+
+/*
+ * Bytes of device workspace uq_decode needs for this shape (0 on invalid
+ * arguments). The analogue of the pooled segm_out / segm_max / segm_sum and
+ * q_fp8 buffers of _SegmBufPool on the flydsl_ultraquant_decode page: query
+ * E4M3 codes, one bf16 partial output and two float32 statistics per
+ * (sequence, query head, partial).
+ */
+size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits);
+
+/*
+ * Decode one query token per sequence against the paged 4-bit cache and
+ * write out = softmax(scale * q8 . K^T) V per query head, where
+ * q8 = E4M3(q H) and query head hq reads KV head hq / (Hq / Hk). Follows
+ * flydsl_ultraquant_decode_attention on the flydsl_ultraquant_decode page
+ * (query, kv_cache, block_table, seq_lens, scale, max_num_kv_splits ->
+ * output (B, Hq, D) in the query dtype) and the split-KV stage 1 / stage 2
+ * structure of triton_turboquant_decode_attention_v2. Enqueues three kernels
+ * (query prologue, split-KV stage 1, log-sum-exp merge) on `stream`; no host
+ * synchronisation and no allocation, so it can be captured in a HIP graph.
+ *   query:       (device) bf16, element (b, hq, d) at b*q_stride_b + hq*q_stride_h + d.
+ *   kv_cache:    (device) uint8 (num_blocks, block_size, Hk, 272), read only.
+ *   block_table: (device) int32 (B, max_blocks_per_seq): logical block j of
+ *                sequence b lives in physical block block_table[b][j].
+ *   seq_lens:    (device) int32 (B,): tokens of each sequence, the current one
+ *                included. Values are clamped to [0, max_blocks_per_seq*block_size];
+ *                a sequence of length 0 yields zeros. Physical block ids outside
+ *                [0, num_blocks) are read as empty blocks.
+ *   scale:       softmax scale applied to q8 . k (finite, > 0).
+ *   num_kv_splits: number of key ranges per sequence, 1..512. Each split
+ *                covers a contiguous run of 16-token tiles; the result does
+ *                not depend on the count beyond rounding.
+ *   out:         (device) bf16 (B, Hq, D) contiguous, written.
+ *   workspace:   (device) at least uq_decode_workspace_bytes(B, Hq, Hk, D,
+ *                num_kv_splits) bytes, 256-byte aligned; contents need no
+ *                initialisation and are overwritten.
+ *   D must be 256; Hq % Hk == 0 with Hq / Hk in {6, 8, 16}; block_size a
+ *   power of two in [16, 256].
+ * Errors: UQ_EINVAL, UQ_EUNSUPPORTED, UQ_EWORKSPACE, UQ_EHIP.
+ */
+int uq_decode(const uint16_t* query, const uint8_t* kv_cache,
+              const int32_t* block_table, const int32_t* seq_lens, float scale,
+              int num_kv_splits, uint16_t* out, int B, int Hq, int Hk, int D,
+              int64_t num_blocks, int block_size, int max_blocks_per_seq,
+              int64_t q_stride_b, int64_t q_stride_h, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * Same as uq_decode, restricted to the stages named in stage_mask:
+ * UQ_STAGE_PROLOGUE (query rotation + E4M3 into the workspace),
+ * UQ_STAGE_SPLIT (stage 1, reads the prologue's output) and UQ_STAGE_MERGE
+ * (stage 2, reads stage 1's output). Running the three masks in that order on
+ * one stream, with the same arguments and workspace, is exactly uq_decode;
+ * it exists so a caller can time or capture each kernel on its own.
+ * Errors: as uq_decode, plus UQ_EINVAL for an empty or unknown mask.
+ */
+#define UQ_STAGE_PROLOGUE 1
+#define UQ_STAGE_SPLIT    2
+#define UQ_STAGE_MERGE    4
+int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_cache,
+                     const int32_t* block_table, const int32_t* seq_lens, float scale,
+                     int num_kv_splits, uint16_t* out, int B, int Hq, int Hk, int D,
+                     int64_t num_blocks, int block_size, int max_blocks_per_seq,
+                     int64_t q_stride_b, int64_t q_stride_h, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Message describing the last non-zero return on the calling thread
+ * ("" if none). The pointer stays valid until the thread's next call. */
+const char* uq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UQ_H */

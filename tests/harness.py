@@ -1,0 +1,114 @@
+"""Helpers shared by the GPU tests: build a workload's cache on the device
+with the library, and compute the oracle's answer for chosen parts of it.
+
+The oracle only ever sees the seeded inputs (never bytes produced on the
+GPU): expected cache bytes and expected outputs are re-derived on the CPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import decode_attention_bit_amd as uq
+from decode_attention_bit_amd import inputs
+from oracle import uq_oracle as O
+
+MAX_ABS = 1e-2        # attention output tolerance: max |gpu - oracle|
+REL_L2 = 5e-3         # and ||gpu - oracle||_2 / ||oracle||_2
+
+
+class Instance:
+    """One workload realised on the GPU: cache stored by uq_store."""
+
+    def __init__(self, w: inputs.Workload, dev="cuda", seq_lens=None):
+        self.w = w
+        self.dev = torch.device(dev)
+        self.layout = inputs.make_layout(w, seq_lens=seq_lens)
+        self.query = inputs.make_query(w)
+        lay = self.layout
+        self.cache = torch.zeros((lay.num_blocks, w.block_size, w.Hk, inputs.SLOT_BYTES),
+                                 dtype=torch.uint8, device=self.dev)
+        self.block_table = torch.from_numpy(lay.block_table).to(self.dev)
+        self.seq_lens = torch.from_numpy(lay.seq_lens).to(self.dev)
+        self.q_dev = self.query.to(self.dev)
+        last = []
+        for b in range(w.B):
+            L = int(lay.seq_lens[b])
+            k, v = inputs.make_kv(w, lay, b)
+            n_pre = L - 1 if w.name == "mixed" else L   # mixed: last token stored in the step
+            if n_pre > 0:
+                slots = inputs.slots_for(lay, b, 0, n_pre)
+                uq.store(k[:n_pre].to(self.dev), v[:n_pre].to(self.dev), self.cache,
+                         torch.from_numpy(slots).to(self.dev))
+            if w.name == "mixed":
+                last.append((k[L - 1:L], v[L - 1:L], inputs.slots_for(lay, b, L - 1, L)))
+        if last:
+            self.step_k = torch.cat([x[0] for x in last]).to(self.dev)
+            self.step_v = torch.cat([x[1] for x in last]).to(self.dev)
+            self.step_slots = torch.from_numpy(np.concatenate([x[2] for x in last])).to(self.dev)
+        torch.cuda.synchronize()
+
+    def store_step(self):
+        uq.store(self.step_k, self.step_v, self.cache, self.step_slots)
+
+    def decode(self, splits=None, **kw):
+        return uq.decode(self.q_dev, self.cache, self.block_table, self.seq_lens, self.w.scale,
+                         splits or self.w.num_kv_splits, **kw)
+
+    # ----------------------------------------------------------- oracle side
+    def oracle_slots(self, b: int, tokens: np.ndarray) -> np.ndarray:
+        """Oracle slot bytes (n, Hk, 272) of the given tokens of sequence b."""
+        k, v = inputs.make_kv_tokens(self.w, self.layout, b, tokens)
+        kb, vb = inputs.bf16_bits(k), inputs.bf16_bits(v)
+        out = []
+        for i in range(0, len(tokens), 4096):
+            out.append(O.encode_slots(kb[i:i + 4096], vb[i:i + 4096]))
+        return np.concatenate(out) if out else np.zeros((0, self.w.Hk, 272), np.uint8)
+
+    def gpu_slots(self, b: int, tokens: np.ndarray) -> np.ndarray:
+        slots = inputs.slots_for(self.layout, b, 0, int(self.layout.seq_lens[b]))[tokens]
+        flat = self.cache.view(-1, self.w.Hk, inputs.SLOT_BYTES)
+        return flat[torch.from_numpy(slots).to(self.dev)].cpu().numpy()
+
+    def oracle_output(self, b: int, h: int) -> np.ndarray:
+        """Oracle output rows (QG, 256) of KV head h of sequence b, from the
+        oracle's own encoding of that sequence."""
+        L = int(self.layout.seq_lens[b])
+
+        def enc(i):
+            k, v = inputs.make_kv(self.w, self.layout, b, i, min(i + 8192, L))
+            return O.decode_slots(O.encode_slots(inputs.bf16_bits(k)[:, h], inputs.bf16_bits(v)[:, h]))
+
+        parts = list(inputs._pool().map(enc, range(0, L, 8192)))
+        K = np.concatenate([p[0] for p in parts])
+        V = np.concatenate([p[1] for p in parts])
+        qg = self.w.QG
+        q8 = O.query_haircut(inputs.bf16_bits(self.query)[b, h * qg:(h + 1) * qg])
+        return O.attention(q8, K, V, self.w.scale)
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 unit in the last place at |x|: the rounding error any bf16
+    output of the exact value may carry."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(int) - 8)
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, what: str, allow_output_rounding=False):
+    """max-abs <= 1e-2 and rel-L2 <= 5e-3 against the float64 oracle.
+
+    allow_output_rounding adds half a bf16 ulp of the reference to the
+    max-abs bound, for inputs (not the workloads) whose outputs are so large
+    that rounding the exact answer to bf16 alone exceeds 1e-2 (|o| >= 4)."""
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    diff = np.abs(got - ref)
+    bound = MAX_ABS + (bf16_half_ulp(ref) if allow_output_rounding else 0.0)
+    err = float(diff.max())
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    assert np.all(diff <= bound) and rel <= REL_L2, f"{what}: max-abs {err:.3e} rel-L2 {rel:.3e}"
+    return err, rel
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)

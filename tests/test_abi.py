@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uq_\w+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("uq_build_hadamard", "uq_store", "uq_decode", "uq_decode_stages",
+              "uq_decode_workspace_bytes", "uq_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(libuq):
+    for name in declared_functions():
+        assert hasattr(libuq, name), name
+
+
+def test_library_has_gfx950_code_object():
+    import decode_attention_bit_amd as uq
+    blob = open(uq.library_path(), "rb").read()
+    assert b"gfx950" in blob
+
+
+def _err(lib):
+    return lib.uq_last_error().decode()
+
+
+def test_build_hadamard_rejects(libuq):
+    assert libuq.uq_build_hadamard(256, None, None) == -1
+    assert "null" in _err(libuq)
+    buf = ctypes.c_void_p(0x1000)   # never dereferenced: the size check fails first
+    assert libuq.uq_build_hadamard(0, buf, None) == -1
+    assert libuq.uq_build_hadamard(384, buf, None) == -1
+    assert libuq.uq_build_hadamard(512, buf, None) == -1
+
+
+FAKE = 0x10000   # 256-byte aligned host address used only for argument checks
+
+
+def store_args(**kw):
+    a = dict(key=FAKE, value=FAKE, kv_cache=FAKE, slot_mapping=FAKE, N=4, Hk=2, D=256,
+             num_blocks=8, block_size=16, slot_size=272, ksn=512, ksh=256, vsn=512, vsh=256,
+             stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=128), -2), (dict(slot_size=256), -2), (dict(block_size=8), -2),
+    (dict(block_size=48), -2), (dict(block_size=512), -2), (dict(N=-1), -1), (dict(Hk=0), -1),
+    (dict(num_blocks=0), -1), (dict(key=None), -1), (dict(slot_mapping=None), -1),
+    (dict(ksh=255), -1), (dict(vsn=-4), -1), (dict(key=FAKE + 2), -1),
+])
+def test_store_rejects(libuq, kw, code):
+    assert libuq.uq_store(*store_args(**kw)) == code
+    assert _err(libuq)
+
+
+def test_store_empty_is_noop(libuq):
+    assert libuq.uq_store(*store_args(N=0, key=None, value=None, slot_mapping=None)) == 0
+    assert _err(libuq) == ""
+
+
+def decode_args(**kw):
+    a = dict(query=FAKE, kv_cache=FAKE, block_table=FAKE, seq_lens=FAKE, scale=0.0625,
+             splits=32, out=FAKE, B=4, Hq=32, Hk=4, D=256, num_blocks=64, block_size=16,
+             max_blocks=16, qsb=8192, qsh=256, workspace=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=128), -2), (dict(Hq=36), -2), (dict(Hq=16), -2), (dict(Hq=12, Hk=4), -2),
+    (dict(Hq=128, Hk=4), -2), (dict(block_size=8), -2), (dict(splits=0), -2),
+    (dict(splits=513), -2), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
+    (dict(scale=float("inf")), -1), (dict(B=0), -1), (dict(query=None), -1),
+    (dict(workspace=None), -1), (dict(out=FAKE + 8), -1), (dict(workspace=FAKE + 16), -1),
+    (dict(qsh=130), -1), (dict(ws_bytes=1024), -3), (dict(num_blocks=0), -1),
+])
+def test_decode_rejects(libuq, kw, code):
+    assert libuq.uq_decode(*decode_args(**kw)) == code
+    assert _err(libuq)
+
+
+@pytest.mark.parametrize("mask", [0, 8, -1, 15])
+def test_decode_stages_rejects_mask(libuq, mask):
+    assert libuq.uq_decode_stages(mask, *decode_args()) == -1
+
+
+def test_workspace_bytes(libuq):
+    f = libuq.uq_decode_workspace_bytes
+    assert f(0, 32, 4, 256, 32) == 0
+    assert f(32, 30, 4, 256, 32) == 0
+    assert f(32, 32, 4, 128, 32) == 0
+    assert f(32, 32, 4, 256, 0) == 0
+    n = f(32, 32, 4, 256, 32)
+    # at least: E4M3 query codes, one bf16 partial row and two floats per partial
+    assert n >= 32 * 32 * 256 + 32 * 32 * 32 * (256 * 2 + 8)
+    assert n % 256 == 0
+    assert f(64, 32, 4, 256, 32) >= n

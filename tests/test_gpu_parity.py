@@ -1,0 +1,296 @@
+"""GPU parity of the HIP library against the CPU oracle, at sizes the oracle
+finishes in seconds: cache bytes bit-exact, attention output within
+max-abs 1e-2 / rel-L2 5e-3. Everything goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import golden_io
+import harness
+from harness import check_close, to_np
+import decode_attention_bit_amd as uq
+from decode_attention_bit_amd import inputs
+from oracle import uq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def bf16(x):
+    return inputs.to_bf16(np.asarray(x, dtype=np.float32))
+
+
+def bits(t):
+    return inputs.bf16_bits(t.cpu())
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ Hadamard
+@pytest.mark.parametrize("D", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_build_hadamard(D):
+    say(f"hadamard D={D}")
+    H = uq.build_hadamard(D, DEV).cpu().numpy()
+    assert np.array_equal(H, O.hadamard(D).astype(np.float32))
+
+
+# --------------------------------------------------------------------- store
+def _store_and_compare(k, v, nb=4, bs=16, slots=None, fill=0):
+    N, Hk, _ = k.shape
+    if slots is None:
+        slots = np.random.default_rng(0).permutation(nb * bs)[:N]
+    cache = torch.full((nb, bs, Hk, 272), fill, dtype=torch.uint8, device=DEV)
+    uq.store(k.to(DEV), v.to(DEV), cache, torch.from_numpy(np.asarray(slots, np.int64)).to(DEV))
+    ref = np.full((nb, bs, Hk, 272), fill, dtype=np.uint8)
+    O.store(bits(k), bits(v), ref, slots)
+    got = cache.cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:4].tolist()}"
+
+
+def test_store_tiny_workload_bit_exact():
+    say("store tiny")
+    w = inputs.WORKLOADS["tiny"]
+    inst = harness.Instance(w, DEV)
+    ref = np.zeros(tuple(inst.cache.shape), dtype=np.uint8)
+    for b in range(w.B):
+        k, v = inputs.make_kv(w, inst.layout, b)
+        O.store(bits(k), bits(v), ref, inputs.slots_for(inst.layout, b, 0, int(inst.layout.seq_lens[b])))
+    assert np.array_equal(inst.cache.cpu().numpy(), ref)
+
+
+def test_store_golden_slots():
+    say("store golden")
+    for case in golden_io.slot_cases():
+        k = bf16(case["key"][None, None, :])
+        v = bf16(case["value"][None, None, :])
+        cache = torch.zeros((1, 16, 1, 272), dtype=torch.uint8, device=DEV)
+        uq.store(k.to(DEV), v.to(DEV), cache, torch.tensor([5], dtype=torch.int64, device=DEV))
+        assert np.array_equal(cache[0, 5, 0].cpu().numpy(), case["bytes"]), case["name"]
+
+
+def test_store_golden_blocks_as_values():
+    """Tie and saturation cases of the E2M1 rounding, through the V path."""
+    say("store golden blocks")
+    blocks = golden_io.mx_blocks()
+    v = np.zeros((len(blocks), 1, 256))
+    for i, blk in enumerate(blocks):
+        v[i, 0] = np.tile(blk["x"], 8)
+    vt = bf16(v)
+    assert np.array_equal(inputs.bf16_bits(vt).astype(np.float64), inputs.bf16_bits(vt))  # sanity
+    _store_and_compare(bf16(np.zeros_like(v)), vt, nb=1, bs=16, slots=np.arange(len(blocks)))
+
+
+def test_store_edge_values():
+    say("store edge values")
+    rng = np.random.default_rng(1)
+    n = 48
+    k = rng.standard_normal((n, 2, 256))
+    v = rng.standard_normal((n, 2, 256))
+    k[0] = 0.0
+    v[0] = -0.0
+    k[1, 0, :] = -0.0
+    k[2, :, :] = 0
+    k[2, 0, 0], k[2, 0, 1] = 1.0, 1.0                   # rotated: exact zeros on odd d
+    k[3, 0, :2] = [5.0, 4.0]                             # rotated lands on ties
+    v[4] = np.ldexp(rng.uniform(0.5, 1, (2, 256)), -130)  # bf16 subnormals, scale clamps
+    v[5] = rng.standard_normal((2, 256)) * 1e37          # near the top of the range
+    k[6] = rng.standard_normal((2, 256)) * 1e30
+    k[7] = np.ldexp(rng.uniform(0.5, 1, (2, 256)), -110)
+    k[8] = rng.standard_t(1.5, (2, 256))                 # heavy tails
+    k[9, :, 5] *= 1e4                                    # one outlier channel
+    for i in range(10, 20):                              # magnitudes spread over 30 binades
+        k[i] = np.ldexp(rng.uniform(0.5, 1, (2, 256)) * rng.choice([-1, 1], (2, 256)),
+                        rng.integers(-15, 15, (2, 256)))
+    for i in range(20, 30):                              # values on E2M1 midpoints
+        v[i] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -5.0], (2, 256))
+    _store_and_compare(bf16(k), bf16(v), nb=4, bs=16)
+
+
+def test_store_canary_negative_and_out_of_range_slots():
+    say("store canary")
+    rng = np.random.default_rng(2)
+    k = bf16(rng.standard_normal((12, 3, 256)))
+    v = bf16(rng.standard_normal((12, 3, 256)))
+    slots = np.array([3, -1, 7, 64, 8, -5, 30, 0, 1000, 2, 63, 31])
+    cache = torch.full((4, 16, 3, 272), 0xA5, dtype=torch.uint8, device=DEV)
+    uq.store(k.to(DEV), v.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+    ref = np.full((4, 16, 3, 272), 0xA5, dtype=np.uint8)
+    keep = (slots >= 0) & (slots < 64)
+    O.store(bits(k)[keep], bits(v)[keep], ref, slots[keep])
+    assert np.array_equal(cache.cpu().numpy(), ref)
+
+
+def test_store_strided_views_and_block_sizes():
+    say("store strided")
+    rng = np.random.default_rng(3)
+    big_k = bf16(rng.standard_normal((20, 4, 512))).to(DEV)
+    big_v = bf16(rng.standard_normal((40, 2, 256))).to(DEV)
+    k = big_k[:, :, 128:384]            # stride_h 512, offset 128
+    v = big_v.view(20, 4, 256)          # plain
+    for bs in (16, 32, 64, 128, 256):
+        nb = 2
+        slots = rng.permutation(nb * bs)[:20]
+        cache = torch.zeros((nb, bs, 4, 272), dtype=torch.uint8, device=DEV)
+        uq.store(k, v, cache, torch.from_numpy(slots).to(DEV))
+        ref = np.zeros((nb, bs, 4, 272), dtype=np.uint8)
+        O.store(bits(k.contiguous()), bits(v), ref, slots)
+        assert np.array_equal(cache.cpu().numpy(), ref), bs
+
+
+def test_store_random_bulk():
+    say("store bulk")
+    rng = np.random.default_rng(4)
+    k = bf16(rng.standard_normal((3000, 4, 256)) * np.exp(rng.uniform(-8, 8, (3000, 4, 1))))
+    v = bf16(rng.standard_t(3, (3000, 4, 256)))
+    _store_and_compare(k, v, nb=200, bs=16)
+
+
+# -------------------------------------------------------------------- decode
+def _decode_case(seq_lens, Hk, qg, bs=16, splits=4, seed=0, scale=1 / 16, q_scale=1.0,
+                 k_gen=None):
+    rng = np.random.default_rng(seed)
+    B = len(seq_lens)
+    Hq = Hk * qg
+    nblk = [(L + bs - 1) // bs for L in seq_lens]
+    width = max(max(nblk), 1)
+    nb = sum(nblk) + 3
+    perm = rng.permutation(nb)
+    table = np.zeros((B, width), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    q = bf16(rng.standard_normal((B, Hq, 256)) * q_scale)
+    cache = torch.zeros((nb, bs, Hk, 272), dtype=torch.uint8, device=DEV)
+    ref_cache = np.zeros((nb, bs, Hk, 272), dtype=np.uint8)
+    for b, L in enumerate(seq_lens):
+        if L == 0:
+            continue
+        kk = k_gen(rng, (L, Hk, 256)) if k_gen else rng.standard_normal((L, Hk, 256))
+        k = bf16(kk)
+        v = bf16(rng.standard_normal((L, Hk, 256)))
+        t = np.arange(L)
+        slots = table[b, t // bs].astype(np.int64) * bs + t % bs
+        uq.store(k.to(DEV), v.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+        O.store(bits(k), bits(v), ref_cache, slots)
+    tbl = torch.from_numpy(table).to(DEV)
+    lens = torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    out = uq.decode(q.to(DEV), cache, tbl, lens, scale, splits)
+    ref = O.decode(bits(q), ref_cache, table, np.array(seq_lens), scale)
+    return out, ref, dict(q=q, cache=cache, table=tbl, lens=lens, ref_cache=ref_cache, scale=scale)
+
+
+def test_decode_tiny_workload():
+    say("decode tiny")
+    w = inputs.WORKLOADS["tiny"]
+    inst = harness.Instance(w, DEV)
+    ref_cache = np.zeros(tuple(inst.cache.shape), dtype=np.uint8)
+    for b in range(w.B):
+        k, v = inputs.make_kv(w, inst.layout, b)
+        O.store(bits(k), bits(v), ref_cache, inputs.slots_for(inst.layout, b, 0, int(inst.layout.seq_lens[b])))
+    ref = O.decode(bits(inst.query), ref_cache, inst.layout.block_table, inst.layout.seq_lens, w.scale)
+    for S in (1, 2, 3, 4, 5, 7, 8, 16, 64, 512):
+        check_close(to_np(inst.decode(S)), ref, f"tiny S={S}")
+
+
+@pytest.mark.parametrize("qg", [6, 8, 16])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_decode_ragged_lengths_block_sizes(qg, bs):
+    say(f"decode ragged qg={qg} bs={bs}")
+    lens = [1, 15, 16, 17, 100, 257, 300, 33]
+    out, ref, _ = _decode_case(lens, Hk=2, qg=qg, bs=bs, splits=3, seed=qg * 1000 + bs)
+    check_close(to_np(out), ref, f"qg={qg} bs={bs}")
+
+
+def test_decode_single_token_is_exact():
+    """L = 1: softmax weight 1, so the bf16 output equals the dequantised
+    value, which bf16 represents exactly."""
+    say("decode L=1")
+    out, ref, ctx = _decode_case([1, 1, 1], Hk=2, qg=8, splits=4, seed=5)
+    assert np.array_equal(to_np(out), ref)
+
+
+def test_decode_zero_query_is_mean():
+    say("decode q=0")
+    rng = np.random.default_rng(6)
+    out, ref, ctx = _decode_case([50, 91], Hk=1, qg=8, splits=2, seed=6, q_scale=0.0)
+    for b, L in enumerate([50, 91]):
+        _, V = O.gather_sequence(ctx["ref_cache"], ctx["table"].cpu().numpy()[b], L, 0)
+        check_close(to_np(out)[b], np.broadcast_to(V.mean(0), (8, 256)), f"mean b={b}")
+
+
+def test_decode_large_scores_rebase():
+    """Scores far above the first tile's maximum exercise the running-max
+    re-basing path."""
+    say("decode rebase")
+    def grow(rng, shape):
+        x = rng.standard_normal(shape)
+        return x * np.linspace(0.2, 3.0, shape[0])[:, None, None]
+    out, ref, _ = _decode_case([400, 1000], Hk=2, qg=8, splits=2, seed=7, scale=0.25, k_gen=grow)
+    # peaked softmax: outputs are single dequantised values of magnitude up to ~6
+    check_close(to_np(out), ref, "rebase", allow_output_rounding=True)
+
+
+def test_decode_golden_two_token():
+    say("decode golden")
+    d = golden_io.decode_two_token()
+    L = d["seq_len"]
+    k = bf16(np.stack([d["key"][t] for t in range(L)])[:, None, :])
+    v = bf16(np.stack([d["value"][t] for t in range(L)])[:, None, :])
+    q = bf16(np.broadcast_to(d["query"], (1, 8, 256)))
+    cache = torch.zeros((1, 16, 1, 272), dtype=torch.uint8, device=DEV)
+    uq.store(k.to(DEV), v.to(DEV), cache, torch.arange(L, dtype=torch.int64, device=DEV))
+    out = uq.decode(q.to(DEV), cache, torch.zeros((1, 1), dtype=torch.int32, device=DEV),
+                    torch.tensor([L], dtype=torch.int32, device=DEV), d["scale"], 1)
+    want = np.zeros(256)
+    for i, x in d["out"].items():
+        want[i] = x
+    check_close(to_np(out)[0], np.broadcast_to(want, (8, 256)), "two-token")
+
+
+def test_decode_empty_sequence_and_clamped_length():
+    say("decode empty")
+    rng = np.random.default_rng(8)
+    out, ref, ctx = _decode_case([0, 40], Hk=1, qg=8, splits=2, seed=8)
+    assert np.all(to_np(out)[0] == 0)
+    check_close(to_np(out)[1], ref[1], "b=1")
+    # a length past the table clamps to the table's capacity (48 tokens here)
+    lens = torch.tensor([0, 10 ** 6], dtype=torch.int32, device=DEV)
+    out2 = uq.decode(ctx["q"].to(DEV), ctx["cache"], ctx["table"], lens, ctx["scale"], 2)
+    assert np.all(np.isfinite(to_np(out2)))
+
+
+def test_decode_query_strides_and_reuse_of_outputs():
+    say("decode strides")
+    out, ref, ctx = _decode_case([70, 130], Hk=2, qg=8, splits=4, seed=9)
+    big = torch.zeros((2, 16, 512), dtype=torch.bfloat16, device=DEV)
+    big[:, :, 256:] = ctx["q"].to(DEV)
+    qv = big[:, :, 256:]
+    o = torch.full((2, 16, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(uq.decode_workspace_bytes(2, 16, 2, 4), dtype=torch.uint8, device=DEV)
+    uq.decode(qv, ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 4, out=o, workspace=ws)
+    assert torch.equal(o, out)
+
+
+def test_decode_stage_masks_compose():
+    say("decode stages")
+    out, ref, ctx = _decode_case([90, 33], Hk=2, qg=8, splits=4, seed=10)
+    o = torch.empty_like(out)
+    for st in (uq.STAGE_PROLOGUE, uq.STAGE_SPLIT, uq.STAGE_MERGE):
+        uq.decode(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 4,
+                  out=o, stages=st)
+    assert torch.equal(o, out)
+
+
+def test_decode_split_count_invariance():
+    say("decode split invariance")
+    out, ref, ctx = _decode_case([2000, 1500, 777], Hk=4, qg=8, splits=1, seed=11)
+    base = to_np(out)
+    check_close(base, ref, "S=1")
+    for S in (2, 8, 32, 64, 128, 512):
+        o = uq.decode(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], S)
+        check_close(to_np(o), ref, f"S={S}")
