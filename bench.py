@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (reference for "
+                         "scaling the profiler's byte counters)")
     return ap.parse_args()
 
 
@@ -166,6 +169,14 @@ def main():
     log(f"setup {w.name}")
     lay, q, caches, bt, sl = setup(w, dev)
     kv_bytes = inputs.kv_bytes(w, lay)
+    if args.copy_ref_mib > 0:
+        n = args.copy_ref_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"reference copy: {n} bytes read, {n} bytes written")
+        del src, dst
     log(f"timing {args.steps} steps ({len(caches)} cache copies)")
     step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9

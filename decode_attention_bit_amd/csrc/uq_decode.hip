@@ -76,40 +76,58 @@ struct Tile {
   int nvalid;        // tokens of the tile that are inside the sequence
 };
 
-__device__ __forceinline__ void load_tile(Tile& T, const uint8_t* __restrict__ cache,
-                                          const int32_t* __restrict__ bt, int t, int L,
-                                          int log2_bs, int64_t num_blocks, size_t row, int h,
-                                          int n16, int grp) {
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A wave streams the 16-token tiles of its own KV head through a private
+// two-slot LDS ring: a tile is 16 slots of 272 bytes (token stride `row` in
+// the cache, 272 in LDS), moved as 272 chunks of 16 bytes by five
+// direct-to-LDS buffer loads (the last one on 16 lanes).
+constexpr int kTileChunks = 17 * kTile;          // 272
+constexpr int kTileU4 = kTileChunks;             // uint4 per tile in LDS
+constexpr int kDmaPerTile = 5;                   // ceil(272 / 64)
+
+__device__ __forceinline__ int issue_tile(uint4* dst, const uint8_t* __restrict__ cache,
+                                           const int32_t* __restrict__ bt, int t, int L,
+                                           int log2_bs, int64_t num_blocks, uint32_t row, int h,
+                                           int lane, const uint32_t goff[kDmaPerTile]) {
   const int tok0 = t * kTile;
-  const int phys = bt[tok0 >> log2_bs];
+  const int phys = __builtin_amdgcn_readfirstlane(bt[tok0 >> log2_bs]);
   const bool ok = phys >= 0 && (int64_t)phys < num_blocks;
   const int nvalid = ok ? min(kTile, L - tok0) : 0;
-  T.nvalid = nvalid;
-  const uint8_t* base = cache +
-                        ((((size_t)(ok ? phys : 0)) << log2_bs) + (tok0 & ((1 << log2_bs) - 1))) * row +
-                        (size_t)h * kSlotBytes;
-  if (n16 < nvalid) {
-    const uint8_t* kp = base + n16 * row;
-    T.ka = ld16(kp + kKCodeOff + 16 * grp);
-    T.kb = ld16(kp + kKCodeOff + 64 + 16 * grp);
-    T.ks = ld8(kp + kKScaleOff);
-  } else {
-    T.ka = make_uint4(0, 0, 0, 0);
-    T.kb = make_uint4(0, 0, 0, 0);
-    T.ks = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  }
+  const size_t tile_off =
+      ((((size_t)(ok ? phys : 0)) << log2_bs) + (size_t)(tok0 & ((1 << log2_bs) - 1))) * row +
+      (size_t)h * kSlotBytes;
+  // the descriptor ends at the last valid token: chunks past it land as zeros
+  const int nrec = nvalid > 0 ? (nvalid - 1) * (int)row + kSlotBytes : 0;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(cache + tile_off), (short)0, nrec, 0x00020000);
+#pragma unroll
+  for (int k = 0; k < kDmaPerTile - 1; ++k)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 64 * k), 16, goff[k], 0, 0, 0);
+  if (lane < kTileChunks - 64 * (kDmaPerTile - 1))
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 64 * (kDmaPerTile - 1)), 16,
+                                             goff[kDmaPerTile - 1], 0, 0, 0);
+  return nvalid;
+}
+
+// s_waitcnt on vector memory only (gfx9 encoding; expcnt and lgkmcnt left free)
+#define UQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+
+// Operands of one staged tile (slot stride 272 bytes).
+__device__ __forceinline__ void read_tile(Tile& T, const uint4* __restrict__ src, int n16, int grp,
+                                          int nvalid) {
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(src);
+  const uint8_t* kp = base + n16 * kSlotBytes;
+  T.ka = *reinterpret_cast<const uint4*>(kp + kKCodeOff + 16 * grp);
+  T.kb = *reinterpret_cast<const uint4*>(kp + kKCodeOff + 64 + 16 * grp);
+  T.ks = *reinterpret_cast<const uint2*>(kp + kKScaleOff);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int tk = 4 * grp + i;
-    if (tk < nvalid) {
-      const uint8_t* vp = base + tk * row;
-      T.vd[i] = ld8(vp + kVCodeOff + 8 * n16);
-      T.vs[i] = ld4(vp + kVScaleOff + 4 * (n16 >> 3));
-    } else {
-      T.vd[i] = make_uint2(0, 0);
-      T.vs[i] = 0x7F7F7F7Fu;
-    }
+    const uint8_t* vp = base + (4 * grp + i) * kSlotBytes;
+    T.vd[i] = *reinterpret_cast<const uint2*>(vp + kVCodeOff + 8 * n16);
+    T.vs[i] = *reinterpret_cast<const uint32_t*>(vp + kVScaleOff + 4 * (n16 >> 3));
   }
+  T.nvalid = nvalid;
 }
 
 // Byte M of each token's 8 V-code bytes holds d = 16*(l%16) + 2M (low nibble)
@@ -135,11 +153,19 @@ __device__ __forceinline__ void pv_step(const Tile& T, const float vscale[4], co
   acc[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pb, acc[2 * M + 1], 0, 0, 0);
 }
 
-template <int QG>
-__device__ __forceinline__ void compute_tile(const Tile& T, const v8i& qb0, const v8i& qb1,
-                                             float scale_log2, int n16, int grp, v4f acc[16],
-                                             float& m_ref, float& l_part) {
-  // ---- scores
+// Maximum over the four 16-lane row groups (lanes l, l^16, l^32, l^48), with
+// the in-register row swaps of gfx950 instead of LDS permutes.
+__device__ __forceinline__ float rowgroup_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Scores of one tile in the log2 domain (lane: q-head l%16, tokens 4*grp+i),
+// -inf past the end of the sequence; mt = the tile maximum for the lane's head.
+__device__ __forceinline__ void qk_tile(const Tile& T, const v8i& qb0, const v8i& qb1,
+                                        float scale_log2, int grp, float sv[4], float& mt) {
   const int sc1 = (int)((T.ks.x >> (8 * grp)) & 0xFF);
   const int sc2 = (int)((T.ks.y >> (8 * grp)) & 0xFF);
   const v8i a1 = {(int)T.ka.x, (int)T.ka.y, (int)T.ka.z, (int)T.ka.w, 0, 0, 0, 0};
@@ -147,33 +173,28 @@ __device__ __forceinline__ void compute_tile(const Tile& T, const v8i& qb0, cons
   v4f sc = {0.f, 0.f, 0.f, 0.f};
   sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qb0, sc, 4, 0, 0, sc1, 0, 127);
   sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, qb1, sc, 4, 0, 0, sc2, 0, 127);
-  float sv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sv[i] = (4 * grp + i < T.nvalid) ? sc[i] * scale_log2 : -INFINITY;
-
-  // ---- online softmax (log2 domain), lazily re-based
-  float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  mt = fmaxf(mt, __shfl_xor(mt, 16));
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  const bool need = mt > m_ref + 8.0f;
-  if (__any(need)) {
-    const float mn = need ? mt : m_ref;
-    const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - mn);
+  for (int i = 0; i < 4; ++i) sv[i] = sc[i] * scale_log2;
+  if (T.nvalid < kTile) {                  // only the sequence's last tile is partial
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] *= alpha;
-    l_part *= alpha;
-    m_ref = mn;
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i >= T.nvalid) sv[i] = -INFINITY;
   }
+  mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mt = rowgroup_max(mt);
+}
+
+// Softmax weights p = 2^(s - m_ref) (<= 2^8 by the re-basing rule), then
+// O^T += V^T P^T. Touches the accumulators only through MFMAs.
+__device__ __forceinline__ void pv_tile(const Tile& T, const float sv[4], float m_ref, int n16,
+                                        v4f acc[16], float& l_part) {
   float p[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = (sv[i] == -INFINITY) ? 0.f : exp2f(sv[i] - m_ref);
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
   const uint32_t p01 = pack_bf16(p[0], p[1]);
   const uint32_t p23 = pack_bf16(p[2], p[3]);
-  l_part += (bf16_to_f32(p01 & 0xFFFF) + bf16_to_f32(p01 >> 16)) +
-            (bf16_to_f32(p23 & 0xFFFF) + bf16_to_f32(p23 >> 16));
+  l_part += (p[0] + p[1]) + (p[2] + p[3]);
   const v4s pb = __builtin_bit_cast(v4s, make_uint2(p01, p23));
-
-  // ---- P.V: V codes -> bf16 with their block scale, then 16 MFMAs
   float vscale[4];
   const int vsh = 8 * ((n16 >> 1) & 3);
 #pragma unroll
@@ -188,35 +209,42 @@ __device__ __forceinline__ void compute_tile(const Tile& T, const v8i& qb0, cons
   pv_step<7>(T, vscale, pb, acc);
 }
 
-template <int QG>
-__global__ __launch_bounds__(512) void stage1_kernel(
+template <int QG, int HPW, int NSLOT>
+__global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float scale_log2, int Hq, int Hk, int hpw, int hgroups, int S, int nsub, int log2_bs,
-    int max_blocks, int64_t num_blocks, uint16_t* __restrict__ part_o,
+    float scale_log2, int Hq, int Hk, int hgroups, int S, int spw, int nsub, int P,
+    int log2_bs, int max_blocks, int64_t num_blocks, uint16_t* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
+  static_assert(NSLOT == 3 || NSLOT == 4, "ring depth");
+  // NSLOT-slot ring per wave; distinct arrays so that the compiler can tell
+  // the slot being read from the slots being filled
+  __shared__ uint4 ring0[HPW][kTileU4];
+  __shared__ uint4 ring1[HPW][kTileU4];
+  __shared__ uint4 ring2[HPW][kTileU4];
+  __shared__ uint4 ring3[NSLOT > 3 ? HPW : 1][NSLOT > 3 ? kTileU4 : 1];
+
   int x = blockIdx.x;
   const int hg = x % hgroups;
   x /= hgroups;
-  const int sub = x % nsub;
-  x /= nsub;
-  const int s = x % S;
-  const int b = x / S;
+  const int part = x % P;             // partial index within (b, head)
+  const int b = x / P;
   const int lane = threadIdx.x & 63;
-  const int h = hg * hpw + (threadIdx.x >> 6);
-  const int P = S * nsub, part = s * nsub + sub;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = hg * HPW + wave;
 
   int L = seq_lens[b];
   const int Lmax = max_blocks << log2_bs;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  // Split s of the sequence covers tiles [s*cs, (s+1)*cs). A partial covers
+  // either spw consecutive splits, or one of nsub equal pieces of one split.
   const int n_tiles = (L + kTile - 1) / kTile;
-  const int per_split = (n_tiles + S - 1) / S;
-  const int t_begin = s * per_split;
-  const int t_end = min(t_begin + per_split, n_tiles);
-  const int span = max(t_end - t_begin, 0);
-  const int per_sub = (span + nsub - 1) / nsub;
-  const int u0 = t_begin + sub * per_sub;
-  const int u1 = min(u0 + per_sub, t_end);
+  const int cs = (n_tiles + S - 1) / S;
+  const int g_lo = (part / nsub) * spw * cs;
+  const int g_hi = min(g_lo + spw * cs, n_tiles);
+  const int sub_len = (spw * cs + nsub - 1) / nsub;
+  const int u0 = g_lo + (part % nsub) * sub_len;
+  const int u1 = min(u0 + sub_len, g_hi);
 
   const int n16 = lane & 15, grp = lane >> 4;
   const bool qlane = n16 < QG;
@@ -231,6 +259,7 @@ __global__ __launch_bounds__(512) void stage1_kernel(
     return;
   }
 
+  // q8 first, so that waiting for it never waits for the tile loads behind it
   v8i qb0 = {0, 0, 0, 0, 0, 0, 0, 0}, qb1 = {0, 0, 0, 0, 0, 0, 0, 0};
   if (qlane) {
     const uint8_t* qp = q8 + ((size_t)b * Hq + hq) * kHeadDim;
@@ -240,19 +269,84 @@ __global__ __launch_bounds__(512) void stage1_kernel(
     qb1 = (v8i){(int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w, (int)x3.x, (int)x3.y, (int)x3.z, (int)x3.w};
   }
 
-  const size_t row = (size_t)Hk * kSlotBytes;
+  const uint32_t row = (uint32_t)Hk * kSlotBytes;
   const int32_t* bt = block_table + (size_t)b * max_blocks;
-  v4f acc[16];
+  uint32_t goff[kDmaPerTile];                 // chunk c -> token c / 17, 16 bytes (c % 17)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_part = 0.f;
+  for (int k = 0; k < kDmaPerTile; ++k) {
+    const int c = min(64 * k + lane, kTileChunks - 1);
+    goff[k] = (c / 17) * row + (c % 17) * 16;
+  }
+  auto issue = [&](uint4* slot, int t) {
+    return issue_tile(slot, cache, bt, t, L, log2_bs, num_blocks, row, h, lane, goff);
+  };
 
-  Tile cur, nxt;
-  load_tile(cur, cache, bt, u0, L, log2_bs, num_blocks, row, h, n16, grp);
-  for (int t = u0; t < u1; ++t) {
-    if (t + 1 < u1) load_tile(nxt, cache, bt, t + 1, L, log2_bs, num_blocks, row, h, n16, grp);
-    compute_tile<QG>(cur, qb0, qb1, scale_log2, n16, grp, acc, m_ref, l_part);
-    cur = nxt;
+  // Softmax reference: the first tile's maximum. The weights 2^(s - m_ref)
+  // are exact for any reference; keeping them <= 2^8 bounds their range. If a
+  // later tile exceeds the reference by more than that (rare), the split is
+  // redone with its true maximum, found by a scores-only pass. No rescaling
+  // of the accumulators is ever needed, so they never leave the MFMA path.
+  v4f acc[16];
+  float m_ref = -INFINITY, l_part = 0.f;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    Tile T;
+    float sv[4], mt;
+    if (attempt == 1) {             // scores-only pass, one tile at a time
+      m_ref = -INFINITY;
+      for (int t = u0; t < u1; ++t) {
+        UQ_WAIT_VMCNT(0);
+        const int nv = issue(ring0[wave], t);
+        UQ_WAIT_VMCNT(0);
+        read_tile(T, ring0[wave], n16, grp, nv);
+        qk_tile(T, qb0, qb1, scale_log2, grp, sv, mt);
+        m_ref = fmaxf(m_ref, mt);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    l_part = 0.f;
+    bool rebased = false;
+    UQ_WAIT_VMCNT(0);
+    // Pipeline: tiles t and t + 1 are in flight when step t starts. Wait for
+    // tile t (tile t + 1 may stay pending), read it, start tile t + 2 into
+    // the slot tile t - 1 used (already consumed), then compute tile t.
+    // valid-token count of the tile in each slot, known when it is issued
+    int nv_ring0 = issue(ring0[wave], u0), nv_ring1 = 0, nv_ring2 = 0, nv_ring3 = 0;
+    if (u0 + 1 < u1) nv_ring1 = issue(ring1[wave], u0 + 1);
+    if (NSLOT > 3 && u0 + 2 < u1) nv_ring2 = issue(ring2[wave], u0 + 2);
+    // Step t: tiles t .. t + NSLOT - 2 are in flight. Wait for tile t (the
+    // later ones may stay pending), read it, start tile t + NSLOT - 1 into the
+    // slot tile t - 1 used (already consumed), then compute tile t.
+#define UQ_STEP(CUR, NXT)                                                        \
+    {                                                                            \
+      if (NSLOT > 3 && t + 2 < u1) { UQ_WAIT_VMCNT(2 * kDmaPerTile); }           \
+      else if (t + 1 < u1) { UQ_WAIT_VMCNT(kDmaPerTile); }                       \
+      else { UQ_WAIT_VMCNT(0); }                                                 \
+      read_tile(T, CUR[wave], n16, grp, nv_##CUR);                               \
+      if (t + NSLOT - 1 < u1) nv_##NXT = issue(NXT[wave], t + NSLOT - 1);        \
+      qk_tile(T, qb0, qb1, scale_log2, grp, sv, mt);                             \
+      if (attempt == 0 && t == u0) m_ref = mt;                                   \
+      if (__any(mt > m_ref + 8.0f)) { rebased = true; break; }                   \
+      if (T.nvalid > 0) pv_tile(T, sv, m_ref, n16, acc, l_part);                 \
+      if (++t >= u1) break;                                                      \
+    }
+    if (NSLOT == 3) {
+      for (int t = u0;;) {
+        UQ_STEP(ring0, ring2)
+        UQ_STEP(ring1, ring0)
+        UQ_STEP(ring2, ring1)
+      }
+    } else {
+      for (int t = u0;;) {
+        UQ_STEP(ring0, ring3)
+        UQ_STEP(ring1, ring0)
+        UQ_STEP(ring2, ring1)
+        UQ_STEP(ring3, ring2)
+      }
+    }
+#undef UQ_STEP
+    if (!rebased) break;
+    UQ_WAIT_VMCNT(0);
   }
 
   const float l1 = l_part + __shfl_xor(l_part, 16);
@@ -284,32 +378,71 @@ __global__ __launch_bounds__(512) void stage1_kernel(
 
 // ---------------------------------------------------------------------------
 // Stage 2: out = sum_p w_p O_p / sum_p w_p with w_p = l_p 2^(m_p - max m),
-// over the partials with l_p > 0. Grid (B*Hq, D/64); the merge is per
-// column, so the chunking does not change any result bit.
+// over the partials with l_p > 0. Grid (B*Hq, D/64): one wave per 64-column
+// chunk; lane l reads columns 4*(l%16) .. +3 of the rows p = l/16 (mod 4), all
+// of them in flight at once, then the four row groups are summed across
+// lanes. The merge is per column, so the chunking changes no result bit.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void stage2_kernel(const uint16_t* __restrict__ part_o,
                                                     const float* __restrict__ part_m,
                                                     const float* __restrict__ part_l,
                                                     uint16_t* __restrict__ out, int P) {
   const size_t bh = blockIdx.x;
-  const int d = blockIdx.y * 64 + threadIdx.x;
+  const int lane = threadIdx.x;
+  const int rg = lane >> 4;                       // row group
+  const int col = blockIdx.y * 64 + 4 * (lane & 15);
   const float* pm = part_m + bh * P;
   const float* pl = part_l + bh * P;
   float M = -INFINITY;
-  for (int p = 0; p < P; ++p)
+  for (int p = lane; p < P; p += 64)
     if (pl[p] > 0.f) M = fmaxf(M, pm[p]);
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < P; ++p) {
-    const float l = pl[p];
-    if (l > 0.f) {
-      const float w = l * exp2f(pm[p] - M);
-      den += w;
-      num += w * bf16_to_f32(part_o[(bh * P + p) * kHeadDim + d]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+  const uint16_t* po = part_o + bh * P * kHeadDim + col;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, den = 0.f;
+  for (int c = 0; c < P; c += 64) {
+    const int pj = c + lane;
+    const float lj = pj < P ? pl[pj] : 0.f;
+    const float wj = lj > 0.f ? lj * exp2f(pm[pj] - M) : 0.f;   // weight of partial c + lane
+    const int n = min(64, P - c);
+    for (int r0 = 0; r0 < n; r0 += 32) {
+      uint2 o[8];
+      float w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {               // rows r0 + 4u + rg, eight in flight per lane
+        const int j = r0 + 4 * u + rg;
+        const int jc = min(j, n - 1);
+        const float wu = __shfl(wj, jc);
+        w[u] = j < n ? wu : 0.f;
+        o[u] = *reinterpret_cast<const uint2*>(po + (size_t)(c + jc) * kHeadDim);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // empty partials (w = 0) hold stale rows: select, never multiply them
+        const bool use = w[u] > 0.f;
+        den += use ? w[u] : 0.f;
+        a0 += use ? w[u] * bf16_to_f32(o[u].x & 0xFFFF) : 0.f;
+        a1 += use ? w[u] * bf16_to_f32(o[u].x >> 16) : 0.f;
+        a2 += use ? w[u] * bf16_to_f32(o[u].y & 0xFFFF) : 0.f;
+        a3 += use ? w[u] * bf16_to_f32(o[u].y >> 16) : 0.f;
+      }
     }
   }
-  const float o = den > 0.f ? num / den : 0.f;
-  const uint32_t w = pack_bf16(o, 0.f);
-  out[bh * kHeadDim + d] = (uint16_t)(w & 0xFFFF);
+#pragma unroll
+  for (int m = 16; m <= 32; m <<= 1) {
+    den += __shfl_xor(den, m);
+    a0 += __shfl_xor(a0, m);
+    a1 += __shfl_xor(a1, m);
+    a2 += __shfl_xor(a2, m);
+    a3 += __shfl_xor(a3, m);
+  }
+  if (rg == 0) {
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    uint2 r;
+    r.x = pack_bf16(a0 * inv, a1 * inv);
+    r.y = pack_bf16(a2 * inv, a3 * inv);
+    *reinterpret_cast<uint2*>(out + bh * kHeadDim + col) = r;
+  }
 }
 
 int largest_divisor_upto(int n, int cap) {
@@ -322,6 +455,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Resident waves per CU of stage 1: the LDS ring (NSLOT tiles of 4352 bytes
+// per wave) and the register budget (three waves per SIMD) both bound it.
+#ifndef UQ_RING_SLOTS
+#define UQ_RING_SLOTS 4
+#endif
+#ifndef UQ_TARGET_WAVES
+#define UQ_TARGET_WAVES 2048
+#endif
+constexpr int kRingSlots = UQ_RING_SLOTS;
+
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits) {
   DecodePlan p{};
   p.B = B;
@@ -329,14 +472,19 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits) {
   p.Hk = Hk;
   p.QG = Hq / Hk;
   p.splits = num_kv_splits;
-  // Enough waves to cover latency: aim for >= 4096 (16 per CU) by cutting each
-  // split into contiguous sub-ranges handled by separate waves.
+  // Partition policy. Every partial is a union of whole splits or a piece of
+  // one split, so the split boundaries are kept. A wave has a fixed cost (its
+  // query, its partial write and the ring fill), so a wave takes several
+  // splits while the grid would still hold at least one full round of
+  // resident waves; with too few (sequence, head, split) units a split is cut
+  // into pieces instead, so that enough waves hide the HBM latency.
   const long units = (long)B * Hk * num_kv_splits;
-  long nsub = (4096 + units - 1) / units;
-  if (nsub < 1) nsub = 1;
-  if (nsub > 8) nsub = 8;
-  p.nsub = (int)nsub;
-  p.parts = num_kv_splits * p.nsub;
+  int spw = 1, nsub = 1;
+  while (spw < num_kv_splits && units / (2L * spw) >= UQ_TARGET_WAVES) spw *= 2;
+  while (nsub < 8 && units * nsub * 2 <= UQ_TARGET_WAVES) nsub *= 2;
+  p.spw = spw;
+  p.nsub = nsub;
+  p.parts = ((num_kv_splits + spw - 1) / spw) * nsub;
   const size_t rows = (size_t)B * Hq;
   size_t off = 0;
   p.q8_off = off;
@@ -372,22 +520,34 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  const dim3 grid1((unsigned)((int64_t)p.B * p.splits * p.nsub * hgroups));
+  const dim3 grid1((unsigned)((int64_t)p.B * p.parts * hgroups));
   const dim3 block1(64 * hpw);
-#define UQ_STAGE1(QGV)                                                                        \
-  hipLaunchKernelGGL(stage1_kernel<QGV>, grid1, block1, 0, stream, q8, a.cache, a.block_table, \
-                     a.seq_lens, scale_log2, p.Hq, p.Hk, hpw, hgroups, p.splits, p.nsub,     \
-                     log2_bs, a.max_blocks_per_seq, a.num_blocks, part_o, part_m, part_l)
+#define UQ_STAGE1(QGV, HPWV)                                                                     \
+  hipLaunchKernelGGL((stage1_kernel<QGV, HPWV, kRingSlots>), grid1, block1, 0, stream, q8,       \
+                     a.cache, a.block_table, a.seq_lens, scale_log2, p.Hq, p.Hk, hgroups,      \
+                     p.splits, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,          \
+                     a.num_blocks, part_o, part_m, part_l)
+#define UQ_STAGE1_HPW(QGV)                      \
+  do {                                          \
+    switch (hpw) {                              \
+      case 1: UQ_STAGE1(QGV, 1); break;         \
+      case 2: UQ_STAGE1(QGV, 2); break;         \
+      case 4: UQ_STAGE1(QGV, 4); break;         \
+      default: UQ_STAGE1(QGV, 8); break;        \
+    }                                           \
+  } while (0)
   if (stage_mask & 2) {
+    if (hpw != 1 && hpw != 2 && hpw != 4 && hpw != 8) return hipErrorInvalidValue;
     switch (p.QG) {
-      case 6: UQ_STAGE1(6); break;
-      case 8: UQ_STAGE1(8); break;
-      case 16: UQ_STAGE1(16); break;
+      case 6: UQ_STAGE1_HPW(6); break;
+      case 8: UQ_STAGE1_HPW(8); break;
+      case 16: UQ_STAGE1_HPW(16); break;
       default: return hipErrorInvalidValue;
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+#undef UQ_STAGE1_HPW
 #undef UQ_STAGE1
   if (stage_mask & 4) {
     hipLaunchKernelGGL(stage2_kernel, dim3((unsigned)vecs, kHeadDim / 64), dim3(64), 0, stream,

@@ -21,8 +21,9 @@ struct StoreArgs {
 struct DecodePlan {
   int B, Hq, Hk, QG;
   int splits;          // num_kv_splits
-  int nsub;            // waves per (sequence, KV head, split); partials = splits * nsub
-  int parts;           // splits * nsub
+  int spw;             // consecutive splits covered by one partial (nsub == 1)
+  int nsub;            // pieces one split is cut into (spw == 1)
+  int parts;           // partials per (sequence, query head): ceil(splits / spw) * nsub
   size_t q8_off, o_off, m_off, l_off, total;   // byte offsets inside the workspace
 };
 

@@ -34,6 +34,8 @@ class Instance:
         last = []
         for b in range(w.B):
             L = int(lay.seq_lens[b])
+            if b % 8 == 0:
+                print(f"  storing {w.name} sequence {b}/{w.B}", flush=True)
             k, v = inputs.make_kv(w, lay, b)
             n_pre = L - 1 if w.name == "mixed" else L   # mixed: last token stored in the step
             if n_pre > 0:
@@ -74,12 +76,15 @@ class Instance:
         """Oracle output rows (QG, 256) of KV head h of sequence b, from the
         oracle's own encoding of that sequence."""
         L = int(self.layout.seq_lens[b])
+        k, v = inputs.make_kv(self.w, self.layout, b)      # uses the thread pool itself
+        kb, vb = inputs.bf16_bits(k)[:, h], inputs.bf16_bits(v)[:, h]
 
         def enc(i):
-            k, v = inputs.make_kv(self.w, self.layout, b, i, min(i + 8192, L))
-            return O.decode_slots(O.encode_slots(inputs.bf16_bits(k)[:, h], inputs.bf16_bits(v)[:, h]))
+            return O.decode_slots(O.encode_slots(kb[i:i + 8192], vb[i:i + 8192]))
 
-        parts = list(inputs._pool().map(enc, range(0, L, 8192)))
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(8) as ex:                   # not the generator's pool: no nesting
+            parts = list(ex.map(enc, range(0, L, 8192)))
         K = np.concatenate([p[0] for p in parts])
         V = np.concatenate([p[1] for p in parts])
         qg = self.w.QG
