@@ -86,7 +86,8 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup):
 
     dev = q.device
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(uq.decode_workspace_bytes(w.B, w.Hq, w.Hk, w.num_kv_splits), dtype=torch.uint8, device=dev)
+    ws = torch.empty(uq.decode_workspace_bytes(w.B, w.Hq, w.Hk, w.num_kv_splits, bt.shape[1], w.block_size),
+                     dtype=torch.uint8, device=dev)
     R = len(caches)
     args = lambda i: (q, caches[i % R], bt, sl, w.scale, w.num_kv_splits)
 

@@ -8,7 +8,7 @@ and raises if the library has not been built (there is no fallback path).
 Entry points mirror include/uq.h:
   build_hadamard(D, device)                         -> (D, D) float32
   store(key, value, kv_cache, slot_mapping)         -> None (kv_cache updated)
-  decode_workspace_bytes(B, Hq, Hk, num_kv_splits)  -> int
+  decode_workspace_bytes(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size)  -> int
   decode(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
          out=None, workspace=None)                  -> (B, Hq, 256) bf16
 """
@@ -55,7 +55,7 @@ def _load():
     lib.uq_build_hadamard.restype = i32
     lib.uq_store.argtypes = [vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, i64, i64, i64, i64, vp]
     lib.uq_store.restype = i32
-    lib.uq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.uq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.uq_decode_workspace_bytes.restype = sz
     lib.uq_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, i32, vp, i32, i32, i32, i32, i64,
                               i32, i32, i64, i64, vp, sz, vp]
@@ -114,8 +114,10 @@ def store(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
                             value.stride(1), _stream(key.device)))
 
 
-def decode_workspace_bytes(B: int, Hq: int, Hk: int, num_kv_splits: int, D: int = HEAD_DIM) -> int:
-    n = _load().uq_decode_workspace_bytes(int(B), int(Hq), int(Hk), int(D), int(num_kv_splits))
+def decode_workspace_bytes(B: int, Hq: int, Hk: int, num_kv_splits: int, max_blocks_per_seq: int,
+                           block_size: int = 16, D: int = HEAD_DIM) -> int:
+    n = _load().uq_decode_workspace_bytes(int(B), int(Hq), int(Hk), int(D), int(num_kv_splits),
+                                          int(max_blocks_per_seq), int(block_size))
     if n == 0:
         raise ValueError("invalid decode shape")
     return int(n)
@@ -161,7 +163,7 @@ def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=query.device)
     elif out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
         raise TypeError("out must be a contiguous (B, Hq, D) bfloat16 tensor")
-    need = _load().uq_decode_workspace_bytes(B, Hq, Hk, D, int(num_kv_splits))
+    need = _load().uq_decode_workspace_bytes(B, Hq, Hk, D, int(num_kv_splits), block_table.shape[1], bs)
     if workspace is None:
         workspace = _workspace(query.device, max(int(need), 256))
     lib = _load()

@@ -71,11 +71,13 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
   return hip_status(uq::launch_store(a, (hipStream_t)stream), "uq_store launch");
 }
 
-size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits) {
+size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits,
+                                 int max_blocks_per_seq, int block_size) {
   if (B < 1 || Hk < 1 || Hq < Hk || Hq % Hk || D != UQ_HEAD_DIM || num_kv_splits < 1 ||
-      num_kv_splits > UQ_MAX_SPLITS)
+      num_kv_splits > UQ_MAX_SPLITS || max_blocks_per_seq < 1 || !pow2_in(block_size, 16, 256) ||
+      (long long)max_blocks_per_seq * block_size > 0x7FFFFFFFLL)
     return 0;
-  return uq::plan_decode(B, Hq, Hk, num_kv_splits).total;
+  return uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size).total;
 }
 
 int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_cache,
@@ -108,10 +110,11 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
   if (!aligned(query, 8) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4))
     return fail(UQ_EINVAL, "uq_decode: misaligned pointer (query 8 B, kv_cache/out 16 B, workspace 256 B)");
-  const uq::DecodePlan plan = uq::plan_decode(B, Hq, Hk, num_kv_splits);
+  const uq::DecodePlan plan =
+      uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size);
   if (workspace_bytes < plan.total)
     return fail(UQ_EWORKSPACE, "uq_decode: workspace %zu bytes < required %zu", workspace_bytes, plan.total);
-  if ((long long)B * num_kv_splits * plan.nsub * Hk > 0x7FFFFFFFLL)
+  if ((long long)B * plan.parts * Hk > 0x7FFFFFFFLL)
     return fail(UQ_EUNSUPPORTED, "uq_decode: grid too large");
   uq::DecodeArgs a{query, kv_cache, block_table, seq_lens, scale, out, num_blocks, block_size,
                    max_blocks_per_seq, q_stride_b, q_stride_h,

@@ -213,7 +213,7 @@ template <int QG, int HPW, int NSLOT>
 __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
-    float scale_log2, int Hq, int Hk, int hgroups, int S, int spw, int nsub, int P,
+    float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
     int log2_bs, int max_blocks, int64_t num_blocks, uint16_t* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
   static_assert(NSLOT == 3 || NSLOT == 4, "ring depth");
@@ -236,10 +236,10 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   int L = seq_lens[b];
   const int Lmax = max_blocks << log2_bs;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  // Split s of the sequence covers tiles [s*cs, (s+1)*cs). A partial covers
-  // either spw consecutive splits, or one of nsub equal pieces of one split.
+  // Split s covers tiles [s*cs, (s+1)*cs) of the sequence (cs from the table
+  // capacity, so that every split is the same size). A partial covers either
+  // spw consecutive splits or one of nsub equal pieces of one split.
   const int n_tiles = (L + kTile - 1) / kTile;
-  const int cs = (n_tiles + S - 1) / S;
   const int g_lo = (part / nsub) * spw * cs;
   const int g_hi = min(g_lo + spw * cs, n_tiles);
   const int sub_len = (spw * cs + nsub - 1) / nsub;
@@ -282,38 +282,29 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   };
 
   // Softmax reference: the first tile's maximum. The weights 2^(s - m_ref)
-  // are exact for any reference; keeping them <= 2^8 bounds their range. If a
-  // later tile exceeds the reference by more than that (rare), the split is
-  // redone with its true maximum, found by a scores-only pass. No rescaling
-  // of the accumulators is ever needed, so they never leave the MFMA path.
-  v4f acc[16];
-  float m_ref = -INFINITY, l_part = 0.f;
-  for (int attempt = 0; attempt < 2; ++attempt) {
+  // are exact for any reference; keeping them <= 2^8 bounds their range. A
+  // tile that exceeds the reference by more than that ends the current
+  // segment: outside the tile loop its sums are folded into `hold`, rescaled
+  // to the raised reference, and the tile loop restarts at that tile. The
+  // running accumulators are only ever written by MFMAs inside the loop, so
+  // they stay in the accumulator registers.
+  v4f acc[16], hold[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) hold[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_part = 0.f, l_hold = 0.f;
+  int t0 = u0;
+  for (;;) {
     Tile T;
     float sv[4], mt;
-    if (attempt == 1) {             // scores-only pass, one tile at a time
-      m_ref = -INFINITY;
-      for (int t = u0; t < u1; ++t) {
-        UQ_WAIT_VMCNT(0);
-        const int nv = issue(ring0[wave], t);
-        UQ_WAIT_VMCNT(0);
-        read_tile(T, ring0[wave], n16, grp, nv);
-        qk_tile(T, qb0, qb1, scale_log2, grp, sv, mt);
-        m_ref = fmaxf(m_ref, mt);
-      }
-    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
     l_part = 0.f;
     bool rebased = false;
-    UQ_WAIT_VMCNT(0);
-    // Pipeline: tiles t and t + 1 are in flight when step t starts. Wait for
-    // tile t (tile t + 1 may stay pending), read it, start tile t + 2 into
-    // the slot tile t - 1 used (already consumed), then compute tile t.
+    int t_stop = 0;
     // valid-token count of the tile in each slot, known when it is issued
-    int nv_ring0 = issue(ring0[wave], u0), nv_ring1 = 0, nv_ring2 = 0, nv_ring3 = 0;
-    if (u0 + 1 < u1) nv_ring1 = issue(ring1[wave], u0 + 1);
-    if (NSLOT > 3 && u0 + 2 < u1) nv_ring2 = issue(ring2[wave], u0 + 2);
+    int nv_ring0 = issue(ring0[wave], t0), nv_ring1 = 0, nv_ring2 = 0, nv_ring3 = 0;
+    if (t0 + 1 < u1) nv_ring1 = issue(ring1[wave], t0 + 1);
+    if (NSLOT > 3 && t0 + 2 < u1) nv_ring2 = issue(ring2[wave], t0 + 2);
     // Step t: tiles t .. t + NSLOT - 2 are in flight. Wait for tile t (the
     // later ones may stay pending), read it, start tile t + NSLOT - 1 into the
     // slot tile t - 1 used (already consumed), then compute tile t.
@@ -325,19 +316,19 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
       read_tile(T, CUR[wave], n16, grp, nv_##CUR);                               \
       if (t + NSLOT - 1 < u1) nv_##NXT = issue(NXT[wave], t + NSLOT - 1);        \
       qk_tile(T, qb0, qb1, scale_log2, grp, sv, mt);                             \
-      if (attempt == 0 && t == u0) m_ref = mt;                                   \
-      if (__any(mt > m_ref + 8.0f)) { rebased = true; break; }                   \
+      if (t == u0) m_ref = mt;                                                   \
+      if (__any(mt > m_ref + 8.0f)) { rebased = true; t_stop = t; break; }       \
       if (T.nvalid > 0) pv_tile(T, sv, m_ref, n16, acc, l_part);                 \
       if (++t >= u1) break;                                                      \
     }
     if (NSLOT == 3) {
-      for (int t = u0;;) {
+      for (int t = t0;;) {
         UQ_STEP(ring0, ring2)
         UQ_STEP(ring1, ring0)
         UQ_STEP(ring2, ring1)
       }
     } else {
-      for (int t = u0;;) {
+      for (int t = t0;;) {
         UQ_STEP(ring0, ring3)
         UQ_STEP(ring1, ring0)
         UQ_STEP(ring2, ring1)
@@ -346,8 +337,21 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     }
 #undef UQ_STEP
     if (!rebased) break;
+    // Raise the reference to cover tile t_stop (never below the old one, so
+    // the factor is <= 1) and fold the segment into `hold`. Drain the ring;
+    // the loop restarts at t_stop, which is then within 2^8 of the reference.
+    const float m_new = fmaxf(m_ref, mt);
+    const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) hold[j] = (hold[j] + acc[j]) * f;
+    l_hold = (l_hold + l_part) * f;
+    m_ref = m_new;
     UQ_WAIT_VMCNT(0);
+    t0 = t_stop;
   }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] += hold[j];
+  l_part += l_hold;
 
   const float l1 = l_part + __shfl_xor(l_part, 16);
   const float l_tot = l1 + __shfl_xor(l1, 32);
@@ -455,33 +459,43 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Resident waves per CU of stage 1: the LDS ring (NSLOT tiles of 4352 bytes
-// per wave) and the register budget (three waves per SIMD) both bound it.
 #ifndef UQ_RING_SLOTS
 #define UQ_RING_SLOTS 4
 #endif
 #ifndef UQ_TARGET_WAVES
-#define UQ_TARGET_WAVES 2048
+#define UQ_TARGET_WAVES 1024
+#endif
+#ifndef UQ_TILES_PER_WAVE_MAX
+#define UQ_TILES_PER_WAVE_MAX 64
 #endif
 constexpr int kRingSlots = UQ_RING_SLOTS;
+constexpr long kTilesPerWaveMin = 4;
 
-DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits) {
+DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
+                       int block_size) {
   DecodePlan p{};
   p.B = B;
   p.Hq = Hq;
   p.Hk = Hk;
   p.QG = Hq / Hk;
   p.splits = num_kv_splits;
-  // Partition policy. Every partial is a union of whole splits or a piece of
-  // one split, so the split boundaries are kept. A wave has a fixed cost (its
-  // query, its partial write and the ring fill), so a wave takes several
-  // splits while the grid would still hold at least one full round of
-  // resident waves; with too few (sequence, head, split) units a split is cut
-  // into pieces instead, so that enough waves hide the HBM latency.
-  const long units = (long)B * Hk * num_kv_splits;
+  // Splits are sized from the table capacity, not from each sequence's
+  // length: every split then holds the same number of tiles, a short
+  // sequence simply has fewer non-empty ones, and waves carry equal work
+  // whatever the length mix.
+  const long max_tiles = ((long)max_blocks_per_seq * block_size + kTile - 1) / kTile;
+  p.cs = (int)((max_tiles + num_kv_splits - 1) / num_kv_splits);
+  // Partition policy: a wave has a fixed cost (its query, its partial write,
+  // the ring fill), so it should stream as many tiles as the machine can
+  // afford while the grid still offers about UQ_TARGET_WAVES waves when every
+  // sequence is full. A partial is then a union of spw consecutive splits, or
+  // one of nsub pieces of a split that is too long for one wave.
+  long budget = (long)B * Hk * max_tiles / UQ_TARGET_WAVES;
+  budget = budget < kTilesPerWaveMin ? kTilesPerWaveMin
+                                     : (budget > UQ_TILES_PER_WAVE_MAX ? UQ_TILES_PER_WAVE_MAX : budget);
   int spw = 1, nsub = 1;
-  while (spw < num_kv_splits && units / (2L * spw) >= UQ_TARGET_WAVES) spw *= 2;
-  while (nsub < 8 && units * nsub * 2 <= UQ_TARGET_WAVES) nsub *= 2;
+  while (2 * spw <= num_kv_splits && 2L * spw * p.cs <= budget) spw *= 2;
+  while (nsub < 8 && p.cs > 2L * nsub * budget) nsub *= 2;
   p.spw = spw;
   p.nsub = nsub;
   p.parts = ((num_kv_splits + spw - 1) / spw) * nsub;
@@ -525,7 +539,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
 #define UQ_STAGE1(QGV, HPWV)                                                                     \
   hipLaunchKernelGGL((stage1_kernel<QGV, HPWV, kRingSlots>), grid1, block1, 0, stream, q8,       \
                      a.cache, a.block_table, a.seq_lens, scale_log2, p.Hq, p.Hk, hgroups,      \
-                     p.splits, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,          \
+                     p.cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,          \
                      a.num_blocks, part_o, part_m, part_l)
 #define UQ_STAGE1_HPW(QGV)                      \
   do {                                          \

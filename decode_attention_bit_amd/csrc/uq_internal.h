@@ -21,6 +21,7 @@ struct StoreArgs {
 struct DecodePlan {
   int B, Hq, Hk, QG;
   int splits;          // num_kv_splits
+  int cs;              // tiles per split: ceil(ceil(max_blocks * block_size / 16) / splits)
   int spw;             // consecutive splits covered by one partial (nsub == 1)
   int nsub;            // pieces one split is cut into (spw == 1)
   int parts;           // partials per (sequence, query head): ceil(splits / spw) * nsub
@@ -41,7 +42,8 @@ struct DecodeArgs {
   uint8_t* workspace;
 };
 
-DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits);
+DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
+                       int block_size);
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_hadamard(int D, float* H, hipStream_t stream);

@@ -98,9 +98,13 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
  * arguments). The analogue of the pooled segm_out / segm_max / segm_sum and
  * q_fp8 buffers of _SegmBufPool on the flydsl_ultraquant_decode page: query
  * E4M3 codes, one bf16 partial output and two float32 statistics per
- * (sequence, query head, partial).
+ * (sequence, query head, partial). The count of partials depends on the
+ * split count and on the block-table capacity max_blocks_per_seq *
+ * block_size, never on the sequence lengths, so one workspace serves every
+ * step of a fixed-shape batch.
  */
-size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits);
+size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits,
+                                 int max_blocks_per_seq, int block_size);
 
 /*
  * Decode one query token per sequence against the paged 4-bit cache and
@@ -121,12 +125,16 @@ size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits
  *                a sequence of length 0 yields zeros. Physical block ids outside
  *                [0, num_blocks) are read as empty blocks.
  *   scale:       softmax scale applied to q8 . k (finite, > 0).
- *   num_kv_splits: number of key ranges per sequence, 1..512. Each split
- *                covers a contiguous run of 16-token tiles; the result does
- *                not depend on the count beyond rounding.
+ *   num_kv_splits: number of key ranges, 1..512. Split s covers the 16-token
+ *                tiles [s*c, (s+1)*c) of every sequence, with
+ *                c = ceil(ceil(max_blocks_per_seq*block_size / 16) / num_kv_splits),
+ *                so splits past a sequence's end are empty. Stage 1 writes
+ *                one partial per run of whole splits (or per piece of a
+ *                split); the result does not depend on the count beyond
+ *                rounding.
  *   out:         (device) bf16 (B, Hq, D) contiguous, written.
  *   workspace:   (device) at least uq_decode_workspace_bytes(B, Hq, Hk, D,
- *                num_kv_splits) bytes, 256-byte aligned; contents need no
+ *                num_kv_splits, max_blocks_per_seq, block_size) bytes, 256-byte aligned; contents need no
  *                initialisation and are overwritten.
  *   D must be 256; Hq % Hk == 0 with Hq / Hk in {6, 8, 16}; block_size a
  *   power of two in [16, 256].

@@ -102,12 +102,16 @@ def test_decode_stages_rejects_mask(libuq, mask):
 
 def test_workspace_bytes(libuq):
     f = libuq.uq_decode_workspace_bytes
-    assert f(0, 32, 4, 256, 32) == 0
-    assert f(32, 30, 4, 256, 32) == 0
-    assert f(32, 32, 4, 128, 32) == 0
-    assert f(32, 32, 4, 256, 0) == 0
-    n = f(32, 32, 4, 256, 32)
+    assert f(0, 32, 4, 256, 32, 256, 16) == 0
+    assert f(32, 30, 4, 256, 32, 256, 16) == 0
+    assert f(32, 32, 4, 128, 32, 256, 16) == 0
+    assert f(32, 32, 4, 256, 0, 256, 16) == 0
+    assert f(32, 32, 4, 256, 32, 0, 16) == 0
+    assert f(32, 32, 4, 256, 32, 256, 24) == 0
+    n = f(32, 32, 4, 256, 32, 256, 16)
     # at least: E4M3 query codes, one bf16 partial row and two floats per partial
-    assert n >= 32 * 32 * 256 + 32 * 32 * 32 * (256 * 2 + 8)
+    assert n >= 32 * 32 * 256 + 32 * 32 * (256 * 2 + 8)
     assert n % 256 == 0
-    assert f(64, 32, 4, 256, 32) >= n
+    assert f(64, 32, 4, 256, 32, 256, 16) >= n
+    # one split over a table of one block: one partial
+    assert f(2, 16, 2, 256, 1, 1, 16) == 2 * 16 * 256 + 2 * 16 * 512 + 2 * 256

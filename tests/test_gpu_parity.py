@@ -271,7 +271,7 @@ def test_decode_query_strides_and_reuse_of_outputs():
     big[:, :, 256:] = ctx["q"].to(DEV)
     qv = big[:, :, 256:]
     o = torch.full((2, 16, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(uq.decode_workspace_bytes(2, 16, 2, 4), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(uq.decode_workspace_bytes(2, 16, 2, 4, ctx["table"].shape[1]), dtype=torch.uint8, device=DEV)
     uq.decode(qv, ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 4, out=o, workspace=ws)
     assert torch.equal(o, out)
 
