@@ -114,7 +114,7 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
       uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size);
   if (workspace_bytes < plan.total)
     return fail(UQ_EWORKSPACE, "uq_decode: workspace %zu bytes < required %zu", workspace_bytes, plan.total);
-  if ((long long)B * plan.parts * Hk > 0x7FFFFFFFLL)
+  if ((long long)B * plan.parts * Hk > 0x7FFFFFFFLL || (long long)B * Hq > 0x7FFFFFFFLL)
     return fail(UQ_EUNSUPPORTED, "uq_decode: grid too large");
   uq::DecodeArgs a{query, kv_cache, block_table, seq_lens, scale, out, num_blocks, block_size,
                    max_blocks_per_seq, q_stride_b, q_stride_h,

@@ -193,7 +193,10 @@ __device__ __forceinline__ void pv_tile(const Tile& T, const float sv[4], float 
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
   const uint32_t p01 = pack_bf16(p[0], p[1]);
   const uint32_t p23 = pack_bf16(p[2], p[3]);
-  l_part += (p[0] + p[1]) + (p[2] + p[3]);
+  // the denominator sums the same bf16 weights the product uses, so a
+  // dominant token passes through with weight exactly 1
+  l_part += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
+            (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
   const v4s pb = __builtin_bit_cast(v4s, make_uint2(p01, p23));
   float vscale[4];
   const int vsh = 8 * ((n16 >> 1) & 3);
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
-    int log2_bs, int max_blocks, int64_t num_blocks, uint16_t* __restrict__ part_o,
+    int log2_bs, int max_blocks, int64_t num_blocks, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
   static_assert(NSLOT == 3 || NSLOT == 4, "ring depth");
   // NSLOT-slot ring per wave; distinct arrays so that the compiler can tell
@@ -362,91 +365,68 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   }
   if (l_tot > 0.f) {
     const float inv = 1.f / l_tot;
-    uint16_t* op = part_o + stat * kHeadDim + 64 * grp;
+    float* op = part_o + stat * kHeadDim + 64 * grp;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 lo, hi;
-      lo.x = pack_bf16(acc[0][i] * inv, acc[1][i] * inv);
-      lo.y = pack_bf16(acc[2][i] * inv, acc[3][i] * inv);
-      lo.z = pack_bf16(acc[4][i] * inv, acc[5][i] * inv);
-      lo.w = pack_bf16(acc[6][i] * inv, acc[7][i] * inv);
-      hi.x = pack_bf16(acc[8][i] * inv, acc[9][i] * inv);
-      hi.y = pack_bf16(acc[10][i] * inv, acc[11][i] * inv);
-      hi.z = pack_bf16(acc[12][i] * inv, acc[13][i] * inv);
-      hi.w = pack_bf16(acc[14][i] * inv, acc[15][i] * inv);
-      reinterpret_cast<uint4*>(op + 16 * i)[0] = lo;
-      reinterpret_cast<uint4*>(op + 16 * i)[1] = hi;
+#pragma unroll
+      for (int j = 0; j < 16; j += 4)
+        *reinterpret_cast<float4*>(op + 16 * i + j) =
+            make_float4(acc[j][i] * inv, acc[j + 1][i] * inv, acc[j + 2][i] * inv, acc[j + 3][i] * inv);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Stage 2: out = sum_p w_p O_p / sum_p w_p with w_p = l_p 2^(m_p - max m),
-// over the partials with l_p > 0. Grid (B*Hq, D/64): one wave per 64-column
-// chunk; lane l reads columns 4*(l%16) .. +3 of the rows p = l/16 (mod 4), all
-// of them in flight at once, then the four row groups are summed across
-// lanes. The merge is per column, so the chunking changes no result bit.
+// over the partials with l_p > 0, in one pass with a running maximum (the sums
+// are rescaled when it rises). One wave per (sequence, query head) row; lane
+// l owns columns 4l .. 4l+3, so a float32 partial row is one coalesced 1 KB read,
+// and eight partial rows are in flight per lane. The statistics are uniform
+// across the wave, so the skip of empty partials is a uniform branch and
+// their (stale) rows are never touched by arithmetic.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void stage2_kernel(const uint16_t* __restrict__ part_o,
-                                                    const float* __restrict__ part_m,
-                                                    const float* __restrict__ part_l,
-                                                    uint16_t* __restrict__ out, int P) {
-  const size_t bh = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int rg = lane >> 4;                       // row group
-  const int col = blockIdx.y * 64 + 4 * (lane & 15);
-  const float* pm = part_m + bh * P;
-  const float* pl = part_l + bh * P;
-  float M = -INFINITY;
-  for (int p = lane; p < P; p += 64)
-    if (pl[p] > 0.f) M = fmaxf(M, pm[p]);
+__global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o,
+                                                     const float* __restrict__ part_m,
+                                                     const float* __restrict__ part_l,
+                                                     uint16_t* __restrict__ out, int rows, int P) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const float* pm = part_m + (size_t)row * P;
+  const float* pl = part_l + (size_t)row * P;
+  const float* po = part_o + (size_t)row * P * kHeadDim + 4 * lane;
+  float M = -INFINITY, den = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = 0; p0 < P; p0 += 8) {
+    float4 o[8];
+    float m[8], l[8];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
-  const uint16_t* po = part_o + bh * P * kHeadDim + col;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, den = 0.f;
-  for (int c = 0; c < P; c += 64) {
-    const int pj = c + lane;
-    const float lj = pj < P ? pl[pj] : 0.f;
-    const float wj = lj > 0.f ? lj * exp2f(pm[pj] - M) : 0.f;   // weight of partial c + lane
-    const int n = min(64, P - c);
-    for (int r0 = 0; r0 < n; r0 += 32) {
-      uint2 o[8];
-      float w[8];
+    for (int u = 0; u < 8; ++u) {
+      const int p = min(p0 + u, P - 1);
+      o[u] = *reinterpret_cast<const float4*>(po + (size_t)p * kHeadDim);
+      m[u] = pm[p];
+      l[u] = p0 + u < P ? pl[p] : 0.f;
+    }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {               // rows r0 + 4u + rg, eight in flight per lane
-        const int j = r0 + 4 * u + rg;
-        const int jc = min(j, n - 1);
-        const float wu = __shfl(wj, jc);
-        w[u] = j < n ? wu : 0.f;
-        o[u] = *reinterpret_cast<const uint2*>(po + (size_t)(c + jc) * kHeadDim);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        // empty partials (w = 0) hold stale rows: select, never multiply them
-        const bool use = w[u] > 0.f;
-        den += use ? w[u] : 0.f;
-        a0 += use ? w[u] * bf16_to_f32(o[u].x & 0xFFFF) : 0.f;
-        a1 += use ? w[u] * bf16_to_f32(o[u].x >> 16) : 0.f;
-        a2 += use ? w[u] * bf16_to_f32(o[u].y & 0xFFFF) : 0.f;
-        a3 += use ? w[u] * bf16_to_f32(o[u].y >> 16) : 0.f;
+    for (int u = 0; u < 8; ++u) {
+      if (l[u] > 0.f) {
+        const float Mn = fmaxf(M, m[u]);
+        const float c = exp2f(M - Mn);            // 0 for the first partial, <= 1 after
+        const float w = l[u] * exp2f(m[u] - Mn);
+        den = den * c + w;
+        a.x = a.x * c + w * o[u].x;
+        a.y = a.y * c + w * o[u].y;
+        a.z = a.z * c + w * o[u].z;
+        a.w = a.w * c + w * o[u].w;
+        M = Mn;
       }
     }
   }
-#pragma unroll
-  for (int m = 16; m <= 32; m <<= 1) {
-    den += __shfl_xor(den, m);
-    a0 += __shfl_xor(a0, m);
-    a1 += __shfl_xor(a1, m);
-    a2 += __shfl_xor(a2, m);
-    a3 += __shfl_xor(a3, m);
-  }
-  if (rg == 0) {
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint2 r;
-    r.x = pack_bf16(a0 * inv, a1 * inv);
-    r.y = pack_bf16(a2 * inv, a3 * inv);
-    *reinterpret_cast<uint2*>(out + bh * kHeadDim + col) = r;
-  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  uint2 r;
+  r.x = pack_bf16(a.x * inv, a.y * inv);
+  r.y = pack_bf16(a.z * inv, a.w * inv);
+  *reinterpret_cast<uint2*>(out + (size_t)row * kHeadDim + 4 * lane) = r;
 }
 
 int largest_divisor_upto(int n, int cap) {
@@ -504,7 +484,7 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_
   p.q8_off = off;
   off = align256(off + rows * kHeadDim);
   p.o_off = off;
-  off = align256(off + rows * p.parts * kHeadDim * sizeof(uint16_t));
+  off = align256(off + rows * p.parts * kHeadDim * sizeof(float));
   p.m_off = off;
   off = align256(off + rows * p.parts * sizeof(float));
   p.l_off = off;
@@ -516,7 +496,7 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mask,
                          hipStream_t stream) {
   uint8_t* q8 = a.workspace + p.q8_off;
-  uint16_t* part_o = reinterpret_cast<uint16_t*>(a.workspace + p.o_off);
+  float* part_o = reinterpret_cast<float*>(a.workspace + p.o_off);
   float* part_m = reinterpret_cast<float*>(a.workspace + p.m_off);
   float* part_l = reinterpret_cast<float*>(a.workspace + p.l_off);
   const int64_t vecs = (int64_t)p.B * p.Hq;
@@ -564,8 +544,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
 #undef UQ_STAGE1_HPW
 #undef UQ_STAGE1
   if (stage_mask & 4) {
-    hipLaunchKernelGGL(stage2_kernel, dim3((unsigned)vecs, kHeadDim / 64), dim3(64), 0, stream,
-                       part_o, part_m, part_l, a.out, p.parts);
+    hipLaunchKernelGGL(stage2_kernel, dim3((unsigned)((vecs + 3) / 4)), dim3(256), 0, stream,
+                       part_o, part_m, part_l, a.out, (int)vecs, p.parts);
     e = hipGetLastError();
   }
   return e;

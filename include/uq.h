@@ -97,7 +97,7 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
  * Bytes of device workspace uq_decode needs for this shape (0 on invalid
  * arguments). The analogue of the pooled segm_out / segm_max / segm_sum and
  * q_fp8 buffers of _SegmBufPool on the flydsl_ultraquant_decode page: query
- * E4M3 codes, one bf16 partial output and two float32 statistics per
+ * E4M3 codes, one float32 partial output row and two float32 statistics per
  * (sequence, query head, partial). The count of partials depends on the
  * split count and on the block-table capacity max_blocks_per_seq *
  * block_size, never on the sequence lengths, so one workspace serves every
@@ -149,7 +149,8 @@ int uq_decode(const uint16_t* query, const uint8_t* kv_cache,
 
 /*
  * Same as uq_decode, restricted to the stages named in stage_mask:
- * UQ_STAGE_PROLOGUE (query rotation + E4M3 into the workspace),
+ * UQ_STAGE_PROLOGUE (query rotation + E4M3 into the workspace: its first
+ * B*Hq*256 bytes then hold the E4M3 codes of q H, row b*Hq + hq),
  * UQ_STAGE_SPLIT (stage 1, reads the prologue's output) and UQ_STAGE_MERGE
  * (stage 2, reads stage 1's output). Running the three masks in that order on
  * one stream, with the same arguments and workspace, is exactly uq_decode;

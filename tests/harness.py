@@ -111,7 +111,9 @@ def check_close(got: np.ndarray, ref: np.ndarray, what: str, allow_output_roundi
     bound = MAX_ABS + (bf16_half_ulp(ref) if allow_output_rounding else 0.0)
     err = float(diff.max())
     rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
-    assert np.all(diff <= bound) and rel <= REL_L2, f"{what}: max-abs {err:.3e} rel-L2 {rel:.3e}"
+    worst = float(np.abs(ref).flat[int(np.argmax(diff))]) if diff.size else 0.0
+    assert np.all(diff <= bound) and rel <= REL_L2, \
+        f"{what}: max-abs {err:.3e} (at |ref| = {worst:.3f}) rel-L2 {rel:.3e}"
     return err, rel
 
 

@@ -109,9 +109,9 @@ def test_workspace_bytes(libuq):
     assert f(32, 32, 4, 256, 32, 0, 16) == 0
     assert f(32, 32, 4, 256, 32, 256, 24) == 0
     n = f(32, 32, 4, 256, 32, 256, 16)
-    # at least: E4M3 query codes, one bf16 partial row and two floats per partial
-    assert n >= 32 * 32 * 256 + 32 * 32 * (256 * 2 + 8)
+    # at least: E4M3 query codes, one float32 partial row and two floats per partial
+    assert n >= 32 * 32 * 256 + 32 * 32 * (256 * 4 + 8)
     assert n % 256 == 0
     assert f(64, 32, 4, 256, 32, 256, 16) >= n
     # one split over a table of one block: one partial
-    assert f(2, 16, 2, 256, 1, 1, 16) == 2 * 16 * 256 + 2 * 16 * 512 + 2 * 256
+    assert f(2, 16, 2, 256, 1, 1, 16) == 2 * 16 * 256 + 2 * 16 * 1024 + 2 * 256

@@ -149,6 +149,41 @@ def test_store_random_bulk():
     _store_and_compare(k, v, nb=200, bs=16)
 
 
+# ------------------------------------------------------------ query prologue
+def test_query_prologue_codes_bit_exact():
+    """The E4M3 codes of q H that the prologue leaves at the start of the
+    workspace equal the oracle's haircut value for value, with the sign of
+    codes that flush to zero: zeros, subnormal-range inputs that flush, saturation above 448,
+    and magnitudes spread over 26 binades (still exact in float64)."""
+    say("query prologue codes")
+    rng = np.random.default_rng(42)
+    B, Hk, qg = 3, 2, 8
+    Hq = Hk * qg
+    q = rng.standard_normal((B, Hq, 256))
+    q[0, 0] = 0.0                                            # all-zero vector
+    q[0, 1] = -0.0
+    q[0, 2] = rng.standard_normal(256) * 2.0 ** -20          # rounds to 0 / subnormals
+    q[0, 3] = rng.standard_normal(256) * 300.0               # saturates at 448
+    q[1, 0] = rng.choice([-1.0, 1.0], 256) * (1 + rng.random(256)) * np.exp2(rng.integers(-12, 13, 256))
+    q[1, 1, :] = 0.0
+    q[1, 1, 7] = 1.0                                         # one-hot: +-1/16 everywhere
+    q[2] *= 1e-2
+    qb = bf16(q)
+    tbl = torch.zeros((B, 1), dtype=torch.int32, device=DEV)
+    lens = torch.ones(B, dtype=torch.int32, device=DEV)
+    cache = torch.zeros((1, 16, Hk, 272), dtype=torch.uint8, device=DEV)
+    ws = torch.full((uq.decode_workspace_bytes(B, Hq, Hk, 1, 1),), 0x55, dtype=torch.uint8, device=DEV)
+    uq.decode(qb.to(DEV), cache, tbl, lens, 1 / 16, 1, workspace=ws, stages=uq.STAGE_PROLOGUE)
+    codes = ws[:B * Hq * 256].cpu()
+    got = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy().reshape(B, Hq, 256)
+    ref = O.query_haircut(bits(qb))
+    assert np.array_equal(got, ref), f"{(got != ref).sum()} codes differ"
+    # a non-zero product that rounds to zero keeps its sign; the sign of an
+    # exactly-zero product is not defined by the method and is not compared
+    nz = O.rotate(O.bf16_to_f64(bits(qb))) != 0
+    assert np.array_equal(np.signbit(got)[nz], np.signbit(ref)[nz]), "sign of a flushed code differs"
+
+
 # -------------------------------------------------------------------- decode
 def _decode_case(seq_lens, Hk, qg, bs=16, splits=4, seed=0, scale=1 / 16, q_scale=1.0,
                  k_gen=None):
