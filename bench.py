@@ -14,8 +14,9 @@ last >= 768 MB of traffic.
 
 Timing: HIP events on the stream the kernels run on. The host first queues a
 spin kernel, then all timed steps, so the GPU runs them back to back without
-waiting on Python. A second pass brackets stage 1 alone with events to give
-the dominant kernel's duration for the roofline.
+waiting on Python. A second pass times each of the three kernels alone, as
+back-to-back launches, which gives the dominant kernel's duration for the
+roofline.
 """
 import argparse
 import json
@@ -40,8 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (reference for "
-                         "scaling the profiler's byte counters)")
+                    help="also run one plain streaming kernel (int32 bitwise_not) that reads and "
+                         "writes this many MiB: the reference that scales the profiler's byte "
+                         "counters")
     return ap.parse_args()
 
 
@@ -105,24 +107,47 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup):
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
 
-    # pass 2: stage 1 bracketed by events, prologue and merge outside
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    busy()
-    for i in range(steps):
-        a, b, c, d = ev[i]
+    # pass 2: each kernel on its own, `steps` back-to-back launches between two
+    # events on the decode stream, so that the average is the kernel's own
+    # duration (what a kernel trace reports). Stage 1 reads the prologue's
+    # query codes (the same for every cache copy) and stage 2 the partials of
+    # the last stage 1, so repeating one stage is well defined.
+    def alone(stage):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        busy()
         a.record()
-        uq.decode(*args(i), out=out, workspace=ws, stages=uq.STAGE_PROLOGUE)
+        for i in range(steps):
+            uq.decode(*args(i), out=out, workspace=ws, stages=stage)
         b.record()
-        uq.decode(*args(i), out=out, workspace=ws, stages=uq.STAGE_SPLIT)
-        c.record()
-        uq.decode(*args(i), out=out, workspace=ws, stages=uq.STAGE_MERGE)
-        d.record()
-    torch.cuda.synchronize()
-    pro = sum(x[0].elapsed_time(x[1]) for x in ev) / steps
-    st1 = sum(x[1].elapsed_time(x[2]) for x in ev) / steps
-    st2 = sum(x[2].elapsed_time(x[3]) for x in ev) / steps
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    pro = alone(uq.STAGE_PROLOGUE)
+    st1 = alone(uq.STAGE_SPLIT)
+    st2 = alone(uq.STAGE_MERGE)
     return step_ms, pro, st1, st2
+
+
+STAGE1_SOURCE = os.path.join(ROOT, "decode_attention_bit_amd", "csrc", "uq_decode.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "stage1_decode_traffic.md")
+
+
+def recorded_traffic(workload):
+    """HBM bytes per stage-1 launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the reference kernel), or None when
+    there is none for this workload or the kernel source has changed since."""
+    import hashlib
+    import re
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    text = open(TRAFFIC_RECORD).read()
+    m = re.search(r"^record: workload=(\S+) source_sha256=([0-9a-f]{64}) fetch_bytes=(\d+) "
+                  r"write_bytes=(\d+)$", text, re.M)
+    if not m or m.group(1) != workload:
+        return None
+    if hashlib.sha256(open(STAGE1_SOURCE, "rb").read()).hexdigest() != m.group(2):
+        return None
+    return int(m.group(3)) + int(m.group(4))
 
 
 def cpu_baseline(w, lay, seconds):
@@ -172,11 +197,12 @@ def main():
     kv_bytes = inputs.kv_bytes(w, lay)
     if args.copy_ref_mib > 0:
         n = args.copy_ref_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"reference copy: {n} bytes read, {n} bytes written")
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"reference kernel bitwise_not: {n} bytes read, {n} bytes written")
         del src, dst
     log(f"timing {args.steps} steps ({len(caches)} cache copies)")
     step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup)
@@ -205,7 +231,7 @@ def main():
         "stage_ms": {"prologue": round(pro_ms, 5), "split_kv": round(st1_ms, 5), "merge": round(st2_ms, 5)},
         "cache_copies": len(caches),
         "roofline": {"bound": "hbm", "achieved": round(st1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(st1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(st1_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
                      "kernel": "stage1_kernel (split-KV)", "bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:
