@@ -86,12 +86,18 @@ constexpr int kTileChunks = 17 * kTile;          // 272
 constexpr int kTileU4 = kTileChunks;             // uint4 per tile in LDS
 constexpr int kDmaPerTile = 5;                   // ceil(272 / 64)
 
+// Block-table entries e0 .. e0 + 63 of the wave's range sit one per lane in
+// `btv`, loaded once; an entry past them (ranges of more than 64 blocks) is
+// read from memory when its tile is issued.
 __device__ __forceinline__ int issue_tile(uint4* dst, const uint8_t* __restrict__ cache,
-                                           const int32_t* __restrict__ bt, int t, int L,
-                                           int log2_bs, int64_t num_blocks, uint32_t row, int h,
-                                           int lane, const uint32_t goff[kDmaPerTile]) {
+                                           const int32_t* __restrict__ bt, int btv, int e0,
+                                           int t, int L, int log2_bs, int64_t num_blocks,
+                                           uint32_t row, int h, int lane,
+                                           const uint32_t goff[kDmaPerTile]) {
   const int tok0 = t * kTile;
-  const int phys = __builtin_amdgcn_readfirstlane(bt[tok0 >> log2_bs]);
+  const int entry = tok0 >> log2_bs;
+  const int phys = entry - e0 < 64 ? __builtin_amdgcn_readlane(btv, entry - e0)
+                                   : __builtin_amdgcn_readfirstlane(bt[entry]);
   const bool ok = phys >= 0 && (int64_t)phys < num_blocks;
   const int nvalid = ok ? min(kTile, L - tok0) : 0;
   const size_t tile_off =
@@ -112,6 +118,21 @@ __device__ __forceinline__ int issue_tile(uint4* dst, const uint8_t* __restrict_
 
 // s_waitcnt on vector memory only (gfx9 encoding; expcnt and lgkmcnt left free)
 #define UQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+
+// Wait until at most min(K, ahead) tiles (kDmaPerTile loads each) are still
+// in flight: the waitcnt immediate must be a constant, so pick it by cases.
+template <int K>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  if constexpr (K == 0) {
+    UQ_WAIT_VMCNT(0);
+  } else {
+    if (ahead >= K) {
+      UQ_WAIT_VMCNT(K * kDmaPerTile);
+    } else {
+      wait_tiles_ahead<K - 1>(ahead);
+    }
+  }
+}
 
 // Operands of one staged tile (slot stride 272 bytes).
 __device__ __forceinline__ void read_tile(Tile& T, const uint4* __restrict__ src, int n16, int grp,
@@ -219,13 +240,14 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
     int log2_bs, int max_blocks, int64_t num_blocks, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
-  static_assert(NSLOT == 3 || NSLOT == 4, "ring depth");
+  static_assert(NSLOT >= 3 && NSLOT <= 8, "ring depth");
+  static_assert(NSLOT * HPW * kTileU4 * 16 <= 160 * 1024, "ring exceeds the LDS of a CU");
   // NSLOT-slot ring per wave; distinct arrays so that the compiler can tell
   // the slot being read from the slots being filled
-  __shared__ uint4 ring0[HPW][kTileU4];
-  __shared__ uint4 ring1[HPW][kTileU4];
-  __shared__ uint4 ring2[HPW][kTileU4];
-  __shared__ uint4 ring3[NSLOT > 3 ? HPW : 1][NSLOT > 3 ? kTileU4 : 1];
+#define UQ_RING_DECL(K) __shared__ uint4 ring##K[NSLOT > K ? HPW : 1][NSLOT > K ? kTileU4 : 1];
+  UQ_RING_DECL(0) UQ_RING_DECL(1) UQ_RING_DECL(2) UQ_RING_DECL(3)
+  UQ_RING_DECL(4) UQ_RING_DECL(5) UQ_RING_DECL(6) UQ_RING_DECL(7)
+#undef UQ_RING_DECL
 
   int x = blockIdx.x;
   const int hg = x % hgroups;
@@ -236,22 +258,36 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = hg * HPW + wave;
 
-  int L = seq_lens[b];
-  const int Lmax = max_blocks << log2_bs;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  // The partial's first tile does not depend on the sequence length, so the
+  // length, the block-table entries and the query codes are all requested
+  // before any of them is waited for.
   // Split s covers tiles [s*cs, (s+1)*cs) of the sequence (cs from the table
   // capacity, so that every split is the same size). A partial covers either
   // spw consecutive splits or one of nsub equal pieces of one split.
-  const int n_tiles = (L + kTile - 1) / kTile;
   const int g_lo = (part / nsub) * spw * cs;
-  const int g_hi = min(g_lo + spw * cs, n_tiles);
   const int sub_len = (spw * cs + nsub - 1) / nsub;
   const int u0 = g_lo + (part % nsub) * sub_len;
-  const int u1 = min(u0 + sub_len, g_hi);
-
   const int n16 = lane & 15, grp = lane >> 4;
   const bool qlane = n16 < QG;
   const int hq = h * QG + (qlane ? n16 : 0);
+  v8i qb0 = {0, 0, 0, 0, 0, 0, 0, 0}, qb1 = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (qlane) {
+    const uint8_t* qp = q8 + ((size_t)b * Hq + hq) * kHeadDim;
+    const uint4 x0 = ld16(qp + 16 * grp), x1 = ld16(qp + 64 + 16 * grp);
+    const uint4 x2 = ld16(qp + 128 + 16 * grp), x3 = ld16(qp + 192 + 16 * grp);
+    qb0 = (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    qb1 = (v8i){(int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w, (int)x3.x, (int)x3.y, (int)x3.z, (int)x3.w};
+  }
+  const int32_t* bt = block_table + (size_t)b * max_blocks;
+  const int e0 = (u0 * kTile) >> log2_bs;
+  const int btv = e0 + lane < max_blocks ? bt[e0 + lane] : 0;
+  int L = seq_lens[b];
+
+  const int Lmax = max_blocks << log2_bs;
+  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  const int n_tiles = (L + kTile - 1) / kTile;
+  const int g_hi = min(g_lo + spw * cs, n_tiles);
+  const int u1 = min(u0 + sub_len, g_hi);
   const size_t stat = ((size_t)b * Hq + hq) * P + part;
 
   if (u0 >= u1) {
@@ -262,18 +298,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     return;
   }
 
-  // q8 first, so that waiting for it never waits for the tile loads behind it
-  v8i qb0 = {0, 0, 0, 0, 0, 0, 0, 0}, qb1 = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (qlane) {
-    const uint8_t* qp = q8 + ((size_t)b * Hq + hq) * kHeadDim;
-    const uint4 x0 = ld16(qp + 16 * grp), x1 = ld16(qp + 64 + 16 * grp);
-    const uint4 x2 = ld16(qp + 128 + 16 * grp), x3 = ld16(qp + 192 + 16 * grp);
-    qb0 = (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    qb1 = (v8i){(int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w, (int)x3.x, (int)x3.y, (int)x3.z, (int)x3.w};
-  }
-
   const uint32_t row = (uint32_t)Hk * kSlotBytes;
-  const int32_t* bt = block_table + (size_t)b * max_blocks;
   uint32_t goff[kDmaPerTile];                 // chunk c -> token c / 17, 16 bytes (c % 17)
 #pragma unroll
   for (int k = 0; k < kDmaPerTile; ++k) {
@@ -281,7 +306,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     goff[k] = (c / 17) * row + (c % 17) * 16;
   }
   auto issue = [&](uint4* slot, int t) {
-    return issue_tile(slot, cache, bt, t, L, log2_bs, num_blocks, row, h, lane, goff);
+    return issue_tile(slot, cache, bt, btv, e0, t, L, log2_bs, num_blocks, row, h, lane, goff);
   };
 
   // Softmax reference: the first tile's maximum. The weights 2^(s - m_ref)
@@ -306,16 +331,17 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     int t_stop = 0;
     // valid-token count of the tile in each slot, known when it is issued
     int nv_ring0 = issue(ring0[wave], t0), nv_ring1 = 0, nv_ring2 = 0, nv_ring3 = 0;
-    if (t0 + 1 < u1) nv_ring1 = issue(ring1[wave], t0 + 1);
-    if (NSLOT > 3 && t0 + 2 < u1) nv_ring2 = issue(ring2[wave], t0 + 2);
+    int nv_ring4 = 0, nv_ring5 = 0, nv_ring6 = 0, nv_ring7 = 0;
+#define UQ_PRE(K) \
+    if constexpr (NSLOT > K + 1) { if (t0 + K < u1) nv_ring##K = issue(ring##K[wave], t0 + K); }
+    UQ_PRE(1) UQ_PRE(2) UQ_PRE(3) UQ_PRE(4) UQ_PRE(5) UQ_PRE(6)
+#undef UQ_PRE
     // Step t: tiles t .. t + NSLOT - 2 are in flight. Wait for tile t (the
     // later ones may stay pending), read it, start tile t + NSLOT - 1 into the
     // slot tile t - 1 used (already consumed), then compute tile t.
 #define UQ_STEP(CUR, NXT)                                                        \
     {                                                                            \
-      if (NSLOT > 3 && t + 2 < u1) { UQ_WAIT_VMCNT(2 * kDmaPerTile); }           \
-      else if (t + 1 < u1) { UQ_WAIT_VMCNT(kDmaPerTile); }                       \
-      else { UQ_WAIT_VMCNT(0); }                                                 \
+      wait_tiles_ahead<NSLOT - 2>(u1 - 1 - t);                                   \
       read_tile(T, CUR[wave], n16, grp, nv_##CUR);                               \
       if (t + NSLOT - 1 < u1) nv_##NXT = issue(NXT[wave], t + NSLOT - 1);        \
       qk_tile(T, qb0, qb1, scale_log2, grp, sv, mt);                             \
@@ -324,18 +350,33 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
       if (T.nvalid > 0) pv_tile(T, sv, m_ref, n16, acc, l_part);                 \
       if (++t >= u1) break;                                                      \
     }
-    if (NSLOT == 3) {
+    if constexpr (NSLOT == 3) {
       for (int t = t0;;) {
-        UQ_STEP(ring0, ring2)
-        UQ_STEP(ring1, ring0)
-        UQ_STEP(ring2, ring1)
+        UQ_STEP(ring0, ring2) UQ_STEP(ring1, ring0) UQ_STEP(ring2, ring1)
+      }
+    } else if constexpr (NSLOT == 4) {
+      for (int t = t0;;) {
+        UQ_STEP(ring0, ring3) UQ_STEP(ring1, ring0) UQ_STEP(ring2, ring1) UQ_STEP(ring3, ring2)
+      }
+    } else if constexpr (NSLOT == 5) {
+      for (int t = t0;;) {
+        UQ_STEP(ring0, ring4) UQ_STEP(ring1, ring0) UQ_STEP(ring2, ring1) UQ_STEP(ring3, ring2)
+        UQ_STEP(ring4, ring3)
+      }
+    } else if constexpr (NSLOT == 6) {
+      for (int t = t0;;) {
+        UQ_STEP(ring0, ring5) UQ_STEP(ring1, ring0) UQ_STEP(ring2, ring1) UQ_STEP(ring3, ring2)
+        UQ_STEP(ring4, ring3) UQ_STEP(ring5, ring4)
+      }
+    } else if constexpr (NSLOT == 7) {
+      for (int t = t0;;) {
+        UQ_STEP(ring0, ring6) UQ_STEP(ring1, ring0) UQ_STEP(ring2, ring1) UQ_STEP(ring3, ring2)
+        UQ_STEP(ring4, ring3) UQ_STEP(ring5, ring4) UQ_STEP(ring6, ring5)
       }
     } else {
       for (int t = t0;;) {
-        UQ_STEP(ring0, ring3)
-        UQ_STEP(ring1, ring0)
-        UQ_STEP(ring2, ring1)
-        UQ_STEP(ring3, ring2)
+        UQ_STEP(ring0, ring7) UQ_STEP(ring1, ring0) UQ_STEP(ring2, ring1) UQ_STEP(ring3, ring2)
+        UQ_STEP(ring4, ring3) UQ_STEP(ring5, ring4) UQ_STEP(ring6, ring5) UQ_STEP(ring7, ring6)
       }
     }
 #undef UQ_STEP
@@ -448,7 +489,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #ifndef UQ_TILES_PER_WAVE_MAX
 #define UQ_TILES_PER_WAVE_MAX 64
 #endif
-constexpr int kRingSlots = UQ_RING_SLOTS;
+// Ring depth per wave: as deep as the LDS of one CU allows for the
+// workgroup's HPW waves (4352 bytes per slot), capped at UQ_RING_SLOTS.
+constexpr int ring_slots(int hpw) {
+  return (160 * 1024) / (hpw * kTileU4 * 16) < UQ_RING_SLOTS ? (160 * 1024) / (hpw * kTileU4 * 16)
+                                                              : UQ_RING_SLOTS;
+}
 constexpr long kTilesPerWaveMin = 4;
 
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
@@ -517,7 +563,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   const dim3 grid1((unsigned)((int64_t)p.B * p.parts * hgroups));
   const dim3 block1(64 * hpw);
 #define UQ_STAGE1(QGV, HPWV)                                                                     \
-  hipLaunchKernelGGL((stage1_kernel<QGV, HPWV, kRingSlots>), grid1, block1, 0, stream, q8,       \
+  hipLaunchKernelGGL((stage1_kernel<QGV, HPWV, ring_slots(HPWV)>), grid1, block1, 0, stream, q8,       \
                      a.cache, a.block_table, a.seq_lens, scale_log2, p.Hq, p.Hk, hgroups,      \
                      p.cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,          \
                      a.num_blocks, part_o, part_m, part_l)
