@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--workload", default="decode",
+                    help="decode (the default line), or tiny / ragged / long / mixed; mixed times a "
+                         "store of one token per sequence together with the decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -81,7 +83,27 @@ def busy():
     torch.cuda._sleep(20_000_000)
 
 
-def gpu_time(w, lay, q, caches, bt, sl, steps, warmup):
+def serving_store(w, lay, dev):
+    """The mixed serving step also stores one new token per sequence: the
+    keys and values of each sequence's last token and their slots (the cache
+    already holds them, so repeating the store leaves it unchanged)."""
+    import numpy as np
+    import torch
+
+    from decode_attention_bit_amd import inputs
+
+    ks, vs, slots = [], [], []
+    for b in range(w.B):
+        L = int(lay.seq_lens[b])
+        k, v = inputs.make_kv(w, lay, b, L - 1, L)
+        ks.append(k)
+        vs.append(v)
+        slots.append(inputs.slots_for(lay, b, L - 1, L))
+    return (torch.cat(ks).to(dev), torch.cat(vs).to(dev),
+            torch.from_numpy(np.concatenate(slots)).to(dev))
+
+
+def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None):
     import torch
 
     import decode_attention_bit_amd as uq
@@ -93,8 +115,13 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup):
     R = len(caches)
     args = lambda i: (q, caches[i % R], bt, sl, w.scale, w.num_kv_splits)
 
-    for i in range(warmup):
+    def step(i):
+        if store_args is not None:
+            uq.store(store_args[0], store_args[1], caches[i % R], store_args[2])
         uq.decode(*args(i), out=out, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
 
     # pass 1: whole steps
@@ -102,7 +129,7 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup):
     busy()                                   # keep the GPU busy while the host queues the steps
     e0.record()
     for i in range(steps):
-        uq.decode(*args(i), out=out, workspace=ws)
+        step(i)
     e1.record()
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
@@ -205,7 +232,9 @@ def main():
         log(f"reference kernel bitwise_not: {n} bytes read, {n} bytes written")
         del src, dst
     log(f"timing {args.steps} steps ({len(caches)} cache copies)")
-    step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup)
+    store_args = serving_store(w, lay, dev) if w.name == "mixed" else None
+    step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup,
+                                               store_args)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
     st1_gbs = kv_bytes / (st1_ms * 1e-3) / 1e9
     res = {
@@ -223,7 +252,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} Hq={w.Hq} Hk={w.Hk} D={w.D} "
                                f"seq_len={int(lay.seq_lens.max())} block_size={w.block_size} "
-                               f"num_kv_splits={w.num_kv_splits}",
+                               f"num_kv_splits={w.num_kv_splits}"
+                               + (" (step = store of one token per sequence + decode)"
+                                  if store_args is not None else ""),
                    "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "block_size": w.block_size,
                    "num_kv_splits": w.num_kv_splits, "kv_bytes_per_step": kv_bytes},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

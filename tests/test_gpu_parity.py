@@ -329,3 +329,61 @@ def test_decode_split_count_invariance():
     for S in (2, 8, 32, 64, 128, 512):
         o = uq.decode(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], S)
         check_close(to_np(o), ref, f"S={S}")
+
+
+# ------------------------------------------------------------- graph capture
+def test_store_and_decode_replay_in_hip_graph():
+    """Neither entry point allocates or synchronises, so a store + decode step
+    can be captured once and replayed: every replay, with new inputs copied in
+    place and eager work in between, equals the same step run eagerly."""
+    say("graph capture")
+    rng = np.random.default_rng(77)
+    B, Hk, qg, bs, width = 4, 2, 8, 16, 12
+    Hq = Hk * qg
+    nb = B * width
+    table = torch.from_numpy(rng.permutation(nb).reshape(B, width).astype(np.int32)).to(DEV)
+    lens = torch.tensor([150, 33, 190, 77], dtype=torch.int32, device=DEV)
+    cache = torch.zeros((nb, bs, Hk, 272), dtype=torch.uint8, device=DEV)
+    for b in range(B):                      # prefix of each sequence, stored eagerly
+        L = int(lens[b])
+        t = torch.arange(L, device=DEV)
+        slots = table[b, t // bs].long() * bs + t % bs
+        uq.store(bf16(rng.standard_normal((L, Hk, 256))).to(DEV), bf16(rng.standard_normal((L, Hk, 256))).to(DEV),
+                 cache, slots)
+    last = lens.long() - 1                  # each step rewrites the last token of every sequence
+    slots_new = table[torch.arange(B, device=DEV), last // bs].long() * bs + last % bs
+    q = torch.empty((B, Hq, 256), dtype=torch.bfloat16, device=DEV)
+    k_new = torch.empty((B, Hk, 256), dtype=torch.bfloat16, device=DEV)
+    v_new = torch.empty_like(k_new)
+    out = torch.empty((B, Hq, 256), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(uq.decode_workspace_bytes(B, Hq, Hk, 4, width), dtype=torch.uint8, device=DEV)
+
+    def fill(i):
+        r = np.random.default_rng(1000 + i)
+        q.copy_(bf16(r.standard_normal((B, Hq, 256))).to(DEV))
+        k_new.copy_(bf16(r.standard_normal((B, Hk, 256))).to(DEV))
+        v_new.copy_(bf16(r.standard_normal((B, Hk, 256))).to(DEV))
+
+    def step(c, o, w):
+        uq.store(k_new, v_new, c, slots_new)
+        uq.decode(q, c, table, lens, 1 / 16, 4, out=o, workspace=w)
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up off the default stream, as capture requires
+        step(cache, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(cache, out, ws)
+    for i in range(1, 6):
+        fill(i)
+        ref_cache = cache.clone()
+        ref_out = torch.empty_like(out)
+        step(ref_cache, ref_out, torch.empty_like(ws))     # eager reference
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cache, ref_cache), f"replay {i}: cache differs"
+        assert torch.equal(out, ref_out), f"replay {i}: output differs"
