@@ -555,7 +555,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
     if (e != hipSuccess) return e;
   }
 
-  const int hpw = largest_divisor_upto(p.Hk, 8);
+  // KV heads per workgroup (one wave each). Reading all heads of a token row
+  // on one CU shares its cache lines, which is what four heads per workgroup
+  // buy at Hk = 4. At Hk = 8, measured on ragged lengths, workgroups of two
+  // heads schedule better than one eight-wave workgroup per CU.
+  const int hpw = largest_divisor_upto(p.Hk, p.Hk >= 8 ? 2 : 4);
   const int hgroups = p.Hk / hpw;
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
