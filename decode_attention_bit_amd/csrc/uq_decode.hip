@@ -236,7 +236,8 @@ __device__ __forceinline__ void pv_tile(const Tile& T, const float sv[4], float 
 template <int QG, int HPW, int NSLOT>
 __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ cache,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ query_row, int n_rows,
+    const int32_t* __restrict__ seq_lens,
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
     int log2_bs, int max_blocks, int64_t num_blocks, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
@@ -278,10 +279,14 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     qb0 = (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     qb1 = (v8i){(int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w, (int)x3.x, (int)x3.y, (int)x3.z, (int)x3.w};
   }
-  const int32_t* bt = block_table + (size_t)b * max_blocks;
+  // Query row b reads block-table row query_row[b] (its own row when there
+  // is no mapping); a row outside the table reads as an empty sequence.
+  const int trow = query_row ? query_row[b] : b;
+  const bool row_ok = trow >= 0 && trow < n_rows;
+  const int32_t* bt = block_table + (size_t)(row_ok ? trow : 0) * max_blocks;
   const int e0 = (u0 * kTile) >> log2_bs;
-  const int btv = e0 + lane < max_blocks ? bt[e0 + lane] : 0;
-  int L = seq_lens[b];
+  const int btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
+  int L = row_ok ? seq_lens[b] : 0;
 
   const int Lmax = max_blocks << log2_bs;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
@@ -568,7 +573,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   const dim3 block1(64 * hpw);
 #define UQ_STAGE1(QGV, HPWV)                                                                     \
   hipLaunchKernelGGL((stage1_kernel<QGV, HPWV, ring_slots(HPWV)>), grid1, block1, 0, stream, q8,       \
-                     a.cache, a.block_table, a.seq_lens, scale_log2, p.Hq, p.Hk, hgroups,      \
+                     a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens, scale_log2,    \
+                     p.Hq, p.Hk, hgroups,                                                      \
                      p.cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,          \
                      a.num_blocks, part_o, part_m, part_l)
 #define UQ_STAGE1_HPW(QGV)                      \

@@ -32,6 +32,8 @@ struct DecodeArgs {
   const uint16_t* query;
   const uint8_t* cache;
   const int32_t* block_table;
+  const int32_t* query_row;   // (B,) block-table row of each query, or null: row b
+  int n_rows;                 // rows in block_table
   const int32_t* seq_lens;
   float scale;
   uint16_t* out;

@@ -321,6 +321,41 @@ def test_decode_stage_masks_compose():
     assert torch.equal(o, out)
 
 
+def test_decode_multi_query_continuation_chunks():
+    """Continuation chunks, decoded one query at a time as the ultraquant_attn
+    page does for short chunks: query i of a chunk over a sequence holding
+    cached_len tokens attends to cached_len + i + 1 tokens through the
+    sequence's block-table row. The oracle is given that row repeated per
+    query; the library gets the compact table and a row index per query."""
+    say("decode multi-query")
+    cached, chunk = [40, 200, 0, 17], [3, 1, 4, 2]
+    full = [c + n for c, n in zip(cached, chunk)]
+    _, _, ctx = _decode_case(full, Hk=2, qg=8, splits=4, seed=21)
+    rows = np.concatenate([np.full(n, s) for s, n in enumerate(chunk)]).astype(np.int32)
+    lens = np.concatenate([c + 1 + np.arange(n) for c, n in zip(cached, chunk)]).astype(np.int32)
+    T = len(rows)
+    rng = np.random.default_rng(22)
+    q = bf16(rng.standard_normal((T, 16, 256)))
+    table = ctx["table"]
+    q_dev, rows_dev, lens_dev = q.to(DEV), torch.from_numpy(rows).to(DEV), torch.from_numpy(lens).to(DEV)
+    for S in (1, 4, 16):
+        out = uq.decode_multi(q_dev, ctx["cache"], table, rows_dev, lens_dev, ctx["scale"], S)
+        ref = O.decode(bits(q), ctx["ref_cache"], table.cpu().numpy()[rows], lens, ctx["scale"])
+        check_close(to_np(out), ref, f"multi-query S={S}")
+        # the same as decoding against the table with each row repeated
+        rep = uq.decode(q_dev, ctx["cache"], table[rows_dev.long()].contiguous(), lens_dev,
+                        ctx["scale"], S)
+        assert torch.equal(out, rep), f"S={S}: differs from the repeated-row decode"
+    # a row index outside the table reads as an empty sequence
+    bad = rows_dev.clone()
+    bad[0], bad[-1] = -1, len(full)
+    out = uq.decode_multi(q_dev, ctx["cache"], table, bad, lens_dev, ctx["scale"], 4)
+    o = to_np(out)
+    assert np.all(o[0] == 0) and np.all(o[-1] == 0)
+    ref = O.decode(bits(q), ctx["ref_cache"], table.cpu().numpy()[rows], lens, ctx["scale"])
+    check_close(o[1:-1], ref[1:-1], "multi-query, valid rows")
+
+
 def test_decode_split_count_invariance():
     say("decode split invariance")
     out, ref, ctx = _decode_case([2000, 1500, 777], Hk=4, qg=8, splits=1, seed=11)
