@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     help="decode (the default line), or tiny / ragged / long / mixed; mixed times a "
                          "store of one token per sequence together with the decode")
+    ap.add_argument("--queries-per-seq", type=int, default=1,
+                    help="decode this many query rows per sequence (a speculative step), each "
+                         "reading its own prefix, through uq_decode_multi")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -103,22 +106,46 @@ def serving_store(w, lay, dev):
             torch.from_numpy(np.concatenate(slots)).to(dev))
 
 
-def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None):
+def multi_query(w, lay, qps, dev):
+    """qps query rows per sequence, as a speculative step verifying qps
+    tokens: row i of sequence b attends to L_b - qps + 1 + i tokens through
+    the sequence's block-table row. Returns the queries, the row of each
+    query and its length."""
+    import numpy as np
+    import torch
+
+    from decode_attention_bit_amd import inputs
+
+    rng = np.random.default_rng([w.seed, 4])
+    qm = inputs.to_bf16(rng.standard_normal((w.B * qps, w.Hq, w.D), dtype=np.float32)).to(dev)
+    rows = np.repeat(np.arange(w.B), qps).astype(np.int32)
+    lens = (lay.seq_lens[rows].astype(np.int64) - qps + 1 + np.tile(np.arange(qps), w.B)).astype(np.int32)
+    return qm, torch.from_numpy(rows).to(dev), torch.from_numpy(lens).to(dev)
+
+
+def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=None):
     import torch
 
     import decode_attention_bit_amd as uq
 
     dev = q.device
-    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(uq.decode_workspace_bytes(w.B, w.Hq, w.Hk, w.num_kv_splits, bt.shape[1], w.block_size),
+    if multi is not None:                    # query rows, their table rows, their lengths
+        q, rows, sl = multi
+        bt_rep = bt[rows.long()].contiguous()  # the same rows repeated, for the per-kernel pass
+    nq = q.shape[0]
+    out = torch.empty((nq, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(uq.decode_workspace_bytes(nq, w.Hq, w.Hk, w.num_kv_splits, bt.shape[1], w.block_size),
                      dtype=torch.uint8, device=dev)
     R = len(caches)
-    args = lambda i: (q, caches[i % R], bt, sl, w.scale, w.num_kv_splits)
+    args = lambda i: (q, caches[i % R], bt if multi is None else bt_rep, sl, w.scale, w.num_kv_splits)
 
     def step(i):
         if store_args is not None:
             uq.store(store_args[0], store_args[1], caches[i % R], store_args[2])
-        uq.decode(*args(i), out=out, workspace=ws)
+        if multi is None:
+            uq.decode(*args(i), out=out, workspace=ws)
+        else:
+            uq.decode_multi(q, caches[i % R], bt, rows, sl, w.scale, w.num_kv_splits, out=out, workspace=ws)
 
     for i in range(warmup):
         step(i)
@@ -233,8 +260,12 @@ def main():
         del src, dst
     log(f"timing {args.steps} steps ({len(caches)} cache copies)")
     store_args = serving_store(w, lay, dev) if w.name == "mixed" else None
+    multi = multi_query(w, lay, args.queries_per_seq, dev) if args.queries_per_seq > 1 else None
+    # every query row of uq_decode_multi reads its own prefix: the logical
+    # bytes count each read, the value counts each cache byte once
+    logical_bytes = (int(multi[2].long().sum()) * w.Hk * inputs.SLOT_BYTES) if multi is not None else kv_bytes
     step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup,
-                                               store_args)
+                                               store_args, multi)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
     st1_gbs = kv_bytes / (st1_ms * 1e-3) / 1e9
     res = {
@@ -254,11 +285,14 @@ def main():
                                f"seq_len={int(lay.seq_lens.max())} block_size={w.block_size} "
                                f"num_kv_splits={w.num_kv_splits}"
                                + (" (step = store of one token per sequence + decode)"
-                                  if store_args is not None else ""),
+                                  if store_args is not None else "")
+                               + (f" ({args.queries_per_seq} query rows per sequence, "
+                                  f"uq_decode_multi)" if multi is not None else ""),
                    "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "block_size": w.block_size,
-                   "num_kv_splits": w.num_kv_splits, "kv_bytes_per_step": kv_bytes},
+                   "num_kv_splits": w.num_kv_splits, "kv_bytes_per_step": kv_bytes,
+                   "logical_kv_bytes_per_step": logical_bytes},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(w.B / (step_ms * 1e-3), 1),
+        "tokens_per_s": round(w.B * max(1, args.queries_per_seq) / (step_ms * 1e-3), 1),
         "stage_ms": {"prologue": round(pro_ms, 5), "split_kv": round(st1_ms, 5), "merge": round(st2_ms, 5)},
         "cache_copies": len(caches),
         "roofline": {"bound": "hbm", "achieved": round(st1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
