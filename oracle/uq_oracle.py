@@ -304,26 +304,39 @@ def gather_sequence(kv_cache: np.ndarray, block_row: np.ndarray, L: int, h: int)
     return decode_slots(kv_cache[phys, t % bs, h])
 
 
-def attention(q8: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+def attention(q8: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, sinks=None) -> np.ndarray:
     """softmax(scale * q8 K^T) V over all tokens, float64; q8 (G, 256).
 
     The decode query is the last position and seq_lens counts it, so no mask.
     Scores use the rotated K directly: (qH).(kH) = q.k because H is orthonormal
     ([UQ-impl] continuation prefill: rotating both sides leaves scores
     unchanged).
+
+    ``sinks`` (G,) are per-head sink logits ([UQ-impl] passes ``self.sinks``
+    to the unified attention kernel; this build's reading, as in attention
+    with sinks: one more logit per head in the softmax normaliser, with no
+    value behind it, in the units of the scaled scores).
     """
     s = scale * (q8 @ K.T)
-    s = s - s.max(axis=-1, keepdims=True)
-    p = np.exp(s)
-    p /= p.sum(axis=-1, keepdims=True)
-    return p @ V
+    if sinks is None:
+        m = s.max(axis=-1, keepdims=True)
+        p = np.exp(s - m)
+        return (p @ V) / p.sum(axis=-1, keepdims=True)
+    sk = np.asarray(sinks, dtype=np.float64)[:, None]
+    m = np.maximum(s.max(axis=-1, keepdims=True) if s.shape[-1] else -np.inf, sk)
+    p = np.exp(s - m)
+    return (p @ V) / (p.sum(axis=-1, keepdims=True) + np.exp(sk - m))
 
 
-def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None) -> np.ndarray:
+def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None, sinks=None,
+           sliding_window=0) -> np.ndarray:
     """Reference output (B, Hq, 256) float64, single softmax per query head.
 
     ``pairs`` optionally restricts the work to a list of (b, kv_head); other
-    rows are left NaN.
+    rows are left NaN. ``sinks`` (Hq,) are per-query-head sink logits (see
+    ``attention``). ``sliding_window`` W > 0 limits each query to the last W
+    tokens of its sequence: the dense path on [UQ-impl] passes the window as
+    (W - 1, 0), i.e. a query sees itself and the W - 1 keys before it.
     """
     query_bits = np.asarray(query_bits)
     B, Hq, _ = query_bits.shape
@@ -339,8 +352,11 @@ def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None) -> np
             out[b, h * qg:(h + 1) * qg] = 0.0
             continue
         K, V = gather_sequence(kv_cache, block_table[b], L, h)
+        if sliding_window and sliding_window > 0:
+            K, V = K[max(0, L - sliding_window):], V[max(0, L - sliding_window):]
         q8 = query_haircut(query_bits[b, h * qg:(h + 1) * qg])
-        out[b, h * qg:(h + 1) * qg] = attention(q8, K, V, scale)
+        sk = None if sinks is None else np.asarray(sinks, dtype=np.float64)[h * qg:(h + 1) * qg]
+        out[b, h * qg:(h + 1) * qg] = attention(q8, K, V, scale, sk)
     return out
 
 

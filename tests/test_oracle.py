@@ -341,3 +341,82 @@ def test_block_permutation_leaves_output_unchanged():
     moved[perm] = cache
     got = O.decode(q, moved, perm[table].astype(np.int32), lens, scale)
     assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------- sinks and sliding window
+def test_sink_one_token_closed_form():
+    """One token and a sink s: the weight of the token is 1 / (1 + e^(s - x))
+    with x its scaled score, computed here by an explicit sum."""
+    q, k, v, cache, table, lens, scale = _tiny_case(31, 1, qg=6)
+    _, V = O.gather_sequence(cache, table[0], 1, 0)
+    K, _ = O.gather_sequence(cache, table[0], 1, 0)
+    sinks = np.array([-3.0, -0.5, 0.0, 0.7, 2.0, 9.0])
+    out = O.decode(q, cache, table, lens, scale, sinks=sinks)
+    for g in range(6):
+        q8 = O.query_haircut(q[0, g])
+        x = scale * sum(q8[d] * K[0, d] for d in range(256))
+        w = 1.0 / (1.0 + math.exp(sinks[g] - x))
+        assert np.allclose(out[0, g], w * V[0], rtol=1e-12, atol=1e-14)
+
+
+def test_sink_matches_library_softmax_with_extra_logit():
+    """torch's softmax over the token logits plus the sink logit, keeping
+    only the tokens' weights."""
+    q, k, v, cache, table, lens, scale = _tiny_case(32, 45, Hk=2, qg=8)
+    rng = np.random.default_rng(33)
+    sinks = rng.normal(0, 2, 16)
+    out = O.decode(q, cache, table, lens, scale, sinks=sinks)
+    for h in range(2):
+        K, V = O.gather_sequence(cache, table[0], 45, h)
+        q8 = torch.from_numpy(O.query_haircut(q[0, h * 8:(h + 1) * 8]))
+        logits = scale * (q8 @ torch.from_numpy(K).T)
+        full = torch.cat([logits, torch.from_numpy(sinks[h * 8:(h + 1) * 8])[:, None]], dim=1)
+        p = torch.softmax(full, dim=1)[:, :45]
+        ref = (p @ torch.from_numpy(V)).numpy()
+        assert np.allclose(out[0, h * 8:(h + 1) * 8], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_sink_minus_infinity_is_no_sink_and_scales_output():
+    q, k, v, cache, table, lens, scale = _tiny_case(34, 60)
+    base = O.decode(q, cache, table, lens, scale)
+    assert np.array_equal(O.decode(q, cache, table, lens, scale, sinks=np.full(8, -np.inf)), base)
+    # a finite sink scales every output element of a head by Z / (Z + e^s),
+    # Z = sum of e^(scores), here summed token by token
+    K, _ = O.gather_sequence(cache, table[0], 60, 0)
+    s = np.linspace(-2, 3, 8)
+    out = O.decode(q, cache, table, lens, scale, sinks=s)
+    for g in range(8):
+        q8 = O.query_haircut(q[0, g])
+        xs = [scale * float(np.dot(q8, K[t])) for t in range(60)]
+        Z = sum(math.exp(x) for x in xs)
+        assert np.allclose(out[0, g], base[0, g] * (Z / (Z + math.exp(s[g]))), rtol=1e-11, atol=1e-14)
+
+
+def test_empty_sequence_with_sink_gives_zeros():
+    q, k, v, cache, table, lens, scale = _tiny_case(35, 10)
+    out = O.decode(q, cache, table, np.array([0]), scale, sinks=np.zeros(8))
+    assert np.array_equal(out, np.zeros_like(out))
+
+
+def test_sliding_window_cases():
+    q, k, v, cache, table, lens, scale = _tiny_case(36, 70, Hk=2, qg=8)
+    base = O.decode(q, cache, table, lens, scale)
+    # a window at least as long as the sequence changes nothing
+    assert np.array_equal(O.decode(q, cache, table, lens, scale, sliding_window=70), base)
+    assert np.array_equal(O.decode(q, cache, table, lens, scale, sliding_window=1000), base)
+    # a window of one token returns that token's value exactly
+    out1 = O.decode(q, cache, table, lens, scale, sliding_window=1)
+    for h in range(2):
+        _, V = O.gather_sequence(cache, table[0], 70, h)
+        assert np.array_equal(out1[0, h * 8:(h + 1) * 8], np.broadcast_to(V[69], (8, 256)))
+    # a window of 23: torch SDPA over the last 23 tokens
+    out = O.decode(q, cache, table, lens, scale, sliding_window=23)
+    for h in range(2):
+        K, V = O.gather_sequence(cache, table[0], 70, h)
+        q8 = O.query_haircut(q[0, h * 8:(h + 1) * 8])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q8)[None, :, None, :],
+            torch.from_numpy(K[47:])[None, None].expand(1, 8, 23, 256),
+            torch.from_numpy(V[47:])[None, None].expand(1, 8, 23, 256),
+            scale=scale)[0, :, 0].numpy()
+        assert np.allclose(out[0, h * 8:(h + 1) * 8], ref, rtol=1e-12, atol=1e-12)
