@@ -42,7 +42,7 @@ def parse():
                          "store of one token per sequence together with the decode")
     ap.add_argument("--queries-per-seq", type=int, default=1,
                     help="decode this many query rows per sequence (a speculative step), each "
-                         "reading its own prefix, through uq_decode_multi")
+                         "reading its own prefix, through uq_decode_ex")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -145,7 +145,8 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
         if multi is None:
             uq.decode(*args(i), out=out, workspace=ws)
         else:
-            uq.decode_multi(q, caches[i % R], bt, rows, sl, w.scale, w.num_kv_splits, out=out, workspace=ws)
+            uq.decode_ex(q, caches[i % R], bt, sl, w.scale, w.num_kv_splits, query_row=rows, out=out,
+                         workspace=ws)
 
     for i in range(warmup):
         step(i)
@@ -261,7 +262,7 @@ def main():
     log(f"timing {args.steps} steps ({len(caches)} cache copies)")
     store_args = serving_store(w, lay, dev) if w.name == "mixed" else None
     multi = multi_query(w, lay, args.queries_per_seq, dev) if args.queries_per_seq > 1 else None
-    # every query row of uq_decode_multi reads its own prefix: the logical
+    # every query row of uq_decode_ex reads its own prefix: the logical
     # bytes count each read, the value counts each cache byte once
     logical_bytes = (int(multi[2].long().sum()) * w.Hk * inputs.SLOT_BYTES) if multi is not None else kv_bytes
     step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup,
@@ -287,7 +288,7 @@ def main():
                                + (" (step = store of one token per sequence + decode)"
                                   if store_args is not None else "")
                                + (f" ({args.queries_per_seq} query rows per sequence, "
-                                  f"uq_decode_multi)" if multi is not None else ""),
+                                  f"uq_decode_ex)" if multi is not None else ""),
                    "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "block_size": w.block_size,
                    "num_kv_splits": w.num_kv_splits, "kv_bytes_per_step": kv_bytes,
                    "logical_kv_bytes_per_step": logical_bytes},

@@ -11,8 +11,9 @@ Entry points mirror include/uq.h:
   decode_workspace_bytes(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size)  -> int
   decode(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
          out=None, workspace=None)                  -> (B, Hq, 256) bf16
-  decode_multi(query, kv_cache, block_table, query_row, seq_lens, scale,
-               num_kv_splits, out=None, workspace=None) -> (B, Hq, 256) bf16
+  decode_ex(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
+            query_row=None, sinks=None, sliding_window=0,
+            out=None, workspace=None)               -> (B, Hq, 256) bf16
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["build_hadamard", "store", "decode", "decode_multi", "decode_workspace_bytes", "library_path",
+__all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_workspace_bytes", "library_path",
            "UQError", "HEAD_DIM", "SLOT_BYTES"]
 
 HEAD_DIM = 256
@@ -62,9 +63,9 @@ def _load():
     lib.uq_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, i32, vp, i32, i32, i32, i32, i64,
                               i32, i32, i64, i64, vp, sz, vp]
     lib.uq_decode.restype = i32
-    lib.uq_decode_multi.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_float, i32, vp, i32, i32, i32,
-                                    i32, i64, i32, i32, i64, i64, vp, sz, vp]
-    lib.uq_decode_multi.restype = i32
+    lib.uq_decode_ex.argtypes = [vp, vp, vp, i32, vp, vp, ctypes.c_float, i32, vp, i32, vp, i32, i32,
+                                 i32, i32, i64, i32, i32, i64, i64, vp, sz, vp]
+    lib.uq_decode_ex.restype = i32
     lib.uq_decode_stages.argtypes = [i32] + lib.uq_decode.argtypes
     lib.uq_decode_stages.restype = i32
     lib.uq_last_error.argtypes = []
@@ -181,24 +182,32 @@ def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     return out
 
 
-def decode_multi(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
-                 query_row: torch.Tensor, seq_lens: torch.Tensor, scale: float, num_kv_splits: int,
-                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode B query rows, row b against block-table row query_row[b] with
-    length seq_lens[b] (uq_decode_multi); returns (B, Hq, 256) bf16."""
+def decode_ex(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+              seq_lens: torch.Tensor, scale: float, num_kv_splits: int,
+              query_row: torch.Tensor | None = None, sinks: torch.Tensor | None = None,
+              sliding_window: int = 0, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """uq_decode_ex: decode with optional per-query table rows (query row b
+    reads block-table row query_row[b]), per-head sink logits and a sliding
+    window of the last `sliding_window` tokens; returns (B, Hq, 256) bf16."""
     if query.dtype != torch.bfloat16 or query.dim() != 3 or query.stride(2) != 1:
         raise TypeError("query must be (B, Hq, D) bfloat16 with a contiguous last dim")
     if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
         raise TypeError("kv_cache must be a contiguous 4-d uint8 tensor")
     if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2:
         raise TypeError("block_table must be a contiguous (rows, max_blocks) int32 tensor")
-    for name, t in (("query_row", query_row), ("seq_lens", seq_lens)):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise TypeError(f"{name} must be a contiguous int32 tensor")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("seq_lens must be a contiguous int32 tensor")
+    if query_row is not None and (query_row.dtype != torch.int32 or not query_row.is_contiguous()):
+        raise TypeError("query_row must be a contiguous int32 tensor")
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise TypeError("sinks must be a contiguous float32 tensor")
     B, Hq, D = query.shape
     nb, bs, Hk, ss = kv_cache.shape
-    if query_row.numel() != B or seq_lens.numel() != B:
-        raise ValueError("query_row / seq_lens must have one entry per query row")
+    if seq_lens.numel() != B or (query_row is not None and query_row.numel() != B):
+        raise ValueError("seq_lens / query_row must have one entry per query row")
+    if sinks is not None and sinks.numel() != Hq:
+        raise ValueError("sinks must have one entry per query head")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=query.device)
     elif out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
@@ -207,9 +216,11 @@ def decode_multi(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch
     need = lib.uq_decode_workspace_bytes(B, Hq, Hk, D, int(num_kv_splits), block_table.shape[1], bs)
     if workspace is None:
         workspace = _workspace(query.device, max(int(need), 256))
-    _check(lib.uq_decode_multi(_ptr(query), _ptr(kv_cache), _ptr(block_table), block_table.shape[0],
-                               _ptr(query_row), _ptr(seq_lens), float(scale), int(num_kv_splits),
-                               _ptr(out), B, Hq, Hk, D, nb, bs, block_table.shape[1], query.stride(0),
-                               query.stride(1), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(query.device)))
+    _check(lib.uq_decode_ex(_ptr(query), _ptr(kv_cache), _ptr(block_table), block_table.shape[0],
+                            _ptr(query_row) if query_row is not None else None, _ptr(seq_lens),
+                            float(scale), int(num_kv_splits),
+                            _ptr(sinks) if sinks is not None else None, int(sliding_window),
+                            _ptr(out), B, Hq, Hk, D, nb, bs, block_table.shape[1], query.stride(0),
+                            query.stride(1), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(query.device)))
     return out

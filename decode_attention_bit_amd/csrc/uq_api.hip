@@ -82,7 +82,8 @@ size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits
 
 static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_cache,
                        const int32_t* block_table, int n_table_rows, const int32_t* query_row,
-                       const int32_t* seq_lens, float scale, int num_kv_splits, uint16_t* out,
+                       const int32_t* seq_lens, float scale, int num_kv_splits,
+                       const float* sinks, int sliding_window, uint16_t* out,
                        int B, int Hq, int Hk, int D, int64_t num_blocks, int block_size,
                        int max_blocks_per_seq, int64_t q_stride_b, int64_t q_stride_h,
                        void* workspace, size_t workspace_bytes, void* stream) {
@@ -92,6 +93,7 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
   if (num_blocks < 1 || max_blocks_per_seq < 1 || n_table_rows < 1)
     return fail(UQ_EINVAL, "uq_decode: num_blocks, max_blocks_per_seq and the table rows must be >= 1");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(UQ_EINVAL, "uq_decode: scale must be finite and > 0");
+  if (sliding_window < 0) return fail(UQ_EINVAL, "uq_decode: sliding_window %d < 0", sliding_window);
   if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_decode: head_dim %d unsupported (only 256)", D);
   if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "uq_decode: Hq=%d is not a multiple of Hk=%d", Hq, Hk);
   const int qg = Hq / Hk;
@@ -108,7 +110,8 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
   if (q_stride_b < 0 || q_stride_h < 0 || q_stride_b % 4 || q_stride_h % 4)
     return fail(UQ_EINVAL, "uq_decode: query strides must be non-negative multiples of 4 elements");
   if (!aligned(query, 8) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
-      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_row, 4))
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_row, 4) ||
+      !aligned(sinks, 4))
     return fail(UQ_EINVAL, "uq_decode: misaligned pointer (query 8 B, kv_cache/out 16 B, workspace 256 B)");
   const uq::DecodePlan plan =
       uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size);
@@ -116,7 +119,8 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
     return fail(UQ_EWORKSPACE, "uq_decode: workspace %zu bytes < required %zu", workspace_bytes, plan.total);
   if ((long long)B * plan.parts * Hk > 0x7FFFFFFFLL || (long long)B * Hq > 0x7FFFFFFFLL)
     return fail(UQ_EUNSUPPORTED, "uq_decode: grid too large");
-  uq::DecodeArgs a{query, kv_cache, block_table, query_row, n_table_rows, seq_lens, scale, out,
+  uq::DecodeArgs a{query, kv_cache, block_table, query_row, n_table_rows, seq_lens, sinks,
+                   sliding_window, scale, out,
                    num_blocks, block_size,
                    max_blocks_per_seq, q_stride_b, q_stride_h,
                    reinterpret_cast<uint8_t*>(workspace)};
@@ -131,22 +135,25 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
                      int64_t q_stride_b, int64_t q_stride_h, void* workspace,
                      size_t workspace_bytes, void* stream) {
   return decode_impl(stage_mask, query, kv_cache, block_table, B, nullptr, seq_lens, scale,
-                     num_kv_splits, out, B, Hq, Hk, D, num_blocks, block_size,
+                     num_kv_splits, nullptr, 0, out, B, Hq, Hk, D, num_blocks, block_size,
                      max_blocks_per_seq, q_stride_b, q_stride_h, workspace, workspace_bytes,
                      stream);
 }
 
-int uq_decode_multi(const uint16_t* query, const uint8_t* kv_cache, const int32_t* block_table,
-                    int n_table_rows, const int32_t* query_row, const int32_t* seq_lens,
-                    float scale, int num_kv_splits, uint16_t* out, int B, int Hq, int Hk, int D,
-                    int64_t num_blocks, int block_size, int max_blocks_per_seq,
-                    int64_t q_stride_b, int64_t q_stride_h, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  if (!query_row) return fail(UQ_EINVAL, "uq_decode_multi: null query_row");
+int uq_decode_ex(const uint16_t* query, const uint8_t* kv_cache, const int32_t* block_table,
+                 int n_table_rows, const int32_t* query_row, const int32_t* seq_lens, float scale,
+                 int num_kv_splits, const float* sinks, int sliding_window, uint16_t* out, int B,
+                 int Hq, int Hk, int D, int64_t num_blocks, int block_size,
+                 int max_blocks_per_seq, int64_t q_stride_b, int64_t q_stride_h, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!query_row && n_table_rows != B)
+    return fail(UQ_EINVAL, "uq_decode_ex: without query_row the table needs B=%d rows, not %d", B,
+                n_table_rows);
   return decode_impl(UQ_STAGE_PROLOGUE | UQ_STAGE_SPLIT | UQ_STAGE_MERGE, query, kv_cache,
-                     block_table, n_table_rows, query_row, seq_lens, scale, num_kv_splits, out,
-                     B, Hq, Hk, D, num_blocks, block_size, max_blocks_per_seq, q_stride_b,
-                     q_stride_h, workspace, workspace_bytes, stream);
+                     block_table, n_table_rows, query_row, seq_lens, scale, num_kv_splits, sinks,
+                     sliding_window, out, B, Hq, Hk, D, num_blocks, block_size,
+                     max_blocks_per_seq, q_stride_b, q_stride_h, workspace, workspace_bytes,
+                     stream);
 }
 
 int uq_decode(const uint16_t* query, const uint8_t* kv_cache, const int32_t* block_table,

@@ -184,9 +184,11 @@ __device__ __forceinline__ float rowgroup_max(float x) {
 }
 
 // Scores of one tile in the log2 domain (lane: q-head l%16, tokens 4*grp+i),
-// -inf past the end of the sequence; mt = the tile maximum for the lane's head.
+// -inf past the end of the sequence and for the tile's first `first` tokens
+// (those before a sliding window); mt = the tile maximum for the lane's head.
 __device__ __forceinline__ void qk_tile(const Tile& T, const v8i& qb0, const v8i& qb1,
-                                        float scale_log2, int grp, float sv[4], float& mt) {
+                                        float scale_log2, int grp, int first, float sv[4],
+                                        float& mt) {
   const int sc1 = (int)((T.ks.x >> (8 * grp)) & 0xFF);
   const int sc2 = (int)((T.ks.y >> (8 * grp)) & 0xFF);
   const v8i a1 = {(int)T.ka.x, (int)T.ka.y, (int)T.ka.z, (int)T.ka.w, 0, 0, 0, 0};
@@ -196,10 +198,10 @@ __device__ __forceinline__ void qk_tile(const Tile& T, const v8i& qb0, const v8i
   sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, qb1, sc, 4, 0, 0, sc2, 0, 127);
 #pragma unroll
   for (int i = 0; i < 4; ++i) sv[i] = sc[i] * scale_log2;
-  if (T.nvalid < kTile) {                  // only the sequence's last tile is partial
+  if (T.nvalid < kTile || first > 0) {     // the sequence's last tile, the window's first
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (4 * grp + i >= T.nvalid) sv[i] = -INFINITY;
+      if (4 * grp + i >= T.nvalid || 4 * grp + i < first) sv[i] = -INFINITY;
   }
   mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mt = rowgroup_max(mt);
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ query_row, int n_rows,
     const int32_t* __restrict__ seq_lens,
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
-    int log2_bs, int max_blocks, int64_t num_blocks, float* __restrict__ part_o,
+    int log2_bs, int max_blocks, int64_t num_blocks, int window, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
   static_assert(NSLOT >= 3 && NSLOT <= 8, "ring depth");
   static_assert(NSLOT * HPW * kTileU4 * 16 <= 160 * 1024, "ring exceeds the LDS of a CU");
@@ -294,8 +296,12 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int g_hi = min(g_lo + spw * cs, n_tiles);
   const int u1 = min(u0 + sub_len, g_hi);
   const size_t stat = ((size_t)b * Hq + hq) * P + part;
+  // A sliding window of W tokens starts at token lo = L - W: the wave skips
+  // the tiles before it and masks the rest of lo's tile.
+  const int lo = (window > 0 && L > window) ? L - window : 0;
+  const int ub = max(u0, lo / kTile);                   // first tile this wave reads
 
-  if (u0 >= u1) {
+  if (ub >= u1) {
     if (qlane && grp == 0) {
       part_m[stat] = -INFINITY;
       part_l[stat] = 0.f;
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 #pragma unroll
   for (int j = 0; j < 16; ++j) hold[j] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f, l_hold = 0.f;
-  int t0 = u0;
+  int t0 = ub;
   for (;;) {
     Tile T;
     float sv[4], mt;
@@ -349,8 +355,8 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
       wait_tiles_ahead<NSLOT - 2>(u1 - 1 - t);                                   \
       read_tile(T, CUR[wave], n16, grp, nv_##CUR);                               \
       if (t + NSLOT - 1 < u1) nv_##NXT = issue(NXT[wave], t + NSLOT - 1);        \
-      qk_tile(T, qb0, qb1, scale_log2, grp, sv, mt);                             \
-      if (t == u0) m_ref = mt;                                                   \
+      qk_tile(T, qb0, qb1, scale_log2, grp, lo - t * kTile, sv, mt);             \
+      if (t == ub) m_ref = mt;                                                   \
       if (__any(mt > m_ref + 8.0f)) { rebased = true; t_stop = t; break; }       \
       if (T.nvalid > 0) pv_tile(T, sv, m_ref, n16, acc, l_part);                 \
       if (++t >= u1) break;                                                      \
@@ -434,6 +440,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o,
                                                      const float* __restrict__ part_m,
                                                      const float* __restrict__ part_l,
+                                                     const float* __restrict__ sinks, int Hq,
                                                      uint16_t* __restrict__ out, int rows, int P) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -442,6 +449,10 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   const float* pl = part_l + (size_t)row * P;
   const float* po = part_o + (size_t)row * P * kHeadDim + 4 * lane;
   float M = -INFINITY, den = 0.f;
+  if (sinks) {              // the sink: a partial of weight 1 at its logit, with no value
+    M = sinks[row % Hq] * 1.4426950408889634f;
+    den = 1.f;
+  }
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int p0 = 0; p0 < P; p0 += 8) {
     float4 o[8];
@@ -576,7 +587,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
                      a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens, scale_log2,    \
                      p.Hq, p.Hk, hgroups,                                                      \
                      p.cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,          \
-                     a.num_blocks, part_o, part_m, part_l)
+                     a.num_blocks, a.window, part_o, part_m, part_l)
 #define UQ_STAGE1_HPW(QGV)                      \
   do {                                          \
     switch (hpw) {                              \
@@ -601,7 +612,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
 #undef UQ_STAGE1
   if (stage_mask & 4) {
     hipLaunchKernelGGL(stage2_kernel, dim3((unsigned)((vecs + 3) / 4)), dim3(256), 0, stream,
-                       part_o, part_m, part_l, a.out, (int)vecs, p.parts);
+                       part_o, part_m, part_l, a.sinks, p.Hq, a.out, (int)vecs, p.parts);
     e = hipGetLastError();
   }
   return e;

@@ -35,6 +35,8 @@ struct DecodeArgs {
   const int32_t* query_row;   // (B,) block-table row of each query, or null: row b
   int n_rows;                 // rows in block_table
   const int32_t* seq_lens;
+  const float* sinks;         // (Hq,) sink logits, or null
+  int window;                 // sliding window in tokens, 0: none
   float scale;
   uint16_t* out;
   int64_t num_blocks;

@@ -148,30 +148,43 @@ int uq_decode(const uint16_t* query, const uint8_t* kv_cache,
               size_t workspace_bytes, void* stream);
 
 /*
- * Multi-query decode: several query rows may read the same sequence, each
- * with its own length. This is how the ultraquant_attn page decodes a short
- * continuation chunk (_prefill_attention, continuation branch): query i of a
- * chunk whose sequence holds cached_len tokens gets the length
- * cached_len + i + 1 and the sequence's block-table row, repeated for every
- * query of the chunk. Here the rows are not repeated: query row b reads
- * block-table row query_row[b].
+ * uq_decode with three options; uq_decode is this call with none of them.
+ *
+ * Multi-query rows (query_row). Several query rows may read the same
+ * sequence, each with its own length. This is how the ultraquant_attn page
+ * decodes a short continuation chunk (_prefill_attention, continuation
+ * branch): query i of a chunk whose sequence holds cached_len tokens gets
+ * the length cached_len + i + 1 and the sequence's block-table row, repeated
+ * for every query of the chunk. Here the rows are not repeated: query row b
+ * reads block-table row query_row[b].
+ *   query_row:    (device) int32 (B,), or NULL for query_row[b] = b (then
+ *                 n_table_rows must be B). A value outside
+ *                 [0, n_table_rows) makes that query's output zeros.
  *   block_table:  (device) int32 (n_table_rows, max_blocks_per_seq).
- *   query_row:    (device) int32 (B,): the table row of each query row; a
- *                 value outside [0, n_table_rows) makes that query's output
- *                 zeros (an empty sequence).
  *   seq_lens:     (device) int32 (B,): the length each query row attends to.
- *   Every other argument is as for uq_decode, with B the number of query
- *   rows (query, out and the workspace size are per query row). uq_decode is
- *   this call with query_row[b] = b.
- * Errors: as uq_decode; UQ_EINVAL also for a null query_row or
- * n_table_rows < 1.
+ *
+ * Attention sinks (sinks). The ultraquant_attn page passes per-head sinks
+ * to its unified kernel. Here a sink is one more logit per query head in
+ * the softmax normaliser, with no value behind it, in the units of
+ * scale * q8 . k: out = sum_t e^(x_t) v_t / (e^(s) + sum_t e^(x_t)).
+ *   sinks:        (device) float32 (Hq,), or NULL; finite or -inf.
+ *
+ * Sliding window (sliding_window). The page's dense path passes a window W
+ * as (W - 1, 0): a query sees itself and the W - 1 keys before it, so each
+ * query row attends to the last min(W, seq_len) tokens. 0 means no window.
+ *
+ * Every other argument is as for uq_decode, with B the number of query rows
+ * (query, out and the workspace are sized per query row).
+ * Errors: as uq_decode; UQ_EINVAL also for n_table_rows < 1 (or != B
+ * without query_row), sliding_window < 0, or a misaligned query_row / sinks.
  */
-int uq_decode_multi(const uint16_t* query, const uint8_t* kv_cache,
-                    const int32_t* block_table, int n_table_rows, const int32_t* query_row,
-                    const int32_t* seq_lens, float scale, int num_kv_splits, uint16_t* out,
-                    int B, int Hq, int Hk, int D, int64_t num_blocks, int block_size,
-                    int max_blocks_per_seq, int64_t q_stride_b, int64_t q_stride_h,
-                    void* workspace, size_t workspace_bytes, void* stream);
+int uq_decode_ex(const uint16_t* query, const uint8_t* kv_cache,
+                 const int32_t* block_table, int n_table_rows, const int32_t* query_row,
+                 const int32_t* seq_lens, float scale, int num_kv_splits,
+                 const float* sinks, int sliding_window, uint16_t* out,
+                 int B, int Hq, int Hk, int D, int64_t num_blocks, int block_size,
+                 int max_blocks_per_seq, int64_t q_stride_b, int64_t q_stride_h,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Same as uq_decode, restricted to the stages named in stage_mask:

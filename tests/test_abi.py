@@ -18,7 +18,7 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ("uq_build_hadamard", "uq_store", "uq_decode", "uq_decode_multi", "uq_decode_stages",
+    for n in ("uq_build_hadamard", "uq_store", "uq_decode", "uq_decode_ex", "uq_decode_stages",
               "uq_decode_workspace_bytes", "uq_last_error"):
         assert n in names
 
@@ -117,19 +117,20 @@ def test_workspace_bytes(libuq):
     assert f(2, 16, 2, 256, 1, 1, 16) == 2 * 16 * 256 + 2 * 16 * 1024 + 2 * 256
 
 
-def decode_multi_args(**kw):
+def decode_ex_args(**kw):
     a = dict(query=FAKE, kv_cache=FAKE, block_table=FAKE, rows=4, query_row=FAKE, seq_lens=FAKE,
-             scale=0.0625, splits=32, out=FAKE, B=8, Hq=32, Hk=4, D=256, num_blocks=64,
-             block_size=16, max_blocks=16, qsb=8192, qsh=256, workspace=FAKE, ws_bytes=1 << 40,
-             stream=None)
+             scale=0.0625, splits=32, sinks=None, window=0, out=FAKE, B=8, Hq=32, Hk=4, D=256,
+             num_blocks=64, block_size=16, max_blocks=16, qsb=8192, qsh=256, workspace=FAKE,
+             ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return list(a.values())
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(query_row=None), -1), (dict(rows=0), -1), (dict(query_row=FAKE + 2), -1),
+    (dict(rows=0), -1), (dict(query_row=FAKE + 2), -1), (dict(query_row=None), -1),
+    (dict(window=-1), -1), (dict(sinks=FAKE + 2), -1),
     (dict(Hq=36), -2), (dict(ws_bytes=1024), -3), (dict(block_table=None), -1),
 ])
-def test_decode_multi_rejects(libuq, kw, code):
-    assert libuq.uq_decode_multi(*decode_multi_args(**kw)) == code
+def test_decode_ex_rejects(libuq, kw, code):
+    assert libuq.uq_decode_ex(*decode_ex_args(**kw)) == code
     assert _err(libuq)

@@ -339,7 +339,7 @@ def test_decode_multi_query_continuation_chunks():
     table = ctx["table"]
     q_dev, rows_dev, lens_dev = q.to(DEV), torch.from_numpy(rows).to(DEV), torch.from_numpy(lens).to(DEV)
     for S in (1, 4, 16):
-        out = uq.decode_multi(q_dev, ctx["cache"], table, rows_dev, lens_dev, ctx["scale"], S)
+        out = uq.decode_ex(q_dev, ctx["cache"], table, lens_dev, ctx["scale"], S, query_row=rows_dev)
         ref = O.decode(bits(q), ctx["ref_cache"], table.cpu().numpy()[rows], lens, ctx["scale"])
         check_close(to_np(out), ref, f"multi-query S={S}")
         # the same as decoding against the table with each row repeated
@@ -349,11 +349,41 @@ def test_decode_multi_query_continuation_chunks():
     # a row index outside the table reads as an empty sequence
     bad = rows_dev.clone()
     bad[0], bad[-1] = -1, len(full)
-    out = uq.decode_multi(q_dev, ctx["cache"], table, bad, lens_dev, ctx["scale"], 4)
+    out = uq.decode_ex(q_dev, ctx["cache"], table, lens_dev, ctx["scale"], 4, query_row=bad)
     o = to_np(out)
     assert np.all(o[0] == 0) and np.all(o[-1] == 0)
     ref = O.decode(bits(q), ctx["ref_cache"], table.cpu().numpy()[rows], lens, ctx["scale"])
     check_close(o[1:-1], ref[1:-1], "multi-query, valid rows")
+
+
+@pytest.mark.parametrize("window", [0, 1, 15, 16, 17, 100, 333, 5000])
+def test_decode_sinks_and_sliding_window(window):
+    """Per-head sink logits and a sliding window of the last W tokens against
+    the oracle, at several split counts, with windows that start mid-tile,
+    on a tile edge, mid-partial and before the sequence."""
+    say(f"decode sinks window={window}")
+    lens = [700, 77, 1, 16, 0, 300]
+    out0, ref0, ctx = _decode_case(lens, Hk=2, qg=8, splits=4, seed=23)
+    rng = np.random.default_rng(24)
+    sinks = rng.normal(0.0, 2.0, 16)
+    sinks[3] = -np.inf
+    sinks_dev = torch.from_numpy(sinks.astype(np.float32)).to(DEV)
+    ref = O.decode(bits(ctx["q"]), ctx["ref_cache"], ctx["table"].cpu().numpy(), np.array(lens),
+                   ctx["scale"], sinks=sinks.astype(np.float32).astype(np.float64),
+                   sliding_window=window)
+    for S in (1, 4, 32):
+        out = uq.decode_ex(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], S,
+                           sinks=sinks_dev, sliding_window=window)
+        check_close(to_np(out), ref, f"sinks, window={window}, S={S}")
+    # the window alone, and no option at all equals uq_decode bit for bit
+    out = uq.decode_ex(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 4,
+                       sliding_window=window)
+    ref_w = O.decode(bits(ctx["q"]), ctx["ref_cache"], ctx["table"].cpu().numpy(), np.array(lens),
+                     ctx["scale"], sliding_window=window)
+    check_close(to_np(out), ref_w, f"window={window}")
+    if window == 0:
+        plain = uq.decode_ex(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 4)
+        assert torch.equal(plain, out0)
 
 
 def test_decode_split_count_invariance():
