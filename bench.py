@@ -43,6 +43,11 @@ def parse():
     ap.add_argument("--queries-per-seq", type=int, default=1,
                     help="decode this many query rows per sequence (a speculative step), each "
                          "reading its own prefix, through uq_decode_ex")
+    ap.add_argument("--sliding-window", type=int, default=0,
+                    help="attend to the last W tokens only (uq_decode_ex); the value counts the "
+                         "cache bytes inside the window")
+    ap.add_argument("--sinks", action="store_true",
+                    help="add seeded per-head sink logits (uq_decode_ex)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -123,7 +128,8 @@ def multi_query(w, lay, qps, dev):
     return qm, torch.from_numpy(rows).to(dev), torch.from_numpy(lens).to(dev)
 
 
-def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=None):
+def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=None, sinks=None,
+             window=0):
     import torch
 
     import decode_attention_bit_amd as uq
@@ -142,11 +148,12 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
     def step(i):
         if store_args is not None:
             uq.store(store_args[0], store_args[1], caches[i % R], store_args[2])
-        if multi is None:
+        if multi is None and sinks is None and not window:
             uq.decode(*args(i), out=out, workspace=ws)
         else:
-            uq.decode_ex(q, caches[i % R], bt, sl, w.scale, w.num_kv_splits, query_row=rows, out=out,
-                         workspace=ws)
+            uq.decode_ex(q, caches[i % R], bt, sl, w.scale, w.num_kv_splits,
+                         query_row=None if multi is None else rows, sinks=sinks, sliding_window=window,
+                         out=out, workspace=ws)
 
     for i in range(warmup):
         step(i)
@@ -177,6 +184,8 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
+    if multi is not None or sinks is not None or window:
+        return step_ms, None, None, None      # the per-kernel entry points take no options
     pro = alone(uq.STAGE_PROLOGUE)
     st1 = alone(uq.STAGE_SPLIT)
     st2 = alone(uq.STAGE_MERGE)
@@ -265,10 +274,19 @@ def main():
     # every query row of uq_decode_ex reads its own prefix: the logical
     # bytes count each read, the value counts each cache byte once
     logical_bytes = (int(multi[2].long().sum()) * w.Hk * inputs.SLOT_BYTES) if multi is not None else kv_bytes
+    sinks = None
+    if args.sinks:
+        import numpy as np
+        sinks = torch.from_numpy(np.random.default_rng([w.seed, 5]).normal(0, 2, w.Hq).astype(np.float32)).to(dev)
+    if args.sliding_window > 0:             # only the window's tokens are read
+        import numpy as np
+        kv_bytes = int(np.minimum(lay.seq_lens.astype(np.int64), args.sliding_window).sum()) * w.Hk * inputs.SLOT_BYTES
+        logical_bytes = kv_bytes
     step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup,
-                                               store_args, multi)
+                                               store_args, multi, sinks, args.sliding_window)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
-    st1_gbs = kv_bytes / (st1_ms * 1e-3) / 1e9
+    plain = st1_ms is not None               # no option: stage 1 timed on its own
+    st1_gbs = kv_bytes / ((st1_ms if plain else step_ms) * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -288,17 +306,22 @@ def main():
                                + (" (step = store of one token per sequence + decode)"
                                   if store_args is not None else "")
                                + (f" ({args.queries_per_seq} query rows per sequence, "
-                                  f"uq_decode_ex)" if multi is not None else ""),
+                                  f"uq_decode_ex)" if multi is not None else "")
+                               + (f" (sliding window {args.sliding_window})" if args.sliding_window > 0 else "")
+                               + (" (with sinks)" if sinks is not None else ""),
                    "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "block_size": w.block_size,
                    "num_kv_splits": w.num_kv_splits, "kv_bytes_per_step": kv_bytes,
                    "logical_kv_bytes_per_step": logical_bytes},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.B * max(1, args.queries_per_seq) / (step_ms * 1e-3), 1),
-        "stage_ms": {"prologue": round(pro_ms, 5), "split_kv": round(st1_ms, 5), "merge": round(st2_ms, 5)},
+        "stage_ms": ({"prologue": round(pro_ms, 5), "split_kv": round(st1_ms, 5), "merge": round(st2_ms, 5)}
+                     if plain else None),
         "cache_copies": len(caches),
         "roofline": {"bound": "hbm", "achieved": round(st1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(st1_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
-                     "kernel": "stage1_kernel (split-KV)", "bytes_per_launch": kv_bytes},
+                     "frac": round(st1_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name) if plain and store_args is None else None,
+                     "kernel": "stage1_kernel (split-KV)" if plain else "the whole step (options on)",
+                     "bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline")

@@ -261,15 +261,14 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = hg * HPW + wave;
 
-  // The partial's first tile does not depend on the sequence length, so the
-  // length, the block-table entries and the query codes are all requested
-  // before any of them is waited for.
-  // Split s covers tiles [s*cs, (s+1)*cs) of the sequence (cs from the table
-  // capacity, so that every split is the same size). A partial covers either
-  // spw consecutive splits or one of nsub equal pieces of one split.
-  const int g_lo = (part / nsub) * spw * cs;
+  // Split s covers tiles [s*cs, (s+1)*cs) counted from the first tile the
+  // query attends to (tile 0, or the tile of a sliding window's first token);
+  // cs comes from the table capacity (or the window), so every split is the
+  // same size. A partial covers either spw consecutive splits or one of nsub
+  // equal pieces of one split.
+  const int g_rel = (part / nsub) * spw * cs;
   const int sub_len = (spw * cs + nsub - 1) / nsub;
-  const int u0 = g_lo + (part % nsub) * sub_len;
+  const int u_rel = g_rel + (part % nsub) * sub_len;
   const int n16 = lane & 15, grp = lane >> 4;
   const bool qlane = n16 < QG;
   const int hq = h * QG + (qlane ? n16 : 0);
@@ -286,22 +285,21 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int trow = query_row ? query_row[b] : b;
   const bool row_ok = trow >= 0 && trow < n_rows;
   const int32_t* bt = block_table + (size_t)(row_ok ? trow : 0) * max_blocks;
-  const int e0 = (u0 * kTile) >> log2_bs;
-  const int btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
   int L = row_ok ? seq_lens[b] : 0;
-
   const int Lmax = max_blocks << log2_bs;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  const int n_tiles = (L + kTile - 1) / kTile;
-  const int g_hi = min(g_lo + spw * cs, n_tiles);
-  const int u1 = min(u0 + sub_len, g_hi);
-  const size_t stat = ((size_t)b * Hq + hq) * P + part;
-  // A sliding window of W tokens starts at token lo = L - W: the wave skips
-  // the tiles before it and masks the rest of lo's tile.
+  // A sliding window of W tokens starts at token lo = L - W: the splits count
+  // from lo's tile, and the tokens of that tile before lo are masked.
   const int lo = (window > 0 && L > window) ? L - window : 0;
-  const int ub = max(u0, lo / kTile);                   // first tile this wave reads
+  const int base = lo / kTile;
+  const int u0 = base + u_rel;
+  const int n_tiles = (L + kTile - 1) / kTile;
+  const int u1 = min(min(u0 + sub_len, base + g_rel + spw * cs), n_tiles);
+  const int e0 = (u0 * kTile) >> log2_bs;
+  const int btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
+  const size_t stat = ((size_t)b * Hq + hq) * P + part;
 
-  if (ub >= u1) {
+  if (u0 >= u1) {
     if (qlane && grp == 0) {
       part_m[stat] = -INFINITY;
       part_l[stat] = 0.f;
@@ -331,7 +329,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 #pragma unroll
   for (int j = 0; j < 16; ++j) hold[j] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f, l_hold = 0.f;
-  int t0 = ub;
+  int t0 = u0;
   for (;;) {
     Tile T;
     float sv[4], mt;
@@ -356,7 +354,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
       read_tile(T, CUR[wave], n16, grp, nv_##CUR);                               \
       if (t + NSLOT - 1 < u1) nv_##NXT = issue(NXT[wave], t + NSLOT - 1);        \
       qk_tile(T, qb0, qb1, scale_log2, grp, lo - t * kTile, sv, mt);             \
-      if (t == ub) m_ref = mt;                                                   \
+      if (t == u0) m_ref = mt;                                                   \
       if (__any(mt > m_ref + 8.0f)) { rebased = true; t_stop = t; break; }       \
       if (T.nvalid > 0) pv_tile(T, sv, m_ref, n16, acc, l_part);                 \
       if (++t >= u1) break;                                                      \
@@ -580,13 +578,23 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;
   const float scale_log2 = a.scale * 1.4426950408889634f;
+  // With a sliding window the splits cut the tiles a window can touch (its
+  // first token may sit mid-tile), not the whole table: the same partition
+  // shape, so the same partial count and workspace, over fewer tiles.
+  int cs = p.cs;
+  if (a.window > 0) {
+    const long max_tiles = ((long)a.max_blocks_per_seq * a.block_size + kTile - 1) / kTile;
+    const long wt = ((long)a.window + kTile - 1) / kTile + 1;
+    const long cmax = wt < max_tiles ? wt : max_tiles;
+    cs = (int)((cmax + p.splits - 1) / p.splits);
+  }
   const dim3 grid1((unsigned)((int64_t)p.B * p.parts * hgroups));
   const dim3 block1(64 * hpw);
 #define UQ_STAGE1(QGV, HPWV)                                                                     \
   hipLaunchKernelGGL((stage1_kernel<QGV, HPWV, ring_slots(HPWV)>), grid1, block1, 0, stream, q8,       \
                      a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens, scale_log2,    \
                      p.Hq, p.Hk, hgroups,                                                      \
-                     p.cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,          \
+                     cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,            \
                      a.num_blocks, a.window, part_o, part_m, part_l)
 #define UQ_STAGE1_HPW(QGV)                      \
   do {                                          \
