@@ -321,6 +321,47 @@ def test_decode_stage_masks_compose():
     assert torch.equal(o, out)
 
 
+def _extreme_queries(rng, B, Hq):
+    """Query rows that stress the E4M3 haircut: zeros, values that flush or
+    land on subnormal codes, saturation above 448, magnitudes spread over 26
+    binades, one-hot rows (+-1/16 everywhere) and small Gaussians."""
+    q = rng.standard_normal((B, Hq, 256))
+    kinds = [
+        lambda: np.zeros(256),
+        lambda: rng.standard_normal(256) * 2.0 ** -20,
+        lambda: rng.standard_normal(256) * 2.0 ** -9,
+        lambda: rng.standard_normal(256) * 300.0,
+        lambda: rng.choice([-1.0, 1.0], 256) * (1 + rng.random(256)) * np.exp2(rng.integers(-12, 13, 256)),
+        lambda: np.eye(256)[rng.integers(256)] * rng.choice([-1.0, 1.0]),
+        lambda: rng.standard_normal(256) * 1e-2,
+    ]
+    for b in range(B):
+        for h in range(Hq):
+            if (b * Hq + h) % 3:
+                q[b, h] = kinds[(b * Hq + h) % len(kinds)]()
+    return bf16(q)
+
+
+@pytest.mark.parametrize("qg", [6, 8, 16])
+def test_decode_extreme_queries(qg):
+    """Query rows of every kind the haircut distinguishes (flushed, subnormal,
+    saturated, wide-range, one-hot) through a whole decode: the output
+    matches the oracle, and bit for bit the output of the prologue run on
+    its own followed by stages 1 and 2."""
+    say(f"decode extreme queries qg={qg}")
+    Hk = 2
+    _, _, ctx = _decode_case([37, 20, 64], Hk=Hk, qg=qg, splits=2, seed=11 + qg)
+    q = _extreme_queries(np.random.default_rng(qg), 3, Hk * qg).to(DEV)
+    full = uq.decode(q, ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 2)
+    o = torch.empty_like(full)
+    for st in (uq.STAGE_PROLOGUE, uq.STAGE_SPLIT | uq.STAGE_MERGE):
+        uq.decode(q, ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 2, out=o, stages=st)
+    assert torch.equal(o, full)
+    ref = O.decode(bits(q.cpu()), ctx["ref_cache"], ctx["table"].cpu().numpy(),
+                   ctx["lens"].cpu().numpy(), ctx["scale"])
+    check_close(to_np(full), ref, f"extreme queries qg={qg}", allow_output_rounding=True)
+
+
 def test_decode_multi_query_continuation_chunks():
     """Continuation chunks, decoded one query at a time as the ultraquant_attn
     page does for short chunks: query i of a chunk over a sequence holding
