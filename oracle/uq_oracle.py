@@ -19,8 +19,9 @@ OCP Microscaling Formats (MX) v1.0 and OCP 8-bit Floating Point specs, as
 stated at each function.
 
 Parity pins: the Hadamard, the rotation, E2M1 values and rounding, UE8M0 and
-E4M3 decoding, and the attention are pinned by closed forms, library routines
-and brute force in tests/. Parity unpinned (no passage of the pages fixes
+E4M3 decoding, the attention, bf16 rounding and the continuation prefill
+(alignment, rotation of both sides, brute force) are pinned by closed forms,
+library routines and brute force in tests/. Parity unpinned (no passage of the pages fixes
 them; they are pinned by their own definitions only): the 32-element block
 partition, the UE8M0 scale-selection rule, the nibble packing order and the
 272-byte slot layout.
@@ -386,3 +387,79 @@ def attention_split(q8, K, V, scale, bounds) -> np.ndarray:
     m = np.stack([p[1] for p in parts])
     l = np.stack([p[2] for p in parts])
     return merge_partials(o, m, l)
+
+
+# --------------------------------------------------------------------------
+# Continuation prefill ([UQ-impl] _prefill_attention, continuation branch for
+# chunks above the decode threshold, and _ultraquant_continuation_prefill:
+# the cached prefix is dequantised in the rotated basis, the chunk's K and the
+# queries are rotated with x @ PiT and cast to the query dtype, and a dense
+# causal attention with unequal query/key lengths aligns the queries to the
+# lower right: query i, at absolute position cached_len + i, sees keys
+# 0 .. cached_len + i)
+# --------------------------------------------------------------------------
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Nearest bf16 value of float64 x, ties to even, in one rounding.
+
+    bf16 keeps 8 significant bits down to 2**-126 and a fixed step of 2**-133
+    below; finite values from 2**128 * (1 - 2**-9) up overflow to infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.frexp(np.where(a > 0, a, 1.0))[1] - 1             # floor(log2 a)
+    step = np.ldexp(1.0, np.maximum(e, -126) - 7)
+    r = np.rint(a / step) * step                             # rint: ties to even
+    r = np.where(r >= 2.0 ** 128, np.inf, r)
+    return np.copysign(np.where(a > 0, r, 0.0), x)
+
+
+def rotate_to_bf16(x_bits: np.ndarray) -> np.ndarray:
+    """bf16 value of x @ H per vector ([UQ-impl] (x.to(float32) @ PiT).to(dtype)).
+
+    This build's reading: the exact product rounded once to bf16 (the pages'
+    float32 product differs from it only where its own rounding error moves a
+    value across a bf16 rounding boundary)."""
+    return bf16_round(rotate(bf16_to_f64(x_bits)))
+
+
+def dequant_prefix(kv_cache: np.ndarray, block_row: np.ndarray, n: int):
+    """Dequantised (K, V) (n, Hk, 256) of a sequence's first n tokens, K in
+    the rotated basis ([UQ-impl] ultraquant_full_dequant_kv into the
+    (1, Hk, alloc_len, D) buffers, read back token-major)."""
+    hk = kv_cache.shape[2]
+    K = np.zeros((n, hk, D))
+    V = np.zeros((n, hk, D))
+    for h in range(hk):
+        K[:, h], V[:, h] = gather_sequence(kv_cache, block_row, n, h)
+    return K, V
+
+
+def continuation_prefill(query_bits, key_bits, value_bits, kv_cache, block_row, cached_len,
+                         scale) -> np.ndarray:
+    """Output (q_len, Hq, 256) float64 of a continuation chunk.
+
+    query_bits (q_len, Hq, 256), key_bits / value_bits (q_len, Hk, 256) are
+    the chunk's bf16 inputs before rotation; the sequence's first cached_len
+    tokens are in kv_cache through block_row. Keys are the dequantised
+    prefix followed by the chunk's rotated keys (as bf16); values are the
+    dequantised prefix followed by the chunk's values. Query head hq reads KV
+    head hq // (Hq // Hk).
+    """
+    query_bits = np.asarray(query_bits)
+    q_len, hq_n, _ = query_bits.shape
+    hk = np.asarray(key_bits).shape[1]
+    qg = hq_n // hk
+    Kp, Vp = dequant_prefix(kv_cache, block_row, cached_len)
+    K = np.concatenate([Kp, rotate_to_bf16(key_bits)], axis=0)
+    V = np.concatenate([Vp, bf16_to_f64(value_bits)], axis=0)
+    q = rotate_to_bf16(query_bits)
+    seq = cached_len + q_len
+    visible = np.arange(seq)[None, :] <= cached_len + np.arange(q_len)[:, None]
+    out = np.zeros((q_len, hq_n, D))
+    for hq in range(hq_n):
+        h = hq // qg
+        s = scale * (q[:, hq] @ K[:, h].T)
+        s = np.where(visible, s, -np.inf)
+        p = np.exp(s - s.max(axis=-1, keepdims=True))
+        out[:, hq] = (p @ V[:, h]) / p.sum(axis=-1, keepdims=True)
+    return out

@@ -420,3 +420,131 @@ def test_sliding_window_cases():
             torch.from_numpy(V[47:])[None, None].expand(1, 8, 23, 256),
             scale=scale)[0, :, 0].numpy()
         assert np.allclose(out[0, h * 8:(h + 1) * 8], ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------- continuation prefill
+def test_bf16_round_matches_library_cast_and_rounds_once():
+    """Where float32 holds the value exactly, one rounding to bf16 is torch's
+    float32 -> bfloat16 cast (nearest, ties to even); a value just above a
+    tie that float32 would first round onto the tie goes up, as one rounding
+    of the exact value must."""
+    rng = np.random.default_rng(0)
+    f = (rng.standard_normal(20000) * np.exp2(rng.integers(-140, 120, 20000))).astype(np.float32)
+    f = np.concatenate([f, np.float32([0.0, -0.0, 1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 3.3961e38, 3.3965e38])])
+    want = torch.from_numpy(f).to(torch.bfloat16).float().numpy().astype(np.float64)
+    got = O.bf16_round(f.astype(np.float64))
+    assert np.array_equal(got, want) and np.array_equal(np.signbit(got), np.signbit(want))
+    assert O.bf16_round(np.array([1 + 2 ** -8 + 2 ** -40]))[0] == 1 + 2 ** -7
+    assert O.bf16_round(np.array([-(1 + 2 ** -8 + 2 ** -40)]))[0] == -(1 + 2 ** -7)
+
+
+def _prefix_cache(rng, cached_len, hk, bs=16, k=None, v=None):
+    """A cache holding a sequence's first cached_len tokens (oracle store),
+    its blocks in a shuffled order."""
+    nblk = max(1, -(-cached_len // bs))
+    row = rng.permutation(nblk + 2)[:nblk].astype(np.int32)
+    cache = np.zeros((nblk + 2, bs, hk, O.SLOT_BYTES), dtype=np.uint8)
+    if cached_len:
+        kk = k if k is not None else bf16(rng.standard_normal((cached_len, hk, 256)))
+        vv = v if v is not None else bf16(rng.standard_normal((cached_len, hk, 256)))
+        t = np.arange(cached_len)
+        O.store(kk, vv, cache, row[t // bs].astype(np.int64) * bs + t % bs)
+    return cache, row
+
+
+@pytest.mark.parametrize("cached_len", [0, 1, 16, 37])
+def test_prefill_zero_query_is_running_mean(cached_len):
+    """q = 0: every visible key weighs the same, so query i returns the mean
+    of values 0 .. cached_len + i (the dequantised prefix, then the chunk):
+    pins the lower-right alignment and the order of prefix and chunk."""
+    rng = np.random.default_rng(cached_len)
+    q_len, hk, qg = 9, 2, 3
+    cache, row = _prefix_cache(rng, cached_len, hk)
+    q = bf16(np.zeros((q_len, hk * qg, 256)))
+    kc = bf16(rng.standard_normal((q_len, hk, 256)))
+    vc = bf16(rng.standard_normal((q_len, hk, 256)))
+    out = O.continuation_prefill(q, kc, vc, cache, row, cached_len, 0.3)
+    _, Vp = O.dequant_prefix(cache, row, cached_len)
+    V = np.concatenate([Vp, O.bf16_to_f64(vc)], axis=0)
+    run = np.cumsum(V, axis=0) / np.arange(1, len(V) + 1)[:, None, None]
+    for i in range(q_len):
+        for hq in range(hk * qg):
+            np.testing.assert_allclose(out[i, hq], run[cached_len + i, hq // qg], rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_rotation_consistent_between_prefix_chunk_and_query():
+    """Rows of 16 H rotate to 16 e_j exactly, and so store exactly as FP4
+    (code 4 under scale 2**2). With query i = 16 H[j_i] and every key a row
+    16 H[j] (prefix through the cache, chunk through the rotation), a score
+    is 256 * scale where the rows match and 0 elsewhere, so each output has
+    a closed form over the visible tokens. A rotation missing or applied
+    differently on one side breaks the match pattern."""
+    rng = np.random.default_rng(5)
+    H16 = O.hadamard(256) * 16
+    cached_len, q_len, hk, qg = 21, 6, 2, 2
+    idx_k = rng.integers(0, 4, (cached_len + q_len, hk))
+    idx_q = rng.integers(0, 4, (q_len, hk * qg))
+    keys = H16[idx_k]                                        # (seq, hk, 256), entries +-1
+    vals = rng.standard_normal((cached_len + q_len, hk, 256))
+    kb, vb = bf16(keys), bf16(vals)
+    cache, row = _prefix_cache(rng, cached_len, hk, k=kb[:cached_len], v=vb[:cached_len])
+    scale = 1 / 64                                           # match score 4
+    out = O.continuation_prefill(bf16(H16[idx_q]), kb[cached_len:], vb[cached_len:], cache, row,
+                                 cached_len, scale)
+    _, Vp = O.dequant_prefix(cache, row, cached_len)
+    V = np.concatenate([Vp, O.bf16_to_f64(vb[cached_len:])], axis=0)
+    for i in range(q_len):
+        n = cached_len + i + 1
+        for hq in range(hk * qg):
+            h = hq // qg
+            w = np.where(idx_k[:n, h] == idx_q[i, hq], math.exp(4.0), 1.0)
+            want = (w[:, None] * V[:n, h]).sum(0) / w.sum()
+            np.testing.assert_allclose(out[i, hq], want, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_first_query_without_prefix_is_first_value():
+    rng = np.random.default_rng(7)
+    q = bf16(rng.standard_normal((4, 8, 256)))
+    kc = bf16(rng.standard_normal((4, 1, 256)))
+    vc = bf16(rng.standard_normal((4, 1, 256)))
+    cache, row = _prefix_cache(rng, 0, 1)
+    out = O.continuation_prefill(q, kc, vc, cache, row, 0, 0.1)
+    assert np.array_equal(out[0], np.broadcast_to(O.bf16_to_f64(vc[0, 0]), (8, 256)))
+
+
+def test_prefill_matches_brute_force_loops():
+    """Tiny case against explicit loops over queries, keys and d, with the
+    rotation as a plain sum over H's entries written (-1)**popcount / 16."""
+    rng = np.random.default_rng(8)
+    cached_len, q_len, hk, qg, bs = 5, 3, 2, 2, 4
+    cache, row = _prefix_cache(rng, cached_len, hk, bs=bs)
+    q = bf16(rng.standard_normal((q_len, hk * qg, 256)))
+    kc = bf16(rng.standard_normal((q_len, hk, 256)))
+    vc = bf16(rng.standard_normal((q_len, hk, 256)))
+    scale = 0.07
+    got = O.continuation_prefill(q, kc, vc, cache, row, cached_len, scale)
+
+    def rot_bf16(bits):
+        x = [float(v) for v in O.bf16_to_f64(bits)]
+        y = [sum(x[i] * (-1) ** bin(i & j).count("1") for i in range(256)) / 16 for j in range(256)]
+        return [float(torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).double()) for v in y]
+
+    for h in range(hk):
+        keys, vals = [], []
+        for t in range(cached_len):
+            slot = cache[row[t // bs], t % bs, h]
+            k_t, v_t = O.decode_slots(slot)
+            keys.append(list(k_t))
+            vals.append(list(v_t))
+        for t in range(q_len):
+            keys.append(rot_bf16(kc[t, h]))
+            vals.append(list(O.bf16_to_f64(vc[t, h])))
+        for hq in range(h * qg, (h + 1) * qg):
+            for i in range(q_len):
+                qi = rot_bf16(q[i, hq])
+                n = cached_len + i + 1
+                s = [scale * sum(qi[d] * keys[j][d] for d in range(256)) for j in range(n)]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                want = [sum(w[j] * vals[j][d] for j in range(n)) / sum(w) for d in range(256)]
+                np.testing.assert_allclose(got[i, hq], want, rtol=1e-9, atol=1e-12)
