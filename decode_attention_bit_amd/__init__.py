@@ -14,6 +14,11 @@ Entry points mirror include/uq.h:
   decode_ex(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
             query_row=None, sinks=None, sliding_window=0,
             out=None, workspace=None)               -> (B, Hq, 256) bf16
+  rotate(x, out=None)                               -> bf16(x H), same shape
+  dequant_kv(kv_cache, block_row, n_tokens)         -> (K, V) (n_tokens, Hk, 256) bf16
+  prefill_attention(q, k, v, scale, out=None)       -> (q_len, Hq, 256) bf16
+  continuation_prefill(query, key, value, kv_cache, block_row, cached_len, scale,
+                       out=None, workspace=None)    -> (q_len, Hq, 256) bf16
 """
 from __future__ import annotations
 
@@ -22,7 +27,9 @@ import os
 
 import torch
 
-__all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_workspace_bytes", "library_path",
+__all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_workspace_bytes", "rotate",
+           "dequant_kv", "prefill_attention", "continuation_prefill",
+           "continuation_prefill_workspace_bytes", "library_path",
            "UQError", "HEAD_DIM", "SLOT_BYTES"]
 
 HEAD_DIM = 256
@@ -68,6 +75,19 @@ def _load():
     lib.uq_decode_ex.restype = i32
     lib.uq_decode_stages.argtypes = [i32] + lib.uq_decode.argtypes
     lib.uq_decode_stages.restype = i32
+    lib.uq_rotate.argtypes = [vp, vp, i64, i32, i32, i64, i64, i64, i64, vp]
+    lib.uq_rotate.restype = i32
+    lib.uq_dequant_kv.argtypes = [vp, vp, i32, vp, vp, i32, i32, i64, i32, i64, i64, vp]
+    lib.uq_dequant_kv.restype = i32
+    lib.uq_prefill_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
+                                         i64, i64, i64, i64, i64, i64, vp]
+    lib.uq_prefill_attention.restype = i32
+    lib.uq_continuation_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.uq_continuation_prefill_workspace_bytes.restype = sz
+    lib.uq_continuation_prefill.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, i32, i32,
+                                            i32, i64, i32, i64, i64, i64, i64, i64, i64, i64, i64,
+                                            vp, sz, vp]
+    lib.uq_continuation_prefill.restype = i32
     lib.uq_last_error.argtypes = []
     lib.uq_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -223,4 +243,116 @@ def decode_ex(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
                             _ptr(out), B, Hq, Hk, D, nb, bs, block_table.shape[1], query.stride(0),
                             query.stride(1), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(query.device)))
+    return out
+
+
+def _bf16_3d(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+        raise TypeError(f"{name} must be a 3-d bfloat16 tensor with a contiguous last dim")
+
+
+def rotate(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """uq_rotate: bf16(x H) for (N, H, 256) bf16 x (exact product, one rounding)."""
+    _bf16_3d(x, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _bf16_3d(out, "out")
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    N, H, D = x.shape
+    _check(_load().uq_rotate(_ptr(x), _ptr(out), N, H, D, x.stride(0), x.stride(1), out.stride(0),
+                             out.stride(1), _stream(x.device)))
+    return out
+
+
+def dequant_kv(kv_cache: torch.Tensor, block_row: torch.Tensor, n_tokens: int,
+               k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None):
+    """uq_dequant_kv: the first n_tokens tokens of the sequence whose logical
+    block j is physical block block_row[j], as (n_tokens, Hk, 256) bf16 K
+    (rotated basis) and V. k_out / v_out may be any (n_tokens, Hk, 256) views
+    with a contiguous last dim."""
+    if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
+        raise TypeError("kv_cache must be a contiguous 4-d uint8 tensor")
+    if block_row.dtype != torch.int32 or not block_row.is_contiguous():
+        raise TypeError("block_row must be a contiguous int32 tensor")
+    nb, bs, Hk, ss = kv_cache.shape
+    if block_row.numel() * bs < n_tokens:
+        raise ValueError("block_row holds fewer blocks than n_tokens needs")
+    shape = (int(n_tokens), Hk, HEAD_DIM)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=torch.bfloat16, device=kv_cache.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=torch.bfloat16, device=kv_cache.device)
+    for t, name in ((k_out, "k_out"), (v_out, "v_out")):
+        _bf16_3d(t, name)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    if k_out.stride() != v_out.stride():
+        raise ValueError("k_out and v_out must share strides")
+    _check(_load().uq_dequant_kv(_ptr(kv_cache), _ptr(block_row), int(n_tokens), _ptr(k_out),
+                                 _ptr(v_out), Hk, HEAD_DIM, nb, bs, k_out.stride(0), k_out.stride(1),
+                                 _stream(kv_cache.device)))
+    return k_out, v_out
+
+
+def prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """uq_prefill_attention: causal attention of (q_len, Hq, 256) bf16 queries
+    over (seq_len, Hk, 256) bf16 keys/values, query i at position
+    seq_len - q_len + i; returns (q_len, Hq, 256) bf16."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _bf16_3d(t, name)
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v must share shape and strides")
+    q_len, Hq, D = q.shape
+    seq_len, Hk, _ = k.shape
+    if out is None:
+        out = torch.empty((q_len, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _bf16_3d(out, "out")
+    _check(_load().uq_prefill_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), q_len, seq_len, Hq, Hk,
+                                        D, float(scale), q.stride(0), q.stride(1), k.stride(0),
+                                        k.stride(1), out.stride(0), out.stride(1), _stream(q.device)))
+    return out
+
+
+def continuation_prefill_workspace_bytes(q_len: int, max_seq_len: int, Hq: int, Hk: int,
+                                         D: int = HEAD_DIM) -> int:
+    n = _load().uq_continuation_prefill_workspace_bytes(int(q_len), int(max_seq_len), int(Hq),
+                                                        int(Hk), int(D))
+    if n == 0:
+        raise ValueError("invalid continuation-prefill shape")
+    return int(n)
+
+
+def continuation_prefill(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                         kv_cache: torch.Tensor, block_row: torch.Tensor | None, cached_len: int,
+                         scale: float, out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """uq_continuation_prefill: a chunk of q_len tokens (query (q_len, Hq, 256),
+    key / value (q_len, Hk, 256), bf16, unrotated) after cached_len cached
+    tokens reached through block_row; returns (q_len, Hq, 256) bf16."""
+    for t, name in ((query, "query"), (key, "key"), (value, "value")):
+        _bf16_3d(t, name)
+    if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
+        raise TypeError("kv_cache must be a contiguous 4-d uint8 tensor")
+    if block_row is not None and (block_row.dtype != torch.int32 or not block_row.is_contiguous()):
+        raise TypeError("block_row must be a contiguous int32 tensor")
+    q_len, Hq, D = query.shape
+    nb, bs, Hk, ss = kv_cache.shape
+    if key.shape != (q_len, Hk, D) or value.shape != (q_len, Hk, D):
+        raise ValueError("key and value must be (q_len, Hk, 256)")
+    if cached_len > 0 and (block_row is None or block_row.numel() * bs < cached_len):
+        raise ValueError("block_row holds fewer blocks than cached_len needs")
+    if out is None:
+        out = torch.empty((q_len, Hq, D), dtype=torch.bfloat16, device=query.device)
+    _bf16_3d(out, "out")
+    lib = _load()
+    need = lib.uq_continuation_prefill_workspace_bytes(q_len, int(cached_len) + q_len, Hq, Hk, D)
+    if workspace is None:
+        workspace = _workspace(query.device, max(int(need), 256))
+    _check(lib.uq_continuation_prefill(
+        _ptr(query), _ptr(key), _ptr(value), _ptr(kv_cache), _ptr(block_row), int(cached_len),
+        float(scale), _ptr(out), q_len, Hq, Hk, D, nb, bs, query.stride(0), query.stride(1),
+        key.stride(0), key.stride(1), value.stride(0), value.stride(1), out.stride(0), out.stride(1),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(query.device)))
     return out

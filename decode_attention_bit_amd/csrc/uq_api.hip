@@ -167,6 +167,173 @@ int uq_decode(const uint16_t* query, const uint8_t* kv_cache, const int32_t* blo
                           workspace, workspace_bytes, stream);
 }
 
+int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t x_stride_n,
+              int64_t x_stride_h, int64_t out_stride_n, int64_t out_stride_h, void* stream) {
+  if (N < 0 || H < 1) return fail(UQ_EINVAL, "uq_rotate: N=%lld H=%d", (long long)N, H);
+  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_rotate: head_dim %d unsupported (only 256)", D);
+  if (N == 0) return ok();
+  if (!x || !out) return fail(UQ_EINVAL, "uq_rotate: null pointer argument");
+  if (x_stride_n < 0 || x_stride_h < 0 || out_stride_n < 0 || out_stride_h < 0 || x_stride_n % 4 ||
+      x_stride_h % 4 || out_stride_n % 4 || out_stride_h % 4)
+    return fail(UQ_EINVAL, "uq_rotate: strides must be non-negative multiples of 4 elements");
+  if (!aligned(x, 8) || !aligned(out, 8)) return fail(UQ_EINVAL, "uq_rotate: x and out must be 8-byte aligned");
+  if ((N * H + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "uq_rotate: N*H too large for one launch");
+  uq::GatherArgs a{};
+  a.job[0] = uq::VecJob{x, x_stride_n, x_stride_h, out, out_stride_n, out_stride_h, N * H, H, 1};
+  return hip_status(uq::launch_gather(a, (hipStream_t)stream), "uq_rotate launch");
+}
+
+int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_tokens, uint16_t* k_out,
+                  uint16_t* v_out, int Hk, int D, int64_t num_blocks, int block_size,
+                  int64_t out_stride_t, int64_t out_stride_h, void* stream) {
+  if (n_tokens < 0 || Hk < 1 || num_blocks < 1)
+    return fail(UQ_EINVAL, "uq_dequant_kv: n_tokens=%d Hk=%d num_blocks=%lld", n_tokens, Hk, (long long)num_blocks);
+  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_dequant_kv: head_dim %d unsupported (only 256)", D);
+  if (!pow2_in(block_size, 16, 256))
+    return fail(UQ_EUNSUPPORTED, "uq_dequant_kv: block_size %d unsupported (16, 32, 64, 128, 256)", block_size);
+  if (n_tokens == 0) return ok();
+  if (!kv_cache || !block_row || !k_out || !v_out) return fail(UQ_EINVAL, "uq_dequant_kv: null pointer argument");
+  if (out_stride_t < 0 || out_stride_h < 0 || out_stride_t % 8 || out_stride_h % 8)
+    return fail(UQ_EINVAL, "uq_dequant_kv: output strides must be non-negative multiples of 8 elements");
+  if (!aligned(kv_cache, 16) || !aligned(block_row, 4) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(UQ_EINVAL, "uq_dequant_kv: misaligned pointer (kv_cache, k_out, v_out 16 B; block_row 4 B)");
+  if (((long long)n_tokens * Hk + 3) / 4 > 0x7FFFFFFFLL)
+    return fail(UQ_EUNSUPPORTED, "uq_dequant_kv: n_tokens*Hk too large for one launch");
+  int log2_bs = 0;
+  while ((1 << log2_bs) < block_size) ++log2_bs;
+  uq::GatherArgs a{};
+  a.cache = kv_cache;
+  a.block_row = block_row;
+  a.n_tok = n_tokens;
+  a.Hk = Hk;
+  a.num_blocks = num_blocks;
+  a.log2_bs = log2_bs;
+  a.kout = k_out;
+  a.vout = v_out;
+  a.os_t = out_stride_t;
+  a.os_h = out_stride_h;
+  return hip_status(uq::launch_gather(a, (hipStream_t)stream), "uq_dequant_kv launch");
+}
+
+static int check_attention_shape(const char* who, int q_len, int seq_len, int Hq, int Hk, int D, float scale) {
+  if (q_len < 0 || seq_len < q_len || Hq < 1 || Hk < 1)
+    return fail(UQ_EINVAL, "%s: q_len=%d seq_len=%d Hq=%d Hk=%d", who, q_len, seq_len, Hq, Hk);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(UQ_EINVAL, "%s: scale must be finite and > 0", who);
+  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "%s: head_dim %d unsupported (only 256)", who, D);
+  if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "%s: Hq=%d is not a multiple of Hk=%d", who, Hq, Hk);
+  if (uq::prefill_positions_per_wg(Hq / Hk) < 1)
+    return fail(UQ_EUNSUPPORTED, "%s: GQA group %d above 128", who, Hq / Hk);
+  if (Hk > 65535) return fail(UQ_EUNSUPPORTED, "%s: Hk=%d above 65535", who, Hk);
+  return ok();
+}
+
+int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                         int q_len, int seq_len, int Hq, int Hk, int D, float scale,
+                         int64_t q_stride_t, int64_t q_stride_h, int64_t kv_stride_t,
+                         int64_t kv_stride_h, int64_t out_stride_t, int64_t out_stride_h,
+                         void* stream) {
+  const int rc = check_attention_shape("uq_prefill_attention", q_len, seq_len, Hq, Hk, D, scale);
+  if (rc != UQ_OK) return rc;
+  if (q_len == 0) return ok();
+  if (!q || !k || !v || !out) return fail(UQ_EINVAL, "uq_prefill_attention: null pointer argument");
+  if (q_stride_t < 0 || q_stride_h < 0 || kv_stride_t < 0 || kv_stride_h < 0 || out_stride_t < 0 ||
+      out_stride_h < 0 || q_stride_t % 8 || q_stride_h % 8 || kv_stride_t % 8 || kv_stride_h % 8 ||
+      out_stride_t % 8 || out_stride_h % 8)
+    return fail(UQ_EINVAL, "uq_prefill_attention: strides must be non-negative multiples of 8 elements");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(UQ_EINVAL, "uq_prefill_attention: q, k, v and out must be 16-byte aligned");
+  uq::PrefillAttnArgs a{q, k, v, out, q_stride_t, q_stride_h, kv_stride_t, kv_stride_h,
+                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale};
+  return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_prefill_attention launch");
+}
+
+// Workspace of uq_continuation_prefill: rotated queries, then keys and
+// values of prefix + chunk, each 256-byte aligned.
+struct PrefillLayout {
+  size_t q_off, k_off, v_off, total;
+};
+
+static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, int Hk) {
+  auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  PrefillLayout l{};
+  l.q_off = 0;
+  l.k_off = a256((size_t)q_len * Hq * UQ_HEAD_DIM * 2);
+  l.v_off = l.k_off + a256((size_t)seq_len * Hk * UQ_HEAD_DIM * 2);
+  l.total = l.v_off + a256((size_t)seq_len * Hk * UQ_HEAD_DIM * 2);
+  return l;
+}
+
+size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int Hq, int Hk, int D) {
+  if (q_len < 0 || max_seq_len < q_len || Hq < 1 || Hk < 1 || Hq % Hk || D != UQ_HEAD_DIM) return 0;
+  const size_t t = prefill_layout(q_len, max_seq_len, Hq, Hk).total;
+  return t > 0 ? t : 256;
+}
+
+int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const uint16_t* value,
+                            const uint8_t* kv_cache, const int32_t* block_row, int cached_len,
+                            float scale, uint16_t* out, int q_len, int Hq, int Hk, int D,
+                            int64_t num_blocks, int block_size, int64_t q_stride_t,
+                            int64_t q_stride_h, int64_t key_stride_t, int64_t key_stride_h,
+                            int64_t val_stride_t, int64_t val_stride_h, int64_t out_stride_t,
+                            int64_t out_stride_h, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const char* who = "uq_continuation_prefill";
+  if (cached_len < 0 || (long long)cached_len + q_len > 0x7FFFFFFFLL)
+    return fail(UQ_EINVAL, "%s: cached_len=%d", who, cached_len);
+  const int seq_len = cached_len + q_len;
+  int rc = check_attention_shape(who, q_len, seq_len, Hq, Hk, D, scale);
+  if (rc != UQ_OK) return rc;
+  if (num_blocks < 1) return fail(UQ_EINVAL, "%s: num_blocks=%lld < 1", who, (long long)num_blocks);
+  if (!pow2_in(block_size, 16, 256))
+    return fail(UQ_EUNSUPPORTED, "%s: block_size %d unsupported (16, 32, 64, 128, 256)", who, block_size);
+  if (q_len == 0) return ok();
+  if (!query || !key || !value || !kv_cache || !out || !workspace || (cached_len > 0 && !block_row))
+    return fail(UQ_EINVAL, "%s: null pointer argument", who);
+  if (q_stride_t < 0 || q_stride_h < 0 || key_stride_t < 0 || key_stride_h < 0 || val_stride_t < 0 ||
+      val_stride_h < 0 || q_stride_t % 4 || q_stride_h % 4 || key_stride_t % 4 || key_stride_h % 4 ||
+      val_stride_t % 4 || val_stride_h % 4)
+    return fail(UQ_EINVAL, "%s: input strides must be non-negative multiples of 4 elements", who);
+  if (out_stride_t < 0 || out_stride_h < 0 || out_stride_t % 8 || out_stride_h % 8)
+    return fail(UQ_EINVAL, "%s: output strides must be non-negative multiples of 8 elements", who);
+  if (!aligned(query, 8) || !aligned(key, 8) || !aligned(value, 8) || !aligned(kv_cache, 16) ||
+      !aligned(block_row, 4) || !aligned(out, 16) || !aligned(workspace, 256))
+    return fail(UQ_EINVAL, "%s: misaligned pointer (query/key/value 8 B, kv_cache/out 16 B, workspace 256 B)", who);
+  const PrefillLayout lay = prefill_layout(q_len, seq_len, Hq, Hk);
+  if (workspace_bytes < lay.total)
+    return fail(UQ_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, lay.total);
+  const long long waves = (long long)seq_len * Hk * 2 + (long long)q_len * Hq;
+  if ((waves + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "%s: too large for one launch", who);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  uint16_t* qr = reinterpret_cast<uint16_t*>(ws + lay.q_off);
+  uint16_t* kf = reinterpret_cast<uint16_t*>(ws + lay.k_off);
+  uint16_t* vf = reinterpret_cast<uint16_t*>(ws + lay.v_off);
+  const int64_t row = (int64_t)Hk * UQ_HEAD_DIM;          // token stride of the key/value buffers
+  int log2_bs = 0;
+  while ((1 << log2_bs) < block_size) ++log2_bs;
+  uq::GatherArgs g{};
+  g.cache = kv_cache;
+  g.block_row = block_row;
+  g.n_tok = cached_len;
+  g.Hk = Hk;
+  g.num_blocks = num_blocks;
+  g.log2_bs = log2_bs;
+  g.kout = kf;
+  g.vout = vf;
+  g.os_t = row;
+  g.os_h = UQ_HEAD_DIM;
+  g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM,
+                        (int64_t)q_len * Hq, Hq, 1};
+  g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, UQ_HEAD_DIM,
+                        (int64_t)q_len * Hk, Hk, 1};
+  g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, vf + (int64_t)cached_len * row, row, UQ_HEAD_DIM,
+                        (int64_t)q_len * Hk, Hk, 0};
+  hipError_t e = uq::launch_gather(g, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");
+  uq::PrefillAttnArgs a{qr, kf, vf, out, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM, row, UQ_HEAD_DIM,
+                        out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale};
+  return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_continuation_prefill attention launch");
+}
+
 const char* uq_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -46,11 +46,51 @@ struct DecodeArgs {
   uint8_t* workspace;
 };
 
+// Continuation prefill operands. A job maps n = N * H vectors of 256 bf16
+// (vector w -> row t = w / H, head h = w % H) from src to dst, rotated
+// (dst = bf16(src H)) or copied.
+struct VecJob {
+  const uint16_t* src;
+  int64_t ss_t, ss_h;
+  uint16_t* dst;
+  int64_t ds_t, ds_h;
+  int64_t n;
+  int H;
+  int rotate;
+};
+
+struct GatherArgs {
+  // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])
+  const uint8_t* cache;
+  const int32_t* block_row;
+  int n_tok;
+  int Hk;
+  int64_t num_blocks;
+  int log2_bs;
+  uint16_t* kout;
+  uint16_t* vout;
+  int64_t os_t, os_h;
+  VecJob job[3];
+};
+
+struct PrefillAttnArgs {
+  const uint16_t* q;         // (q_len, Hq, 256) rotated queries, bf16
+  const uint16_t* k;         // (cached_len + q_len, Hk, 256) rotated keys, bf16
+  const uint16_t* v;         // same shape, values
+  uint16_t* out;             // (q_len, Hq, 256)
+  int64_t qs_t, qs_h, kvs_t, kvs_h, os_t, os_h;
+  int q_len, cached_len, Hk, QG;
+  float scale;
+};
+
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
                        int block_size);
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_hadamard(int D, float* H, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream);
+int prefill_positions_per_wg(int QG);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mask, hipStream_t stream);
 
 }  // namespace uq

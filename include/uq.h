@@ -206,6 +206,102 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
                      int64_t q_stride_b, int64_t q_stride_h, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * Continuation prefill (ultraquant_attn page, _prefill_attention continuation
+ * branch for chunks above the decode threshold, and
+ * _ultraquant_continuation_prefill): a chunk of q_len new tokens of one
+ * sequence, whose first cached_len tokens are already in the cache, attends
+ * to the dequantised prefix and to itself. Query i of the chunk sits at
+ * absolute position cached_len + i and sees keys 0 .. cached_len + i (causal
+ * attention with unequal query/key lengths, aligned to the lower right).
+ * The four calls below are the steps of that path; uq_continuation_prefill
+ * runs all of them.
+ */
+
+/*
+ * out[n, h, :] = bf16(x[n, h, :] H) for n < N, h < H: the rotation the page
+ * applies to the chunk's keys and queries ((x.float() @ PiT).to(bf16)). The
+ * product is computed exactly (float64 butterfly) and rounded once to bf16,
+ * nearest-even; the sign of an exactly-zero result is not defined.
+ *   x, out:   (device) bf16, last dim contiguous, 8-byte aligned; strides in
+ *             elements, non-negative multiples of 4. out may equal x (with
+ *             the same strides); other overlaps are undefined.
+ *   D:        256 only (UQ_EUNSUPPORTED otherwise).
+ * Errors: UQ_EINVAL for N < 0, H < 1, a null pointer (N > 0), bad strides
+ * or alignment; UQ_EHIP for a launch failure.
+ */
+int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t x_stride_n,
+              int64_t x_stride_h, int64_t out_stride_n, int64_t out_stride_h, void* stream);
+
+/*
+ * Dequantise a sequence's first n_tokens tokens (ultraquant_full_dequant_kv
+ * on the page): k_out[t, h, :] and v_out[t, h, :] = E2M1 code * 2^(scale - 127)
+ * as bf16, K left in the rotated basis. Exact: every such value is a bf16
+ * value (0.5 * 2^-127 and up); codes of magnitude 0 give signed zeros.
+ *   kv_cache:  (device) the uq_store cache, 16-byte aligned.
+ *   block_row: (device) int32, at least ceil(n_tokens / block_size) entries:
+ *              physical block of logical block j. An entry outside
+ *              [0, num_blocks) reads as zeros.
+ *   k_out, v_out: (device) bf16, 16-byte aligned; element [t, h, d] at
+ *              t * out_stride_t + h * out_stride_h + d, strides non-negative
+ *              multiples of 8 (e.g. Hk*256 and 256 for (n, Hk, 256), or 256
+ *              and n*256 for the page's (Hk, n, 256) buffers).
+ * Errors: UQ_EINVAL / UQ_EUNSUPPORTED for bad shapes, pointers, strides or
+ * block sizes; UQ_EHIP for a launch failure.
+ */
+int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_tokens, uint16_t* k_out,
+                  uint16_t* v_out, int Hk, int D, int64_t num_blocks, int block_size,
+                  int64_t out_stride_t, int64_t out_stride_h, void* stream);
+
+/*
+ * Dense causal attention over bf16 operands already in the rotated basis:
+ * out[i, hq] = softmax_j(scale * q[i, hq] . k[j, hk]) v[j, hk] over
+ * j <= seq_len - q_len + i, with hk = hq / (Hq / Hk) (the flash-attention
+ * step of the page's path, causal=True with q_len <= seq_len).
+ *   q:    (device) bf16 (q_len, Hq, 256); k, v: (seq_len, Hk, 256) sharing
+ *         strides; out: (q_len, Hq, 256) bf16. All 16-byte aligned, strides
+ *         in elements, non-negative multiples of 8.
+ *   scale: finite, > 0. Hq / Hk at most 128.
+ * Errors: UQ_EINVAL for q_len < 0, seq_len < q_len, a null pointer, bad
+ * strides or alignment; UQ_EUNSUPPORTED for D != 256 or Hq % Hk; UQ_EHIP.
+ */
+int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
+                         int q_len, int seq_len, int Hq, int Hk, int D, float scale,
+                         int64_t q_stride_t, int64_t q_stride_h, int64_t kv_stride_t,
+                         int64_t kv_stride_h, int64_t out_stride_t, int64_t out_stride_h,
+                         void* stream);
+
+/* Workspace bytes of uq_continuation_prefill for chunks of up to q_len
+ * tokens and sequences of up to max_seq_len tokens (0 on invalid shapes). */
+size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int Hq, int Hk, int D);
+
+/*
+ * The whole continuation prefill of one sequence: dequantise the prefix,
+ * rotate the chunk's keys and the queries, append the chunk's values, then
+ * attend (uq_dequant_kv, uq_rotate and uq_prefill_attention on buffers in
+ * the workspace; two launches on `stream`).
+ *   query:  (device) bf16 (q_len, Hq, 256) before rotation; key, value:
+ *           (q_len, Hk, 256) of the chunk (key before rotation). 8-byte
+ *           aligned, strides non-negative multiples of 4 elements.
+ *   kv_cache, block_row, num_blocks, block_size: as uq_dequant_kv, for the
+ *           cached_len tokens already stored (block_row may be NULL when
+ *           cached_len is 0).
+ *   out:    (device) bf16 (q_len, Hq, 256), 16-byte aligned, strides
+ *           multiples of 8.
+ *   workspace: (device) 256-byte aligned, at least
+ *           uq_continuation_prefill_workspace_bytes(q_len, cached_len + q_len,
+ *           Hq, Hk, D) bytes; owned by the caller, clobbered.
+ * Errors: as the three calls, plus UQ_EWORKSPACE.
+ */
+int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const uint16_t* value,
+                            const uint8_t* kv_cache, const int32_t* block_row, int cached_len,
+                            float scale, uint16_t* out, int q_len, int Hq, int Hk, int D,
+                            int64_t num_blocks, int block_size, int64_t q_stride_t,
+                            int64_t q_stride_h, int64_t key_stride_t, int64_t key_stride_h,
+                            int64_t val_stride_t, int64_t val_stride_h, int64_t out_stride_t,
+                            int64_t out_stride_h, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Message describing the last non-zero return on the calling thread
  * ("" if none). The pointer stays valid until the thread's next call. */
 const char* uq_last_error(void);

@@ -435,7 +435,7 @@ def dequant_prefix(kv_cache: np.ndarray, block_row: np.ndarray, n: int):
 
 
 def continuation_prefill(query_bits, key_bits, value_bits, kv_cache, block_row, cached_len,
-                         scale) -> np.ndarray:
+                         scale, rows=None) -> np.ndarray:
     """Output (q_len, Hq, 256) float64 of a continuation chunk.
 
     query_bits (q_len, Hq, 256), key_bits / value_bits (q_len, Hk, 256) are
@@ -443,7 +443,8 @@ def continuation_prefill(query_bits, key_bits, value_bits, kv_cache, block_row, 
     tokens are in kv_cache through block_row. Keys are the dequantised
     prefix followed by the chunk's rotated keys (as bf16); values are the
     dequantised prefix followed by the chunk's values. Query head hq reads KV
-    head hq // (Hq // Hk).
+    head hq // (Hq // Hk). ``rows`` optionally lists the chunk positions to
+    compute (the others are left NaN); every key and value is still used.
     """
     query_bits = np.asarray(query_bits)
     q_len, hq_n, _ = query_bits.shape
@@ -452,14 +453,15 @@ def continuation_prefill(query_bits, key_bits, value_bits, kv_cache, block_row, 
     Kp, Vp = dequant_prefix(kv_cache, block_row, cached_len)
     K = np.concatenate([Kp, rotate_to_bf16(key_bits)], axis=0)
     V = np.concatenate([Vp, bf16_to_f64(value_bits)], axis=0)
-    q = rotate_to_bf16(query_bits)
+    rows = np.arange(q_len) if rows is None else np.asarray(rows, dtype=np.int64)
+    q = rotate_to_bf16(query_bits[rows])
     seq = cached_len + q_len
-    visible = np.arange(seq)[None, :] <= cached_len + np.arange(q_len)[:, None]
-    out = np.zeros((q_len, hq_n, D))
+    visible = np.arange(seq)[None, :] <= cached_len + rows[:, None]
+    out = np.full((q_len, hq_n, D), np.nan)
     for hq in range(hq_n):
         h = hq // qg
         s = scale * (q[:, hq] @ K[:, h].T)
         s = np.where(visible, s, -np.inf)
         p = np.exp(s - s.max(axis=-1, keepdims=True))
-        out[:, hq] = (p @ V[:, h]) / p.sum(axis=-1, keepdims=True)
+        out[rows, hq] = (p @ V[:, h]) / p.sum(axis=-1, keepdims=True)
     return out

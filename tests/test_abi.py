@@ -19,7 +19,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("uq_build_hadamard", "uq_store", "uq_decode", "uq_decode_ex", "uq_decode_stages",
-              "uq_decode_workspace_bytes", "uq_last_error"):
+              "uq_decode_workspace_bytes", "uq_rotate", "uq_dequant_kv", "uq_prefill_attention",
+              "uq_continuation_prefill", "uq_continuation_prefill_workspace_bytes", "uq_last_error"):
         assert n in names
 
 
@@ -134,3 +135,87 @@ def decode_ex_args(**kw):
 def test_decode_ex_rejects(libuq, kw, code):
     assert libuq.uq_decode_ex(*decode_ex_args(**kw)) == code
     assert _err(libuq)
+
+
+# ------------------------------------------------------ continuation prefill
+def rotate_args(**kw):
+    a = dict(x=FAKE, out=FAKE, N=4, H=2, D=256, xsn=512, xsh=256, osn=512, osh=256, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), -1), (dict(H=0), -1), (dict(D=128), -2), (dict(x=None), -1),
+    (dict(xsh=6), -1), (dict(osn=-4), -1), (dict(out=FAKE + 4), -1),
+])
+def test_rotate_rejects(libuq, kw, code):
+    assert libuq.uq_rotate(*rotate_args(**kw)) == code
+    assert _err(libuq)
+
+
+def test_rotate_empty_is_noop(libuq):
+    assert libuq.uq_rotate(*rotate_args(N=0, x=None, out=None)) == 0
+
+
+def dequant_args(**kw):
+    a = dict(kv_cache=FAKE, block_row=FAKE, n=40, k_out=FAKE, v_out=FAKE, Hk=2, D=256,
+             num_blocks=8, block_size=16, ost=512, osh=256, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), -1), (dict(Hk=0), -1), (dict(num_blocks=0), -1), (dict(D=512), -2),
+    (dict(block_size=8), -2), (dict(block_row=None), -1), (dict(ost=4), -1),
+    (dict(k_out=FAKE + 8), -1), (dict(kv_cache=FAKE + 4), -1),
+])
+def test_dequant_kv_rejects(libuq, kw, code):
+    assert libuq.uq_dequant_kv(*dequant_args(**kw)) == code
+    assert _err(libuq)
+
+
+def prefill_attention_args(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, q_len=8, seq_len=20, Hq=16, Hk=2, D=256,
+             scale=0.0625, qst=4096, qsh=256, kvst=512, kvsh=256, ost=4096, osh=256, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_len=-1), -1), (dict(seq_len=7), -1), (dict(scale=0.0), -1),
+    (dict(scale=float("inf")), -1), (dict(D=128), -2), (dict(Hq=15), -2),
+    (dict(Hq=258, Hk=2), -2), (dict(v=None), -1), (dict(kvst=508), -1), (dict(out=FAKE + 8), -1),
+])
+def test_prefill_attention_rejects(libuq, kw, code):
+    assert libuq.uq_prefill_attention(*prefill_attention_args(**kw)) == code
+    assert _err(libuq)
+
+
+def continuation_args(**kw):
+    a = dict(query=FAKE, key=FAKE, value=FAKE, kv_cache=FAKE, block_row=FAKE, cached_len=100,
+             scale=0.0625, out=FAKE, q_len=8, Hq=16, Hk=2, D=256, num_blocks=64, block_size=16,
+             qst=4096, qsh=256, kst=512, ksh=256, vst=512, vsh=256, ost=4096, osh=256,
+             workspace=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cached_len=-1), -1), (dict(block_row=None), -1), (dict(workspace=FAKE + 16), -1),
+    (dict(ws_bytes=4096), -3), (dict(block_size=48), -2), (dict(Hq=17), -2),
+    (dict(ost=4), -1), (dict(kst=2), -1), (dict(query=FAKE + 2), -1),
+])
+def test_continuation_prefill_rejects(libuq, kw, code):
+    assert libuq.uq_continuation_prefill(*continuation_args(**kw)) == code
+    assert _err(libuq)
+
+
+def test_continuation_prefill_workspace_bytes(libuq):
+    f = libuq.uq_continuation_prefill_workspace_bytes
+    assert f(8, 7, 16, 2, 256) == 0
+    assert f(8, 100, 15, 2, 256) == 0
+    assert f(8, 100, 16, 2, 128) == 0
+    n = f(8, 100, 16, 2, 256)
+    # rotated queries, then keys and values of the whole sequence, as bf16
+    assert n == 8 * 16 * 512 + 2 * 100 * 2 * 512
+    assert f(8, 101, 16, 2, 256) > n
