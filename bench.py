@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     help="decode (the default line), or tiny / ragged / long / mixed; mixed times a "
-                         "store of one token per sequence together with the decode")
+                         "store of one token per sequence together with the decode; prefill times "
+                         "uq_continuation_prefill (a 2048-token chunk after 4096 cached tokens)")
     ap.add_argument("--queries-per-seq", type=int, default=1,
                     help="decode this many query rows per sequence (a speculative step), each "
                          "reading its own prefix, through uq_decode_ex")
@@ -243,6 +244,122 @@ def cpu_baseline(w, lay, seconds):
                       f"({done_bytes / 1e6:.1f} MB of cache), {elapsed:.1f} s, cache encoding untimed"}
 
 
+# Continuation prefill: one sequence of the decode workload's shape (Hq 32,
+# Hk 4, D 256) holding 4096 cached tokens receives a 2048-token chunk.
+PREFILL = dict(cached=4096, q_len=2048, Hq=32, Hk=4, block_size=16, scale=1 / 16, seed=7)
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(cached, q_len, Hq):
+    """QK and PV multiply-adds over the visible (query, key) pairs:
+    4 * D * Hq * sum_i (cached + i + 1)."""
+    return 4 * 256 * Hq * (q_len * cached + q_len * (q_len + 1) // 2)
+
+
+def time_events(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    busy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds):
+    """The oracle, untuned, on sampled chunk positions (every key still
+    dequantised and rotated), one BLAS thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from decode_attention_bit_amd import inputs
+    from oracle import uq_oracle as O
+
+    qb, kb, vb = (inputs.bf16_bits(t.cpu()) for t in (q, kc, vc))
+    cache_np, row_np = cache.cpu().numpy(), row.cpu().numpy()
+    rng = np.random.default_rng(0)
+    done, flops, elapsed = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while elapsed < seconds and done < P["q_len"]:
+            rows = rng.integers(0, P["q_len"], 4)
+            t = time.perf_counter()
+            O.continuation_prefill(qb, kb, vb, cache_np, row_np, P["cached"], P["scale"], rows=rows)
+            elapsed += time.perf_counter() - t
+            done += len(rows)
+            flops += sum(4 * 256 * P["Hq"] * (P["cached"] + int(i) + 1) for i in rows)
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} chunk positions of this workload, each call dequantising the whole "
+                      f"prefix and rotating the whole chunk, {elapsed:.1f} s"}
+
+
+def prefill_main(args):
+    import numpy as np
+    import torch
+
+    import decode_attention_bit_amd as uq
+
+    P = PREFILL
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(P["seed"])
+    bs, Hk, Hq, cached, q_len = P["block_size"], P["Hk"], P["Hq"], P["cached"], P["q_len"]
+    nblk = cached // bs
+    log(f"setup prefill: {cached} cached + {q_len} chunk tokens")
+    cache = torch.zeros((nblk + 64, bs, Hk, 272), dtype=torch.uint8, device=dev)
+    row = torch.randperm(nblk + 64, generator=g)[:nblk].to(torch.int32).to(dev)
+    randn = lambda *shape: torch.randn(shape, generator=g).to(torch.bfloat16).to(dev)
+    k, v = randn(cached, Hk, 256), randn(cached, Hk, 256)
+    t = torch.arange(cached, device=dev)
+    uq.store(k, v, cache, row[t // bs].long() * bs + t % bs)
+    q, kc, vc = randn(q_len, Hq, 256), randn(q_len, Hk, 256), randn(q_len, Hk, 256)
+    out = torch.empty((q_len, Hq, 256), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(uq.continuation_prefill_workspace_bytes(q_len, cached + q_len, Hq, Hk),
+                     dtype=torch.uint8, device=dev)
+    steps = max(1, args.steps // 4)
+    warmup = max(1, args.warmup // 4)
+    log(f"timing {steps} calls")
+    call = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, P["scale"], out=out, workspace=ws)
+    ms = time_events(call, steps, warmup)
+    # the attention kernel alone, on operands of the same shapes
+    qr, kf, vf = randn(q_len, Hq, 256), randn(cached + q_len, Hk, 256), randn(cached + q_len, Hk, 256)
+    attn = lambda: uq.prefill_attention(qr, kf, vf, P["scale"], out=out)
+    attn_ms = time_events(attn, steps, warmup)
+    fl = prefill_flops(cached, q_len, Hq)
+    tf = fl / (ms * 1e-3) / 1e12
+    attn_tf = fl / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": f"continuation prefill TFLOP/s (bf16 MFMA), {q_len}-token chunk after {cached} cached "
+                  f"tokens, GQA-8 D=256",
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-mfma",
+        "data": "synthetic",
+        "config": {"workload": f"prefill: cached_len={cached} q_len={q_len} Hq={Hq} Hk={Hk} D=256 "
+                               f"block_size={bs} (step = one uq_continuation_prefill)",
+                   "flops_per_step": fl},
+        "tokens_per_s": round(q_len / (ms * 1e-3), 1),
+        "stage_ms": {"whole_call": round(ms, 5), "attention_alone": round(attn_ms, 5)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_attn_kernel", "flops_per_launch": fl},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        res["cpu_baseline"] = prefill_cpu_baseline(P, q, kc, vc, cache, row, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -250,6 +367,8 @@ def main():
                                    "part of this build (see DESIGN.md for how the path would shard)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.workload == "prefill":
+        return prefill_main(args)
     import torch
 
     from decode_attention_bit_amd import inputs

@@ -119,8 +119,11 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
 // are (position, query head) pairs of that KV head, column c -> position
 // p0 + c / QG, head hk * QG + c % QG, so the QG heads sharing a KV head share
 // every K/V tile. Wave w owns columns 32w .. 32w+31 as two 16-column blocks.
-// Keys stream in tiles of 32 through a double-buffered LDS copy (rows padded
-// to 528 bytes so that the reads below hit distinct banks).
+// Keys stream in tiles of 32 through a kStages-deep LDS ring filled by
+// direct-to-LDS buffer loads (each wave moves 8 of the 32 rows of K and of V,
+// two rows per load); the rows are 512 bytes with their 16-byte chunks
+// permuted (chunk c of row r stored at c ^ f(r)) so that the reads below hit
+// distinct banks: f(r) = r & 15 for K, ((r >> 2) & 3) << 2 for V.
 //
 // V_MFMA_F32_16X16X32_BF16, lane l: row/col l%16, k-slots (l/16, 0..7);
 // result lane l: col l%16, rows 4*(l/16) + i. Which k a slot stands for is
@@ -129,18 +132,42 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
 //     step j (16 contiguous bytes of a K row), B = the same d of the query
 //     (held in registers). The result leaves lane (col, g) with keys
 //     16kb + 4g + i of its column.
-//   O^T (dims x cols) += V^T P^T: slot (g, s) = key 4g + s (s < 4) or
-//     16 + 4g + s - 4, exactly the keys lane (col, g) holds, so P^T needs no
-//     data movement. A = V^T: lane (r, g) reads the dword holding dims
-//     32b + 2r, 2r + 1 of those 8 keys and feeds two MFMAs, one for the even
-//     dims (row r -> dim 32b + 2r) and one for the odd ones.
+//   O (cols x dims) += P V: slot (g, s) = key 4g + s (s < 4) or
+//     16 + 4g + s - 4, exactly the keys lane (col, g) holds, so P as the A
+//     operand needs no data movement. B = V: lane (r, g) reads the dword
+//     holding dims 32b + 2r, 2r + 1 of those 8 keys and feeds two MFMAs, one
+//     for the even dims (col r -> dim 32b + 2r) and one for the odd ones.
+//     Rows of O are query columns, so a rescale is diag(f) O (see below).
 // Online softmax in the log2 domain with a reference maximum that is only
 // raised when a tile exceeds it by more than 8 (weights stay <= 2^8 in bf16);
 // the denominator sums the same bf16 weights the product uses.
 // ---------------------------------------------------------------------------
 constexpr int kKeyTile = 32;
-constexpr int kRowBytes = 2 * kHeadDim + 16;
+constexpr int kRowBytes = 2 * kHeadDim;
+constexpr int kTileU4 = kKeyTile * kRowBytes / 16;      // 1024 chunks of 16 bytes
 constexpr int kColsPerWg = 128;
+constexpr int kStages = 4;
+constexpr int kDmaPerTile = 8;                          // per wave: 4 for K, 4 for V
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt on vector memory only (gfx9 encoding; expcnt and lgkmcnt left free)
+#define UQP_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+
+// Wait until at most min(K, ahead) tiles are still in flight (the waitcnt
+// immediate must be a constant).
+template <int K>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if constexpr (K == 0) {
+    UQP_WAIT_VMCNT(0);
+  } else {
+    if (ahead >= K) {
+      UQP_WAIT_VMCNT(K * kDmaPerTile);
+    } else {
+      wait_tiles<K - 1>(ahead);
+    }
+  }
+}
 
 __device__ __forceinline__ float rowgroup_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -153,15 +180,18 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
     int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kKeyTile * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][kKeyTile * kRowBytes];
+  // one array per stage and operand, so that the compiler can tell the slot
+  // being read from the slots being filled
+  __shared__ uint4 kr0[kTileU4], kr1[kTileU4], kr2[kTileU4], kr3[kTileU4];
+  __shared__ uint4 vr0[kTileU4], vr1[kTileU4], vr2[kTileU4], vr3[kTileU4];
 
   const int n_ptiles = (q_len + ppw - 1) / ppw;
   const int p0 = (n_ptiles - 1 - (int)blockIdx.x) * ppw;    // latest positions (most keys) first
   const int hk = blockIdx.y;
   const int p_end = min(p0 + ppw, q_len);
   const int kend = cached_len + p_end;                      // keys the last position sees
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
 
   int klim[2], cpos[2], chead[2];
@@ -174,7 +204,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     cval[cb] = c < ppw * QG && cpos[cb] < q_len;
     klim[cb] = cached_len + cpos[cb] + 1;
   }
-  // addresses stay inside the tensors even for columns past the chunk
+  // the query first, so that waiting for it never waits for a tile; the
+  // addresses stay inside the tensor even for columns past the chunk
   v8bf qb[2][8];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -189,30 +220,30 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     }
   }
 
-  // tile t: 32 keys x 512 bytes of K and of V, 8 chunks of 16 bytes per thread
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int t) {
+  // Load i of this wave moves rows 8w + 2i + l/32 of the tile, LDS chunk l%32.
+  const uint32_t row_bytes = (uint32_t)(kvs_t * 2);
+  uint32_t koff[4], voff[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int ci = tid + 256 * rr;
-      const int key = t * kKeyTile + (ci >> 5);
-      const int64_t off = (int64_t)min(key, kend - 1) * kvs_t + (int64_t)hk * kvs_h + 8 * (ci & 31);
-      kreg[rr] = make_uint4(0, 0, 0, 0);
-      vreg[rr] = make_uint4(0, 0, 0, 0);
-      if (key < kend) {
-        kreg[rr] = ld16(k + off);
-        vreg[rr] = ld16(v + off);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * wave + 2 * i + (lane >> 5), c = lane & 31;
+    koff[i] = r * row_bytes + 16 * (c ^ (r & 15));
+    voff[i] = r * row_bytes + 16 * (c ^ (((r >> 2) & 3) << 2));
+  }
+  const int n_kt = (kend + kKeyTile - 1) / kKeyTile;
+  auto issue = [&](uint4* ks, uint4* vs, int t) {
+    const int key0 = t * kKeyTile;
+    const int nv = min(kKeyTile, kend - key0);
+    // the descriptors end at the last key the workgroup needs: rows past it land as zeros
+    const int nrec = (nv - 1) * (int)row_bytes + kRowBytes;
+    const int64_t base = (int64_t)key0 * kvs_t + (int64_t)hk * kvs_h;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, nrec, 0x00020000);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int ci = tid + 256 * rr;
-      const int off = (ci >> 5) * kRowBytes + 16 * (ci & 31);
-      *reinterpret_cast<uint4*>(kbuf[buf] + off) = kreg[rr];
-      *reinterpret_cast<uint4*>(vbuf[buf] + off) = vreg[rr];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ks + 64 * (4 * wave + i)), 16, koff[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + 64 * (4 * wave + i)), 16, voff[i], 0, 0, 0);
   };
 
   v4f acc[2][16];
@@ -220,76 +251,104 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[cb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  v4f lsum[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};   // row sums of the weights
+  float m_ref[2] = {-INFINITY, -INFINITY};
+  const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  const int n_kt = (kend + kKeyTile - 1) / kKeyTile;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < n_kt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_kt) load_tile(t + 1);
-    const uint8_t* kb_ = kbuf[buf];
-    const uint8_t* vb_ = vbuf[buf];
-
+  auto compute = [&](const uint4* ks, const uint4* vs, int t) {
+    const uint8_t* kb_ = reinterpret_cast<const uint8_t*>(ks);
+    const uint8_t* vb_ = reinterpret_cast<const uint8_t*>(vs);
+    // K operands four steps ahead of the score MFMAs
     v4f s[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) s[kb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int h = 0; h < 2; ++h) {
+      v8bf ka[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const v8bf a = __builtin_bit_cast(v8bf, ld16(kb_ + (16 * kb + r16) * kRowBytes + 64 * j + 16 * g));
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          s[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[cb][j], s[kb][cb], 0, 0, 0);
-      }
+        for (int kb = 0; kb < 2; ++kb)
+          ka[kb][j] = __builtin_bit_cast(
+              v8bf, ld16(kb_ + (16 * kb + r16) * kRowBytes + 16 * ((4 * (4 * h + j) + g) ^ r16)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            s[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][j], qb[cb][4 * h + j], s[kb][cb], 0, 0, 0);
     }
 
+    // raw scores; only tiles that reach past the first position's last
+    // visible key need the causal mask (a workgroup-uniform test)
     const int key0 = t * kKeyTile;
     float sv[2][8], mt[2];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * kb + 4 * g + i;
-          sv[cb][4 * kb + i] = key < klim[cb] ? s[kb][cb][i] * scale_log2 : -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i) sv[cb][4 * kb + i] = s[kb][cb][i];
+    if (key0 + kKeyTile > cached_len + p0 + 1) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + 16 * kb + 4 * g + i >= klim[cb]) sv[cb][4 * kb + i] = -INFINITY;
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
       float x = sv[cb][0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) x = fmaxf(x, sv[cb][i]);
-      mt[cb] = rowgroup_max(x);
+      mt[cb] = rowgroup_max(x) * scale_log2;                  // scale > 0: max commutes
       if (t == 0) m_ref[cb] = mt[cb];
     }
     if (__any(mt[0] > m_ref[0] + 8.0f || mt[1] > m_ref[1] + 8.0f)) {
+      // Rare: raise the reference and rescale row r of O by f_r, as the
+      // product diag(f) O on float32 MFMAs, so that the accumulators are
+      // only ever touched by MFMAs. V_MFMA_F32_16X16X4_F32 takes A[r][k]
+      // from lane (r, k) and B[k][c] from lane (c, k); register i of an
+      // accumulator, used as B, is O[4k + i][c], so A_i[r][k] = f_r when
+      // r = 4k + i (this lane's own column factor) and 0 otherwise.
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         const float m_new = fmaxf(m_ref[cb], mt[cb]);
         const float f = m_new > m_ref[cb] ? exp2f(m_ref[cb] - m_new) : 1.f;
+        float fsel[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[cb][j] *= f;
-        l_part[cb] *= f;
+        for (int i = 0; i < 4; ++i) fsel[i] = r16 == 4 * g + i ? f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 17; ++j) {
+          v4f& a = j < 16 ? acc[cb][j] : lsum[cb];
+          v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_mfma_f32_16x16x4f32(fsel[i], a[i], d, 0, 0, 0);
+          a = d;
+        }
         m_ref[cb] = m_new;
       }
     }
+    // weights p = 2^(s * scale_log2 - m_ref) in bf16; their row sums come
+    // from one more MFMA against ones, so they are the sums of exactly the
+    // bf16 weights the product uses and land in O's row layout
     v8bf pb[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       uint32_t pw[4];
-      float lsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p0_ = __builtin_amdgcn_exp2f(sv[cb][2 * i] - m_ref[cb]);
-        const float p1_ = __builtin_amdgcn_exp2f(sv[cb][2 * i + 1] - m_ref[cb]);
-        pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p0_, p1_}, v2bf));
-        lsum += __uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xFFFF0000u);
+        const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[cb][2 * i], scale_log2, -m_ref[cb]));
+        const float pc = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[cb][2 * i + 1], scale_log2, -m_ref[cb]));
+        pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pa, pc}, v2bf));
       }
-      l_part[cb] += lsum;
       pb[cb] = __builtin_bit_cast(v8bf, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ones, lsum[cb], 0, 0, 0);
     }
 
 #pragma unroll
@@ -298,7 +357,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
 #pragma unroll
       for (int s_ = 0; s_ < 8; ++s_) {
         const int key = s_ < 4 ? 4 * g + s_ : 16 + 4 * g + (s_ - 4);
-        w[s_] = *reinterpret_cast<const uint32_t*>(vb_ + key * kRowBytes + 64 * b + 4 * r16);
+        const int chunk = (4 * b + (r16 >> 2)) ^ (((key >> 2) & 3) << 2);
+        w[s_] = *reinterpret_cast<const uint32_t*>(vb_ + key * kRowBytes + 16 * chunk + 4 * (r16 & 3));
       }
       const uint4 ev = make_uint4(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
                                   __builtin_amdgcn_perm(w[3], w[2], 0x05040100u),
@@ -311,30 +371,50 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
       const v8bf ae = __builtin_bit_cast(v8bf, ev), ao = __builtin_bit_cast(v8bf, od);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        acc[cb][2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, pb[cb], acc[cb][2 * b], 0, 0, 0);
-        acc[cb][2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, pb[cb], acc[cb][2 * b + 1], 0, 0, 0);
+        acc[cb][2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ae, acc[cb][2 * b], 0, 0, 0);
+        acc[cb][2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ao, acc[cb][2 * b + 1], 0, 0, 0);
       }
     }
+  };
 
-    if (t + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+  // Tiles 0 .. kStages-2 in flight; step t waits for tile t, makes it visible
+  // to the whole workgroup (which also ends every wave's reads of tile t-1),
+  // refills tile t-1's stage with tile t + kStages - 1, then computes tile t.
+  issue(kr0, vr0, 0);
+  if (1 < n_kt) issue(kr1, vr1, 1);
+  if (2 < n_kt) issue(kr2, vr2, 2);
+#define UQP_STEP(KC, VC, KN, VN)                              \
+  {                                                           \
+    wait_tiles<kStages - 2>(n_kt - 1 - t);                    \
+    __syncthreads();                                          \
+    if (t + kStages - 1 < n_kt) issue(KN, VN, t + kStages - 1); \
+    compute(KC, VC, t);                                       \
+    if (++t >= n_kt) break;                                   \
   }
+  for (int t = 0;;) {
+    UQP_STEP(kr0, vr0, kr3, vr3)
+    UQP_STEP(kr1, vr1, kr0, vr0)
+    UQP_STEP(kr2, vr2, kr1, vr1)
+    UQP_STEP(kr3, vr3, kr2, vr2)
+  }
+#undef UQP_STEP
 
+  // Epilogue: lane (r, g) holds O[column 4g + i][dims 32b + 2r, 2r + 1]
+  // (even / odd accumulators) and that column's weight sum.
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const float l1 = l_part[cb] + __shfl_xor(l_part[cb], 16);
-    const float l_tot = l1 + __shfl_xor(l1, 32);
-    if (!cval[cb]) continue;
-    const float inv = 1.f / l_tot;
-    uint16_t* op = out + (int64_t)cpos[cb] * os_t + (int64_t)chead[cb] * os_h + 8 * g;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const v4f e = acc[cb][2 * b], o = acc[cb][2 * b + 1];
-      uint32_t r[4];
+    for (int i = 0; i < 4; ++i) {
+      const int cl = 4 * g + i;                                   // column within the block
+      const float inv = 1.f / lsum[cb][i];
+      const int c = 32 * wave + 16 * cb + cl;
+      const int pos = p0 + c / QG;
+      if (!(c < ppw * QG && pos < q_len)) continue;
+      uint16_t* op = out + (int64_t)pos * os_t + (int64_t)(hk * QG + c % QG) * os_h + 2 * r16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){e[i] * inv, o[i] * inv}, v2bf));
-      *reinterpret_cast<uint4*>(op + 32 * b) = make_uint4(r[0], r[1], r[2], r[3]);
+      for (int b = 0; b < 8; ++b)
+        *reinterpret_cast<uint32_t*>(op + 32 * b) = __builtin_bit_cast(
+            uint32_t, __builtin_convertvector((v2f){acc[cb][2 * b][i] * inv, acc[cb][2 * b + 1][i] * inv}, v2bf));
     }
   }
 }
