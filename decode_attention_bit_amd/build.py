@@ -25,6 +25,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed building libuq.so")
     if verbose:
         sys.stderr.write(r.stderr)
+    # every symbol must resolve (a kernel whose host stub was not emitted
+    # links but does not load); checked in a child so no handle stays open
+    chk = subprocess.run([sys.executable, "-c", f"import ctypes; ctypes.CDLL({tmp!r})"],
+                         capture_output=True, text=True)
+    if chk.returncode != 0:
+        os.remove(tmp)
+        sys.stderr.write(chk.stderr)
+        raise RuntimeError("libuq.so built but does not load")
     os.replace(tmp, out)
     return out
 

@@ -179,7 +179,7 @@ int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t
   if (!aligned(x, 8) || !aligned(out, 8)) return fail(UQ_EINVAL, "uq_rotate: x and out must be 8-byte aligned");
   if ((N * H + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "uq_rotate: N*H too large for one launch");
   uq::GatherArgs a{};
-  a.job[0] = uq::VecJob{x, x_stride_n, x_stride_h, out, out_stride_n, out_stride_h, N * H, H, 1};
+  a.job[0] = uq::VecJob{x, x_stride_n, x_stride_h, out, out_stride_n, out_stride_h, N * H, H, 1, 0, 0};
   return hip_status(uq::launch_gather(a, (hipStream_t)stream), "uq_rotate launch");
 }
 
@@ -242,24 +242,31 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
     return fail(UQ_EINVAL, "uq_prefill_attention: strides must be non-negative multiples of 8 elements");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(UQ_EINVAL, "uq_prefill_attention: q, k, v and out must be 16-byte aligned");
+  // key rows are staged 32 at a time through one buffer descriptor each
+  if (kv_stride_t < UQ_HEAD_DIM || kv_stride_t >= (1LL << 25))
+    return fail(UQ_EUNSUPPORTED, "uq_prefill_attention: kv_stride_t %lld outside [256, 2^25)", (long long)kv_stride_t);
   uq::PrefillAttnArgs a{q, k, v, out, q_stride_t, q_stride_h, kv_stride_t, kv_stride_h,
-                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale};
+                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale, 0};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_prefill_attention launch");
 }
 
-// Workspace of uq_continuation_prefill: rotated queries, then keys and
-// values of prefix + chunk, each 256-byte aligned.
+// Workspace of uq_continuation_prefill: rotated queries, keys of prefix +
+// chunk (token-major), then the values in the tiled layout of the attention
+// kernel (per KV head, ceil(seq_len / 32) tiles of 16 KB), each section
+// 256-byte aligned.
 struct PrefillLayout {
   size_t q_off, k_off, v_off, total;
+  long long vt_tiles;
 };
 
 static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, int Hk) {
   auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   PrefillLayout l{};
+  l.vt_tiles = (seq_len + 31) / 32;
   l.q_off = 0;
   l.k_off = a256((size_t)q_len * Hq * UQ_HEAD_DIM * 2);
   l.v_off = l.k_off + a256((size_t)seq_len * Hk * UQ_HEAD_DIM * 2);
-  l.total = l.v_off + a256((size_t)seq_len * Hk * UQ_HEAD_DIM * 2);
+  l.total = l.v_off + (size_t)Hk * l.vt_tiles * 32 * UQ_HEAD_DIM * 2;
   return l;
 }
 
@@ -301,7 +308,7 @@ int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const ui
   const PrefillLayout lay = prefill_layout(q_len, seq_len, Hq, Hk);
   if (workspace_bytes < lay.total)
     return fail(UQ_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, lay.total);
-  const long long waves = (long long)seq_len * Hk * 2 + (long long)q_len * Hq;
+  const long long waves = (long long)(seq_len + 32) * Hk * 2 + (long long)q_len * Hq;
   if ((waves + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "%s: too large for one launch", who);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + lay.q_off);
@@ -318,19 +325,23 @@ int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const ui
   g.num_blocks = num_blocks;
   g.log2_bs = log2_bs;
   g.kout = kf;
-  g.vout = vf;
+  g.vout = nullptr;
   g.os_t = row;
   g.os_h = UQ_HEAD_DIM;
+  g.vt = vf;
+  g.vt_tiles = lay.vt_tiles;
+  g.vt_pad0 = seq_len;
+  g.vt_pad = lay.vt_tiles * 32 - seq_len;
   g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM,
-                        (int64_t)q_len * Hq, Hq, 1};
+                        (int64_t)q_len * Hq, Hq, 1, 0, 0};
   g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, UQ_HEAD_DIM,
-                        (int64_t)q_len * Hk, Hk, 1};
-  g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, vf + (int64_t)cached_len * row, row, UQ_HEAD_DIM,
-                        (int64_t)q_len * Hk, Hk, 0};
+                        (int64_t)q_len * Hk, Hk, 1, 0, 0};
+  g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, nullptr, 0, 0, (int64_t)q_len * Hk, Hk, 0, 1,
+                        (int64_t)cached_len};
   hipError_t e = uq::launch_gather(g, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");
   uq::PrefillAttnArgs a{qr, kf, vf, out, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM, row, UQ_HEAD_DIM,
-                        out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale};
+                        out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale, lay.vt_tiles};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_continuation_prefill attention launch");
 }
 

@@ -57,8 +57,14 @@ struct VecJob {
   int64_t n;
   int H;
   int rotate;
+  int to_vt;                 // write row t as key vt_key0 + t of the tiled value layout instead
+  int64_t vt_key0;
 };
 
+// Tiled value layout of the continuation prefill (vt != null): per KV head,
+// tiles of 32 keys, each 256 dim rows of 64 bytes; row d of tile j holds the
+// 32 keys in the order the attention's P operand uses, its 16-byte chunks
+// permuted by chunk ^ ((d >> 2) & 3).
 struct GatherArgs {
   // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])
   const uint8_t* cache;
@@ -70,6 +76,9 @@ struct GatherArgs {
   uint16_t* kout;
   uint16_t* vout;
   int64_t os_t, os_h;
+  uint16_t* vt;              // values go here (tiled) instead of vout when set
+  int64_t vt_tiles;          // tiles per KV head
+  int64_t vt_pad0, vt_pad;   // keys vt_pad0 .. vt_pad0 + vt_pad - 1 are zero padding
   VecJob job[3];
 };
 
@@ -81,6 +90,7 @@ struct PrefillAttnArgs {
   int64_t qs_t, qs_h, kvs_t, kvs_h, os_t, os_h;
   int q_len, cached_len, Hk, QG;
   float scale;
+  int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,

@@ -52,6 +52,14 @@ __device__ __forceinline__ uint32_t e2m1_bf16_bits(uint32_t code, int e) {
   return sign | ((2u + half) << (E + 132));                 // value / 2**-133
 }
 
+// Element offset of (key, head h, dim) in the tiled value layout: key
+// 16kb + 4g + i of a tile sits at slot s = i + 4kb of chunk g of its dim row.
+__device__ __forceinline__ int64_t vt_offset(int64_t key, int h, int dim, int64_t tiles) {
+  const int kk = (int)(key & 31);
+  const int g = (kk & 15) >> 2, s = (kk & 3) + ((kk >> 4) << 2);
+  return (((int64_t)h * tiles + (key >> 5)) * kHeadDim + dim) * 32 + 8 * (g ^ ((dim >> 2) & 3)) + s;
+}
+
 // ---------------------------------------------------------------------------
 // Gather: one wave per unit of work, the role chosen by the wave's index
 // (wave-uniform): first the prefix slots (token, KV head) to dequantise, then
@@ -86,11 +94,26 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
       o[i] = ok ? (e2m1_bf16_bits((codes >> (8 * i)) & 0xF, e) |
                    (e2m1_bf16_bits((codes >> (8 * i + 4)) & 0xF, e) << 16))
                 : 0u;
+    if (is_v && a.vt) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        a.vt[vt_offset(t, h, 8 * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+      return;
+    }
     uint16_t* dst = (is_v ? a.vout : a.kout) + t * a.os_t + (int64_t)h * a.os_h + 8 * l;
     *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
     return;
   }
   w -= n_slots;
+  const int64_t n_pad = a.vt_pad * a.Hk;
+  if (w < n_pad) {                          // zero the keys past the sequence in its last tile
+    const int64_t key = a.vt_pad0 + w / a.Hk;
+    const int h = (int)(w % a.Hk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.vt[vt_offset(key, h, 4 * lane + i, a.vt_tiles)] = 0;
+    return;
+  }
+  w -= n_pad;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const VecJob& jb = a.job[j];
@@ -108,6 +131,13 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
       fwht256_wave(v, lane);
       res.x = bf16_bits_rne(v[0] * 0.0625) | (bf16_bits_rne(v[1] * 0.0625) << 16);
       res.y = bf16_bits_rne(v[2] * 0.0625) | (bf16_bits_rne(v[3] * 0.0625) << 16);
+    }
+    if (jb.to_vt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a.vt[vt_offset(jb.vt_key0 + t, h, 4 * lane + i, a.vt_tiles)] =
+            (uint16_t)((i < 2 ? res.x : res.y) >> (16 * (i & 1)));
+      return;
     }
     *reinterpret_cast<uint2*>(jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + 4 * lane) = res;
     return;
@@ -147,7 +177,6 @@ constexpr int kRowBytes = 2 * kHeadDim;
 constexpr int kTileU4 = kKeyTile * kRowBytes / 16;      // 1024 chunks of 16 bytes
 constexpr int kColsPerWg = 128;
 constexpr int kStages = 4;
-constexpr int kDmaPerTile = 8;                          // per wave: 4 for K, 4 for V
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -156,15 +185,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Wait until at most min(K, ahead) tiles are still in flight (the waitcnt
 // immediate must be a constant).
-template <int K>
+template <int K, int PER_TILE>
 __device__ __forceinline__ void wait_tiles(int ahead) {
   if constexpr (K == 0) {
     UQP_WAIT_VMCNT(0);
   } else {
     if (ahead >= K) {
-      UQP_WAIT_VMCNT(K * kDmaPerTile);
+      UQP_WAIT_VMCNT(K * PER_TILE);
     } else {
-      wait_tiles<K - 1>(ahead);
+      wait_tiles<K - 1, PER_TILE>(ahead);
     }
   }
 }
@@ -176,15 +205,29 @@ __device__ __forceinline__ float rowgroup_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__global__ __launch_bounds__(256) void prefill_attn_kernel(
+// VT: values in the tiled layout the gather writes (one 16 KB block per tile
+// and head, dim-major), so that a lane's 8 keys of one dim are one 16-byte
+// read and O's columns are dims directly; otherwise values are token-major
+// like the keys and each read dword feeds an even-dim and an odd-dim MFMA.
+#ifndef UQ_PREFILL_CB
+#define UQ_PREFILL_CB 1
+#endif
+constexpr int CB = UQ_PREFILL_CB;           // 16-column blocks per wave: 1 or 2
+
+template <bool VT>
+__global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
-    int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2) {
+    int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2,
+    int64_t vt_tiles) {
   // one array per stage and operand, so that the compiler can tell the slot
   // being read from the slots being filled
   __shared__ uint4 kr0[kTileU4], kr1[kTileU4], kr2[kTileU4], kr3[kTileU4];
   __shared__ uint4 vr0[kTileU4], vr1[kTileU4], vr2[kTileU4], vr3[kTileU4];
 
+  // CB column blocks of 16 per wave, 128 / (16 CB) waves; each wave moves
+  // ROWS of the 32 rows of every K and V tile, NDMA loads of 1 KB each
+  constexpr int WAVES = 8 / CB, ROWS = kKeyTile / WAVES, NDMA = 16 / WAVES;
   const int n_ptiles = (q_len + ppw - 1) / ppw;
   const int p0 = (n_ptiles - 1 - (int)blockIdx.x) * ppw;    // latest positions (most keys) first
   const int hk = blockIdx.y;
@@ -194,11 +237,11 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
 
-  int klim[2], cpos[2], chead[2];
-  bool cval[2];
+  int klim[CB], cpos[CB], chead[CB];
+  bool cval[CB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int c = 32 * wave + 16 * cb + r16;
+  for (int cb = 0; cb < CB; ++cb) {
+    const int c = 16 * CB * wave + 16 * cb + r16;
     cpos[cb] = p0 + c / QG;
     chead[cb] = hk * QG + c % QG;
     cval[cb] = c < ppw * QG && cpos[cb] < q_len;
@@ -206,9 +249,9 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   }
   // the query first, so that waiting for it never waits for a tile; the
   // addresses stay inside the tensor even for columns past the chunk
-  v8bf qb[2][8];
+  v8bf qb[CB][8];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     const int pos = cval[cb] ? cpos[cb] : 0;
     const int head = cval[cb] ? chead[cb] : 0;
     const uint16_t* qp = q + (int64_t)pos * qs_t + (int64_t)head * qs_h + 8 * g;
@@ -220,14 +263,14 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     }
   }
 
-  // Load i of this wave moves rows 8w + 2i + l/32 of the tile, LDS chunk l%32.
+  // Load i of this wave moves rows ROWS*w + 2i + l/32 of the tile, LDS chunk l%32.
   const uint32_t row_bytes = (uint32_t)(kvs_t * 2);
-  uint32_t koff[4], voff[4];
+  uint32_t koff[NDMA], voff[NDMA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * wave + 2 * i + (lane >> 5), c = lane & 31;
+  for (int i = 0; i < NDMA; ++i) {
+    const int r = ROWS * wave + 2 * i + (lane >> 5), c = lane & 31;
     koff[i] = r * row_bytes + 16 * (c ^ (r & 15));
-    voff[i] = r * row_bytes + 16 * (c ^ (((r >> 2) & 3) << 2));
+    voff[i] = VT ? 1024 * (NDMA * wave + i) + 16 * lane : r * row_bytes + 16 * (c ^ (((r >> 2) & 3) << 2));
   }
   const int n_kt = (kend + kKeyTile - 1) / kKeyTile;
   auto issue = [&](uint4* ks, uint4* vs, int t) {
@@ -237,33 +280,41 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     const int nrec = (nv - 1) * (int)row_bytes + kRowBytes;
     const int64_t base = (int64_t)key0 * kvs_t + (int64_t)hk * kvs_h;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        VT ? __builtin_amdgcn_make_buffer_rsrc((void*)(v + ((int64_t)hk * vt_tiles + t) * (kKeyTile * kHeadDim)),
+                                               (short)0, kKeyTile * kRowBytes, 0x00020000)
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, nrec, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ks + 64 * (4 * wave + i)), 16, koff[i], 0, 0, 0);
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ks + 64 * (NDMA * wave + i)), 16, koff[i], 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + 64 * (4 * wave + i)), 16, voff[i], 0, 0, 0);
+    for (int i = 0; i < NDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + 64 * (NDMA * wave + i)), 16, voff[i], 0, 0, 0);
   };
 
-  v4f acc[2][16];
+  v4f acc[CB][16];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[cb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  v4f lsum[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};   // row sums of the weights
-  float m_ref[2] = {-INFINITY, -INFINITY};
+  v4f lsum[CB];                                            // row sums of the weights
+  float m_ref[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    lsum[cb] = (v4f){0.f, 0.f, 0.f, 0.f};
+    m_ref[cb] = -INFINITY;
+  }
   const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
   auto compute = [&](const uint4* ks, const uint4* vs, int t) {
     const uint8_t* kb_ = reinterpret_cast<const uint8_t*>(ks);
     const uint8_t* vb_ = reinterpret_cast<const uint8_t*>(vs);
     // K operands four steps ahead of the score MFMAs
-    v4f s[2][2];
+    v4f s[2][CB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) s[kb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < CB; ++cb) s[kb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       v8bf ka[2][4];
@@ -278,23 +329,23 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
+          for (int cb = 0; cb < CB; ++cb)
             s[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][j], qb[cb][4 * h + j], s[kb][cb], 0, 0, 0);
     }
 
     // raw scores; only tiles that reach past the first position's last
     // visible key need the causal mask (a workgroup-uniform test)
     const int key0 = t * kKeyTile;
-    float sv[2][8], mt[2];
+    float sv[CB][8], mt[CB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[cb][4 * kb + i] = s[kb][cb][i];
     if (key0 + kKeyTile > cached_len + p0 + 1) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -302,14 +353,17 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
             if (key0 + 16 * kb + 4 * g + i >= klim[cb]) sv[cb][4 * kb + i] = -INFINITY;
     }
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       float x = sv[cb][0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) x = fmaxf(x, sv[cb][i]);
       mt[cb] = rowgroup_max(x) * scale_log2;                  // scale > 0: max commutes
       if (t == 0) m_ref[cb] = mt[cb];
     }
-    if (__any(mt[0] > m_ref[0] + 8.0f || mt[1] > m_ref[1] + 8.0f)) {
+    bool raise = false;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) raise = raise || mt[cb] > m_ref[cb] + 8.0f;
+    if (__any(raise)) {
       // Rare: raise the reference and rescale row r of O by f_r, as the
       // product diag(f) O on float32 MFMAs, so that the accumulators are
       // only ever touched by MFMAs. V_MFMA_F32_16X16X4_F32 takes A[r][k]
@@ -317,7 +371,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
       // accumulator, used as B, is O[4k + i][c], so A_i[r][k] = f_r when
       // r = 4k + i (this lane's own column factor) and 0 otherwise.
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         const float m_new = fmaxf(m_ref[cb], mt[cb]);
         const float f = m_new > m_ref[cb] ? exp2f(m_ref[cb] - m_new) : 1.f;
         float fsel[4];
@@ -337,9 +391,9 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     // weights p = 2^(s * scale_log2 - m_ref) in bf16; their row sums come
     // from one more MFMA against ones, so they are the sums of exactly the
     // bf16 weights the product uses and land in O's row layout
-    v8bf pb[2];
+    v8bf pb[CB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
       uint32_t pw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -351,6 +405,17 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
       lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ones, lsum[cb], 0, 0, 0);
     }
 
+    if constexpr (VT) {
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int dim = 16 * n + r16;
+        const v8bf vb = __builtin_bit_cast(v8bf, ld16(vb_ + dim * 64 + 16 * (g ^ ((r16 >> 2) & 3))));
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[cb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], vb, acc[cb][n], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       uint32_t w[8];
@@ -370,7 +435,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
                                   __builtin_amdgcn_perm(w[7], w[6], 0x07060302u));
       const v8bf ae = __builtin_bit_cast(v8bf, ev), ao = __builtin_bit_cast(v8bf, od);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         acc[cb][2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ae, acc[cb][2 * b], 0, 0, 0);
         acc[cb][2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ao, acc[cb][2 * b + 1], 0, 0, 0);
       }
@@ -385,7 +450,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   if (2 < n_kt) issue(kr2, vr2, 2);
 #define UQP_STEP(KC, VC, KN, VN)                              \
   {                                                           \
-    wait_tiles<kStages - 2>(n_kt - 1 - t);                    \
+    wait_tiles<kStages - 2, 2 * NDMA>(n_kt - 1 - t);                    \
     __syncthreads();                                          \
     if (t + kStages - 1 < n_kt) issue(KN, VN, t + kStages - 1); \
     compute(KC, VC, t);                                       \
@@ -399,22 +464,29 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   }
 #undef UQP_STEP
 
-  // Epilogue: lane (r, g) holds O[column 4g + i][dims 32b + 2r, 2r + 1]
-  // (even / odd accumulators) and that column's weight sum.
+  // Epilogue: lane (r, g) holds, for column 4g + i, O at dims 16n + r (VT)
+  // or at dims 32b + 2r, 2r + 1 (even / odd accumulators), and that
+  // column's weight sum.
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int cl = 4 * g + i;                                   // column within the block
       const float inv = 1.f / lsum[cb][i];
-      const int c = 32 * wave + 16 * cb + cl;
+      const int c = 16 * CB * wave + 16 * cb + cl;
       const int pos = p0 + c / QG;
       if (!(c < ppw * QG && pos < q_len)) continue;
-      uint16_t* op = out + (int64_t)pos * os_t + (int64_t)(hk * QG + c % QG) * os_h + 2 * r16;
+      uint16_t* op = out + (int64_t)pos * os_t + (int64_t)(hk * QG + c % QG) * os_h;
+      if constexpr (VT) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
-        *reinterpret_cast<uint32_t*>(op + 32 * b) = __builtin_bit_cast(
-            uint32_t, __builtin_convertvector((v2f){acc[cb][2 * b][i] * inv, acc[cb][2 * b + 1][i] * inv}, v2bf));
+        for (int n = 0; n < 16; ++n)
+          op[16 * n + r16] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][n][i] * inv));
+      } else {
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          *reinterpret_cast<uint32_t*>(op + 32 * b + 2 * r16) = __builtin_bit_cast(
+              uint32_t, __builtin_convertvector((v2f){acc[cb][2 * b][i] * inv, acc[cb][2 * b + 1][i] * inv}, v2bf));
+      }
     }
   }
 }
@@ -422,7 +494,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
-  const int64_t waves = (int64_t)a.n_tok * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
+  const int64_t waves = (int64_t)a.n_tok * a.Hk + a.vt_pad * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
   if (waves == 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_gather_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -434,9 +506,15 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
   if (a.q_len == 0) return hipSuccess;
   const int ppw = prefill_positions_per_wg(a.QG);
   const int n_ptiles = (a.q_len + ppw - 1) / ppw;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)n_ptiles, (unsigned)a.Hk), dim3(256), 0, stream,
-                     a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len,
-                     a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f);
+  const dim3 grid((unsigned)n_ptiles, (unsigned)a.Hk), block(64 * (8 / CB));
+  if (a.vt_tiles > 0)
+    hipLaunchKernelGGL(prefill_attn_kernel<true>, grid, block, 0, stream,
+                       a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len,
+                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, a.vt_tiles);
+  else
+    hipLaunchKernelGGL(prefill_attn_kernel<false>, grid, block, 0, stream,
+                       a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len,
+                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, (int64_t)0);
   return hipGetLastError();
 }
 

@@ -261,9 +261,10 @@ int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_token
  *   q:    (device) bf16 (q_len, Hq, 256); k, v: (seq_len, Hk, 256) sharing
  *         strides; out: (q_len, Hq, 256) bf16. All 16-byte aligned, strides
  *         in elements, non-negative multiples of 8.
- *   scale: finite, > 0. Hq / Hk at most 128.
+ *   scale: finite, > 0. Hq / Hk at most 128. kv_stride_t in [256, 2^25).
  * Errors: UQ_EINVAL for q_len < 0, seq_len < q_len, a null pointer, bad
- * strides or alignment; UQ_EUNSUPPORTED for D != 256 or Hq % Hk; UQ_EHIP.
+ * strides or alignment; UQ_EUNSUPPORTED for D != 256, Hq % Hk or a key
+ * stride outside that range; UQ_EHIP.
  */
 int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
                          int q_len, int seq_len, int Hq, int Hk, int D, float scale,
@@ -278,8 +279,9 @@ size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int H
 /*
  * The whole continuation prefill of one sequence: dequantise the prefix,
  * rotate the chunk's keys and the queries, append the chunk's values, then
- * attend (uq_dequant_kv, uq_rotate and uq_prefill_attention on buffers in
- * the workspace; two launches on `stream`).
+ * attend (the steps of uq_dequant_kv, uq_rotate and uq_prefill_attention on
+ * buffers in the workspace, the values kept there in 32-key tiles laid out
+ * for the attention; two launches on `stream`).
  *   query:  (device) bf16 (q_len, Hq, 256) before rotation; key, value:
  *           (q_len, Hk, 256) of the chunk (key before rotation). 8-byte
  *           aligned, strides non-negative multiples of 4 elements.

@@ -185,6 +185,7 @@ def prefill_attention_args(**kw):
     (dict(q_len=-1), -1), (dict(seq_len=7), -1), (dict(scale=0.0), -1),
     (dict(scale=float("inf")), -1), (dict(D=128), -2), (dict(Hq=15), -2),
     (dict(Hq=258, Hk=2), -2), (dict(v=None), -1), (dict(kvst=508), -1), (dict(out=FAKE + 8), -1),
+    (dict(kvst=248), -2), (dict(kvst=1 << 25), -2),
 ])
 def test_prefill_attention_rejects(libuq, kw, code):
     assert libuq.uq_prefill_attention(*prefill_attention_args(**kw)) == code
@@ -216,6 +217,6 @@ def test_continuation_prefill_workspace_bytes(libuq):
     assert f(8, 100, 15, 2, 256) == 0
     assert f(8, 100, 16, 2, 128) == 0
     n = f(8, 100, 16, 2, 256)
-    # rotated queries, then keys and values of the whole sequence, as bf16
-    assert n == 8 * 16 * 512 + 2 * 100 * 2 * 512
+    # rotated queries, keys of the whole sequence, then values in tiles of 32 keys, as bf16
+    assert n == 8 * 16 * 512 + 100 * 2 * 512 + 2 * 4 * 32 * 512
     assert f(8, 101, 16, 2, 256) > n
