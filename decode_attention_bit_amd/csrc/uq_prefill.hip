@@ -306,15 +306,17 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
   }
   const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  auto compute = [&](const uint4* ks, const uint4* vs, int t) {
-    const uint8_t* kb_ = reinterpret_cast<const uint8_t*>(ks);
-    const uint8_t* vb_ = reinterpret_cast<const uint8_t*>(vs);
-    // K operands four steps ahead of the score MFMAs
+  // Scores of one tile, S^T = K Q^T (K operands read four steps ahead).
+  struct Scores {
     v4f s[2][CB];
+  };
+  auto scores = [&](const uint4* ks) {
+    const uint8_t* kb_ = reinterpret_cast<const uint8_t*>(ks);
+    Scores r;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) s[kb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < CB; ++cb) r.s[kb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       v8bf ka[2][4];
@@ -330,9 +332,15 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
-            s[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][j], qb[cb][4 * h + j], s[kb][cb], 0, 0, 0);
+            r.s[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][j], qb[cb][4 * h + j], r.s[kb][cb], 0, 0, 0);
     }
+    return r;
+  };
 
+  // Softmax and P.V of tile t from its scores.
+  auto weigh = [&](const Scores& sc, const uint4* vs, int t) {
+    const uint8_t* vb_ = reinterpret_cast<const uint8_t*>(vs);
+    const auto& s = sc.s;
     // raw scores; only tiles that reach past the first position's last
     // visible key need the causal mask (a workgroup-uniform test)
     const int key0 = t * kKeyTile;
@@ -442,25 +450,33 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
     }
   };
 
-  // Tiles 0 .. kStages-2 in flight; step t waits for tile t, makes it visible
-  // to the whole workgroup (which also ends every wave's reads of tile t-1),
-  // refills tile t-1's stage with tile t + kStages - 1, then computes tile t.
+  // Software pipeline, one tile deep: step t makes tile t+1 visible to the
+  // whole workgroup (the barrier also ends every wave's use of tile t-1),
+  // refills tile t-1's stage with tile t+3, issues tile t+1's score MFMAs and
+  // only then works through tile t's softmax and P.V, so the matrix cores
+  // have work while the softmax runs. Past the last tile the extra scores
+  // are computed from a stale stage and dropped.
   issue(kr0, vr0, 0);
   if (1 < n_kt) issue(kr1, vr1, 1);
   if (2 < n_kt) issue(kr2, vr2, 2);
-#define UQP_STEP(KC, VC, KN, VN)                              \
-  {                                                           \
-    wait_tiles<kStages - 2, 2 * NDMA>(n_kt - 1 - t);                    \
-    __syncthreads();                                          \
-    if (t + kStages - 1 < n_kt) issue(KN, VN, t + kStages - 1); \
-    compute(KC, VC, t);                                       \
-    if (++t >= n_kt) break;                                   \
+  wait_tiles<kStages - 2, 2 * NDMA>(n_kt - 1);
+  __syncthreads();
+  Scores cur = scores(kr0);
+#define UQP_STEP(KC, VC, KN, KF, VF)                                 \
+  {                                                                  \
+    wait_tiles<kStages - 3, 2 * NDMA>(n_kt - 2 - t);                 \
+    __syncthreads();                                                 \
+    if (t + kStages - 1 < n_kt) issue(KF, VF, t + kStages - 1);      \
+    const Scores nxt = scores(KN);                                   \
+    weigh(cur, VC, t);                                               \
+    cur = nxt;                                                       \
+    if (++t >= n_kt) break;                                          \
   }
   for (int t = 0;;) {
-    UQP_STEP(kr0, vr0, kr3, vr3)
-    UQP_STEP(kr1, vr1, kr0, vr0)
-    UQP_STEP(kr2, vr2, kr1, vr1)
-    UQP_STEP(kr3, vr3, kr2, vr2)
+    UQP_STEP(kr0, vr0, kr1, kr3, vr3)
+    UQP_STEP(kr1, vr1, kr2, kr0, vr0)
+    UQP_STEP(kr2, vr2, kr3, kr1, vr1)
+    UQP_STEP(kr3, vr3, kr0, kr2, vr2)
   }
 #undef UQP_STEP
 
