@@ -324,9 +324,12 @@ def prefill_main(args):
     log(f"timing {steps} calls")
     call = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, P["scale"], out=out, workspace=ws)
     ms = time_events(call, steps, warmup)
-    # the attention kernel alone, on operands of the same shapes
-    qr, kf, vf = randn(q_len, Hq, 256), randn(cached + q_len, Hk, 256), randn(cached + q_len, Hk, 256)
-    attn = lambda: uq.prefill_attention(qr, kf, vf, P["scale"], out=out)
+    # each launch of the call alone, on the workspace the whole call left
+    gather = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, P["scale"], out=out,
+                                             workspace=ws, stages=uq.PREFILL_GATHER)
+    attn = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, P["scale"], out=out,
+                                           workspace=ws, stages=uq.PREFILL_ATTEND)
+    gather_ms = time_events(gather, steps, warmup)
     attn_ms = time_events(attn, steps, warmup)
     fl = prefill_flops(cached, q_len, Hq)
     tf = fl / (ms * 1e-3) / 1e12
@@ -349,7 +352,8 @@ def prefill_main(args):
                                f"block_size={bs} (step = one uq_continuation_prefill)",
                    "flops_per_step": fl},
         "tokens_per_s": round(q_len / (ms * 1e-3), 1),
-        "stage_ms": {"whole_call": round(ms, 5), "attention_alone": round(attn_ms, 5)},
+        "stage_ms": {"whole_call": round(ms, 5), "gather_alone": round(gather_ms, 5),
+                     "attention_alone": round(attn_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "prefill_attn_kernel", "flops_per_launch": fl},

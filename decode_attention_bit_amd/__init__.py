@@ -88,6 +88,8 @@ def _load():
                                             i32, i64, i32, i64, i64, i64, i64, i64, i64, i64, i64,
                                             vp, sz, vp]
     lib.uq_continuation_prefill.restype = i32
+    lib.uq_continuation_prefill_stages.argtypes = [i32] + lib.uq_continuation_prefill.argtypes
+    lib.uq_continuation_prefill_stages.restype = i32
     lib.uq_last_error.argtypes = []
     lib.uq_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -324,13 +326,18 @@ def continuation_prefill_workspace_bytes(q_len: int, max_seq_len: int, Hq: int, 
     return int(n)
 
 
+PREFILL_GATHER, PREFILL_ATTEND = 1, 2
+
+
 def continuation_prefill(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                          kv_cache: torch.Tensor, block_row: torch.Tensor | None, cached_len: int,
                          scale: float, out: torch.Tensor | None = None,
-                         workspace: torch.Tensor | None = None) -> torch.Tensor:
+                         workspace: torch.Tensor | None = None, stages: int = 3) -> torch.Tensor:
     """uq_continuation_prefill: a chunk of q_len tokens (query (q_len, Hq, 256),
     key / value (q_len, Hk, 256), bf16, unrotated) after cached_len cached
-    tokens reached through block_row; returns (q_len, Hq, 256) bf16."""
+    tokens reached through block_row; returns (q_len, Hq, 256) bf16.
+    ``stages`` selects the gather and/or the attention launch
+    (uq_continuation_prefill_stages); the default runs both."""
     for t, name in ((query, "query"), (key, "key"), (value, "value")):
         _bf16_3d(t, name)
     if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
@@ -350,7 +357,9 @@ def continuation_prefill(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     need = lib.uq_continuation_prefill_workspace_bytes(q_len, int(cached_len) + q_len, Hq, Hk, D)
     if workspace is None:
         workspace = _workspace(query.device, max(int(need), 256))
-    _check(lib.uq_continuation_prefill(
+    fn = lib.uq_continuation_prefill if stages == 3 else (
+        lambda *a: lib.uq_continuation_prefill_stages(int(stages), *a))
+    _check(fn(
         _ptr(query), _ptr(key), _ptr(value), _ptr(kv_cache), _ptr(block_row), int(cached_len),
         float(scale), _ptr(out), q_len, Hq, Hk, D, nb, bs, query.stride(0), query.stride(1),
         key.stride(0), key.stride(1), value.stride(0), value.stride(1), out.stride(0), out.stride(1),

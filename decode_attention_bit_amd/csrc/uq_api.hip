@@ -276,15 +276,18 @@ size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int H
   return t > 0 ? t : 256;
 }
 
-int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const uint16_t* value,
-                            const uint8_t* kv_cache, const int32_t* block_row, int cached_len,
-                            float scale, uint16_t* out, int q_len, int Hq, int Hk, int D,
-                            int64_t num_blocks, int block_size, int64_t q_stride_t,
-                            int64_t q_stride_h, int64_t key_stride_t, int64_t key_stride_h,
-                            int64_t val_stride_t, int64_t val_stride_h, int64_t out_stride_t,
-                            int64_t out_stride_h, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const uint16_t* key,
+                                   const uint16_t* value, const uint8_t* kv_cache,
+                                   const int32_t* block_row, int cached_len, float scale,
+                                   uint16_t* out, int q_len, int Hq, int Hk, int D,
+                                   int64_t num_blocks, int block_size, int64_t q_stride_t,
+                                   int64_t q_stride_h, int64_t key_stride_t, int64_t key_stride_h,
+                                   int64_t val_stride_t, int64_t val_stride_h, int64_t out_stride_t,
+                                   int64_t out_stride_h, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   const char* who = "uq_continuation_prefill";
+  if (stage_mask <= 0 || (stage_mask & ~3))
+    return fail(UQ_EINVAL, "%s: stage_mask %d is not a non-empty subset of 1|2", who, stage_mask);
   if (cached_len < 0 || (long long)cached_len + q_len > 0x7FFFFFFFLL)
     return fail(UQ_EINVAL, "%s: cached_len=%d", who, cached_len);
   const int seq_len = cached_len + q_len;
@@ -338,11 +341,29 @@ int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const ui
                         (int64_t)q_len * Hk, Hk, 1, 0, 0};
   g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, nullptr, 0, 0, (int64_t)q_len * Hk, Hk, 0, 1,
                         (int64_t)cached_len};
-  hipError_t e = uq::launch_gather(g, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");
+  if (stage_mask & UQ_PREFILL_GATHER) {
+    hipError_t e = uq::launch_gather(g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");
+  }
+  if (!(stage_mask & UQ_PREFILL_ATTEND)) return ok();
   uq::PrefillAttnArgs a{qr, kf, vf, out, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM, row, UQ_HEAD_DIM,
                         out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale, lay.vt_tiles};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_continuation_prefill attention launch");
+}
+
+int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const uint16_t* value,
+                            const uint8_t* kv_cache, const int32_t* block_row, int cached_len,
+                            float scale, uint16_t* out, int q_len, int Hq, int Hk, int D,
+                            int64_t num_blocks, int block_size, int64_t q_stride_t,
+                            int64_t q_stride_h, int64_t key_stride_t, int64_t key_stride_h,
+                            int64_t val_stride_t, int64_t val_stride_h, int64_t out_stride_t,
+                            int64_t out_stride_h, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return uq_continuation_prefill_stages(UQ_PREFILL_GATHER | UQ_PREFILL_ATTEND, query, key, value,
+                                        kv_cache, block_row, cached_len, scale, out, q_len, Hq, Hk,
+                                        D, num_blocks, block_size, q_stride_t, q_stride_h,
+                                        key_stride_t, key_stride_h, val_stride_t, val_stride_h,
+                                        out_stride_t, out_stride_h, workspace, workspace_bytes, stream);
 }
 
 const char* uq_last_error(void) { return g_err.c_str(); }

@@ -304,6 +304,28 @@ int uq_continuation_prefill(const uint16_t* query, const uint16_t* key, const ui
                             int64_t out_stride_h, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * Same as uq_continuation_prefill, restricted to the launches named in
+ * stage_mask: UQ_PREFILL_GATHER (dequantised prefix, rotated chunk keys and
+ * queries and the chunk's values into the workspace) and UQ_PREFILL_ATTEND
+ * (the attention over them). Both masks in that order on one stream, with
+ * the same arguments and workspace, are exactly uq_continuation_prefill; it
+ * exists so that each kernel can be timed or captured alone.
+ * Errors: as uq_continuation_prefill, plus UQ_EINVAL for an empty or
+ * unknown mask.
+ */
+#define UQ_PREFILL_GATHER 1
+#define UQ_PREFILL_ATTEND 2
+int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const uint16_t* key,
+                                   const uint16_t* value, const uint8_t* kv_cache,
+                                   const int32_t* block_row, int cached_len, float scale,
+                                   uint16_t* out, int q_len, int Hq, int Hk, int D,
+                                   int64_t num_blocks, int block_size, int64_t q_stride_t,
+                                   int64_t q_stride_h, int64_t key_stride_t, int64_t key_stride_h,
+                                   int64_t val_stride_t, int64_t val_stride_h, int64_t out_stride_t,
+                                   int64_t out_stride_h, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Message describing the last non-zero return on the calling thread
  * ("" if none). The pointer stays valid until the thread's next call. */
 const char* uq_last_error(void);

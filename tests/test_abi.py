@@ -20,7 +20,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("uq_build_hadamard", "uq_store", "uq_decode", "uq_decode_ex", "uq_decode_stages",
               "uq_decode_workspace_bytes", "uq_rotate", "uq_dequant_kv", "uq_prefill_attention",
-              "uq_continuation_prefill", "uq_continuation_prefill_workspace_bytes", "uq_last_error"):
+              "uq_continuation_prefill", "uq_continuation_prefill_stages",
+              "uq_continuation_prefill_workspace_bytes", "uq_last_error"):
         assert n in names
 
 
@@ -220,3 +221,9 @@ def test_continuation_prefill_workspace_bytes(libuq):
     # rotated queries, keys of the whole sequence, then values in tiles of 32 keys, as bf16
     assert n == 8 * 16 * 512 + 100 * 2 * 512 + 2 * 4 * 32 * 512
     assert f(8, 101, 16, 2, 256) > n
+
+
+@pytest.mark.parametrize("mask", [0, 4, -1, 7])
+def test_continuation_prefill_stages_rejects_mask(libuq, mask):
+    assert libuq.uq_continuation_prefill_stages(mask, *continuation_args()) == -1
+    assert "stage_mask" in _err(libuq)

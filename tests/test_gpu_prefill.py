@@ -190,6 +190,20 @@ def test_continuation_prefill_large_sampled_rows():
     check_close(to_np(out)[rows], want[rows], "large sampled rows", allow_output_rounding=True)
 
 
+def test_continuation_prefill_stages_compose():
+    """The gather launch and the attention launch run one after the other
+    give the whole call's output bit for bit."""
+    say("prefill stages")
+    rng = np.random.default_rng(13)
+    out1, c = _prefill_case(rng, 77, 40, 2, 8)
+    ws = torch.empty(uq.continuation_prefill_workspace_bytes(40, 117, 16, 2), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(out1)
+    for st in (uq.PREFILL_GATHER, uq.PREFILL_ATTEND):
+        uq.continuation_prefill(c["q"].to(DEV), c["kc"].to(DEV), c["vc"].to(DEV), c["cache"], c["brow"], 77,
+                                c["scale"], out=o, workspace=ws, stages=st)
+    assert torch.equal(o, out1)
+
+
 def test_continuation_prefill_reuses_workspace_and_empty_chunk():
     say("prefill workspace reuse")
     rng = np.random.default_rng(12)
