@@ -30,11 +30,26 @@ from __future__ import annotations
 
 import numpy as np
 
-D = 256
+D = 256                             # the head dim of the pages' decode path
 MX_BLOCK = 32                       # elements per UE8M0 scale
-SLOT_BYTES = 272                    # 128 K codes + 128 V codes + 8 + 8 scales
+SLOT_BYTES = 272                    # 128 K codes + 128 V codes + 8 + 8 scales (D = 256)
 K_CODE_OFF, V_CODE_OFF = 0, 128
 K_SCALE_OFF, V_SCALE_OFF = 256, 264
+HEAD_DIMS = (128, 256, 512)         # head dims of the slot format
+
+
+def slot_layout(d: int):
+    """(slot bytes, K code, V code, K scale, V scale offsets) for head dim d:
+    d/2 bytes of K codes, d/2 of V codes, then d/32 K and d/32 V scale bytes
+    (272 bytes and offsets 0, 128, 256, 264 at d = 256)."""
+    assert d in HEAD_DIMS
+    return d * 17 // 16, 0, d // 2, d, d + d // MX_BLOCK
+
+
+def head_dim_of_slot(slot_bytes: int) -> int:
+    d = slot_bytes * 16 // 17
+    assert slot_layout(d)[0] == slot_bytes
+    return d
 
 # OCP MX v1.0, FP4 E2M1: magnitudes of the eight non-negative codes
 # (exponent bias 1, one mantissa bit, code 0b001 is the subnormal 0.5).
@@ -88,30 +103,51 @@ def hadamard(n: int = D) -> np.ndarray:
 
 
 _H = hadamard(D)
+_SYLVESTER = {}
+
+
+def sylvester(n: int) -> np.ndarray:
+    """The unnormalised Sylvester Hadamard, entries +-1 (H = sylvester / sqrt(n))."""
+    if n not in _SYLVESTER:
+        _SYLVESTER[n] = np.rint(hadamard(n) * np.sqrt(n))
+    return _SYLVESTER[n]
+
 
 # A +-subset sum of 256 bf16 values (8 significant bits each) fits in float64's
 # 53 bits when the exponents of the non-zero inputs span at most 36 binades:
 # 53 >= span + 8 (significand) + 9 (carry of 256 terms). Then x @ H is exact
-# in any summation order and the GPU butterfly sees the same value.
+# in any summation order and the GPU butterfly sees the same value. For n
+# terms the carry is log2(n) + 1 bits.
 MAX_EXACT_SPAN = 36
 
 
+def max_exact_span(n: int) -> int:
+    return 44 - int(np.log2(n))
+
+
 def exact_span_ok(x: np.ndarray) -> np.ndarray:
-    """Per vector (last axis): True when x @ H is exact in float64."""
+    """Per vector (last axis): True when the +-1 sums of x are exact in float64."""
     a = np.abs(np.asarray(x, dtype=np.float64))
     nz = a > 0
     e = np.where(nz, np.frexp(np.where(nz, a, 1.0))[1], 0)
     emax = np.where(nz, e, np.iinfo(np.int64).min).max(axis=-1)
     emin = np.where(nz, e, np.iinfo(np.int64).max).min(axis=-1)
-    return (~nz.any(axis=-1)) | (emax - emin <= MAX_EXACT_SPAN)
+    return (~nz.any(axis=-1)) | (emax - emin <= max_exact_span(a.shape[-1]))
 
 
 def rotate(x: np.ndarray) -> np.ndarray:
-    """y = x @ H over the last axis ([UQ-impl] _store_kv; key_chunk @ PiT)."""
+    """y = x @ H over the last axis ([UQ-impl] _store_kv; key_chunk @ PiT).
+
+    Computed as the exact +-1 sums x @ sylvester(n) times fl64(1/sqrt(n)),
+    one rounding (this build's reading where sqrt(n) is not a power of two,
+    n = 128 or 512; for n = 256 the scale 1/16 is exact and so is y)."""
     x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
     if not np.all(exact_span_ok(x)):
-        raise ValueError("input spans more than 36 binades: x @ H would not be exact")
-    return x @ _H
+        raise ValueError(f"input spans more than {max_exact_span(n)} binades: the sums would not be exact")
+    if n == D:
+        return x @ _H
+    return (x @ sylvester(n)) * (1.0 / np.sqrt(n))
 
 
 # --------------------------------------------------------------------------
@@ -165,12 +201,12 @@ def e2m1_value(code: np.ndarray) -> np.ndarray:
 
 
 def quantize_blocks(x: np.ndarray):
-    """Split the last axis (256) into 8 blocks of 32 consecutive elements.
+    """Split the last axis (d) into d/32 blocks of 32 consecutive elements.
 
-    Returns (codes (..., 256) uint8 in 0..15, scale bytes (..., 8) uint8).
+    Returns (codes (..., d) uint8 in 0..15, scale bytes (..., d/32) uint8).
     """
     x = np.asarray(x, dtype=np.float64)
-    xb = x.reshape(*x.shape[:-1], D // MX_BLOCK, MX_BLOCK)
+    xb = x.reshape(*x.shape[:-1], x.shape[-1] // MX_BLOCK, MX_BLOCK)
     e = ue8m0_exponent(np.abs(xb).max(axis=-1))
     codes = e2m1_encode(xb, e[..., None]).reshape(x.shape)
     return codes, (e + 127).astype(np.uint8)
@@ -200,7 +236,8 @@ def encode_slots(key_bits: np.ndarray, value_bits: np.ndarray) -> np.ndarray:
 
     Slot layout: [0,128) K codes, [128,256) V codes, [256,264) K scale bytes,
     [264,272) V scale bytes. K is rotated before quantisation, V is not
-    ([UQ-impl] continuation prefill copies V unrotated).
+    ([UQ-impl] continuation prefill copies V unrotated). Other head dims d
+    scale every section (slot_layout).
     """
     # A rotated coordinate that is exactly zero has no sign of its own (its
     # float sign would depend on the summation order); it is encoded as +0.
@@ -209,11 +246,13 @@ def encode_slots(key_bits: np.ndarray, value_bits: np.ndarray) -> np.ndarray:
     v = bf16_to_f64(value_bits)
     kc, ks = quantize_blocks(k)
     vc, vs = quantize_blocks(v)
-    out = np.empty(k.shape[:-1] + (SLOT_BYTES,), dtype=np.uint8)
-    out[..., K_CODE_OFF:K_CODE_OFF + 128] = pack_nibbles(kc)
-    out[..., V_CODE_OFF:V_CODE_OFF + 128] = pack_nibbles(vc)
-    out[..., K_SCALE_OFF:K_SCALE_OFF + 8] = ks
-    out[..., V_SCALE_OFF:V_SCALE_OFF + 8] = vs
+    d = k.shape[-1]
+    nbytes, kco, vco, kso, vso = slot_layout(d)
+    out = np.empty(k.shape[:-1] + (nbytes,), dtype=np.uint8)
+    out[..., kco:kco + d // 2] = pack_nibbles(kc)
+    out[..., vco:vco + d // 2] = pack_nibbles(vc)
+    out[..., kso:kso + d // MX_BLOCK] = ks
+    out[..., vso:vso + d // MX_BLOCK] = vs
     return out
 
 
@@ -225,7 +264,7 @@ def store(key_bits, value_bits, kv_cache: np.ndarray, slot_mapping) -> None:
     value_bits = np.asarray(value_bits)
     slots = np.asarray(slot_mapping, dtype=np.int64)
     nb, bs, hk, ss = kv_cache.shape
-    assert ss == SLOT_BYTES and key_bits.shape[1] == hk
+    assert ss == slot_layout(key_bits.shape[-1])[0] and key_bits.shape[1] == hk
     flat = kv_cache.reshape(nb * bs, hk, ss)
     keep = slots >= 0
     if not np.any(keep):
@@ -234,19 +273,23 @@ def store(key_bits, value_bits, kv_cache: np.ndarray, slot_mapping) -> None:
 
 
 def decode_slots(slot_bytes: np.ndarray):
-    """Dequantised (K, V) float64 (..., 256) of slot bytes (..., 272).
+    """Dequantised (K, V) float64 (..., d) of slot bytes (..., 17 d / 16)
+    (d = 256: 272-byte slots).
 
     K stays in the rotated basis. value = E2M1(code) * 2**(byte - 127).
     """
     s = np.asarray(slot_bytes, dtype=np.uint8)
+    d = head_dim_of_slot(s.shape[-1])
+    _, kco, vco, kso, vso = slot_layout(d)
+    nblk = d // MX_BLOCK
 
     def part(code_off, scale_off):
-        codes = unpack_nibbles(s[..., code_off:code_off + 128])
-        e = s[..., scale_off:scale_off + 8].astype(np.int64) - 127
-        vals = e2m1_value(codes).reshape(*codes.shape[:-1], 8, MX_BLOCK)
+        codes = unpack_nibbles(s[..., code_off:code_off + d // 2])
+        e = s[..., scale_off:scale_off + nblk].astype(np.int64) - 127
+        vals = e2m1_value(codes).reshape(*codes.shape[:-1], nblk, MX_BLOCK)
         return np.ldexp(vals, e[..., None]).reshape(codes.shape)
 
-    return part(K_CODE_OFF, K_SCALE_OFF), part(V_CODE_OFF, V_SCALE_OFF)
+    return part(kco, kso), part(vco, vso)
 
 
 # --------------------------------------------------------------------------
@@ -340,10 +383,10 @@ def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None, sinks
     (W - 1, 0), i.e. a query sees itself and the W - 1 keys before it.
     """
     query_bits = np.asarray(query_bits)
-    B, Hq, _ = query_bits.shape
+    B, Hq, d = query_bits.shape
     hk = kv_cache.shape[2]
     qg = Hq // hk
-    out = np.full((B, Hq, D), np.nan)
+    out = np.full((B, Hq, d), np.nan)
     todo = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(hk)]
     for b, h in todo:
         L = int(seq_lens[b])
@@ -365,7 +408,7 @@ def partial_attention(q8, K, V, scale):
     """One split of [TQ-v2] stage 1: normalised partial output, running max
     and sum of exponentials (m = -inf, l = 0 for an empty range)."""
     if K.shape[0] == 0:
-        return np.zeros((q8.shape[0], D)), np.full(q8.shape[0], -np.inf), np.zeros(q8.shape[0])
+        return np.zeros(q8.shape), np.full(q8.shape[0], -np.inf), np.zeros(q8.shape[0])
     s = scale * (q8 @ K.T)
     m = s.max(axis=-1)
     p = np.exp(s - m[:, None])
@@ -427,8 +470,9 @@ def dequant_prefix(kv_cache: np.ndarray, block_row: np.ndarray, n: int):
     the rotated basis ([UQ-impl] ultraquant_full_dequant_kv into the
     (1, Hk, alloc_len, D) buffers, read back token-major)."""
     hk = kv_cache.shape[2]
-    K = np.zeros((n, hk, D))
-    V = np.zeros((n, hk, D))
+    d = head_dim_of_slot(kv_cache.shape[3])
+    K = np.zeros((n, hk, d))
+    V = np.zeros((n, hk, d))
     for h in range(hk):
         K[:, h], V[:, h] = gather_sequence(kv_cache, block_row, n, h)
     return K, V
@@ -447,7 +491,7 @@ def continuation_prefill(query_bits, key_bits, value_bits, kv_cache, block_row, 
     compute (the others are left NaN); every key and value is still used.
     """
     query_bits = np.asarray(query_bits)
-    q_len, hq_n, _ = query_bits.shape
+    q_len, hq_n, d = query_bits.shape
     hk = np.asarray(key_bits).shape[1]
     qg = hq_n // hk
     Kp, Vp = dequant_prefix(kv_cache, block_row, cached_len)
@@ -457,7 +501,7 @@ def continuation_prefill(query_bits, key_bits, value_bits, kv_cache, block_row, 
     q = rotate_to_bf16(query_bits[rows])
     seq = cached_len + q_len
     visible = np.arange(seq)[None, :] <= cached_len + rows[:, None]
-    out = np.full((q_len, hq_n, D), np.nan)
+    out = np.full((q_len, hq_n, d), np.nan)
     for hq in range(hq_n):
         h = hq // qg
         s = scale * (q[:, hq] @ K[:, h].T)

@@ -548,3 +548,62 @@ def test_prefill_matches_brute_force_loops():
                 w = [math.exp(x - mx) for x in s]
                 want = [sum(w[j] * vals[j][d] for j in range(n)) / sum(w) for d in range(256)]
                 np.testing.assert_allclose(got[i, hq], want, rtol=1e-9, atol=1e-12)
+
+
+# ------------------------------------------------------------ other head dims
+@pytest.mark.parametrize("n", [128, 512])
+def test_rotation_other_head_dims_is_exact_sum_then_one_rounding(n):
+    """For n where sqrt(n) is not a power of two the rotation is the exact
+    +-1 sum times fl64(1/sqrt(n)), rounded once: checked with Fractions."""
+    rng = np.random.default_rng(n)
+    x = O.bf16_to_f64(bf16(rng.standard_normal((3, n)) * np.exp2(rng.integers(-6, 6, (3, n)))))
+    y = O.rotate(x)
+    c = fractions.Fraction(1.0 / math.sqrt(n))
+    for r in range(3):
+        for j in rng.integers(0, n, 12):
+            s = sum(fractions.Fraction(float(x[r, i])) * (-1) ** bin(i & int(j)).count("1") for i in range(n))
+            assert y[r, j] == float(s * c)
+    # orthonormal: scores survive the rotation up to float64 rounding
+    q, k = rng.standard_normal(n), rng.standard_normal(n)
+    qb, kb = O.bf16_to_f64(bf16(q)), O.bf16_to_f64(bf16(k))
+    assert abs(O.rotate(qb) @ O.rotate(kb) - qb @ kb) < 1e-12 * n
+
+
+@pytest.mark.parametrize("n", [128, 512])
+def test_slot_layout_other_head_dims_round_trip(n):
+    """Values E2M1 represents exactly under their block scale survive
+    encode/decode; the sections have the sizes of the layout."""
+    rng = np.random.default_rng(n + 1)
+    nbytes, kco, vco, kso, vso = O.slot_layout(n)
+    assert (nbytes, kco, vco, kso, vso) == (n * 17 // 16, 0, n // 2, n, n + n // 32)
+    blocks = n // 32
+    v = rng.choice(O.E2M1_MAGNITUDES, (5, n)) * rng.choice([-1, 1], (5, n))
+    v[:, ::32] = 6.0                                          # every block's amax is 6: scale byte 127
+    v = v * np.repeat(np.exp2(rng.integers(-3, 4, (5, blocks))), 32, axis=1)
+    vb = bf16(v)
+    kb = bf16(np.zeros((5, n)))
+    slots = O.encode_slots(kb[:, None, :], vb[:, None, :])
+    assert slots.shape == (5, 1, nbytes)
+    K, V = O.decode_slots(slots)
+    assert np.array_equal(V[:, 0], O.bf16_to_f64(vb)) and np.all(K == 0)
+
+
+@pytest.mark.parametrize("n", [128, 512])
+def test_decode_other_head_dims_matches_brute_force(n):
+    rng = np.random.default_rng(n + 2)
+    L, hk, qg, bs = 21, 1, 2, 16
+    k = bf16(rng.standard_normal((L, hk, n)))
+    v = bf16(rng.standard_normal((L, hk, n)))
+    cache = np.zeros((3, bs, hk, O.slot_layout(n)[0]), dtype=np.uint8)
+    O.store(k, v, cache, np.arange(L) + 5)
+    table = np.array([[0, 1, 2]], dtype=np.int32)
+    lens = np.array([L + 5])                               # tokens 0..4 are empty slots (zeros)
+    q = bf16(rng.standard_normal((1, hk * qg, n)))
+    out = O.decode(q, cache, table, lens, 0.1)
+    Kq, Vq = O.decode_slots(cache.reshape(-1, hk, cache.shape[-1])[:L + 5, 0])
+    for hq in range(qg):
+        q8 = O.e4m3_round(O.rotate(O.bf16_to_f64(q[0, hq])))
+        s = [0.1 * float(np.dot(q8, Kq[t])) for t in range(L + 5)]
+        w = [math.exp(x - max(s)) for x in s]
+        want = sum(wi * Vq[t] for t, wi in enumerate(w)) / sum(w)
+        np.testing.assert_allclose(out[0, hq], want, rtol=1e-12, atol=1e-12)
