@@ -135,19 +135,29 @@ def exact_span_ok(x: np.ndarray) -> np.ndarray:
     return (~nz.any(axis=-1)) | (emax - emin <= max_exact_span(a.shape[-1]))
 
 
+def rot_scale(n: int) -> float:
+    """The float64 nearest 1/sqrt(n) for n a power of two: 2**(-e/2) for
+    n = 2**e with e even, else sqrt(2) * 2**(-(e+1)/2) (IEEE sqrt is
+    correctly rounded and the power of two is exact)."""
+    e = int(np.log2(n))
+    assert 1 << e == n
+    return 2.0 ** (-(e // 2)) if e % 2 == 0 else np.sqrt(2.0) * 2.0 ** (-((e + 1) // 2))
+
+
 def rotate(x: np.ndarray) -> np.ndarray:
     """y = x @ H over the last axis ([UQ-impl] _store_kv; key_chunk @ PiT).
 
-    Computed as the exact +-1 sums x @ sylvester(n) times fl64(1/sqrt(n)),
-    one rounding (this build's reading where sqrt(n) is not a power of two,
-    n = 128 or 512; for n = 256 the scale 1/16 is exact and so is y)."""
+    Computed as the exact +-1 sums x @ sylvester(n) times rot_scale(n) (the
+    float64 nearest 1/sqrt(n)), one rounding (this build's reading where
+    sqrt(n) is not a power of two, n = 128 or 512; for n = 256 the scale
+    1/16 is exact and so is y)."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[-1]
     if not np.all(exact_span_ok(x)):
         raise ValueError(f"input spans more than {max_exact_span(n)} binades: the sums would not be exact")
     if n == D:
         return x @ _H
-    return (x @ sylvester(n)) * (1.0 / np.sqrt(n))
+    return (x @ sylvester(n)) * rot_scale(n)
 
 
 # --------------------------------------------------------------------------

@@ -558,7 +558,10 @@ def test_rotation_other_head_dims_is_exact_sum_then_one_rounding(n):
     rng = np.random.default_rng(n)
     x = O.bf16_to_f64(bf16(rng.standard_normal((3, n)) * np.exp2(rng.integers(-6, 6, (3, n)))))
     y = O.rotate(x)
-    c = fractions.Fraction(1.0 / math.sqrt(n))
+    c = fractions.Fraction(O.rot_scale(n))
+    # the scale is the float64 nearest 1/sqrt(n): c^2 n closest to 1 among its neighbours
+    err = lambda f: abs(fractions.Fraction(f) ** 2 * n - 1)
+    assert err(O.rot_scale(n)) < min(err(np.nextafter(O.rot_scale(n), 0)), err(np.nextafter(O.rot_scale(n), 1)))
     for r in range(3):
         for j in rng.integers(0, n, 12):
             s = sum(fractions.Fraction(float(x[r, i])) * (-1) ** bin(i & int(j)).count("1") for i in range(n))
