@@ -54,8 +54,10 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
   if (N < 0) return fail(UQ_EINVAL, "uq_store: N=%lld < 0", (long long)N);
   if (Hk < 1) return fail(UQ_EINVAL, "uq_store: Hk=%d < 1", Hk);
   if (num_blocks < 1) return fail(UQ_EINVAL, "uq_store: num_blocks=%lld < 1", (long long)num_blocks);
-  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_store: head_dim %d unsupported (only 256)", D);
-  if (slot_size != UQ_SLOT_BYTES) return fail(UQ_EUNSUPPORTED, "uq_store: slot_size %d unsupported (only 272)", slot_size);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(UQ_EUNSUPPORTED, "uq_store: head_dim %d unsupported (128, 256, 512)", D);
+  if (slot_size != D * 17 / 16)
+    return fail(UQ_EUNSUPPORTED, "uq_store: slot_size %d unsupported (17 * head_dim / 16 = %d)", slot_size, D * 17 / 16);
   if (!pow2_in(block_size, 16, 256))
     return fail(UQ_EUNSUPPORTED, "uq_store: block_size %d unsupported (16, 32, 64, 128, 256)", block_size);
   if (N == 0) return ok();
@@ -66,18 +68,18 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
   if (!aligned(key, 8) || !aligned(value, 8) || !aligned(kv_cache, 16) || !aligned(slot_mapping, 8))
     return fail(UQ_EINVAL, "uq_store: misaligned pointer (key/value 8 B, kv_cache 16 B, slot_mapping 8 B)");
   if ((N * Hk + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "uq_store: N*Hk too large for one launch");
-  uq::StoreArgs a{key, value, kv_cache, slot_mapping, N, Hk, num_blocks, block_size,
+  uq::StoreArgs a{D, key, value, kv_cache, slot_mapping, N, Hk, num_blocks, block_size,
                   key_stride_n, key_stride_h, val_stride_n, val_stride_h};
   return hip_status(uq::launch_store(a, (hipStream_t)stream), "uq_store launch");
 }
 
 size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits,
                                  int max_blocks_per_seq, int block_size) {
-  if (B < 1 || Hk < 1 || Hq < Hk || Hq % Hk || D != UQ_HEAD_DIM || num_kv_splits < 1 ||
+  if (B < 1 || Hk < 1 || Hq < Hk || Hq % Hk || (D != 128 && D != 256 && D != 512) || num_kv_splits < 1 ||
       num_kv_splits > UQ_MAX_SPLITS || max_blocks_per_seq < 1 || !pow2_in(block_size, 16, 256) ||
       (long long)max_blocks_per_seq * block_size > 0x7FFFFFFFLL)
     return 0;
-  return uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size).total;
+  return uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).total;
 }
 
 static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_cache,
@@ -94,7 +96,8 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
     return fail(UQ_EINVAL, "uq_decode: num_blocks, max_blocks_per_seq and the table rows must be >= 1");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(UQ_EINVAL, "uq_decode: scale must be finite and > 0");
   if (sliding_window < 0) return fail(UQ_EINVAL, "uq_decode: sliding_window %d < 0", sliding_window);
-  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_decode: head_dim %d unsupported (only 256)", D);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(UQ_EUNSUPPORTED, "uq_decode: head_dim %d unsupported (128, 256, 512)", D);
   if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "uq_decode: Hq=%d is not a multiple of Hk=%d", Hq, Hk);
   const int qg = Hq / Hk;
   if (qg != 6 && qg != 8 && qg != 16)
@@ -114,7 +117,7 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
       !aligned(sinks, 4))
     return fail(UQ_EINVAL, "uq_decode: misaligned pointer (query 8 B, kv_cache/out 16 B, workspace 256 B)");
   const uq::DecodePlan plan =
-      uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size);
+      uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D);
   if (workspace_bytes < plan.total)
     return fail(UQ_EWORKSPACE, "uq_decode: workspace %zu bytes < required %zu", workspace_bytes, plan.total);
   if ((long long)B * plan.parts * Hk > 0x7FFFFFFFLL || (long long)B * Hq > 0x7FFFFFFFLL)

@@ -24,26 +24,49 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
-// Query prologue: q8 = E4M3(q H), one wave per (sequence, query head).
+// Query prologue: q8 = E4M3(q H), one wave per (sequence, query head), for
+// head dims 128, 256 and 512.
 // The rotation runs in float64 and is exact, so the E4M3 rounding decision is
 // taken on the exact product.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restrict__ query,
                                                         uint8_t* __restrict__ q8, int B, int Hq,
                                                         int64_t qsb, int64_t qsh) {
+  constexpr int E = D / 64;                    // elements per lane
   const int64_t vec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (vec >= (int64_t)B * Hq) return;
   const int lane = threadIdx.x & 63;
   const int64_t b = vec / Hq;
   const int64_t hq = vec - b * Hq;
-  const uint2 r = *reinterpret_cast<const uint2*>(query + b * qsb + hq * qsh + 4 * lane);
-  double v[4] = {bf16_to_f64(r.x & 0xFFFF), bf16_to_f64(r.x >> 16), bf16_to_f64(r.y & 0xFFFF),
-                 bf16_to_f64(r.y >> 16)};
-  fwht256_wave(v, lane);
-  uint32_t w = 0;
+  const uint16_t* qp = query + b * qsb + hq * qsh + E * lane;
+  double v[E];
+  if constexpr (E == 2) {
+    const uint32_t r = *reinterpret_cast<const uint32_t*>(qp);
+    v[0] = bf16_to_f64(r & 0xFFFF);
+    v[1] = bf16_to_f64(r >> 16);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w |= e4m3_code(v[i] * 0.0625) << (8 * i);
-  reinterpret_cast<uint32_t*>(q8 + vec * kHeadDim)[lane] = w;
+    for (int c = 0; c < E / 4; ++c) {
+      const uint2 r = *reinterpret_cast<const uint2*>(qp + 4 * c);
+      v[4 * c] = bf16_to_f64(r.x & 0xFFFF);
+      v[4 * c + 1] = bf16_to_f64(r.x >> 16);
+      v[4 * c + 2] = bf16_to_f64(r.y & 0xFFFF);
+      v[4 * c + 3] = bf16_to_f64(r.y >> 16);
+    }
+  }
+  fwht_wave<E>(v, lane);
+  uint32_t w[(E + 3) / 4] = {};
+#pragma unroll
+  for (int i = 0; i < E; ++i) w[i / 4] |= e4m3_code(v[i] * rot_scale<D>()) << (8 * (i % 4));
+  uint8_t* dst = q8 + vec * D + E * lane;
+  if constexpr (E == 2) {
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+  } else if constexpr (E == 4) {
+    *reinterpret_cast<uint32_t*>(dst) = w[0];
+  } else {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -68,85 +91,131 @@ __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restri
 // P.V product, and the O^T accumulator of lane l holds q-head l%16,
 // d = 64*grp + 16*i + j (i = element, j = MFMA index).
 // ---------------------------------------------------------------------------
+template <int D>
 struct Tile {
-  uint4 ka, kb;      // K codes: bytes [16*grp, +16) and [64 + 16*grp, +16) of token l%16
-  uint2 ks;          // K scale bytes of token l%16
-  uint2 vd[4];       // V codes: bytes [8*(l%16), +8) of tokens 4*grp + i
-  uint32_t vs[4];    // the V-scale dword holding block (l%16)/2 of tokens 4*grp + i
-  int nvalid;        // tokens of the tile that are inside the sequence
+  uint4 kc[D / 128];           // K codes of token l%16: bytes [64m + 16*grp, +16), m < D/128
+  uint32_t ks[D / 128];        // K scale bytes 4m .. 4m+3 of token l%16
+  uint32_t vd[4][D / 128];     // V codes: bytes [(D/32)*(l%16), +D/32) of tokens 4*grp + i
+  uint32_t vs[4];              // the V-scale dword holding block D*(l%16)/512 of tokens 4*grp + i
+  int nvalid;                  // tokens of the tile that are inside the sequence
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // A wave streams the 16-token tiles of its own KV head through a private
-// two-slot LDS ring: a tile is 16 slots of 272 bytes (token stride `row` in
-// the cache, 272 in LDS), moved as 272 chunks of 16 bytes by five
-// direct-to-LDS buffer loads (the last one on 16 lanes).
-constexpr int kTileChunks = 17 * kTile;          // 272
-constexpr int kTileU4 = kTileChunks;             // uint4 per tile in LDS
-constexpr int kDmaPerTile = 5;                   // ceil(272 / 64)
+// LDS ring: a tile is 16 slots (token stride `row` in the cache), moved by
+// direct-to-LDS buffer loads of kDma bytes per lane. At D = 256 a 272-byte
+// slot is 17 chunks of 16 bytes and a tile five loads (the last on 16
+// lanes); at D = 512, 34 chunks and nine loads. At D = 128 a slot is 136
+// bytes, only 8-byte aligned in the cache, so it moves as 34 dwords into an
+// LDS token stride of 144 bytes (36 dwords, the last two filler), which
+// keeps every LDS operand read 16-byte aligned.
+template <int D>
+struct Stage {
+  static constexpr int kDma = D == 128 ? 4 : 16;
+  static constexpr int kValid = Fmt<D>::kSlot / kDma;        // 34, 17, 34
+  static constexpr int kPer = D == 128 ? 36 : kValid;        // per token in LDS
+  static constexpr int kTokStride = kPer * kDma;             // 144, 272, 544
+  static constexpr int kTileChunks = kTile * kPer;
+  static constexpr int kLoads = (kTileChunks + 63) / 64;     // 9, 5, 9
+  static constexpr int kTileU4 = kTile * kTokStride / 16;    // uint4 per tile in LDS
+};
 
 // Block-table entries e0 .. e0 + 63 of the wave's range sit one per lane in
 // `btv`, loaded once; an entry past them (ranges of more than 64 blocks) is
 // read from memory when its tile is issued.
-__device__ __forceinline__ int issue_tile(uint4* dst, const uint8_t* __restrict__ cache,
-                                           const int32_t* __restrict__ bt, int btv, int e0,
-                                           int t, int L, int log2_bs, int64_t num_blocks,
-                                           uint32_t row, int h, int lane,
-                                           const uint32_t goff[kDmaPerTile]) {
-  const int tok0 = t * kTile;
-  const int entry = tok0 >> log2_bs;
-  const int phys = entry - e0 < 64 ? __builtin_amdgcn_readlane(btv, entry - e0)
-                                   : __builtin_amdgcn_readfirstlane(bt[entry]);
-  const bool ok = phys >= 0 && (int64_t)phys < num_blocks;
-  const int nvalid = ok ? min(kTile, L - tok0) : 0;
-  const size_t tile_off =
-      ((((size_t)(ok ? phys : 0)) << log2_bs) + (size_t)(tok0 & ((1 << log2_bs) - 1))) * row +
-      (size_t)h * kSlotBytes;
-  // the descriptor ends at the last valid token: chunks past it land as zeros
-  const int nrec = nvalid > 0 ? (nvalid - 1) * (int)row + kSlotBytes : 0;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(cache + tile_off), (short)0, nrec, 0x00020000);
-#pragma unroll
-  for (int k = 0; k < kDmaPerTile - 1; ++k)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 64 * k), 16, goff[k], 0, 0, 0);
-  if (lane < kTileChunks - 64 * (kDmaPerTile - 1))
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 64 * (kDmaPerTile - 1)), 16,
-                                             goff[kDmaPerTile - 1], 0, 0, 0);
-  return nvalid;
-}
+// One plain function per head dim, with literal constants (a function
+// template holding these builtins is not viable in the host pass, and
+// constants passed as arguments cost the loads' alias information, after
+// which the compiler drains the ring before every LDS read).
+#define UQ_DEFINE_ISSUE(NAME, SLOT, LOADS, CHUNKS, DMA)                                                \
+  __device__ __forceinline__ int NAME(uint4* dst, const uint8_t* __restrict__ cache,                  \
+                                      const int32_t* __restrict__ bt, int btv, int e0, int t, int L,   \
+                                      int log2_bs, int64_t num_blocks, uint32_t row, int h, int lane,  \
+                                      const uint32_t goff[LOADS]) {                                    \
+    const int tok0 = t * kTile;                                                                        \
+    const int entry = tok0 >> log2_bs;                                                                 \
+    const int phys = entry - e0 < 64 ? __builtin_amdgcn_readlane(btv, entry - e0)                      \
+                                     : __builtin_amdgcn_readfirstlane(bt[entry]);                      \
+    const bool ok = phys >= 0 && (int64_t)phys < num_blocks;                                           \
+    const int nvalid = ok ? min(kTile, L - tok0) : 0;                                                  \
+    const size_t tile_off =                                                                            \
+        ((((size_t)(ok ? phys : 0)) << log2_bs) + (size_t)(tok0 & ((1 << log2_bs) - 1))) * row +       \
+        (size_t)h * (SLOT);                                                                            \
+    /* the descriptor ends at the last valid token: chunks past it land as zeros */                  \
+    const int nrec = nvalid > 0 ? (nvalid - 1) * (int)row + (SLOT) : 0;                                \
+    const __amdgpu_buffer_rsrc_t rs =                                                                  \
+        __builtin_amdgcn_make_buffer_rsrc((void*)(cache + tile_off), (short)0, nrec, 0x00020000);      \
+    _Pragma("unroll") for (int k = 0; k < (LOADS) - 1; ++k)                                            \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (64 * (DMA) / 16) * k), DMA,      \
+                                               goff[k], 0, 0, 0);                                      \
+    if (lane < (CHUNKS) - 64 * ((LOADS) - 1))                                                          \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (64 * (DMA) / 16) * ((LOADS) - 1)), \
+                                               DMA, goff[(LOADS) - 1], 0, 0, 0);                       \
+    return nvalid;                                                                                     \
+  }
+UQ_DEFINE_ISSUE(issue_tile_d128, 136, 9, 576, 4)
+UQ_DEFINE_ISSUE(issue_tile_d256, 272, 5, 272, 16)
+UQ_DEFINE_ISSUE(issue_tile_d512, 544, 9, 544, 16)
+#undef UQ_DEFINE_ISSUE
 
 // s_waitcnt on vector memory only (gfx9 encoding; expcnt and lgkmcnt left free)
 #define UQ_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
 
-// Wait until at most min(K, ahead) tiles (kDmaPerTile loads each) are still
-// in flight: the waitcnt immediate must be a constant, so pick it by cases.
-template <int K>
+// Wait until at most min(K, ahead) tiles (PER loads each) are still in
+// flight: the waitcnt immediate must be a constant, so pick it by cases.
+template <int K, int PER>
 __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
   if constexpr (K == 0) {
     UQ_WAIT_VMCNT(0);
   } else {
     if (ahead >= K) {
-      UQ_WAIT_VMCNT(K * kDmaPerTile);
+      UQ_WAIT_VMCNT(K * PER);
     } else {
-      wait_tiles_ahead<K - 1>(ahead);
+      wait_tiles_ahead<K - 1, PER>(ahead);
     }
   }
 }
 
-// Operands of one staged tile (slot stride 272 bytes).
-__device__ __forceinline__ void read_tile(Tile& T, const uint4* __restrict__ src, int n16, int grp,
+// Operands of one staged tile (LDS token stride Stage<D>::kTokStride).
+template <int D>
+__device__ __forceinline__ void read_tile(Tile<D>& T, const uint4* __restrict__ src, int n16, int grp,
                                           int nvalid) {
+  using F = Fmt<D>;
+  constexpr int C = D / 128;
   const uint8_t* base = reinterpret_cast<const uint8_t*>(src);
-  const uint8_t* kp = base + n16 * kSlotBytes;
-  T.ka = *reinterpret_cast<const uint4*>(kp + kKCodeOff + 16 * grp);
-  T.kb = *reinterpret_cast<const uint4*>(kp + kKCodeOff + 64 + 16 * grp);
-  T.ks = *reinterpret_cast<const uint2*>(kp + kKScaleOff);
+  const uint8_t* kp = base + n16 * Stage<D>::kTokStride;
+#pragma unroll
+  for (int m = 0; m < C; ++m) T.kc[m] = *reinterpret_cast<const uint4*>(kp + F::kKCode + 64 * m + 16 * grp);
+  if constexpr (C == 1) {
+    T.ks[0] = *reinterpret_cast<const uint32_t*>(kp + F::kKScale);
+  } else if constexpr (C == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(kp + F::kKScale);
+    T.ks[0] = x.x;
+    T.ks[1] = x.y;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(kp + F::kKScale);
+    T.ks[0] = x.x; T.ks[1] = x.y; T.ks[2] = x.z; T.ks[3] = x.w;
+  }
+  // V-scale dword of lane row n16: block D*n16/512, i.e. byte n16 >> (9 - log2 D)
+  constexpr int vsh = D == 128 ? 4 : (D == 256 ? 3 : 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint8_t* vp = base + (4 * grp + i) * kSlotBytes;
-    T.vd[i] = *reinterpret_cast<const uint2*>(vp + kVCodeOff + 8 * n16);
-    T.vs[i] = *reinterpret_cast<const uint32_t*>(vp + kVScaleOff + 4 * (n16 >> 3));
+    const uint8_t* vp = base + (4 * grp + i) * Stage<D>::kTokStride;
+    // (read through the pointer, field by field: this form keeps the loads'
+    // alias information, without which the ring is drained before the read)
+    if constexpr (C == 1) {
+      T.vd[i][0] = *reinterpret_cast<const uint32_t*>(vp + F::kVCode + 4 * n16);
+    } else if constexpr (C == 2) {
+      T.vd[i][0] = reinterpret_cast<const uint2*>(vp + F::kVCode + 8 * n16)->x;
+      T.vd[i][1] = reinterpret_cast<const uint2*>(vp + F::kVCode + 8 * n16)->y;
+    } else {
+      T.vd[i][0] = reinterpret_cast<const uint4*>(vp + F::kVCode + 16 * n16)->x;
+      T.vd[i][1] = reinterpret_cast<const uint4*>(vp + F::kVCode + 16 * n16)->y;
+      T.vd[i][2] = reinterpret_cast<const uint4*>(vp + F::kVCode + 16 * n16)->z;
+      T.vd[i][3] = reinterpret_cast<const uint4*>(vp + F::kVCode + 16 * n16)->w;
+    }
+    T.vs[i] = *reinterpret_cast<const uint32_t*>(vp + F::kVScale + 4 * (n16 >> vsh));
   }
   T.nvalid = nvalid;
 }
@@ -154,13 +223,13 @@ __device__ __forceinline__ void read_tile(Tile& T, const uint4* __restrict__ src
 // Byte M of each token's 8 V-code bytes holds d = 16*(l%16) + 2M (low nibble)
 // and 2M + 1 (high nibble). Convert them for the lane's 4 tokens, regroup the
 // bf16 halves by d, and accumulate two MFMAs (d even / odd).
-template <int M>
-__device__ __forceinline__ void pv_step(const Tile& T, const float vscale[4], const v4s& pb,
-                                        v4f acc[16]) {
+template <int D, int M>
+__device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4], const v4s& pb,
+                                        v4f acc[D / 16]) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t src = (M < 4) ? T.vd[i].x : T.vd[i].y;
+    const uint32_t src = T.vd[i][M >> 2];
     w[i] = __builtin_bit_cast(uint32_t,
                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, vscale[i], M & 3));
   }
@@ -186,16 +255,16 @@ __device__ __forceinline__ float rowgroup_max(float x) {
 // Scores of one tile in the log2 domain (lane: q-head l%16, tokens 4*grp+i),
 // -inf past the end of the sequence and for the tile's first `first` tokens
 // (those before a sliding window); mt = the tile maximum for the lane's head.
-__device__ __forceinline__ void qk_tile(const Tile& T, const v8i& qb0, const v8i& qb1,
-                                        float scale_log2, int grp, int first, float sv[4],
-                                        float& mt) {
-  const int sc1 = (int)((T.ks.x >> (8 * grp)) & 0xFF);
-  const int sc2 = (int)((T.ks.y >> (8 * grp)) & 0xFF);
-  const v8i a1 = {(int)T.ka.x, (int)T.ka.y, (int)T.ka.z, (int)T.ka.w, 0, 0, 0, 0};
-  const v8i a2 = {(int)T.kb.x, (int)T.kb.y, (int)T.kb.z, (int)T.kb.w, 0, 0, 0, 0};
+template <int D>
+__device__ __forceinline__ void qk_tile(const Tile<D>& T, const v8i qb[D / 128], float scale_log2,
+                                        int grp, int first, float sv[4], float& mt) {
   v4f sc = {0.f, 0.f, 0.f, 0.f};
-  sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, qb0, sc, 4, 0, 0, sc1, 0, 127);
-  sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a2, qb1, sc, 4, 0, 0, sc2, 0, 127);
+#pragma unroll
+  for (int m = 0; m < D / 128; ++m) {
+    const int scm = (int)((T.ks[m] >> (8 * grp)) & 0xFF);
+    const v8i a = {(int)T.kc[m].x, (int)T.kc[m].y, (int)T.kc[m].z, (int)T.kc[m].w, 0, 0, 0, 0};
+    sc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qb[m], sc, 4, 0, 0, scm, 0, 127);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) sv[i] = sc[i] * scale_log2;
   if (T.nvalid < kTile || first > 0) {     // the sequence's last tile, the window's first
@@ -209,8 +278,9 @@ __device__ __forceinline__ void qk_tile(const Tile& T, const v8i& qb0, const v8i
 
 // Softmax weights p = 2^(s - m_ref) (<= 2^8 by the re-basing rule), then
 // O^T += V^T P^T. Touches the accumulators only through MFMAs.
-__device__ __forceinline__ void pv_tile(const Tile& T, const float sv[4], float m_ref, int n16,
-                                        v4f acc[16], float& l_part) {
+template <int D>
+__device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], float m_ref, int n16,
+                                        v4f acc[D / 16], float& l_part) {
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
@@ -222,20 +292,32 @@ __device__ __forceinline__ void pv_tile(const Tile& T, const float sv[4], float 
             (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
   const v4s pb = __builtin_bit_cast(v4s, make_uint2(p01, p23));
   float vscale[4];
-  const int vsh = 8 * ((n16 >> 1) & 3);
+  const int vsh = 8 * (((D * n16) / 512) & 3);
 #pragma unroll
   for (int i = 0; i < 4; ++i) vscale[i] = __uint_as_float(((T.vs[i] >> vsh) & 0xFFu) << 23);
-  pv_step<0>(T, vscale, pb, acc);
-  pv_step<1>(T, vscale, pb, acc);
-  pv_step<2>(T, vscale, pb, acc);
-  pv_step<3>(T, vscale, pb, acc);
-  pv_step<4>(T, vscale, pb, acc);
-  pv_step<5>(T, vscale, pb, acc);
-  pv_step<6>(T, vscale, pb, acc);
-  pv_step<7>(T, vscale, pb, acc);
+  pv_step<D, 0>(T, vscale, pb, acc);
+  pv_step<D, 1>(T, vscale, pb, acc);
+  pv_step<D, 2>(T, vscale, pb, acc);
+  pv_step<D, 3>(T, vscale, pb, acc);
+  if constexpr (D >= 256) {
+    pv_step<D, 4>(T, vscale, pb, acc);
+    pv_step<D, 5>(T, vscale, pb, acc);
+    pv_step<D, 6>(T, vscale, pb, acc);
+    pv_step<D, 7>(T, vscale, pb, acc);
+  }
+  if constexpr (D >= 512) {
+    pv_step<D, 8>(T, vscale, pb, acc);
+    pv_step<D, 9>(T, vscale, pb, acc);
+    pv_step<D, 10>(T, vscale, pb, acc);
+    pv_step<D, 11>(T, vscale, pb, acc);
+    pv_step<D, 12>(T, vscale, pb, acc);
+    pv_step<D, 13>(T, vscale, pb, acc);
+    pv_step<D, 14>(T, vscale, pb, acc);
+    pv_step<D, 15>(T, vscale, pb, acc);
+  }
 }
 
-template <int QG, int HPW, int NSLOT>
+template <int D, int QG, int HPW, int NSLOT>
 __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ query_row, int n_rows,
@@ -244,10 +326,13 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     int log2_bs, int max_blocks, int64_t num_blocks, int window, float* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l) {
   static_assert(NSLOT >= 3 && NSLOT <= 8, "ring depth");
-  static_assert(NSLOT * HPW * kTileU4 * 16 <= 160 * 1024, "ring exceeds the LDS of a CU");
+  using S = Stage<D>;
+  static_assert(NSLOT * HPW * S::kTileU4 * 16 <= 160 * 1024, "ring exceeds the LDS of a CU");
+  constexpr int C = D / 128;               // scaled MFMAs per score tile
+  constexpr int NA = D / 16;               // O^T accumulators
   // NSLOT-slot ring per wave; distinct arrays so that the compiler can tell
   // the slot being read from the slots being filled
-#define UQ_RING_DECL(K) __shared__ uint4 ring##K[NSLOT > K ? HPW : 1][NSLOT > K ? kTileU4 : 1];
+#define UQ_RING_DECL(K) __shared__ uint4 ring##K[NSLOT > K ? HPW : 1][NSLOT > K ? S::kTileU4 : 1];
   UQ_RING_DECL(0) UQ_RING_DECL(1) UQ_RING_DECL(2) UQ_RING_DECL(3)
   UQ_RING_DECL(4) UQ_RING_DECL(5) UQ_RING_DECL(6) UQ_RING_DECL(7)
 #undef UQ_RING_DECL
@@ -272,13 +357,16 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int n16 = lane & 15, grp = lane >> 4;
   const bool qlane = n16 < QG;
   const int hq = h * QG + (qlane ? n16 : 0);
-  v8i qb0 = {0, 0, 0, 0, 0, 0, 0, 0}, qb1 = {0, 0, 0, 0, 0, 0, 0, 0};
+  v8i qb[C];
+#pragma unroll
+  for (int m = 0; m < C; ++m) qb[m] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
   if (qlane) {
-    const uint8_t* qp = q8 + ((size_t)b * Hq + hq) * kHeadDim;
-    const uint4 x0 = ld16(qp + 16 * grp), x1 = ld16(qp + 64 + 16 * grp);
-    const uint4 x2 = ld16(qp + 128 + 16 * grp), x3 = ld16(qp + 192 + 16 * grp);
-    qb0 = (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    qb1 = (v8i){(int)x2.x, (int)x2.y, (int)x2.z, (int)x2.w, (int)x3.x, (int)x3.y, (int)x3.z, (int)x3.w};
+    const uint8_t* qp = q8 + ((size_t)b * Hq + hq) * D;
+#pragma unroll
+    for (int m = 0; m < C; ++m) {
+      const uint4 x0 = ld16(qp + 128 * m + 16 * grp), x1 = ld16(qp + 128 * m + 64 + 16 * grp);
+      qb[m] = (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    }
   }
   // Query row b reads block-table row query_row[b] (its own row when there
   // is no mapping); a row outside the table reads as an empty sequence.
@@ -307,16 +395,22 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     return;
   }
 
-  const uint32_t row = (uint32_t)Hk * kSlotBytes;
-  uint32_t goff[kDmaPerTile];                 // chunk c -> token c / 17, 16 bytes (c % 17)
+  const uint32_t row = (uint32_t)Hk * Fmt<D>::kSlot;
+  uint32_t goff[S::kLoads];   // load k, lane -> chunk c: token c / kPer, piece c % kPer (filler: piece 0)
 #pragma unroll
-  for (int k = 0; k < kDmaPerTile; ++k) {
-    const int c = min(64 * k + lane, kTileChunks - 1);
-    goff[k] = (c / 17) * row + (c % 17) * 16;
+  for (int k = 0; k < S::kLoads; ++k) {
+    const int c = min(64 * k + lane, S::kTileChunks - 1);
+    const int piece = c % S::kPer;
+    goff[k] = (c / S::kPer) * row + (piece < S::kValid ? piece : 0) * S::kDma;
   }
-  auto issue = [&](uint4* slot, int t) {
-    return issue_tile(slot, cache, bt, btv, e0, t, L, log2_bs, num_blocks, row, h, lane, goff);
-  };
+  static_assert(Fmt<D>::kSlot == (D == 128 ? 136 : D == 256 ? 272 : 544) &&
+                    S::kLoads == (D == 256 ? 5 : 9) && S::kTileChunks == (D == 128 ? 576 : D == 256 ? 272 : 544) &&
+                    S::kDma == (D == 128 ? 4 : 16),
+                "the issue_tile_d* constants follow Stage<D>");
+#define issue(SLOT, TT)                                                                                 \
+  (D == 128 ? issue_tile_d128(SLOT, cache, bt, btv, e0, TT, L, log2_bs, num_blocks, row, h, lane, goff) \
+   : D == 256 ? issue_tile_d256(SLOT, cache, bt, btv, e0, TT, L, log2_bs, num_blocks, row, h, lane, goff) \
+              : issue_tile_d512(SLOT, cache, bt, btv, e0, TT, L, log2_bs, num_blocks, row, h, lane, goff))
 
   // Softmax reference: the first tile's maximum. The weights 2^(s - m_ref)
   // are exact for any reference; keeping them <= 2^8 bounds their range. A
@@ -325,16 +419,16 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   // to the raised reference, and the tile loop restarts at that tile. The
   // running accumulators are only ever written by MFMAs inside the loop, so
   // they stay in the accumulator registers.
-  v4f acc[16], hold[16];
+  v4f acc[NA], hold[NA];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) hold[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NA; ++j) hold[j] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f, l_hold = 0.f;
   int t0 = u0;
   for (;;) {
-    Tile T;
+    Tile<D> T;
     float sv[4], mt;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NA; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
     l_part = 0.f;
     bool rebased = false;
     int t_stop = 0;
@@ -350,13 +444,13 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     // slot tile t - 1 used (already consumed), then compute tile t.
 #define UQ_STEP(CUR, NXT)                                                        \
     {                                                                            \
-      wait_tiles_ahead<NSLOT - 2>(u1 - 1 - t);                                   \
-      read_tile(T, CUR[wave], n16, grp, nv_##CUR);                               \
+      wait_tiles_ahead<NSLOT - 2, S::kLoads>(u1 - 1 - t);                        \
+      read_tile<D>(T, CUR[wave], n16, grp, nv_##CUR);                            \
       if (t + NSLOT - 1 < u1) nv_##NXT = issue(NXT[wave], t + NSLOT - 1);        \
-      qk_tile(T, qb0, qb1, scale_log2, grp, lo - t * kTile, sv, mt);             \
+      qk_tile<D>(T, qb, scale_log2, grp, lo - t * kTile, sv, mt);                \
       if (t == u0) m_ref = mt;                                                   \
       if (__any(mt > m_ref + 8.0f)) { rebased = true; t_stop = t; break; }       \
-      if (T.nvalid > 0) pv_tile(T, sv, m_ref, n16, acc, l_part);                 \
+      if (T.nvalid > 0) pv_tile<D>(T, sv, m_ref, n16, acc, l_part);              \
       if (++t >= u1) break;                                                      \
     }
     if constexpr (NSLOT == 3) {
@@ -396,14 +490,15 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const float m_new = fmaxf(m_ref, mt);
     const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) hold[j] = (hold[j] + acc[j]) * f;
+    for (int j = 0; j < NA; ++j) hold[j] = (hold[j] + acc[j]) * f;
     l_hold = (l_hold + l_part) * f;
     m_ref = m_new;
     UQ_WAIT_VMCNT(0);
     t0 = t_stop;
   }
+#undef issue
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] += hold[j];
+  for (int j = 0; j < NA; ++j) acc[j] += hold[j];
   l_part += l_hold;
 
   const float l1 = l_part + __shfl_xor(l_part, 16);
@@ -414,13 +509,14 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     part_l[stat] = l_tot;
   }
   if (l_tot > 0.f) {
+    // lane (head l%16, grp) holds dims NA*(4*grp + i) + j
     const float inv = 1.f / l_tot;
-    float* op = part_o + stat * kHeadDim + 64 * grp;
+    float* op = part_o + stat * D + NA * 4 * grp;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 16; j += 4)
-        *reinterpret_cast<float4*>(op + 16 * i + j) =
+      for (int j = 0; j < NA; j += 4)
+        *reinterpret_cast<float4*>(op + NA * i + j) =
             make_float4(acc[j][i] * inv, acc[j + 1][i] * inv, acc[j + 2][i] * inv, acc[j + 3][i] * inv);
     }
   }
@@ -435,6 +531,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 // across the wave, so the skip of empty partials is a uniform branch and
 // their (stale) rows are never touched by arithmetic.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o,
                                                      const float* __restrict__ part_m,
                                                      const float* __restrict__ part_l,
@@ -445,20 +542,33 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   const int lane = threadIdx.x & 63;
   const float* pm = part_m + (size_t)row * P;
   const float* pl = part_l + (size_t)row * P;
-  const float* po = part_o + (size_t)row * P * kHeadDim + 4 * lane;
+  constexpr int E = D / 64;                  // columns per lane: E l .. E l + E - 1
+  const float* po = part_o + (size_t)row * P * D + E * lane;
   float M = -INFINITY, den = 0.f;
   if (sinks) {              // the sink: a partial of weight 1 at its logit, with no value
     M = sinks[row % Hq] * 1.4426950408889634f;
     den = 1.f;
   }
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float a[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) a[e] = 0.f;
   for (int p0 = 0; p0 < P; p0 += 8) {
-    float4 o[8];
+    float o[8][E];
     float m[8], l[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int p = min(p0 + u, P - 1);
-      o[u] = *reinterpret_cast<const float4*>(po + (size_t)p * kHeadDim);
+      const float* src = po + (size_t)p * D;
+      if constexpr (E == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        o[u][0] = x.x; o[u][1] = x.y;
+      } else {
+#pragma unroll
+        for (int c = 0; c < E / 4; ++c) {
+          const float4 x = *reinterpret_cast<const float4*>(src + 4 * c);
+          o[u][4 * c] = x.x; o[u][4 * c + 1] = x.y; o[u][4 * c + 2] = x.z; o[u][4 * c + 3] = x.w;
+        }
+      }
       m[u] = pm[p];
       l[u] = p0 + u < P ? pl[p] : 0.f;
     }
@@ -469,19 +579,24 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
         const float c = exp2f(M - Mn);            // 0 for the first partial, <= 1 after
         const float w = l[u] * exp2f(m[u] - Mn);
         den = den * c + w;
-        a.x = a.x * c + w * o[u].x;
-        a.y = a.y * c + w * o[u].y;
-        a.z = a.z * c + w * o[u].z;
-        a.w = a.w * c + w * o[u].w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] = a[e] * c + w * o[u][e];
         M = Mn;
       }
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint2 r;
-  r.x = pack_bf16(a.x * inv, a.y * inv);
-  r.y = pack_bf16(a.z * inv, a.w * inv);
-  *reinterpret_cast<uint2*>(out + (size_t)row * kHeadDim + 4 * lane) = r;
+  uint32_t r[E / 2];
+#pragma unroll
+  for (int e = 0; e < E / 2; ++e) r[e] = pack_bf16(a[2 * e] * inv, a[2 * e + 1] * inv);
+  uint16_t* dst = out + (size_t)row * D + E * lane;
+  if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = r[0];
+  } else if constexpr (E == 4) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(r[0], r[1]);
+  } else {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(r[0], r[1], r[2], r[3]);
+  }
 }
 
 int largest_divisor_upto(int n, int cap) {
@@ -505,15 +620,18 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #endif
 // Ring depth per wave: as deep as the LDS of one CU allows for the
 // workgroup's HPW waves (4352 bytes per slot), capped at UQ_RING_SLOTS.
+template <int D>
 constexpr int ring_slots(int hpw) {
-  return (160 * 1024) / (hpw * kTileU4 * 16) < UQ_RING_SLOTS ? (160 * 1024) / (hpw * kTileU4 * 16)
-                                                              : UQ_RING_SLOTS;
+  return (160 * 1024) / (hpw * Stage<D>::kTileU4 * 16) < UQ_RING_SLOTS
+             ? (160 * 1024) / (hpw * Stage<D>::kTileU4 * 16)
+             : UQ_RING_SLOTS;
 }
 constexpr long kTilesPerWaveMin = 4;
 
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
-                       int block_size) {
+                       int block_size, int D) {
   DecodePlan p{};
+  p.D = D;
   p.B = B;
   p.Hq = Hq;
   p.Hk = Hk;
@@ -542,9 +660,9 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_
   const size_t rows = (size_t)B * Hq;
   size_t off = 0;
   p.q8_off = off;
-  off = align256(off + rows * kHeadDim);
+  off = align256(off + rows * D);
   p.o_off = off;
-  off = align256(off + rows * p.parts * kHeadDim * sizeof(float));
+  off = align256(off + rows * p.parts * D * sizeof(float));
   p.m_off = off;
   off = align256(off + rows * p.parts * sizeof(float));
   p.l_off = off;
@@ -561,10 +679,16 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   float* part_l = reinterpret_cast<float*>(a.workspace + p.l_off);
   const int64_t vecs = (int64_t)p.B * p.Hq;
 
+  if (p.D != 128 && p.D != 256 && p.D != 512) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
   if (stage_mask & 1) {
-    hipLaunchKernelGGL(qprologue_kernel, dim3((unsigned)((vecs + 3) / 4)), dim3(256), 0, stream,
-                       a.query, q8, p.B, p.Hq, a.qsb, a.qsh);
+    const dim3 g((unsigned)((vecs + 3) / 4));
+    if (p.D == 128)
+      hipLaunchKernelGGL(qprologue_kernel<128>, g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, a.qsb, a.qsh);
+    else if (p.D == 256)
+      hipLaunchKernelGGL(qprologue_kernel<256>, g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, a.qsb, a.qsh);
+    else
+      hipLaunchKernelGGL(qprologue_kernel<512>, g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, a.qsb, a.qsh);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -590,37 +714,48 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   }
   const dim3 grid1((unsigned)((int64_t)p.B * p.parts * hgroups));
   const dim3 block1(64 * hpw);
-#define UQ_STAGE1(QGV, HPWV)                                                                     \
-  hipLaunchKernelGGL((stage1_kernel<QGV, HPWV, ring_slots(HPWV)>), grid1, block1, 0, stream, q8,       \
+#define UQ_STAGE1(DV, QGV, HPWV)                                                                  \
+  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, ring_slots<DV>(HPWV)>), grid1, block1, 0, stream, q8, \
                      a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens, scale_log2,    \
                      p.Hq, p.Hk, hgroups,                                                      \
                      cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,            \
                      a.num_blocks, a.window, part_o, part_m, part_l)
-#define UQ_STAGE1_HPW(QGV)                      \
+#define UQ_STAGE1_HPW(DV, QGV)                  \
   do {                                          \
     switch (hpw) {                              \
-      case 1: UQ_STAGE1(QGV, 1); break;         \
-      case 2: UQ_STAGE1(QGV, 2); break;         \
-      case 4: UQ_STAGE1(QGV, 4); break;         \
-      default: UQ_STAGE1(QGV, 8); break;        \
+      case 1: UQ_STAGE1(DV, QGV, 1); break;     \
+      case 2: UQ_STAGE1(DV, QGV, 2); break;     \
+      default: UQ_STAGE1(DV, QGV, 4); break;    \
+    }                                           \
+  } while (0)
+#define UQ_STAGE1_QG(DV)                        \
+  do {                                          \
+    switch (p.QG) {                             \
+      case 6: UQ_STAGE1_HPW(DV, 6); break;      \
+      case 8: UQ_STAGE1_HPW(DV, 8); break;      \
+      default: UQ_STAGE1_HPW(DV, 16); break;    \
     }                                           \
   } while (0)
   if (stage_mask & 2) {
-    if (hpw != 1 && hpw != 2 && hpw != 4 && hpw != 8) return hipErrorInvalidValue;
-    switch (p.QG) {
-      case 6: UQ_STAGE1_HPW(6); break;
-      case 8: UQ_STAGE1_HPW(8); break;
-      case 16: UQ_STAGE1_HPW(16); break;
-      default: return hipErrorInvalidValue;
-    }
+    if (hpw != 1 && hpw != 2 && hpw != 4) return hipErrorInvalidValue;
+    if (p.QG != 6 && p.QG != 8 && p.QG != 16) return hipErrorInvalidValue;
+    if (p.D == 128) UQ_STAGE1_QG(128);
+    else if (p.D == 256) UQ_STAGE1_QG(256);
+    else UQ_STAGE1_QG(512);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+#undef UQ_STAGE1_QG
 #undef UQ_STAGE1_HPW
 #undef UQ_STAGE1
   if (stage_mask & 4) {
-    hipLaunchKernelGGL(stage2_kernel, dim3((unsigned)((vecs + 3) / 4)), dim3(256), 0, stream,
-                       part_o, part_m, part_l, a.sinks, p.Hq, a.out, (int)vecs, p.parts);
+    const dim3 g((unsigned)((vecs + 3) / 4));
+#define UQ_STAGE2(DV) hipLaunchKernelGGL(stage2_kernel<DV>, g, dim3(256), 0, stream, part_o, part_m, \
+                                         part_l, a.sinks, p.Hq, a.out, (int)vecs, p.parts)
+    if (p.D == 128) UQ_STAGE2(128);
+    else if (p.D == 256) UQ_STAGE2(256);
+    else UQ_STAGE2(512);
+#undef UQ_STAGE2
     e = hipGetLastError();
   }
   return e;

@@ -11,6 +11,23 @@ constexpr int kSlotBytes = 272;
 constexpr int kKCodeOff = 0, kVCodeOff = 128, kKScaleOff = 256, kVScaleOff = 264;
 constexpr int kTile = 16;        // tokens per decode tile
 
+// Slot format for head dim D (128, 256 or 512): D/2 bytes of K codes, D/2 of
+// V codes, then D/32 K scale bytes and D/32 V scale bytes, 17 D / 16 bytes.
+template <int D>
+struct Fmt {
+  static_assert(D == 128 || D == 256 || D == 512, "head dim");
+  static constexpr int kSlot = D * 17 / 16;
+  static constexpr int kKCode = 0, kVCode = D / 2, kKScale = D, kVScale = D + D / 32;
+  static constexpr int kPerLane = D / 64;          // elements per lane of a one-wave vector
+};
+
+// The float64 nearest 1/sqrt(D): sqrt(2) = 0x1.6a09e667f3bcdp+0 correctly
+// rounded, scaled by a power of two where D is an odd power of two.
+template <int D>
+constexpr double rot_scale() {
+  return D == 256 ? 0.0625 : (D == 128 ? 0x1.6a09e667f3bcdp-4 : 0x1.6a09e667f3bcdp-5);
+}
+
 typedef int   v8i  __attribute__((ext_vector_type(8)));
 typedef float v4f  __attribute__((ext_vector_type(4)));
 typedef short v4s  __attribute__((ext_vector_type(4)));
@@ -38,6 +55,31 @@ __device__ __forceinline__ int floor_log2(double a) {
 // are lane bits 0-5. Each stage maps (a, b) -> (a + b, a - b). In float64 the
 // result is exact whenever every +-sum of the inputs fits 53 bits, which
 // holds for bf16 inputs whose non-zero magnitudes span at most 36 binades.
+template <int E>
+__device__ __forceinline__ void fwht_wave(double v[E], int lane) {
+  // D-point butterfly, D = 64 E: index bits below log2(E) inside a lane, the
+  // rest are lane bits 0-5 (same exactness condition as below)
+#pragma unroll
+  for (int m = 1; m < E; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if (i & m) continue;
+      const double a = v[i], b = v[i + m];
+      v[i] = a + b;
+      v[i + m] = a - b;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const double o = __shfl_xor(v[i], m);
+      v[i] = upper ? (o - v[i]) : (v[i] + o);
+    }
+  }
+}
+
 __device__ __forceinline__ void fwht256_wave(double v[4], int lane) {
   const double a0 = v[0] + v[1], a1 = v[0] - v[1];
   const double a2 = v[2] + v[3], a3 = v[2] - v[3];

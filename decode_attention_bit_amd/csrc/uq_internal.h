@@ -6,6 +6,7 @@
 namespace uq {
 
 struct StoreArgs {
+  int D;                      // head dim: 128, 256 or 512
   const uint16_t* key;
   const uint16_t* value;
   uint8_t* cache;
@@ -19,6 +20,7 @@ struct StoreArgs {
 
 // Partial results of split-KV stage 1, carved out of the caller's workspace.
 struct DecodePlan {
+  int D;               // head dim: 128, 256 or 512
   int B, Hq, Hk, QG;
   int splits;          // num_kv_splits
   int cs;              // tiles per split: ceil(ceil(max_blocks * block_size / 16) / splits)
@@ -94,7 +96,7 @@ struct PrefillAttnArgs {
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
-                       int block_size);
+                       int block_size, int D);
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_hadamard(int D, float* H, hipStream_t stream);

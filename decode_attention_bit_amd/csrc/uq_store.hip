@@ -1,5 +1,6 @@
-// Store: rotate K by the 256-point Hadamard, quantise K and V to FP4 E2M1 with
-// one UE8M0 scale per 32 elements, and write 272-byte cache slots.
+// Store: rotate K by the D-point Hadamard, quantise K and V to FP4 E2M1 with
+// one UE8M0 scale per 32 elements, and write 17 D / 16-byte cache slots
+// (272 bytes at D = 256).
 // (vLLM API docs, UltraQuantAttentionImpl: _ensure_on_device builds the pure
 // Hadamard, orthonormal and symmetric; _store_kv rotates K and packs K+V into
 // FP4/UE8M0 slots of kv_cache (num_blocks, block_size, Hk, slot_size).)
@@ -7,14 +8,18 @@
 
 namespace uq {
 
-// One wave per (token, KV head): lane l owns elements 4l .. 4l+3, so a 32-
-// element scale block is 8 consecutive lanes and the 128 code bytes of a
-// region are written as 64 contiguous 2-byte stores.
+// One wave per (token, KV head): lane l owns elements E l .. E l + E - 1
+// (E = D / 64), so a 32-element scale block is 32 / E consecutive lanes and
+// the D/2 code bytes of a region are written as 64 contiguous stores of E/2
+// bytes.
+template <int D>
 __global__ __launch_bounds__(256) void store_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
     int64_t n_pairs, int Hk, int64_t num_slots, int64_t ksn, int64_t ksh,
     int64_t vsn, int64_t vsh) {
+  using F = Fmt<D>;
+  constexpr int E = F::kPerLane, LPB = 32 / E;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= n_pairs) return;
   const int lane = threadIdx.x & 63;
@@ -23,24 +28,40 @@ __global__ __launch_bounds__(256) void store_kernel(
   const int64_t slot = slot_mapping[n];
   if (slot < 0 || slot >= num_slots) return;
 
-  const uint2 kr = *reinterpret_cast<const uint2*>(key + n * ksn + h * ksh + 4 * lane);
-  const uint2 vr = *reinterpret_cast<const uint2*>(value + n * vsn + h * vsh + 4 * lane);
-  double k[4] = {bf16_to_f64(kr.x & 0xFFFF), bf16_to_f64(kr.x >> 16),
-                 bf16_to_f64(kr.y & 0xFFFF), bf16_to_f64(kr.y >> 16)};
-  double v[4] = {bf16_to_f64(vr.x & 0xFFFF), bf16_to_f64(vr.x >> 16),
-                 bf16_to_f64(vr.y & 0xFFFF), bf16_to_f64(vr.y >> 16)};
-
-  fwht256_wave(k, lane);
+  double k[E], v[E];
+  const uint16_t* kp = key + n * ksn + h * ksh + E * lane;
+  const uint16_t* vp = value + n * vsn + h * vsh + E * lane;
+  if constexpr (E == 2) {
+    const uint32_t kr = *reinterpret_cast<const uint32_t*>(kp), vr = *reinterpret_cast<const uint32_t*>(vp);
+    k[0] = bf16_to_f64(kr & 0xFFFF); k[1] = bf16_to_f64(kr >> 16);
+    v[0] = bf16_to_f64(vr & 0xFFFF); v[1] = bf16_to_f64(vr >> 16);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    k[i] *= 0.0625;                    // 1/sqrt(256), exact
+    for (int c = 0; c < E / 4; ++c) {
+      const uint2 kr = *reinterpret_cast<const uint2*>(kp + 4 * c);
+      const uint2 vr = *reinterpret_cast<const uint2*>(vp + 4 * c);
+      k[4 * c] = bf16_to_f64(kr.x & 0xFFFF); k[4 * c + 1] = bf16_to_f64(kr.x >> 16);
+      k[4 * c + 2] = bf16_to_f64(kr.y & 0xFFFF); k[4 * c + 3] = bf16_to_f64(kr.y >> 16);
+      v[4 * c] = bf16_to_f64(vr.x & 0xFFFF); v[4 * c + 1] = bf16_to_f64(vr.x >> 16);
+      v[4 * c + 2] = bf16_to_f64(vr.y & 0xFFFF); v[4 * c + 3] = bf16_to_f64(vr.y >> 16);
+    }
+  }
+
+  fwht_wave<E>(k, lane);
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    k[i] *= rot_scale<D>();            // 1/16 exact at D = 256; one rounding otherwise
     if (k[i] == 0.0) k[i] = 0.0;       // an exact zero carries no sign: +0
   }
 
-  double ka = fmax(fmax(fabs(k[0]), fabs(k[1])), fmax(fabs(k[2]), fabs(k[3])));
-  double va = fmax(fmax(fabs(v[0]), fabs(v[1])), fmax(fabs(v[2]), fabs(v[3])));
+  double ka = 0.0, va = 0.0;
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
+  for (int i = 0; i < E; ++i) {
+    ka = fmax(ka, fabs(k[i]));
+    va = fmax(va, fabs(v[i]));
+  }
+#pragma unroll
+  for (int m = 1; m < LPB; m <<= 1) {
     ka = fmax(ka, __shfl_xor(ka, m));
     va = fmax(va, __shfl_xor(va, m));
   }
@@ -48,18 +69,26 @@ __global__ __launch_bounds__(256) void store_kernel(
   const int ve = mx_block_exponent(va);
   const double kinv = pow2(-ke), vinv = pow2(-ve);
 
-  uint32_t kp = 0, vp = 0;
+  uint32_t kc = 0, vc = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    kp |= e2m1_code(k[i], kinv) << (4 * i);
-    vp |= e2m1_code(v[i], vinv) << (4 * i);
+  for (int i = 0; i < E; ++i) {
+    kc |= e2m1_code(k[i], kinv) << (4 * i);
+    vc |= e2m1_code(v[i], vinv) << (4 * i);
   }
-  uint8_t* dst = cache + ((size_t)slot * Hk + h) * kSlotBytes;
-  reinterpret_cast<uint16_t*>(dst + kKCodeOff)[lane] = (uint16_t)kp;
-  reinterpret_cast<uint16_t*>(dst + kVCodeOff)[lane] = (uint16_t)vp;
-  if ((lane & 7) == 0) {
-    dst[kKScaleOff + (lane >> 3)] = (uint8_t)(ke + 127);
-    dst[kVScaleOff + (lane >> 3)] = (uint8_t)(ve + 127);
+  uint8_t* dst = cache + ((size_t)slot * Hk + h) * F::kSlot;
+  if constexpr (E == 2) {
+    dst[F::kKCode + lane] = (uint8_t)kc;
+    dst[F::kVCode + lane] = (uint8_t)vc;
+  } else if constexpr (E == 4) {
+    reinterpret_cast<uint16_t*>(dst + F::kKCode)[lane] = (uint16_t)kc;
+    reinterpret_cast<uint16_t*>(dst + F::kVCode)[lane] = (uint16_t)vc;
+  } else {
+    reinterpret_cast<uint32_t*>(dst + F::kKCode)[lane] = kc;
+    reinterpret_cast<uint32_t*>(dst + F::kVCode)[lane] = vc;
+  }
+  if (lane % LPB == 0) {
+    dst[F::kKScale + lane / LPB] = (uint8_t)(ke + 127);
+    dst[F::kVScale + lane / LPB] = (uint8_t)(ve + 127);
   }
 }
 
@@ -71,9 +100,17 @@ __global__ void hadamard_kernel(int D, float* __restrict__ H, float v) {
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t pairs = a.N * a.Hk;
   const int64_t blocks = (pairs + 3) / 4;
-  hipLaunchKernelGGL(store_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.key,
-                     a.value, a.cache, a.slot_mapping, pairs, a.Hk,
-                     a.num_blocks * (int64_t)a.block_size, a.ksn, a.ksh, a.vsn, a.vsh);
+#define UQ_STORE(DV)                                                                         \
+  hipLaunchKernelGGL(store_kernel<DV>, dim3((unsigned)blocks), dim3(256), 0, stream, a.key, a.value, \
+                     a.cache, a.slot_mapping, pairs, a.Hk, a.num_blocks * (int64_t)a.block_size,   \
+                     a.ksn, a.ksh, a.vsn, a.vsh)
+  switch (a.D) {
+    case 128: UQ_STORE(128); break;
+    case 256: UQ_STORE(256); break;
+    case 512: UQ_STORE(512); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef UQ_STORE
   return hipGetLastError();
 }
 

@@ -61,7 +61,8 @@ def store_args(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(D=128), -2), (dict(slot_size=256), -2), (dict(block_size=8), -2),
+    (dict(D=64), -2), (dict(D=384), -2), (dict(slot_size=256), -2), (dict(D=128), -2),
+    (dict(D=512, slot_size=272), -2), (dict(block_size=8), -2),
     (dict(block_size=48), -2), (dict(block_size=512), -2), (dict(N=-1), -1), (dict(Hk=0), -1),
     (dict(num_blocks=0), -1), (dict(key=None), -1), (dict(slot_mapping=None), -1),
     (dict(ksh=255), -1), (dict(vsn=-4), -1), (dict(key=FAKE + 2), -1),
@@ -85,7 +86,7 @@ def decode_args(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(D=128), -2), (dict(Hq=36), -2), (dict(Hq=16), -2), (dict(Hq=12, Hk=4), -2),
+    (dict(D=64), -2), (dict(D=1024), -2), (dict(Hq=36), -2), (dict(Hq=16), -2), (dict(Hq=12, Hk=4), -2),
     (dict(Hq=128, Hk=4), -2), (dict(block_size=8), -2), (dict(splits=0), -2),
     (dict(splits=513), -2), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
     (dict(scale=float("inf")), -1), (dict(B=0), -1), (dict(query=None), -1),
@@ -106,7 +107,8 @@ def test_workspace_bytes(libuq):
     f = libuq.uq_decode_workspace_bytes
     assert f(0, 32, 4, 256, 32, 256, 16) == 0
     assert f(32, 30, 4, 256, 32, 256, 16) == 0
-    assert f(32, 32, 4, 128, 32, 256, 16) == 0
+    assert f(32, 32, 4, 64, 32, 256, 16) == 0
+    assert f(32, 32, 4, 384, 32, 256, 16) == 0
     assert f(32, 32, 4, 256, 0, 256, 16) == 0
     assert f(32, 32, 4, 256, 32, 0, 16) == 0
     assert f(32, 32, 4, 256, 32, 256, 24) == 0
@@ -227,3 +229,15 @@ def test_continuation_prefill_workspace_bytes(libuq):
 def test_continuation_prefill_stages_rejects_mask(libuq, mask):
     assert libuq.uq_continuation_prefill_stages(mask, *continuation_args()) == -1
     assert "stage_mask" in _err(libuq)
+
+
+@pytest.mark.parametrize("d", [128, 512])
+def test_other_head_dims_accepted(libuq, d):
+    """D = 128 and 512 pass every host check of store and decode; the
+    workspace scales with D (query codes D bytes, partial rows D floats)."""
+    # store with the matching slot size: all checks pass, then N = 0 returns before any HIP call
+    assert libuq.uq_store(*store_args(D=d, slot_size=d * 17 // 16, N=0)) == 0
+    f = libuq.uq_decode_workspace_bytes
+    n = f(2, 16, 2, d, 1, 1, 16)
+    assert n == 2 * 16 * d + 2 * 16 * d * 4 + 2 * 256
+    assert f(2, 16, 2, d, 1, 1, 16) < f(2, 16, 2, 2 * d, 1, 1, 16) if d < 512 else True

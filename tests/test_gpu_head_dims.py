@@ -1,0 +1,163 @@
+"""Head dims 128 and 512 (the pages' other head sizes): the slot format
+scales with D (17 D / 16 bytes), the store is bit-exact against the oracle
+and decode is within max-abs 1e-2 / rel-L2 5e-3. Through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from harness import check_close, to_np
+import decode_attention_bit_amd as uq
+from decode_attention_bit_amd import inputs
+from oracle import uq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+DIMS = [128, 512]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def bf16(x):
+    return inputs.to_bf16(np.asarray(x, dtype=np.float32))
+
+
+def bits(t):
+    return inputs.bf16_bits(t.cpu())
+
+
+def slot(d):
+    return O.slot_layout(d)[0]
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_store_bit_exact(d):
+    say(f"store d={d}")
+    rng = np.random.default_rng(d)
+    n, hk, bs = 70, 3, 16
+    k = rng.standard_normal((n, hk, d))
+    v = rng.standard_t(3, (n, hk, d))
+    k[0] = 0.0
+    v[1] = -0.0
+    k[2, :, :] = 0
+    k[2, 0, :2] = [1.0, 1.0]                               # rotated: exact zeros on odd indices
+    v[3] = np.ldexp(rng.uniform(0.5, 1, (hk, d)), -130)    # bf16 subnormals, scale clamps
+    k[4] = rng.standard_normal((hk, d)) * 1e30
+    for i in range(5, 15):                                  # magnitudes over 24 binades
+        k[i] = np.ldexp(rng.uniform(0.5, 1, (hk, d)) * rng.choice([-1, 1], (hk, d)),
+                        rng.integers(-12, 12, (hk, d)))
+    for i in range(15, 25):                                 # values on E2M1 midpoints
+        v[i] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -5.0], (hk, d))
+    kb, vb = bf16(k), bf16(v)
+    nb = 8
+    slots = rng.permutation(nb * bs)[:n]
+    cache = torch.full((nb, bs, hk, slot(d)), 0xA5, dtype=torch.uint8, device=DEV)
+    uq.store(kb.to(DEV), vb.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+    ref = np.full(tuple(cache.shape), 0xA5, dtype=np.uint8)
+    O.store(bits(kb), bits(vb), ref, slots)
+    bad = np.argwhere(cache.cpu().numpy() != ref)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_query_prologue_codes_bit_exact(d):
+    say(f"prologue d={d}")
+    rng = np.random.default_rng(d + 1)
+    B, hk, qg = 2, 2, 8
+    q = rng.standard_normal((B, hk * qg, d))
+    q[0, 0] = 0.0
+    q[0, 1] = rng.standard_normal(d) * 2.0 ** -20
+    q[0, 2] = rng.standard_normal(d) * 300.0
+    q[1, 0] = rng.choice([-1.0, 1.0], d) * (1 + rng.random(d)) * np.exp2(rng.integers(-12, 13, d))
+    qb = bf16(q)
+    cache = torch.zeros((1, 16, hk, slot(d)), dtype=torch.uint8, device=DEV)
+    ws = torch.full((uq.decode_workspace_bytes(B, hk * qg, hk, 1, 1, 16, d),), 0x55, dtype=torch.uint8, device=DEV)
+    uq.decode(qb.to(DEV), cache, torch.zeros((B, 1), dtype=torch.int32, device=DEV),
+              torch.ones(B, dtype=torch.int32, device=DEV), 1 / 16, 1, workspace=ws, stages=uq.STAGE_PROLOGUE)
+    got = ws[:B * hk * qg * d].cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy().reshape(B, hk * qg, d)
+    ref = O.query_haircut(bits(qb))
+    assert np.array_equal(got, ref), f"{(got != ref).sum()} codes differ"
+
+
+def _decode_case(d, seq_lens, hk, qg, bs=16, splits=3, seed=0, scale=None):
+    rng = np.random.default_rng(seed)
+    B = len(seq_lens)
+    nblk = [(L + bs - 1) // bs for L in seq_lens]
+    width = max(max(nblk), 1)
+    nb = sum(nblk) + 3
+    perm = rng.permutation(nb)
+    table = np.zeros((B, width), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    q = bf16(rng.standard_normal((B, hk * qg, d)))
+    cache = torch.zeros((nb, bs, hk, slot(d)), dtype=torch.uint8, device=DEV)
+    ref_cache = np.zeros(tuple(cache.shape), dtype=np.uint8)
+    for b, L in enumerate(seq_lens):
+        if L == 0:
+            continue
+        k = bf16(rng.standard_normal((L, hk, d)))
+        v = bf16(rng.standard_normal((L, hk, d)))
+        t = np.arange(L)
+        slots = table[b, t // bs].astype(np.int64) * bs + t % bs
+        uq.store(k.to(DEV), v.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+        O.store(bits(k), bits(v), ref_cache, slots)
+    scale = scale if scale is not None else 1 / np.sqrt(d)
+    out = uq.decode(q.to(DEV), cache, torch.from_numpy(table).to(DEV),
+                    torch.tensor(seq_lens, dtype=torch.int32, device=DEV), scale, splits)
+    ref = O.decode(bits(q), ref_cache, table, np.array(seq_lens), scale)
+    return out, ref
+
+
+@pytest.mark.parametrize("d", DIMS)
+@pytest.mark.parametrize("qg", [6, 8, 16])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_decode_ragged(d, qg, bs):
+    say(f"decode d={d} qg={qg} bs={bs}")
+    lens = [1, 15, 16, 17, 100, 257, 300, 0, 33]
+    out, ref = _decode_case(d, lens, hk=2, qg=qg, bs=bs, seed=d + qg + bs)
+    check_close(to_np(out), ref, f"d={d} qg={qg} bs={bs}")
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_decode_long_split_invariance(d):
+    """One long sequence per KV head group at several split counts, against
+    the single-softmax oracle."""
+    say(f"decode long d={d}")
+    lens = [3000, 1234]
+    for splits in (1, 8, 32):
+        out, ref = _decode_case(d, lens, hk=4, qg=8, splits=splits, seed=d + 7)
+        check_close(to_np(out), ref, f"d={d} splits={splits}")
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_decode_ex_window_and_sinks(d):
+    say(f"decode_ex d={d}")
+    rng = np.random.default_rng(d + 9)
+    B, hk, qg, bs = 3, 2, 8, 16
+    lens = [200, 31, 90]
+    nb = sum((L + bs - 1) // bs for L in lens) + 2
+    table = np.zeros((B, 13), dtype=np.int32)
+    perm = rng.permutation(nb)
+    off = 0
+    cache = torch.zeros((nb, bs, hk, slot(d)), dtype=torch.uint8, device=DEV)
+    ref_cache = np.zeros(tuple(cache.shape), dtype=np.uint8)
+    for b, L in enumerate(lens):
+        n = (L + bs - 1) // bs
+        table[b, :n] = perm[off:off + n]
+        off += n
+        k, v = bf16(rng.standard_normal((L, hk, d))), bf16(rng.standard_normal((L, hk, d)))
+        t = np.arange(L)
+        slots = table[b, t // bs].astype(np.int64) * bs + t % bs
+        uq.store(k.to(DEV), v.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+        O.store(bits(k), bits(v), ref_cache, slots)
+    q = bf16(rng.standard_normal((B, hk * qg, d)))
+    sinks = rng.normal(0, 2, hk * qg).astype(np.float32)
+    out = uq.decode_ex(q.to(DEV), cache, torch.from_numpy(table).to(DEV),
+                       torch.tensor(lens, dtype=torch.int32, device=DEV), 0.1, 4,
+                       sinks=torch.from_numpy(sinks).to(DEV), sliding_window=50)
+    ref = O.decode(bits(q), ref_cache, table, np.array(lens), 0.1, sinks=sinks, sliding_window=50)
+    check_close(to_np(out), ref, f"decode_ex d={d}")
