@@ -6,8 +6,10 @@ block_size 16 with a shuffled block table, 32 KV splits, bf16 q/k/v ~ N(0,1)
 (seeded, synthetic). One step = one full uq_decode (query prologue, split-KV
 stage 1, stage-2 merge) over the resident cache.
 
-Metric: cache bytes streamed per step (sum_b L_b * Hk * 272) / step time, in
-GB/s, with the fraction of the 8 TB/s HBM peak and tokens/s (B per step).
+Metric: cache bytes streamed per step (sum_b L_b * Hk * 17 D / 16; 272 bytes
+per token and KV head at D = 256) / step time, in GB/s, with the fraction of
+the 8 TB/s HBM peak and tokens/s (B per step). --head-dim 128 / 512 runs the
+same workload at another head dim.
 The 142.6 MB cache would fit the 256 MB Infinity Cache, so steps rotate over
 enough stored copies of the cache that each step reads one untouched for the
 last >= 768 MB of traffic.
@@ -29,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-METRIC = "decode KV-bytes GB/s (% of HBM peak) + decode tokens/s, B=32 GQA-8 D=256 4K ctx"
+METRIC = "decode KV-bytes GB/s (% of HBM peak) + decode tokens/s, B=32 GQA-8 D={D} 4K ctx"
 
 
 def parse():
@@ -49,6 +51,8 @@ def parse():
                          "cache bytes inside the window")
     ap.add_argument("--sinks", action="store_true",
                     help="add seeded per-head sink logits (uq_decode_ex)")
+    ap.add_argument("--head-dim", type=int, default=256, choices=(128, 256, 512),
+                    help="head dim of the decode workloads (slot 17*D/16 bytes, scale 1/sqrt(D))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -71,7 +75,7 @@ def setup(w, dev):
 
     lay = inputs.make_layout(w)
     q = inputs.make_query(w).to(dev)
-    cache = torch.zeros((lay.num_blocks, w.block_size, w.Hk, inputs.SLOT_BYTES), dtype=torch.uint8, device=dev)
+    cache = torch.zeros((lay.num_blocks, w.block_size, w.Hk, w.slot_bytes), dtype=torch.uint8, device=dev)
     for b in range(w.B):
         k, v = inputs.make_kv(w, lay, b)
         slots = inputs.slots_for(lay, b, 0, int(lay.seq_lens[b]))
@@ -141,7 +145,7 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
         bt_rep = bt[rows.long()].contiguous()  # the same rows repeated, for the per-kernel pass
     nq = q.shape[0]
     out = torch.empty((nq, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(uq.decode_workspace_bytes(nq, w.Hq, w.Hk, w.num_kv_splits, bt.shape[1], w.block_size),
+    ws = torch.empty(uq.decode_workspace_bytes(nq, w.Hq, w.Hk, w.num_kv_splits, bt.shape[1], w.block_size, w.D),
                      dtype=torch.uint8, device=dev)
     R = len(caches)
     args = lambda i: (q, caches[i % R], bt if multi is None else bt_rep, sl, w.scale, w.num_kv_splits)
@@ -215,9 +219,11 @@ def recorded_traffic(workload):
     return int(m.group(3)) + int(m.group(4))
 
 
-def cpu_baseline(w, lay, seconds):
+def cpu_baseline(w, lay, seconds, wall_cap=150.0):
     """The oracle, untuned, on a bounded sample: whole (sequence, KV head)
-    decodes of this workload, one BLAS thread."""
+    decodes of this workload, one BLAS thread. Sequences are drawn at random;
+    each is encoded once (untimed) and decoded for all its KV heads, until
+    the timed decodes reach `seconds` or the whole loop reaches `wall_cap`."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -225,20 +231,24 @@ def cpu_baseline(w, lay, seconds):
     from oracle import uq_oracle as O
 
     q_bits = inputs.bf16_bits(inputs.make_query(w))
-    rng = np.random.default_rng(0)
-    with threadpool_limits(limits=1):
-        pairs, done_bytes, elapsed = [], 0, 0.0
-        while elapsed < seconds and len(pairs) < w.B * w.Hk:
-            b, h = int(rng.integers(w.B)), int(rng.integers(w.Hk))
-            L = int(lay.seq_lens[b])
-            cache = np.zeros((lay.num_blocks, w.block_size, w.Hk, 272), dtype=np.uint8)
-            k, v = inputs.make_kv(w, lay, b)
-            O.store(inputs.bf16_bits(k), inputs.bf16_bits(v), cache, inputs.slots_for(lay, b, 0, L))
+    order = np.random.default_rng(0).permutation(w.B)
+    start = time.perf_counter()
+    pairs, done_bytes, elapsed = [], 0, 0.0
+    for b in order.tolist():
+        if elapsed >= seconds or time.perf_counter() - start >= wall_cap:
+            break
+        L = int(lay.seq_lens[b])
+        cache = np.zeros((lay.num_blocks, w.block_size, w.Hk, w.slot_bytes), dtype=np.uint8)
+        k, v = inputs.make_kv(w, lay, b)
+        O.store(inputs.bf16_bits(k), inputs.bf16_bits(v), cache, inputs.slots_for(lay, b, 0, L))
+        todo = [(b, h) for h in range(w.Hk)]
+        with threadpool_limits(limits=1):
             t = time.perf_counter()
-            O.decode(q_bits, cache, lay.block_table, lay.seq_lens, w.scale, pairs=[(b, h)])
+            O.decode(q_bits, cache, lay.block_table, lay.seq_lens, w.scale, pairs=todo)
             elapsed += time.perf_counter() - t
-            done_bytes += L * 272
-            pairs.append((b, h))
+        done_bytes += L * w.Hk * w.slot_bytes
+        pairs += todo
+        log(f"cpu baseline: sequence {b} decoded, {elapsed:.1f} s timed")
     return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(pairs)} whole (sequence, KV head) decodes of this workload "
                       f"({done_bytes / 1e6:.1f} MB of cache), {elapsed:.1f} s, cache encoding untimed"}
@@ -378,6 +388,9 @@ def main():
     from decode_attention_bit_amd import inputs
 
     w = inputs.WORKLOADS[args.workload]
+    if args.head_dim != w.D:
+        import dataclasses
+        w = dataclasses.replace(w, D=args.head_dim, scale=1.0 / math.sqrt(args.head_dim))
     dev = torch.device("cuda:0")
     log(f"setup {w.name}")
     lay, q, caches, bt, sl = setup(w, dev)
@@ -396,14 +409,14 @@ def main():
     multi = multi_query(w, lay, args.queries_per_seq, dev) if args.queries_per_seq > 1 else None
     # every query row of uq_decode_ex reads its own prefix: the logical
     # bytes count each read, the value counts each cache byte once
-    logical_bytes = (int(multi[2].long().sum()) * w.Hk * inputs.SLOT_BYTES) if multi is not None else kv_bytes
+    logical_bytes = (int(multi[2].long().sum()) * w.Hk * w.slot_bytes) if multi is not None else kv_bytes
     sinks = None
     if args.sinks:
         import numpy as np
         sinks = torch.from_numpy(np.random.default_rng([w.seed, 5]).normal(0, 2, w.Hq).astype(np.float32)).to(dev)
     if args.sliding_window > 0:             # only the window's tokens are read
         import numpy as np
-        kv_bytes = int(np.minimum(lay.seq_lens.astype(np.int64), args.sliding_window).sum()) * w.Hk * inputs.SLOT_BYTES
+        kv_bytes = int(np.minimum(lay.seq_lens.astype(np.int64), args.sliding_window).sum()) * w.Hk * w.slot_bytes
         logical_bytes = kv_bytes
     step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup,
                                                store_args, multi, sinks, args.sliding_window)
@@ -411,7 +424,7 @@ def main():
     plain = st1_ms is not None               # no option: stage 1 timed on its own
     st1_gbs = kv_bytes / ((st1_ms if plain else step_ms) * 1e-3) / 1e9
     res = {
-        "metric": METRIC,
+        "metric": METRIC.format(D=w.D),
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -442,7 +455,7 @@ def main():
         "cache_copies": len(caches),
         "roofline": {"bound": "hbm", "achieved": round(st1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(st1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(w.name) if plain and store_args is None else None,
+                     "traffic": recorded_traffic(w.name) if plain and store_args is None and w.D == 256 else None,
                      "kernel": "stage1_kernel (split-KV)" if plain else "the whole step (options on)",
                      "bytes_per_launch": kv_bytes},
     }

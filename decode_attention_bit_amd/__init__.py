@@ -8,12 +8,14 @@ and raises if the library has not been built (there is no fallback path).
 Entry points mirror include/uq.h:
   build_hadamard(D, device)                         -> (D, D) float32
   store(key, value, kv_cache, slot_mapping)         -> None (kv_cache updated)
-  decode_workspace_bytes(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size)  -> int
+  decode_workspace_bytes(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D)  -> int
   decode(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
-         out=None, workspace=None)                  -> (B, Hq, 256) bf16
+         out=None, workspace=None)                  -> (B, Hq, D) bf16
   decode_ex(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
             query_row=None, sinks=None, sliding_window=0,
-            out=None, workspace=None)               -> (B, Hq, 256) bf16
+            out=None, workspace=None)               -> (B, Hq, D) bf16
+Store and decode take head dims D in {128, 256, 512} (slot 17*D/16 bytes);
+the continuation-prefill calls take D = 256.
   rotate(x, out=None)                               -> bf16(x H), same shape
   dequant_kv(kv_cache, block_row, n_tokens)         -> (K, V) (n_tokens, Hk, 256) bf16
   prefill_attention(q, k, v, scale, out=None)       -> (q_len, Hq, 256) bf16
@@ -30,10 +32,17 @@ import torch
 __all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_workspace_bytes", "rotate",
            "dequant_kv", "prefill_attention", "continuation_prefill",
            "continuation_prefill_workspace_bytes", "library_path",
-           "UQError", "HEAD_DIM", "SLOT_BYTES"]
+           "UQError", "HEAD_DIM", "HEAD_DIMS", "SLOT_BYTES", "slot_bytes"]
 
 HEAD_DIM = 256
 SLOT_BYTES = 272
+HEAD_DIMS = (128, 256, 512)
+
+
+def slot_bytes(D: int = HEAD_DIM) -> int:
+    """Cache bytes per (token, KV head) for head dim D."""
+    return D * 17 // 16
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libuq.so"
 _lib = None
@@ -123,8 +132,9 @@ def build_hadamard(D: int = HEAD_DIM, device="cuda") -> torch.Tensor:
 
 def store(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
           slot_mapping: torch.Tensor) -> None:
-    """Quantise (N, Hk, 256) bf16 key/value into kv_cache (num_blocks,
-    block_size, Hk, 272) uint8 at flat slots slot_mapping (int64, (N,))."""
+    """Quantise (N, Hk, D) bf16 key/value, D in {128, 256, 512}, into
+    kv_cache (num_blocks, block_size, Hk, 17*D/16) uint8 at flat slots
+    slot_mapping (int64, (N,))."""
     if key.dtype != torch.bfloat16 or value.dtype != torch.bfloat16:
         raise TypeError("key and value must be bfloat16")
     if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
@@ -171,7 +181,7 @@ def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
            seq_lens: torch.Tensor, scale: float, num_kv_splits: int,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
            stages: int = 7) -> torch.Tensor:
-    """Split-KV decode over the 4-bit cache; returns (B, Hq, 256) bf16.
+    """Split-KV decode over the 4-bit cache; returns (B, Hq, D) bf16.
 
     ``stages`` selects a subset of the three kernels (uq_decode_stages); the
     default runs all of them (uq_decode)."""
@@ -211,7 +221,7 @@ def decode_ex(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """uq_decode_ex: decode with optional per-query table rows (query row b
     reads block-table row query_row[b]), per-head sink logits and a sliding
-    window of the last `sliding_window` tokens; returns (B, Hq, 256) bf16."""
+    window of the last `sliding_window` tokens; returns (B, Hq, D) bf16."""
     if query.dtype != torch.bfloat16 or query.dim() != 3 or query.stride(2) != 1:
         raise TypeError("query must be (B, Hq, D) bfloat16 with a contiguous last dim")
     if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:

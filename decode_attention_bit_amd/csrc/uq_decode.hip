@@ -627,6 +627,10 @@ constexpr int ring_slots(int hpw) {
              : UQ_RING_SLOTS;
 }
 constexpr long kTilesPerWaveMin = 4;
+// At D = 128 a tile carries half the bytes for much the same serial work per
+// wave (scores, softmax, the value MFMAs), so twice the waves stream it
+// faster; at D = 256 and 512 more waves only add partials (measured).
+static int target_waves(int D) { return D == 128 ? 2 * UQ_TARGET_WAVES : UQ_TARGET_WAVES; }
 
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
                        int block_size, int D) {
@@ -645,10 +649,10 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_
   p.cs = (int)((max_tiles + num_kv_splits - 1) / num_kv_splits);
   // Partition policy: a wave has a fixed cost (its query, its partial write,
   // the ring fill), so it should stream as many tiles as the machine can
-  // afford while the grid still offers about UQ_TARGET_WAVES waves when every
+  // afford while the grid still offers about target_waves(D) waves when every
   // sequence is full. A partial is then a union of spw consecutive splits, or
   // one of nsub pieces of a split that is too long for one wave.
-  long budget = (long)B * Hk * max_tiles / UQ_TARGET_WAVES;
+  long budget = (long)B * Hk * max_tiles / target_waves(D);
   budget = budget < kTilesPerWaveMin ? kTilesPerWaveMin
                                      : (budget > UQ_TILES_PER_WAVE_MAX ? UQ_TILES_PER_WAVE_MAX : budget);
   int spw = 1, nsub = 1;

@@ -66,6 +66,11 @@ class Workload:
     def QG(self) -> int:
         return self.Hq // self.Hk
 
+    @property
+    def slot_bytes(self) -> int:
+        """Cache bytes per (token, KV head): 17 * D / 16."""
+        return self.D * 17 // 16
+
 
 WORKLOADS = {
     "tiny": Workload("tiny", 0, B=2, Hq=8, Hk=1, num_kv_splits=4,
@@ -217,8 +222,8 @@ def slots_for(layout: Layout, b: int, t0: int, t1: int, block_size: int = BLOCK_
 
 
 def kv_bytes(w: Workload, layout: Layout) -> int:
-    """Cache bytes one decode step streams: sum_b L_b * Hk * 272."""
-    return int(layout.seq_lens.astype(np.int64).sum()) * w.Hk * SLOT_BYTES
+    """Cache bytes one decode step streams: sum_b L_b * Hk * 17 D / 16."""
+    return int(layout.seq_lens.astype(np.int64).sum()) * w.Hk * w.slot_bytes
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -22,19 +22,27 @@
  *     run on the host before any HIP call, so a rejected call enqueues
  *     nothing; uq_last_error() returns a message for the calling thread.
  *
- * Cache slot (one token, one KV head), 272 bytes:
- *   [0,128)   K codes: byte i holds element 2i in bits 0-3, 2i+1 in bits 4-7;
- *             K is in the rotated basis
- *   [128,256) V codes, same packing, not rotated
- *   [256,264) K scale bytes, one per 32 consecutive elements (UE8M0: 2**(b-127))
- *   [264,272) V scale bytes
+ * Cache slot (one token, one KV head) of head dim D, 17*D/16 bytes (272 for
+ * D = 256, 136 for 128, 544 for 512):
+ *   [0, D/2)          K codes: byte i holds element 2i in bits 0-3, 2i+1 in
+ *                     bits 4-7; K is in the rotated basis
+ *   [D/2, D)          V codes, same packing, not rotated
+ *   [D, D + D/32)     K scale bytes, one per 32 consecutive elements
+ *                     (UE8M0: 2**(b-127))
+ *   [D + D/32, 17D/16) V scale bytes
  *   A 4-bit code is sign (bit 3) plus E2M1 magnitude {0,.5,1,1.5,2,3,4,6}.
  *   The scale byte of a block with maximum magnitude a is
  *   clamp(floor(log2 a) - 2, -127, 127) + 127 (0 for an all-zero block), the
  *   OCP MX shared-exponent rule; codes are rounded to nearest, ties to even,
  *   saturating at 6.
- * The cache is (num_blocks, block_size, Hk, 272) bytes, contiguous: slot s of
- * KV head h starts at byte (s * Hk + h) * 272.
+ * The cache is (num_blocks, block_size, Hk, 17*D/16) bytes, contiguous: slot s
+ * of KV head h starts at byte (s * Hk + h) * 17*D/16.
+ * The rotation of head dim D is the Sylvester Hadamard matrix with entries
+ * (-1)**popcount(i & j) times one float64 scale, the nearest double to
+ * 1/sqrt(D) (exactly 1/16 for D = 256).
+ * Store and decode take D in {128, 256, 512}; the continuation-prefill entry
+ * points (uq_rotate, uq_dequant_kv, uq_prefill_attention,
+ * uq_continuation_prefill) take D = 256.
  */
 #ifndef UQ_H
 #define UQ_H
@@ -52,8 +60,9 @@ extern "C" {
 #define UQ_EWORKSPACE   -3   /* workspace smaller than uq_decode_workspace_bytes() */
 #define UQ_EHIP         -4   /* a HIP launch failed                          */
 
-#define UQ_HEAD_DIM   256
-#define UQ_SLOT_BYTES 272
+#define UQ_HEAD_DIM   256                       /* the default head dim */
+#define UQ_SLOT_BYTES 272                       /* its slot: 17 * 256 / 16 */
+#define UQ_SLOT_BYTES_FOR(D) ((D) * 17 / 16)
 #define UQ_MAX_SPLITS 512
 
 /*
@@ -75,15 +84,15 @@ int uq_build_hadamard(int D, float* H, void* stream);
  * (num_blocks, block_size, Hk, slot_size); slot_mapping).
  *   key, value:   (device) bf16, element (n, h, d) at n*stride_n + h*stride_h + d
  *                 (strides in elements; d is contiguous).
- *   kv_cache:     (device) uint8, (num_blocks, block_size, Hk, 272), in/out;
- *                 only the written slots change.
+ *   kv_cache:     (device) uint8, (num_blocks, block_size, Hk, 17*D/16),
+ *                 in/out; only the written slots change.
  *   slot_mapping: (device) int64, (N,). A slot outside
  *                 [0, num_blocks * block_size) - for instance -1 for padding -
  *                 is skipped.
- *   D must be 256, slot_size 272, block_size a power of two in [16, 256].
- *   N == 0 is a no-op.
+ *   D in {128, 256, 512}, slot_size 17*D/16, block_size a power of two in
+ *   [16, 256]. N == 0 is a no-op.
  * Exactness: the rotation is exact when the non-zero magnitudes of a key
- * vector span at most 36 binades (always true for bf16 data of ordinary
+ * vector span at most 44 - log2(D) binades (36 for D = 256) (always true for bf16 data of ordinary
  * range); the cache bytes are then a function of the inputs alone.
  * Errors: UQ_EINVAL, UQ_EUNSUPPORTED, UQ_EHIP.
  */
@@ -117,7 +126,7 @@ size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits
  * (query prologue, split-KV stage 1, log-sum-exp merge) on `stream`; no host
  * synchronisation and no allocation, so it can be captured in a HIP graph.
  *   query:       (device) bf16, element (b, hq, d) at b*q_stride_b + hq*q_stride_h + d.
- *   kv_cache:    (device) uint8 (num_blocks, block_size, Hk, 272), read only.
+ *   kv_cache:    (device) uint8 (num_blocks, block_size, Hk, 17*D/16), read only.
  *   block_table: (device) int32 (B, max_blocks_per_seq): logical block j of
  *                sequence b lives in physical block block_table[b][j].
  *   seq_lens:    (device) int32 (B,): tokens of each sequence, the current one
@@ -136,8 +145,8 @@ size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits
  *   workspace:   (device) at least uq_decode_workspace_bytes(B, Hq, Hk, D,
  *                num_kv_splits, max_blocks_per_seq, block_size) bytes, 256-byte aligned; contents need no
  *                initialisation and are overwritten.
- *   D must be 256; Hq % Hk == 0 with Hq / Hk in {6, 8, 16}; block_size a
- *   power of two in [16, 256].
+ *   D in {128, 256, 512}; Hq % Hk == 0 with Hq / Hk in {6, 8, 16}; block_size
+ *   a power of two in [16, 256].
  * Errors: UQ_EINVAL, UQ_EUNSUPPORTED, UQ_EWORKSPACE, UQ_EHIP.
  */
 int uq_decode(const uint16_t* query, const uint8_t* kv_cache,
@@ -189,7 +198,7 @@ int uq_decode_ex(const uint16_t* query, const uint8_t* kv_cache,
 /*
  * Same as uq_decode, restricted to the stages named in stage_mask:
  * UQ_STAGE_PROLOGUE (query rotation + E4M3 into the workspace: its first
- * B*Hq*256 bytes then hold the E4M3 codes of q H, row b*Hq + hq),
+ * B*Hq*D bytes then hold the E4M3 codes of q H, row b*Hq + hq),
  * UQ_STAGE_SPLIT (stage 1, reads the prologue's output) and UQ_STAGE_MERGE
  * (stage 2, reads stage 1's output). Running the three masks in that order on
  * one stream, with the same arguments and workspace, is exactly uq_decode;

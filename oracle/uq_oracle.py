@@ -384,7 +384,7 @@ def attention(q8: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, sinks=
 
 def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None, sinks=None,
            sliding_window=0) -> np.ndarray:
-    """Reference output (B, Hq, 256) float64, single softmax per query head.
+    """Reference output (B, Hq, d) float64, single softmax per query head.
 
     ``pairs`` optionally restricts the work to a list of (b, kv_head); other
     rows are left NaN. ``sinks`` (Hq,) are per-query-head sink logits (see

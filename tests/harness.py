@@ -26,7 +26,7 @@ class Instance:
         self.layout = inputs.make_layout(w, seq_lens=seq_lens)
         self.query = inputs.make_query(w)
         lay = self.layout
-        self.cache = torch.zeros((lay.num_blocks, w.block_size, w.Hk, inputs.SLOT_BYTES),
+        self.cache = torch.zeros((lay.num_blocks, w.block_size, w.Hk, self.w.slot_bytes),
                                  dtype=torch.uint8, device=self.dev)
         self.block_table = torch.from_numpy(lay.block_table).to(self.dev)
         self.seq_lens = torch.from_numpy(lay.seq_lens).to(self.dev)
@@ -65,11 +65,11 @@ class Instance:
         out = []
         for i in range(0, len(tokens), 4096):
             out.append(O.encode_slots(kb[i:i + 4096], vb[i:i + 4096]))
-        return np.concatenate(out) if out else np.zeros((0, self.w.Hk, 272), np.uint8)
+        return np.concatenate(out) if out else np.zeros((0, self.w.Hk, self.w.slot_bytes), np.uint8)
 
     def gpu_slots(self, b: int, tokens: np.ndarray) -> np.ndarray:
         slots = inputs.slots_for(self.layout, b, 0, int(self.layout.seq_lens[b]))[tokens]
-        flat = self.cache.view(-1, self.w.Hk, inputs.SLOT_BYTES)
+        flat = self.cache.view(-1, self.w.Hk, self.w.slot_bytes)
         return flat[torch.from_numpy(slots).to(self.dev)].cpu().numpy()
 
     def oracle_output(self, b: int, h: int) -> np.ndarray:
