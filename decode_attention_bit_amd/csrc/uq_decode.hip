@@ -337,11 +337,18 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   UQ_RING_DECL(4) UQ_RING_DECL(5) UQ_RING_DECL(6) UQ_RING_DECL(7)
 #undef UQ_RING_DECL
 
-  int x = blockIdx.x;
-  const int hg = x % hgroups;
-  x /= hgroups;
-  const int part = x % P;             // partial index within (b, head)
-  const int b = x / P;
+  // Workgroups are dealt to the 8 XCDs round-robin by index. The grid is
+  // ordered partial-major (every (sequence, head group) of partial 0 first),
+  // and within each band of n1 = B * hgroups workgroups the items rotate by
+  // the partial index, so the partials of one sequence land on different
+  // XCDs: the late, often empty, partials of short sequences are then spread
+  // over the chip instead of all sitting on the same XCD.
+  const int n1 = (int)(gridDim.x / (unsigned)P);
+  const int part = (int)blockIdx.x / n1;           // partial index within (b, head)
+  int j = (int)blockIdx.x - part * n1 + part % n1;
+  j = j >= n1 ? j - n1 : j;
+  const int hg = j % hgroups;
+  const int b = j / hgroups;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = hg * HPW + wave;
@@ -503,6 +510,51 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 
   const float l1 = l_part + __shfl_xor(l_part, 16);
   const float l_tot = l1 + __shfl_xor(l1, 32);
+  // O / l leaves as one contiguous row per query head: the lanes first place
+  // their dims in the wave's own ring, free now that every tile it issued has
+  // been consumed (row stride D*4 + 16 bytes, RPS rows per slot), then each
+  // row is read back across the wave and stored whole, instead of 64
+  // scattered 16-byte pieces per store.
+  constexpr int RS = D * 4 + 16;
+  constexpr int RPS = S::kTileU4 * 16 / RS;
+  if constexpr ((QG + RPS - 1) / RPS <= NSLOT) {
+#define UQ_OWN_PTR(K) (NSLOT > K ? &ring##K[NSLOT > K ? wave : 0][0] : &ring0[0][0])
+    uint4* const own[8] = {UQ_OWN_PTR(0), UQ_OWN_PTR(1), UQ_OWN_PTR(2), UQ_OWN_PTR(3),
+                           UQ_OWN_PTR(4), UQ_OWN_PTR(5), UQ_OWN_PTR(6), UQ_OWN_PTR(7)};
+#undef UQ_OWN_PTR
+    if (qlane && grp == 0) {
+      part_m[stat] = m_ref;
+      part_l[stat] = l_tot;
+    }
+    if (__builtin_amdgcn_readfirstlane(__float_as_int(l_tot)) == 0) return;   // empty range: l = +0
+    const float inv = 1.f / l_tot;
+    if (qlane) {
+      float* rowp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(own[n16 / RPS]) + (n16 % RPS) * RS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < NA; j += 4)
+          *reinterpret_cast<float4*>(rowp + NA * (4 * grp + i) + j) =
+              make_float4(acc[j][i] * inv, acc[j + 1][i] * inv, acc[j + 2][i] * inv, acc[j + 3][i] * inv);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const size_t row0 = ((size_t)b * Hq + (size_t)h * QG) * P + part;   // first query head of the group
+#pragma unroll
+    for (int r = 0; r < QG; ++r) {
+      const float* rowp = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(own[r / RPS]) + (r % RPS) * RS);
+      float* dst = part_o + (row0 + (size_t)r * P) * D;
+      if constexpr (D == 128) {
+        if (lane < 32) *reinterpret_cast<float4*>(dst + 4 * lane) = *reinterpret_cast<const float4*>(rowp + 4 * lane);
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 256; ++c)
+          *reinterpret_cast<float4*>(dst + 256 * c + 4 * lane) =
+              *reinterpret_cast<const float4*>(rowp + 256 * c + 4 * lane);
+      }
+    }
+    return;
+  }
   if (!qlane) return;
   if (grp == 0) {
     part_m[stat] = m_ref;
