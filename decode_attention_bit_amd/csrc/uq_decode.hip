@@ -23,6 +23,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
 }
 
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+// two floats to fp16, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2h));
+}
+
 // ---------------------------------------------------------------------------
 // Query prologue: q8 = E4M3(q H), one wave per (sequence, query head), for
 // head dims 128, 256 and 512.
@@ -323,8 +331,8 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ query_row, int n_rows,
     const int32_t* __restrict__ seq_lens,
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
-    int log2_bs, int max_blocks, int64_t num_blocks, int window, float* __restrict__ part_o,
-    float* __restrict__ part_m, float* __restrict__ part_l) {
+    int log2_bs, int max_blocks, int64_t num_blocks, int window, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_m, float* __restrict__ part_l, int* __restrict__ part_e) {
   static_assert(NSLOT >= 3 && NSLOT <= 8, "ring depth");
   using S = Stage<D>;
   static_assert(NSLOT * HPW * S::kTileU4 * 16 <= 160 * 1024, "ring exceeds the LDS of a CU");
@@ -380,6 +388,11 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int trow = query_row ? query_row[b] : b;
   const bool row_ok = trow >= 0 && trow < n_rows;
   const int32_t* bt = block_table + (size_t)(row_ok ? trow : 0) * max_blocks;
+  // The wave's first table entry does not depend on the length unless a
+  // sliding window moves the range, so its entries are requested together
+  // with seq_lens: one round trip before the first tile is issued, not two.
+  int e0 = (u_rel * kTile) >> log2_bs;
+  int btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
   int L = row_ok ? seq_lens[b] : 0;
   const int Lmax = max_blocks << log2_bs;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
@@ -390,8 +403,10 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int u0 = base + u_rel;
   const int n_tiles = (L + kTile - 1) / kTile;
   const int u1 = min(min(u0 + sub_len, base + g_rel + spw * cs), n_tiles);
-  const int e0 = (u0 * kTile) >> log2_bs;
-  const int btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
+  if (base > 0) {
+    e0 = (u0 * kTile) >> log2_bs;
+    btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
+  }
   const size_t stat = ((size_t)b * Hq + hq) * P + part;
 
   if (u0 >= u1) {
@@ -510,66 +525,62 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 
   const float l1 = l_part + __shfl_xor(l_part, 16);
   const float l_tot = l1 + __shfl_xor(l1, 32);
-  // O / l leaves as one contiguous row per query head: the lanes first place
-  // their dims in the wave's own ring, free now that every tile it issued has
-  // been consumed (row stride D*4 + 16 bytes, RPS rows per slot), then each
-  // row is read back across the wave and stored whole, instead of 64
-  // scattered 16-byte pieces per store.
-  constexpr int RS = D * 4 + 16;
+  // The partial O / l of each query head is stored as an fp16 row times
+  // 2^ex, with ex chosen from the row's largest magnitude so that it lands in
+  // [2^14, 2^15): the rounding error is at most 2^-11 of the row maximum. The
+  // row leaves as one contiguous store: the lanes first place their dims in
+  // the wave's own ring, free now that every tile it issued has been
+  // consumed (row stride 2 D + 16 bytes, RPS rows per slot), then each row is
+  // read back across the wave.
+  constexpr int RS = D * 2 + 16;
   constexpr int RPS = S::kTileU4 * 16 / RS;
-  if constexpr ((QG + RPS - 1) / RPS <= NSLOT) {
+  static_assert((QG + RPS - 1) / RPS <= NSLOT, "the ring cannot stage the partial rows");
 #define UQ_OWN_PTR(K) (NSLOT > K ? &ring##K[NSLOT > K ? wave : 0][0] : &ring0[0][0])
-    uint4* const own[8] = {UQ_OWN_PTR(0), UQ_OWN_PTR(1), UQ_OWN_PTR(2), UQ_OWN_PTR(3),
-                           UQ_OWN_PTR(4), UQ_OWN_PTR(5), UQ_OWN_PTR(6), UQ_OWN_PTR(7)};
+  uint4* const own[8] = {UQ_OWN_PTR(0), UQ_OWN_PTR(1), UQ_OWN_PTR(2), UQ_OWN_PTR(3),
+                         UQ_OWN_PTR(4), UQ_OWN_PTR(5), UQ_OWN_PTR(6), UQ_OWN_PTR(7)};
 #undef UQ_OWN_PTR
-    if (qlane && grp == 0) {
-      part_m[stat] = m_ref;
-      part_l[stat] = l_tot;
-    }
-    if (__builtin_amdgcn_readfirstlane(__float_as_int(l_tot)) == 0) return;   // empty range: l = +0
-    const float inv = 1.f / l_tot;
-    if (qlane) {
-      float* rowp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(own[n16 / RPS]) + (n16 % RPS) * RS);
+  // a non-empty range has l >= 1 (its largest weight is exactly 1)
+  const float inv = 1.f / l_tot;
+  float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+  for (int j = 0; j < NA; ++j)
 #pragma unroll
-        for (int j = 0; j < NA; j += 4)
-          *reinterpret_cast<float4*>(rowp + NA * (4 * grp + i) + j) =
-              make_float4(acc[j][i] * inv, acc[j + 1][i] * inv, acc[j + 2][i] * inv, acc[j + 3][i] * inv);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    const size_t row0 = ((size_t)b * Hq + (size_t)h * QG) * P + part;   // first query head of the group
-#pragma unroll
-    for (int r = 0; r < QG; ++r) {
-      const float* rowp = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(own[r / RPS]) + (r % RPS) * RS);
-      float* dst = part_o + (row0 + (size_t)r * P) * D;
-      if constexpr (D == 128) {
-        if (lane < 32) *reinterpret_cast<float4*>(dst + 4 * lane) = *reinterpret_cast<const float4*>(rowp + 4 * lane);
-      } else {
-#pragma unroll
-        for (int c = 0; c < D / 256; ++c)
-          *reinterpret_cast<float4*>(dst + 256 * c + 4 * lane) =
-              *reinterpret_cast<const float4*>(rowp + 256 * c + 4 * lane);
-      }
-    }
-    return;
-  }
-  if (!qlane) return;
-  if (grp == 0) {
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[j][i]));
+  amax = rowgroup_max(amax * inv);
+  const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14 : 0;
+  if (qlane && grp == 0) {
     part_m[stat] = m_ref;
     part_l[stat] = l_tot;
+    part_e[stat] = ex;
   }
-  if (l_tot > 0.f) {
+  if (qlane) {
     // lane (head l%16, grp) holds dims NA*(4*grp + i) + j
-    const float inv = 1.f / l_tot;
-    float* op = part_o + stat * D + NA * 4 * grp;
+    uint8_t* rowp = reinterpret_cast<uint8_t*>(own[n16 / RPS]) + (n16 % RPS) * RS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < NA; j += 4)
-        *reinterpret_cast<float4*>(op + NA * i + j) =
-            make_float4(acc[j][i] * inv, acc[j + 1][i] * inv, acc[j + 2][i] * inv, acc[j + 3][i] * inv);
+      for (int j = 0; j < NA; j += 8) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          w[k] = pack_f16(__builtin_amdgcn_ldexpf(acc[j + 2 * k][i] * inv, -ex),
+                          __builtin_amdgcn_ldexpf(acc[j + 2 * k + 1][i] * inv, -ex));
+        *reinterpret_cast<uint4*>(rowp + 2 * (NA * (4 * grp + i) + j)) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const size_t row0 = ((size_t)b * Hq + (size_t)h * QG) * P + part;   // first query head of the group
+#pragma unroll
+  for (int r = 0; r < QG; ++r) {
+    const uint8_t* rowp = reinterpret_cast<const uint8_t*>(own[r / RPS]) + (r % RPS) * RS;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(part_o + (row0 + (size_t)r * P) * D);
+    if constexpr (D == 128) {
+      *reinterpret_cast<uint32_t*>(dst + 4 * lane) = *reinterpret_cast<const uint32_t*>(rowp + 4 * lane);
+    } else if constexpr (D == 256) {
+      *reinterpret_cast<uint2*>(dst + 8 * lane) = *reinterpret_cast<const uint2*>(rowp + 8 * lane);
+    } else {
+      *reinterpret_cast<uint4*>(dst + 16 * lane) = *reinterpret_cast<const uint4*>(rowp + 16 * lane);
     }
   }
 }
@@ -577,16 +588,17 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 // ---------------------------------------------------------------------------
 // Stage 2: out = sum_p w_p O_p / sum_p w_p with w_p = l_p 2^(m_p - max m),
 // over the partials with l_p > 0, in one pass with a running maximum (the sums
-// are rescaled when it rises). One wave per (sequence, query head) row; lane
-// l owns columns 4l .. 4l+3, so a float32 partial row is one coalesced 1 KB read,
-// and eight partial rows are in flight per lane. The statistics are uniform
-// across the wave, so the skip of empty partials is a uniform branch and
-// their (stale) rows are never touched by arithmetic.
+// are rescaled when it rises); O_p is the stored fp16 row times 2^ex_p. One
+// wave per (sequence, query head) row; lane l owns columns E l .. E l + E - 1
+// (E = D / 64), so a partial row is one coalesced read, and eight partial rows
+// are in flight per lane. The statistics are uniform across the wave: the
+// rows of empty partials (never written) are neither read nor used.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void stage2_kernel(const uint16_t* __restrict__ part_o,
                                                      const float* __restrict__ part_m,
                                                      const float* __restrict__ part_l,
+                                                     const int* __restrict__ part_e,
                                                      const float* __restrict__ sinks, int Hq,
                                                      uint16_t* __restrict__ out, int rows, int P) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -594,8 +606,9 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
   const int lane = threadIdx.x & 63;
   const float* pm = part_m + (size_t)row * P;
   const float* pl = part_l + (size_t)row * P;
+  const int* pe = part_e + (size_t)row * P;
   constexpr int E = D / 64;                  // columns per lane: E l .. E l + E - 1
-  const float* po = part_o + (size_t)row * P * D + E * lane;
+  const uint16_t* po = part_o + (size_t)row * P * D + E * lane;
   float M = -INFINITY, den = 0.f;
   if (sinks) {              // the sink: a partial of weight 1 at its logit, with no value
     M = sinks[row % Hq] * 1.4426950408889634f;
@@ -605,24 +618,34 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
 #pragma unroll
   for (int e = 0; e < E; ++e) a[e] = 0.f;
   for (int p0 = 0; p0 < P; p0 += 8) {
-    float o[8][E];
+    uint32_t h[8][E / 2];
     float m[8], l[8];
+    int ex[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int p = min(p0 + u, P - 1);
-      const float* src = po + (size_t)p * D;
-      if constexpr (E == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(src);
-        o[u][0] = x.x; o[u][1] = x.y;
-      } else {
-#pragma unroll
-        for (int c = 0; c < E / 4; ++c) {
-          const float4 x = *reinterpret_cast<const float4*>(src + 4 * c);
-          o[u][4 * c] = x.x; o[u][4 * c + 1] = x.y; o[u][4 * c + 2] = x.z; o[u][4 * c + 3] = x.w;
-        }
-      }
       m[u] = pm[p];
       l[u] = p0 + u < P ? pl[p] : 0.f;
+      ex[u] = pe[p];
+    }
+    // only the rows of non-empty partials are read (an empty one was never written)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint16_t* src = po + (size_t)min(p0 + u, P - 1) * D;
+      if (l[u] > 0.f) {
+        if constexpr (E == 2) {
+          h[u][0] = *reinterpret_cast<const uint32_t*>(src);
+        } else if constexpr (E == 4) {
+          const uint2 x = *reinterpret_cast<const uint2*>(src);
+          h[u][0] = x.x; h[u][1] = x.y;
+        } else {
+          const uint4 x = *reinterpret_cast<const uint4*>(src);
+          h[u][0] = x.x; h[u][1] = x.y; h[u][2] = x.z; h[u][3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E / 2; ++e) h[u][e] = 0;
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -632,7 +655,11 @@ __global__ __launch_bounds__(256) void stage2_kernel(const float* __restrict__ p
         const float w = l[u] * exp2f(m[u] - Mn);
         den = den * c + w;
 #pragma unroll
-        for (int e = 0; e < E; ++e) a[e] = a[e] * c + w * o[u][e];
+        for (int e = 0; e < E / 2; ++e) {
+          const v2h x = __builtin_bit_cast(v2h, h[u][e]);
+          a[2 * e] = a[2 * e] * c + w * __builtin_amdgcn_ldexpf((float)x[0], ex[u]);
+          a[2 * e + 1] = a[2 * e + 1] * c + w * __builtin_amdgcn_ldexpf((float)x[1], ex[u]);
+        }
         M = Mn;
       }
     }
@@ -718,11 +745,13 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_
   p.q8_off = off;
   off = align256(off + rows * D);
   p.o_off = off;
-  off = align256(off + rows * p.parts * D * sizeof(float));
+  off = align256(off + rows * p.parts * D * sizeof(uint16_t));
   p.m_off = off;
   off = align256(off + rows * p.parts * sizeof(float));
   p.l_off = off;
   off = align256(off + rows * p.parts * sizeof(float));
+  p.e_off = off;
+  off = align256(off + rows * p.parts * sizeof(int));
   p.total = off;
   return p;
 }
@@ -730,9 +759,10 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mask,
                          hipStream_t stream) {
   uint8_t* q8 = a.workspace + p.q8_off;
-  float* part_o = reinterpret_cast<float*>(a.workspace + p.o_off);
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(a.workspace + p.o_off);
   float* part_m = reinterpret_cast<float*>(a.workspace + p.m_off);
   float* part_l = reinterpret_cast<float*>(a.workspace + p.l_off);
+  int* part_e = reinterpret_cast<int*>(a.workspace + p.e_off);
   const int64_t vecs = (int64_t)p.B * p.Hq;
 
   if (p.D != 128 && p.D != 256 && p.D != 512) return hipErrorInvalidValue;
@@ -775,7 +805,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
                      a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens, scale_log2,    \
                      p.Hq, p.Hk, hgroups,                                                      \
                      cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,            \
-                     a.num_blocks, a.window, part_o, part_m, part_l)
+                     a.num_blocks, a.window, part_o, part_m, part_l, part_e)
 #define UQ_STAGE1_HPW(DV, QGV)                  \
   do {                                          \
     switch (hpw) {                              \
@@ -807,7 +837,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   if (stage_mask & 4) {
     const dim3 g((unsigned)((vecs + 3) / 4));
 #define UQ_STAGE2(DV) hipLaunchKernelGGL(stage2_kernel<DV>, g, dim3(256), 0, stream, part_o, part_m, \
-                                         part_l, a.sinks, p.Hq, a.out, (int)vecs, p.parts)
+                                         part_l, part_e, a.sinks, p.Hq, a.out, (int)vecs, p.parts)
     if (p.D == 128) UQ_STAGE2(128);
     else if (p.D == 256) UQ_STAGE2(256);
     else UQ_STAGE2(512);

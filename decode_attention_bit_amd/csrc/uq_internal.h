@@ -27,7 +27,7 @@ struct DecodePlan {
   int spw;             // consecutive splits covered by one partial (nsub == 1)
   int nsub;            // pieces one split is cut into (spw == 1)
   int parts;           // partials per (sequence, query head): ceil(splits / spw) * nsub
-  size_t q8_off, o_off, m_off, l_off, total;   // byte offsets inside the workspace
+  size_t q8_off, o_off, m_off, l_off, e_off, total;   // byte offsets inside the workspace
 };
 
 struct DecodeArgs {

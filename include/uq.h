@@ -106,8 +106,9 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
  * Bytes of device workspace uq_decode needs for this shape (0 on invalid
  * arguments). The analogue of the pooled segm_out / segm_max / segm_sum and
  * q_fp8 buffers of _SegmBufPool on the flydsl_ultraquant_decode page: query
- * E4M3 codes, one float32 partial output row and two float32 statistics per
- * (sequence, query head, partial). The count of partials depends on the
+ * E4M3 codes, one fp16 partial output row (with a power-of-two row scale)
+ * and three 4-byte statistics (max, sum, scale exponent) per (sequence,
+ * query head, partial). The count of partials depends on the
  * split count and on the block-table capacity max_blocks_per_seq *
  * block_size, never on the sequence lengths, so one workspace serves every
  * step of a fixed-shape batch.

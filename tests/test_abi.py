@@ -113,12 +113,12 @@ def test_workspace_bytes(libuq):
     assert f(32, 32, 4, 256, 32, 0, 16) == 0
     assert f(32, 32, 4, 256, 32, 256, 24) == 0
     n = f(32, 32, 4, 256, 32, 256, 16)
-    # at least: E4M3 query codes, one float32 partial row and two floats per partial
-    assert n >= 32 * 32 * 256 + 32 * 32 * (256 * 4 + 8)
+    # at least: E4M3 query codes, one fp16 partial row and three 4-byte statistics per partial
+    assert n >= 32 * 32 * 256 + 32 * 32 * (256 * 2 + 12)
     assert n % 256 == 0
     assert f(64, 32, 4, 256, 32, 256, 16) >= n
     # one split over a table of one block: one partial
-    assert f(2, 16, 2, 256, 1, 1, 16) == 2 * 16 * 256 + 2 * 16 * 1024 + 2 * 256
+    assert f(2, 16, 2, 256, 1, 1, 16) == 2 * 16 * 256 + 2 * 16 * 512 + 3 * 256
 
 
 def decode_ex_args(**kw):
@@ -234,10 +234,10 @@ def test_continuation_prefill_stages_rejects_mask(libuq, mask):
 @pytest.mark.parametrize("d", [128, 512])
 def test_other_head_dims_accepted(libuq, d):
     """D = 128 and 512 pass every host check of store and decode; the
-    workspace scales with D (query codes D bytes, partial rows D floats)."""
+    workspace scales with D (query codes D bytes, partial rows D fp16 values)."""
     # store with the matching slot size: all checks pass, then N = 0 returns before any HIP call
     assert libuq.uq_store(*store_args(D=d, slot_size=d * 17 // 16, N=0)) == 0
     f = libuq.uq_decode_workspace_bytes
     n = f(2, 16, 2, d, 1, 1, 16)
-    assert n == 2 * 16 * d + 2 * 16 * d * 4 + 2 * 256
+    assert n == 2 * 16 * d + 2 * 16 * d * 2 + 3 * 256
     assert f(2, 16, 2, d, 1, 1, 16) < f(2, 16, 2, 2 * d, 1, 1, 16) if d < 512 else True
