@@ -594,44 +594,54 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 // are in flight per lane. The statistics are uniform across the wave: the
 // rows of empty partials (never written) are neither read nor used.
 // ---------------------------------------------------------------------------
-template <int D>
+// With many partials per row (G = 2 or 4), G waves of the workgroup share a
+// row: wave g merges partials [g P / G, (g + 1) P / G) and the first wave
+// folds the others' (max, denominator, sums) in from LDS.
+template <int D, int G>
 __global__ __launch_bounds__(256) void stage2_kernel(const uint16_t* __restrict__ part_o,
                                                      const float* __restrict__ part_m,
                                                      const float* __restrict__ part_l,
                                                      const int* __restrict__ part_e,
                                                      const float* __restrict__ sinks, int Hq,
                                                      uint16_t* __restrict__ out, int rows, int P) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  const float* pm = part_m + (size_t)row * P;
-  const float* pl = part_l + (size_t)row * P;
-  const int* pe = part_e + (size_t)row * P;
+  static_assert(G == 1 || G == 2 || G == 4, "waves per row");
   constexpr int E = D / 64;                  // columns per lane: E l .. E l + E - 1
-  const uint16_t* po = part_o + (size_t)row * P * D + E * lane;
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * (4 / G) + wave / G;
+  const int g = wave % G;
+  if (G == 1 && row >= rows) return;
+  const bool valid = row < rows;
+  const int lane = threadIdx.x & 63;
+  const size_t rowc = valid ? (size_t)row : 0;
+  const float* pm = part_m + rowc * P;
+  const float* pl = part_l + rowc * P;
+  const int* pe = part_e + rowc * P;
+  const uint16_t* po = part_o + rowc * P * D + E * lane;
+  const int pb = valid ? (int)(((long)g * P) / G) : 0;
+  const int pend = valid ? (int)(((long)(g + 1) * P) / G) : 0;
   float M = -INFINITY, den = 0.f;
-  if (sinks) {              // the sink: a partial of weight 1 at its logit, with no value
+  if (sinks && g == 0 && valid) {   // the sink: a partial of weight 1 at its logit, with no value
     M = sinks[row % Hq] * 1.4426950408889634f;
     den = 1.f;
   }
   float a[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) a[e] = 0.f;
-  for (int p0 = 0; p0 < P; p0 += 8) {
+  for (int p0 = pb; p0 < pend; p0 += 8) {
     uint32_t h[8][E / 2];
     float m[8], l[8];
     int ex[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int p = min(p0 + u, P - 1);
+      const int p = min(p0 + u, pend - 1);
       m[u] = pm[p];
-      l[u] = p0 + u < P ? pl[p] : 0.f;
+      l[u] = p0 + u < pend ? pl[p] : 0.f;
       ex[u] = pe[p];
     }
     // only the rows of non-empty partials are read (an empty one was never written)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const uint16_t* src = po + (size_t)min(p0 + u, P - 1) * D;
+      const uint16_t* src = po + (size_t)min(p0 + u, pend - 1) * D;
       if (l[u] > 0.f) {
         if constexpr (E == 2) {
           h[u][0] = *reinterpret_cast<const uint32_t*>(src);
@@ -660,6 +670,29 @@ __global__ __launch_bounds__(256) void stage2_kernel(const uint16_t* __restrict_
           a[2 * e] = a[2 * e] * c + w * __builtin_amdgcn_ldexpf((float)x[0], ex[u]);
           a[2 * e + 1] = a[2 * e + 1] * c + w * __builtin_amdgcn_ldexpf((float)x[1], ex[u]);
         }
+        M = Mn;
+      }
+    }
+  }
+  if constexpr (G > 1) {
+    __shared__ float xs[4][64][E + 2];
+    if (g > 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) xs[wave][lane][e] = a[e];
+      xs[wave][lane][E] = M;
+      xs[wave][lane][E + 1] = den;
+    }
+    __syncthreads();
+    if (g > 0 || !valid) return;
+#pragma unroll
+    for (int k = 1; k < G; ++k) {
+      const float m2 = xs[wave + k][lane][E], d2 = xs[wave + k][lane][E + 1];
+      if (d2 > 0.f) {
+        const float Mn = fmaxf(M, m2);
+        const float c1 = exp2f(M - Mn), c2 = exp2f(m2 - Mn);
+        den = den * c1 + d2 * c2;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[e] = a[e] * c1 + xs[wave + k][lane][e] * c2;
         M = Mn;
       }
     }
@@ -835,12 +868,17 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
 #undef UQ_STAGE1_HPW
 #undef UQ_STAGE1
   if (stage_mask & 4) {
-    const dim3 g((unsigned)((vecs + 3) / 4));
-#define UQ_STAGE2(DV) hipLaunchKernelGGL(stage2_kernel<DV>, g, dim3(256), 0, stream, part_o, part_m, \
-                                         part_l, part_e, a.sinks, p.Hq, a.out, (int)vecs, p.parts)
-    if (p.D == 128) UQ_STAGE2(128);
-    else if (p.D == 256) UQ_STAGE2(256);
-    else UQ_STAGE2(512);
+    // waves per row: one up to 16 partials, then two, then four
+    const int gw = p.parts > 32 ? 4 : (p.parts > 16 ? 2 : 1);
+    const dim3 g((unsigned)((vecs * gw + 3) / 4));
+#define UQ_STAGE2(DV, GV) hipLaunchKernelGGL((stage2_kernel<DV, GV>), g, dim3(256), 0, stream, part_o, \
+                                             part_m, part_l, part_e, a.sinks, p.Hq, a.out, (int)vecs, p.parts)
+#define UQ_STAGE2_G(DV) do { if (gw == 1) UQ_STAGE2(DV, 1); else if (gw == 2) UQ_STAGE2(DV, 2); \
+                             else UQ_STAGE2(DV, 4); } while (0)
+    if (p.D == 128) UQ_STAGE2_G(128);
+    else if (p.D == 256) UQ_STAGE2_G(256);
+    else UQ_STAGE2_G(512);
+#undef UQ_STAGE2_G
 #undef UQ_STAGE2
     e = hipGetLastError();
   }

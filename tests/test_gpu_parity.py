@@ -412,7 +412,7 @@ def test_decode_sinks_and_sliding_window(window):
     ref = O.decode(bits(ctx["q"]), ctx["ref_cache"], ctx["table"].cpu().numpy(), np.array(lens),
                    ctx["scale"], sinks=sinks.astype(np.float32).astype(np.float64),
                    sliding_window=window)
-    for S in (1, 4, 32):
+    for S in (1, 4, 32, 512):    # 512 splits: the merge shares each row among four waves
         out = uq.decode_ex(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], S,
                            sinks=sinks_dev, sliding_window=window)
         check_close(to_np(out), ref, f"sinks, window={window}, S={S}")
