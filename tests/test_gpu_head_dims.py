@@ -61,11 +61,12 @@ def test_store_bit_exact(d):
     assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:4].tolist()}"
 
 
+@pytest.mark.parametrize("qg", [6, 8, 16])
 @pytest.mark.parametrize("d", DIMS)
-def test_query_prologue_codes_bit_exact(d):
-    say(f"prologue d={d}")
+def test_query_prologue_codes_bit_exact(d, qg):
+    say(f"prologue d={d} qg={qg}")
     rng = np.random.default_rng(d + 1)
-    B, hk, qg = 2, 2, 8
+    B, hk = 2, 2
     q = rng.standard_normal((B, hk * qg, d))
     q[0, 0] = 0.0
     q[0, 1] = rng.standard_normal(d) * 2.0 ** -20

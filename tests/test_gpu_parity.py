@@ -150,14 +150,15 @@ def test_store_random_bulk():
 
 
 # ------------------------------------------------------------ query prologue
-def test_query_prologue_codes_bit_exact():
+@pytest.mark.parametrize("qg", [6, 8, 16])
+def test_query_prologue_codes_bit_exact(qg):
     """The E4M3 codes of q H that the prologue leaves at the start of the
     workspace equal the oracle's haircut value for value, with the sign of
     codes that flush to zero: zeros, subnormal-range inputs that flush, saturation above 448,
     and magnitudes spread over 26 binades (still exact in float64)."""
     say("query prologue codes")
     rng = np.random.default_rng(42)
-    B, Hk, qg = 3, 2, 8
+    B, Hk = 3, 2
     Hq = Hk * qg
     q = rng.standard_normal((B, Hq, 256))
     q[0, 0] = 0.0                                            # all-zero vector
