@@ -129,22 +129,16 @@ struct Stage {
   static constexpr int kTileU4 = kTile * kTokStride / 16;    // uint4 per tile in LDS
 };
 
-// Block-table entries e0 .. e0 + 63 of the wave's range sit one per lane in
-// `btv`, loaded once; an entry past them (ranges of more than 64 blocks) is
-// read from memory when its tile is issued.
+// The caller passes the tile's physical block (see stage1_kernel).
 // One plain function per head dim, with literal constants (a function
 // template holding these builtins is not viable in the host pass, and
 // constants passed as arguments cost the loads' alias information, after
 // which the compiler drains the ring before every LDS read).
 #define UQ_DEFINE_ISSUE(NAME, SLOT, LOADS, CHUNKS, DMA)                                                \
-  __device__ __forceinline__ int NAME(uint4* dst, const uint8_t* __restrict__ cache,                  \
-                                      const int32_t* __restrict__ bt, int btv, int e0, int t, int L,   \
-                                      int log2_bs, int64_t num_blocks, uint32_t row, int h, int lane,  \
-                                      const uint32_t goff[LOADS]) {                                    \
+  __device__ __forceinline__ int NAME(uint4* dst, const uint8_t* __restrict__ cache, int phys, int t,  \
+                                      int L, int log2_bs, int64_t num_blocks, uint32_t row, int h,     \
+                                      int lane, const uint32_t goff[LOADS]) {                          \
     const int tok0 = t * kTile;                                                                        \
-    const int entry = tok0 >> log2_bs;                                                                 \
-    const int phys = entry - e0 < 64 ? __builtin_amdgcn_readlane(btv, entry - e0)                      \
-                                     : __builtin_amdgcn_readfirstlane(bt[entry]);                      \
     const bool ok = phys >= 0 && (int64_t)phys < num_blocks;                                           \
     const int nvalid = ok ? min(kTile, L - tok0) : 0;                                                  \
     const size_t tile_off =                                                                            \
@@ -393,6 +387,12 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   // with seq_lens: one round trip before the first tile is issued, not two.
   int e0 = (u_rel * kTile) >> log2_bs;
   int btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
+  // entries e0 .. e0 + 7 also as scalars, which arrive with seq_lens: the
+  // tiles that fill the ring at the start are issued from them, without
+  // waiting for the vector load of btv
+  int s_ent[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s_ent[k] = bt[min(e0 + k, max_blocks - 1)];
   int L = row_ok ? seq_lens[b] : 0;
   const int Lmax = max_blocks << log2_bs;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
@@ -406,6 +406,8 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   if (base > 0) {
     e0 = (u0 * kTile) >> log2_bs;
     btv = (row_ok && e0 + lane < max_blocks) ? bt[e0 + lane] : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s_ent[k] = bt[min(e0 + k, max_blocks - 1)];
   }
   const size_t stat = ((size_t)b * Hq + hq) * P + part;
 
@@ -429,10 +431,21 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
                     S::kLoads == (D == 256 ? 5 : 9) && S::kTileChunks == (D == 128 ? 576 : D == 256 ? 272 : 544) &&
                     S::kDma == (D == 128 ? 4 : 16),
                 "the issue_tile_d* constants follow Stage<D>");
-#define issue(SLOT, TT)                                                                                 \
-  (D == 128 ? issue_tile_d128(SLOT, cache, bt, btv, e0, TT, L, log2_bs, num_blocks, row, h, lane, goff) \
-   : D == 256 ? issue_tile_d256(SLOT, cache, bt, btv, e0, TT, L, log2_bs, num_blocks, row, h, lane, goff) \
-              : issue_tile_d512(SLOT, cache, bt, btv, e0, TT, L, log2_bs, num_blocks, row, h, lane, goff))
+  // Physical block of tile TT: entries e0 .. e0 + 63 sit one per lane in
+  // `btv`, loaded once; an entry past them (ranges of more than 64 blocks) is
+  // read from memory when its tile is issued. The first fill of the ring
+  // takes entries e0 .. e0 + 7 from the scalars (at most 7 tiles, at most one
+  // entry each).
+#define UQ_PHYS_B(TT)                                                                                  \
+  ((((TT) * kTile) >> log2_bs) - e0 < 64                                                               \
+       ? __builtin_amdgcn_readlane(btv, (((TT) * kTile) >> log2_bs) - e0)                              \
+       : __builtin_amdgcn_readfirstlane(bt[((TT) * kTile) >> log2_bs]))
+#define UQ_PHYS_S(TT) s_ent[((((TT) * kTile) >> log2_bs) - e0) & 7]
+#define issue_at(SLOT, TT, PH)                                                                          \
+  (D == 128 ? issue_tile_d128(SLOT, cache, PH, TT, L, log2_bs, num_blocks, row, h, lane, goff)         \
+   : D == 256 ? issue_tile_d256(SLOT, cache, PH, TT, L, log2_bs, num_blocks, row, h, lane, goff)       \
+              : issue_tile_d512(SLOT, cache, PH, TT, L, log2_bs, num_blocks, row, h, lane, goff))
+#define issue(SLOT, TT) issue_at(SLOT, TT, UQ_PHYS_B(TT))
 
   // Softmax reference: the first tile's maximum. The weights 2^(s - m_ref)
   // are exact for any reference; keeping them <= 2^8 bounds their range. A
@@ -446,6 +459,15 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   for (int j = 0; j < NA; ++j) hold[j] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_part = 0.f, l_hold = 0.f;
   int t0 = u0;
+  // valid-token count of the tile in each slot, known when it is issued
+  int nv_ring0 = 0, nv_ring1 = 0, nv_ring2 = 0, nv_ring3 = 0;
+  int nv_ring4 = 0, nv_ring5 = 0, nv_ring6 = 0, nv_ring7 = 0;
+#define UQ_PRE(K, PHYS) \
+  if constexpr (NSLOT > K + 1) { if (t0 + K < u1) nv_ring##K = issue_at(ring##K[wave], t0 + K, PHYS(t0 + K)); }
+  nv_ring0 = issue_at(ring0[wave], t0, UQ_PHYS_S(t0));
+  UQ_PRE(1, UQ_PHYS_S) UQ_PRE(2, UQ_PHYS_S) UQ_PRE(3, UQ_PHYS_S) UQ_PRE(4, UQ_PHYS_S) UQ_PRE(5, UQ_PHYS_S)
+  UQ_PRE(6, UQ_PHYS_S)
+  bool filled = true;
   for (;;) {
     Tile<D> T;
     float sv[4], mt;
@@ -454,13 +476,12 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     l_part = 0.f;
     bool rebased = false;
     int t_stop = 0;
-    // valid-token count of the tile in each slot, known when it is issued
-    int nv_ring0 = issue(ring0[wave], t0), nv_ring1 = 0, nv_ring2 = 0, nv_ring3 = 0;
-    int nv_ring4 = 0, nv_ring5 = 0, nv_ring6 = 0, nv_ring7 = 0;
-#define UQ_PRE(K) \
-    if constexpr (NSLOT > K + 1) { if (t0 + K < u1) nv_ring##K = issue(ring##K[wave], t0 + K); }
-    UQ_PRE(1) UQ_PRE(2) UQ_PRE(3) UQ_PRE(4) UQ_PRE(5) UQ_PRE(6)
-#undef UQ_PRE
+    if (!filled) {              // a segment after a re-base refills the ring at t0
+      nv_ring0 = issue(ring0[wave], t0);
+      UQ_PRE(1, UQ_PHYS_B) UQ_PRE(2, UQ_PHYS_B) UQ_PRE(3, UQ_PHYS_B) UQ_PRE(4, UQ_PHYS_B) UQ_PRE(5, UQ_PHYS_B)
+      UQ_PRE(6, UQ_PHYS_B)
+    }
+    filled = false;
     // Step t: tiles t .. t + NSLOT - 2 are in flight. Wait for tile t (the
     // later ones may stay pending), read it, start tile t + NSLOT - 1 into the
     // slot tile t - 1 used (already consumed), then compute tile t.
@@ -518,7 +539,11 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     UQ_WAIT_VMCNT(0);
     t0 = t_stop;
   }
+#undef UQ_PRE
 #undef issue
+#undef issue_at
+#undef UQ_PHYS_S
+#undef UQ_PHYS_B
 #pragma unroll
   for (int j = 0; j < NA; ++j) acc[j] += hold[j];
   l_part += l_hold;
