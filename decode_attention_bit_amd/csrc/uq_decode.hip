@@ -736,9 +736,12 @@ __global__ __launch_bounds__(256) void stage2_kernel(const uint16_t* __restrict_
   }
 }
 
-int largest_divisor_upto(int n, int cap) {
-  for (int d = cap < n ? cap : n; d > 1; --d)
-    if (n % d == 0) return d;
+// KV heads per stage-1 workgroup, one wave each: 4, 2 or 1, the largest
+// that divides Hk, capped at 2 from eight heads on (an odd count such as 3
+// takes one head per workgroup).
+int heads_per_workgroup(int hk) {
+  for (int d = hk >= 8 ? 2 : 4; d > 1; d /= 2)
+    if (hk % d == 0) return d;
   return 1;
 }
 
@@ -841,7 +844,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   // on one CU shares its cache lines, which is what four heads per workgroup
   // buy at Hk = 4. At Hk = 8, measured on ragged lengths, workgroups of two
   // heads schedule better than one eight-wave workgroup per CU.
-  const int hpw = largest_divisor_upto(p.Hk, p.Hk >= 8 ? 2 : 4);
+  const int hpw = heads_per_workgroup(p.Hk);
   const int hgroups = p.Hk / hpw;
   int log2_bs = 0;
   while ((1 << log2_bs) < a.block_size) ++log2_bs;

@@ -124,6 +124,18 @@ def test_decode_ragged(d, qg, bs):
 
 
 @pytest.mark.parametrize("d", DIMS)
+@pytest.mark.parametrize("hk", [1, 3, 8])
+def test_decode_head_counts(d, hk):
+    """KV head counts that give stage 1 one head per workgroup (1, and the
+    odd 3) or two heads per workgroup (8)."""
+    say(f"decode d={d} hk={hk}")
+    lens = [700, 5, 16, 129]
+    for qg in (6, 8):
+        out, ref = _decode_case(d, lens, hk=hk, qg=qg, splits=4, seed=40 + hk + qg)
+        check_close(to_np(out), ref, f"d={d} hk={hk} qg={qg}")
+
+
+@pytest.mark.parametrize("d", DIMS)
 def test_decode_long_split_invariance(d):
     """One long sequence per KV head group at several split counts, against
     the single-softmax oracle."""

@@ -242,6 +242,14 @@ def test_decode_ragged_lengths_block_sizes(qg, bs):
     check_close(to_np(out), ref, f"qg={qg} bs={bs}")
 
 
+@pytest.mark.parametrize("qg", [6, 8, 16])
+def test_decode_odd_head_count(qg):
+    """Three KV heads: stage 1 then runs one head per workgroup."""
+    say(f"decode Hk=3 qg={qg}")
+    out, ref, _ = _decode_case([300, 17, 1, 64], Hk=3, qg=qg, splits=4, seed=60 + qg)
+    check_close(to_np(out), ref, f"Hk=3 qg={qg}")
+
+
 def test_decode_single_token_is_exact():
     """L = 1: softmax weight 1, so the bf16 output equals the dequantised
     value, which bf16 represents exactly."""
