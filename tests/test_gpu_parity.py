@@ -250,6 +250,24 @@ def test_decode_odd_head_count(qg):
     check_close(to_np(out), ref, f"Hk=3 qg={qg}")
 
 
+def test_decode_large_grid_many_empty_partials():
+    """A grid of several rounds of the chip (40 ragged sequences, 128 splits:
+    2560 stage-1 waves), most of whose partials lie past their sequence's
+    end; with a window and sinks too."""
+    say("decode large grid")
+    rng = np.random.default_rng(70)
+    lens = [int(x) for x in rng.integers(0, 1025, 40)]
+    lens[0], lens[1], lens[2] = 1024, 1, 0
+    out, ref, ctx = _decode_case(lens, Hk=2, qg=8, splits=128, seed=71)
+    check_close(to_np(out), ref, "large grid")
+    sinks = rng.normal(0.0, 2.0, 16).astype(np.float32)
+    o = uq.decode_ex(ctx["q"].to(DEV), ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 128,
+                     sinks=torch.from_numpy(sinks).to(DEV), sliding_window=333)
+    r = O.decode(bits(ctx["q"]), ctx["ref_cache"], ctx["table"].cpu().numpy(), np.array(lens), ctx["scale"],
+                 sinks=sinks.astype(np.float64), sliding_window=333)
+    check_close(to_np(o), r, "large grid, window and sinks")
+
+
 def test_decode_single_token_is_exact():
     """L = 1: softmax weight 1, so the bf16 output equals the dequantised
     value, which bf16 represents exactly."""
