@@ -377,8 +377,9 @@ def prefill_main(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not "
-                                   "part of this build (see DESIGN.md for how the path would shard)",
+        print(json.dumps({"error": "this benchmark runs on one GPU only. Every (sequence, KV head) "
+                                   "unit is independent, so the path shards across GPUs by sequence "
+                                   "or by KV head with no exchange; that is not run here",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.workload == "prefill":
