@@ -15,8 +15,9 @@ enough stored copies of the cache that each step reads one untouched for the
 last >= 768 MB of traffic.
 
 Timing: HIP events on the stream the kernels run on. The host first queues a
-spin kernel, then all timed steps, so the GPU runs them back to back without
-waiting on Python. A second pass times each of the three kernels alone, as
+spin kernel, then a few untimed steps (the first launches after the idle spin
+run slower than the steady state), then all timed steps, so the GPU runs them
+back to back without waiting on Python. A second pass times each of the three kernels alone, as
 back-to-back launches, which gives the dominant kernel's duration for the
 roofline.
 """
@@ -37,7 +38,9 @@ METRIC = "decode KV-bytes GB/s (% of HBM peak) + decode tokens/s, B=32 GQA-8 D={
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    # 1000 steps: averages over 200 steps varied by about 5% from run to run,
+    # over 1000 they repeat within 1% (about 0.1 s of timed GPU work)
+    ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode",
                     help="decode (the default line), or tiny / ragged / long / mixed; mixed times a "
@@ -90,10 +93,15 @@ def setup(w, dev):
     return lay, q, caches, bt, sl
 
 
-def busy():
-    """A bounded spin kernel so that the queued steps start back to back."""
+PREROLL = 10      # untimed launches between the spin and the start event
+
+
+def busy(launches=200):
+    """A bounded spin kernel that keeps the GPU busy while the host queues
+    `launches` calls, so that they run back to back (about 60k cycles, ~25
+    us, of spin per call: more than the host needs to queue one)."""
     import torch
-    torch.cuda._sleep(20_000_000)
+    torch.cuda._sleep(20_000_000 + 60_000 * launches)
 
 
 def serving_store(w, lay, dev):
@@ -164,9 +172,13 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
         step(i)
     torch.cuda.synchronize()
 
-    # pass 1: whole steps
+    # pass 1: whole steps. The first launches after the idle spin run slower
+    # than the steady state (about 1 ms per pass in all, measured), so a few
+    # untimed steps are queued between the spin and the start event.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    busy()                                   # keep the GPU busy while the host queues the steps
+    busy(steps + PREROLL)                    # keep the GPU busy while the host queues the steps
+    for i in range(PREROLL):
+        step(i)
     e0.record()
     for i in range(steps):
         step(i)
@@ -181,7 +193,9 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
     # the last stage 1, so repeating one stage is well defined.
     def alone(stage):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        busy()
+        busy(steps + PREROLL)
+        for i in range(PREROLL):
+            uq.decode(*args(i), out=out, workspace=ws, stages=stage)
         a.record()
         for i in range(steps):
             uq.decode(*args(i), out=out, workspace=ws, stages=stage)
@@ -271,7 +285,9 @@ def time_events(fn, steps, warmup):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    busy()
+    busy(steps + PREROLL)
+    for _ in range(PREROLL):
+        fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
