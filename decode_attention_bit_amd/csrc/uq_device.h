@@ -50,6 +50,43 @@ __device__ __forceinline__ int floor_log2(double a) {
   return (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;
 }
 
+// The value lane (l xor m) holds, m a power of two below 64, without the LDS
+// pipe: DPP quad permutes for m = 1, 2; DPP row shifts and a select for m = 4,
+// 8 (a lane with bit m clear reads m lanes up, one with it set m lanes down,
+// both inside the lane's row of 16); the gfx950 row / half swaps for m = 16,
+// 32 (with both operands the same value, the first result holds the even
+// row's (lower half's) value and the second the odd row's (upper half's)).
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x, int m, int lane) {
+  switch (m) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x104, 0xF, 0xF, false);
+      const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+      return (lane & 4) ? dn : up;
+    }
+    case 8: {
+      const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x108, 0xF, 0xF, false);
+      const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
+      return (lane & 8) ? dn : up;
+    }
+    case 16: {
+      const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      return (lane & 16) ? r[0] : r[1];
+    }
+    default: {
+      const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      return (lane & 32) ? r[0] : r[1];
+    }
+  }
+}
+
+__device__ __forceinline__ double xor_lane(double v, int m, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = xor_lane_u32((uint32_t)u, m, lane), hi = xor_lane_u32((uint32_t)(u >> 32), m, lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // 256-point Walsh-Hadamard butterfly (unnormalised) over one wave: lane l
 // holds x[4l .. 4l+3] in v[0..3]. Index bits 0-1 live inside a lane, bits 2-7
 // are lane bits 0-5. Each stage maps (a, b) -> (a + b, a - b). In float64 the
@@ -74,7 +111,7 @@ __device__ __forceinline__ void fwht_wave(double v[E], int lane) {
     const bool upper = (lane & m) != 0;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
-      const double o = __shfl_xor(v[i], m);
+      const double o = xor_lane(v[i], m, lane);
       v[i] = upper ? (o - v[i]) : (v[i] + o);
     }
   }
@@ -89,7 +126,7 @@ __device__ __forceinline__ void fwht256_wave(double v[4], int lane) {
     const bool upper = (lane & m) != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const double o = __shfl_xor(v[i], m);
+      const double o = xor_lane(v[i], m, lane);
       v[i] = upper ? (o - v[i]) : (v[i] + o);
     }
   }
