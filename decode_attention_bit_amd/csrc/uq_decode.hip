@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restri
       v[4 * c + 3] = bf16_to_f64(r.y >> 16);
     }
   }
-  fwht_wave<E>(v, lane);
+  fwht_wave<E, true>(v, lane);
   uint32_t w[(E + 3) / 4] = {};
 #pragma unroll
   for (int i = 0; i < E; ++i) w[i / 4] |= e4m3_code(v[i] * rot_scale<D>()) << (8 * (i % 4));
