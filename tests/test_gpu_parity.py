@@ -268,6 +268,41 @@ def test_decode_large_grid_many_empty_partials():
     check_close(to_np(o), r, "large grid, window and sinks")
 
 
+@pytest.mark.parametrize("k", [-100, -60, 40, 90])
+def test_decode_value_scale_equivariance(k):
+    """Values scaled by 2^k (exact in bf16) shift every UE8M0 value exponent
+    by k and leave the weights alone, so the output scales by exactly 2^k:
+    bit for bit, through the fp16 partial rows and their power-of-two row
+    scales, at magnitudes far from 1."""
+    say(f"decode value scale 2^{k}")
+    rng = np.random.default_rng(80)
+    lens, Hk, qg, bs = [600, 40, 1, 333], 2, 8, 16
+    B, Hq = len(lens), Hk * qg
+    nblk = [(L + bs - 1) // bs for L in lens]
+    nb = sum(nblk) + 1
+    table = np.zeros((B, max(nblk)), dtype=np.int32)
+    perm, off = rng.permutation(nb), 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    c0 = torch.zeros((nb, bs, Hk, 272), dtype=torch.uint8, device=DEV)
+    c1 = torch.zeros_like(c0)
+    for b, L in enumerate(lens):
+        kk = bf16(rng.standard_normal((L, Hk, 256)))
+        vv = bf16(rng.standard_normal((L, Hk, 256)))
+        t = np.arange(L)
+        slots = torch.from_numpy(table[b, t // bs].astype(np.int64) * bs + t % bs).to(DEV)
+        uq.store(kk.to(DEV), vv.to(DEV), c0, slots)
+        uq.store(kk.to(DEV), (vv.double() * 2.0 ** k).to(torch.bfloat16).to(DEV), c1, slots)
+    q = bf16(rng.standard_normal((B, Hq, 256))).to(DEV)
+    tbl = torch.from_numpy(table).to(DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    for S in (1, 4, 32):
+        o0 = uq.decode(q, c0, tbl, sl, 1 / 16, S)
+        o1 = uq.decode(q, c1, tbl, sl, 1 / 16, S)
+        assert torch.equal(o1, (o0.double() * 2.0 ** k).to(torch.bfloat16)), (k, S)
+
+
 def test_decode_single_token_is_exact():
     """L = 1: softmax weight 1, so the bf16 output equals the dequantised
     value, which bf16 represents exactly."""
