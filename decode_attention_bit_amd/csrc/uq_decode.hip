@@ -327,7 +327,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
     int log2_bs, int max_blocks, int64_t num_blocks, int window, uint16_t* __restrict__ part_o,
     float* __restrict__ part_m, float* __restrict__ part_l, int* __restrict__ part_e) {
-  static_assert(NSLOT >= 3 && NSLOT <= 8, "ring depth");
+  static_assert(NSLOT >= 2 && NSLOT <= 8, "ring depth");
   using S = Stage<D>;
   static_assert(NSLOT * HPW * S::kTileU4 * 16 <= 160 * 1024, "ring exceeds the LDS of a CU");
   constexpr int C = D / 128;               // scaled MFMAs per score tile
@@ -496,7 +496,11 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
       if (T.nvalid > 0) pv_tile<D>(T, sv, m_ref, n16, acc, l_part);              \
       if (++t >= u1) break;                                                      \
     }
-    if constexpr (NSLOT == 3) {
+    if constexpr (NSLOT == 2) {
+      for (int t = t0;;) {
+        UQ_STEP(ring0, ring1) UQ_STEP(ring1, ring0)
+      }
+    } else if constexpr (NSLOT == 3) {
       for (int t = t0;;) {
         UQ_STEP(ring0, ring2) UQ_STEP(ring1, ring0) UQ_STEP(ring2, ring1)
       }
@@ -862,14 +866,26 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
     const long cmax = wt < max_tiles ? wt : max_tiles;
     cs = (int)((cmax + p.splits - 1) / p.splits);
   }
-  const dim3 grid1((unsigned)((int64_t)p.B * p.parts * hgroups));
+  const int64_t n_wg = (int64_t)p.B * p.parts * hgroups;
+  const dim3 grid1((unsigned)n_wg);
   const dim3 block1(64 * hpw);
-#define UQ_STAGE1(DV, QGV, HPWV)                                                                  \
-  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, ring_slots<DV>(HPWV)>), grid1, block1, 0, stream, q8, \
+  // At head dim 256 a grid of several rounds of the chip (more than two waves
+  // per SIMD) streams through a two-slot ring (one tile in flight while one
+  // is computed): mixed 246.7 against 251.6 us, ragged 252.8 against 260.8
+  // with three slots; a grid of one round keeps three (decode 36.0 against
+  // 39.9 us with two).
+  const bool two_slots = p.D == 256 && n_wg * hpw > 2 * 1024;
+#define UQ_STAGE1S(DV, QGV, HPWV, NS)                                                             \
+  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, NS>), grid1, block1, 0, stream, q8,              \
                      a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens, scale_log2,    \
                      p.Hq, p.Hk, hgroups,                                                      \
                      cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,            \
                      a.num_blocks, a.window, part_o, part_m, part_l, part_e)
+#define UQ_STAGE1(DV, QGV, HPWV)                                      \
+  do {                                                                \
+    if (DV == 256 && two_slots) UQ_STAGE1S(DV, QGV, HPWV, 2);         \
+    else UQ_STAGE1S(DV, QGV, HPWV, ring_slots<DV>(HPWV));             \
+  } while (0)
 #define UQ_STAGE1_HPW(DV, QGV)                  \
   do {                                          \
     switch (hpw) {                              \
@@ -898,6 +914,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
 #undef UQ_STAGE1_QG
 #undef UQ_STAGE1_HPW
 #undef UQ_STAGE1
+#undef UQ_STAGE1S
   if (stage_mask & 4) {
     // waves per row: one up to 16 partials, then two, then four
     const int gw = p.parts > 32 ? 4 : (p.parts > 16 ? 2 : 1);
