@@ -14,10 +14,10 @@ Entry points mirror include/uq.h:
   decode_ex(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
             query_row=None, sinks=None, sliding_window=0,
             out=None, workspace=None)               -> (B, Hq, D) bf16
-Store and decode take head dims D in {128, 256, 512} (slot 17*D/16 bytes);
-the continuation-prefill calls take D = 256.
+Store, decode, rotate and dequant_kv take head dims D in {128, 256, 512}
+(slot 17*D/16 bytes); prefill_attention and continuation_prefill take D = 256.
   rotate(x, out=None)                               -> bf16(x H), same shape
-  dequant_kv(kv_cache, block_row, n_tokens)         -> (K, V) (n_tokens, Hk, 256) bf16
+  dequant_kv(kv_cache, block_row, n_tokens)         -> (K, V) (n_tokens, Hk, D) bf16
   prefill_attention(q, k, v, scale, out=None)       -> (q_len, Hq, 256) bf16
   continuation_prefill(query, key, value, kv_cache, block_row, cached_len, scale,
                        out=None, workspace=None)    -> (q_len, Hq, 256) bf16
@@ -264,7 +264,8 @@ def _bf16_3d(t: torch.Tensor, name: str) -> None:
 
 
 def rotate(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """uq_rotate: bf16(x H) for (N, H, 256) bf16 x (exact product, one rounding)."""
+    """uq_rotate: bf16(x H) for (N, H, D) bf16 x, D in {128, 256, 512} (exact
+    product times the float64 nearest 1/sqrt(D), one rounding)."""
     _bf16_3d(x, "x")
     if out is None:
         out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
@@ -280,17 +281,20 @@ def rotate(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
 def dequant_kv(kv_cache: torch.Tensor, block_row: torch.Tensor, n_tokens: int,
                k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None):
     """uq_dequant_kv: the first n_tokens tokens of the sequence whose logical
-    block j is physical block block_row[j], as (n_tokens, Hk, 256) bf16 K
-    (rotated basis) and V. k_out / v_out may be any (n_tokens, Hk, 256) views
-    with a contiguous last dim."""
+    block j is physical block block_row[j], as (n_tokens, Hk, D) bf16 K
+    (rotated basis) and V, D = 16/17 of the slot size. k_out / v_out may be
+    any (n_tokens, Hk, D) views with a contiguous last dim."""
     if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
         raise TypeError("kv_cache must be a contiguous 4-d uint8 tensor")
     if block_row.dtype != torch.int32 or not block_row.is_contiguous():
         raise TypeError("block_row must be a contiguous int32 tensor")
     nb, bs, Hk, ss = kv_cache.shape
+    D = ss * 16 // 17
+    if D not in HEAD_DIMS or slot_bytes(D) != ss:
+        raise ValueError(f"kv_cache slot size {ss} is not 17*D/16 for D in {HEAD_DIMS}")
     if block_row.numel() * bs < n_tokens:
         raise ValueError("block_row holds fewer blocks than n_tokens needs")
-    shape = (int(n_tokens), Hk, HEAD_DIM)
+    shape = (int(n_tokens), Hk, D)
     if k_out is None:
         k_out = torch.empty(shape, dtype=torch.bfloat16, device=kv_cache.device)
     if v_out is None:
@@ -302,7 +306,7 @@ def dequant_kv(kv_cache: torch.Tensor, block_row: torch.Tensor, n_tokens: int,
     if k_out.stride() != v_out.stride():
         raise ValueError("k_out and v_out must share strides")
     _check(_load().uq_dequant_kv(_ptr(kv_cache), _ptr(block_row), int(n_tokens), _ptr(k_out),
-                                 _ptr(v_out), Hk, HEAD_DIM, nb, bs, k_out.stride(0), k_out.stride(1),
+                                 _ptr(v_out), Hk, D, nb, bs, k_out.stride(0), k_out.stride(1),
                                  _stream(kv_cache.device)))
     return k_out, v_out
 

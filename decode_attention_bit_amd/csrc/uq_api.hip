@@ -173,7 +173,8 @@ int uq_decode(const uint16_t* query, const uint8_t* kv_cache, const int32_t* blo
 int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t x_stride_n,
               int64_t x_stride_h, int64_t out_stride_n, int64_t out_stride_h, void* stream) {
   if (N < 0 || H < 1) return fail(UQ_EINVAL, "uq_rotate: N=%lld H=%d", (long long)N, H);
-  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_rotate: head_dim %d unsupported (only 256)", D);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(UQ_EUNSUPPORTED, "uq_rotate: head_dim %d unsupported (128, 256, 512)", D);
   if (N == 0) return ok();
   if (!x || !out) return fail(UQ_EINVAL, "uq_rotate: null pointer argument");
   if (x_stride_n < 0 || x_stride_h < 0 || out_stride_n < 0 || out_stride_h < 0 || x_stride_n % 4 ||
@@ -182,6 +183,7 @@ int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t
   if (!aligned(x, 8) || !aligned(out, 8)) return fail(UQ_EINVAL, "uq_rotate: x and out must be 8-byte aligned");
   if ((N * H + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "uq_rotate: N*H too large for one launch");
   uq::GatherArgs a{};
+  a.D = D;
   a.job[0] = uq::VecJob{x, x_stride_n, x_stride_h, out, out_stride_n, out_stride_h, N * H, H, 1, 0, 0};
   return hip_status(uq::launch_gather(a, (hipStream_t)stream), "uq_rotate launch");
 }
@@ -191,7 +193,8 @@ int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_token
                   int64_t out_stride_t, int64_t out_stride_h, void* stream) {
   if (n_tokens < 0 || Hk < 1 || num_blocks < 1)
     return fail(UQ_EINVAL, "uq_dequant_kv: n_tokens=%d Hk=%d num_blocks=%lld", n_tokens, Hk, (long long)num_blocks);
-  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "uq_dequant_kv: head_dim %d unsupported (only 256)", D);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(UQ_EUNSUPPORTED, "uq_dequant_kv: head_dim %d unsupported (128, 256, 512)", D);
   if (!pow2_in(block_size, 16, 256))
     return fail(UQ_EUNSUPPORTED, "uq_dequant_kv: block_size %d unsupported (16, 32, 64, 128, 256)", block_size);
   if (n_tokens == 0) return ok();
@@ -205,6 +208,7 @@ int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_token
   int log2_bs = 0;
   while ((1 << log2_bs) < block_size) ++log2_bs;
   uq::GatherArgs a{};
+  a.D = D;
   a.cache = kv_cache;
   a.block_row = block_row;
   a.n_tok = n_tokens;
@@ -324,6 +328,7 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   int log2_bs = 0;
   while ((1 << log2_bs) < block_size) ++log2_bs;
   uq::GatherArgs g{};
+  g.D = UQ_HEAD_DIM;
   g.cache = kv_cache;
   g.block_row = block_row;
   g.n_tok = cached_len;

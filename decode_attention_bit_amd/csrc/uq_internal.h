@@ -48,7 +48,7 @@ struct DecodeArgs {
   uint8_t* workspace;
 };
 
-// Continuation prefill operands. A job maps n = N * H vectors of 256 bf16
+// Continuation prefill operands. A job maps n = N * H vectors of D bf16
 // (vector w -> row t = w / H, head h = w % H) from src to dst, rotated
 // (dst = bf16(src H)) or copied.
 struct VecJob {
@@ -68,6 +68,7 @@ struct VecJob {
 // 32 keys in the order the attention's P operand uses, its 16-byte chunks
 // permuted by chunk ^ ((d >> 2) & 3).
 struct GatherArgs {
+  int D;                     // head dim: 128, 256 or 512 (vt and to_vt: 256 only)
   // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])
   const uint8_t* cache;
   const int32_t* block_row;

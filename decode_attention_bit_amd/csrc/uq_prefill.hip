@@ -63,12 +63,21 @@ __device__ __forceinline__ int64_t vt_offset(int64_t key, int h, int dim, int64_
 // ---------------------------------------------------------------------------
 // Gather: one wave per unit of work, the role chosen by the wave's index
 // (wave-uniform): first the prefix slots (token, KV head) to dequantise, then
-// up to three jobs over vectors of 256 bf16 (rotate or copy).
-// Dequant: lanes 0-31 write K elements 8l .. 8l+7, lanes 32-63 the same V
-// elements; each reads the 4 code bytes and the scale byte that cover them.
-// Rotate: lane l holds x[4l .. 4l+3] through the float64 butterfly.
+// up to three jobs over vectors of D bf16 (rotate or copy).
+// Dequant: lanes 0-31 write K elements D/32 l .. D/32 l + D/32 - 1, lanes
+// 32-63 the same V elements; each reads the code bytes and the one scale
+// byte that cover them (D/32 <= 16 consecutive elements never straddle a
+// 32-element block).
+// Rotate: lane l holds x[D/64 l .. D/64 l + D/64 - 1] through the float64
+// butterfly, then the float64 nearest 1/sqrt(D) and one rounding to bf16.
+// The tiled value layout (vt, vt_pad, to_vt) exists for D = 256 only.
 // ---------------------------------------------------------------------------
+template <int D>
 __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
+  using F = Fmt<D>;
+  constexpr int EPL = D / 32;              // dequantised elements per lane
+  constexpr int NCB = EPL / 2;             // code bytes per lane: 2, 4 or 8
+  constexpr int E = F::kPerLane;           // rotated elements per lane: 2, 4 or 8
   int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t n_slots = (int64_t)a.n_tok * a.Hk;
@@ -80,37 +89,53 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
     const bool ok = phys >= 0 && (int64_t)phys < a.num_blocks;
     const bool is_v = lane >= 32;
     const int l = lane & 31;
-    uint32_t codes = 0;
+    uint64_t codes = 0;
     int e = 0;
     if (ok) {
       const uint8_t* slot =
-          a.cache + ((((int64_t)phys << a.log2_bs) + (t & ((1 << a.log2_bs) - 1))) * a.Hk + h) * kSlotBytes;
-      codes = *reinterpret_cast<const uint32_t*>(slot + (is_v ? kVCodeOff : kKCodeOff) + 4 * l);
-      e = (int)slot[(is_v ? kVScaleOff : kKScaleOff) + (l >> 2)] - 127;
+          a.cache + ((((int64_t)phys << a.log2_bs) + (t & ((1 << a.log2_bs) - 1))) * a.Hk + h) * F::kSlot;
+      const uint8_t* src = slot + (is_v ? F::kVCode : F::kKCode) + NCB * l;
+      if constexpr (NCB == 2)
+        codes = *reinterpret_cast<const uint16_t*>(src);
+      else if constexpr (NCB == 4)
+        codes = *reinterpret_cast<const uint32_t*>(src);
+      else
+        codes = *reinterpret_cast<const uint64_t*>(src);
+      e = (int)slot[(is_v ? F::kVScale : F::kKScale) + (EPL * l) / 32] - 127;
     }
-    uint32_t o[4];
+    uint32_t o[NCB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = ok ? (e2m1_bf16_bits((codes >> (8 * i)) & 0xF, e) |
-                   (e2m1_bf16_bits((codes >> (8 * i + 4)) & 0xF, e) << 16))
+    for (int i = 0; i < NCB; ++i)
+      o[i] = ok ? (e2m1_bf16_bits((uint32_t)(codes >> (8 * i)) & 0xF, e) |
+                   (e2m1_bf16_bits((uint32_t)(codes >> (8 * i + 4)) & 0xF, e) << 16))
                 : 0u;
-    if (is_v && a.vt) {
+    if constexpr (D == kHeadDim) {
+      if (is_v && a.vt) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        a.vt[vt_offset(t, h, 8 * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
-      return;
+        for (int i = 0; i < 8; ++i)
+          a.vt[vt_offset(t, h, 8 * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+        return;
+      }
     }
-    uint16_t* dst = (is_v ? a.vout : a.kout) + t * a.os_t + (int64_t)h * a.os_h + 8 * l;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    uint16_t* dst = (is_v ? a.vout : a.kout) + t * a.os_t + (int64_t)h * a.os_h + EPL * l;
+    if constexpr (NCB == 2) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCB / 4; ++i)
+        *reinterpret_cast<uint4*>(dst + 8 * i) = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    }
     return;
   }
   w -= n_slots;
   const int64_t n_pad = a.vt_pad * a.Hk;
   if (w < n_pad) {                          // zero the keys past the sequence in its last tile
-    const int64_t key = a.vt_pad0 + w / a.Hk;
-    const int h = (int)(w % a.Hk);
+    if constexpr (D == kHeadDim) {
+      const int64_t key = a.vt_pad0 + w / a.Hk;
+      const int h = (int)(w % a.Hk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a.vt[vt_offset(key, h, 4 * lane + i, a.vt_tiles)] = 0;
+      for (int i = 0; i < 4; ++i) a.vt[vt_offset(key, h, 4 * lane + i, a.vt_tiles)] = 0;
+    }
     return;
   }
   w -= n_pad;
@@ -123,23 +148,47 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
     }
     const int64_t t = w / jb.H;
     const int h = (int)(w - t * jb.H);
-    const uint2 r = *reinterpret_cast<const uint2*>(jb.src + t * jb.ss_t + (int64_t)h * jb.ss_h + 4 * lane);
-    uint2 res = r;
-    if (jb.rotate) {
-      double v[4] = {bf16_to_f64(r.x & 0xFFFF), bf16_to_f64(r.x >> 16), bf16_to_f64(r.y & 0xFFFF),
-                     bf16_to_f64(r.y >> 16)};
-      fwht256_wave(v, lane);
-      res.x = bf16_bits_rne(v[0] * 0.0625) | (bf16_bits_rne(v[1] * 0.0625) << 16);
-      res.y = bf16_bits_rne(v[2] * 0.0625) | (bf16_bits_rne(v[3] * 0.0625) << 16);
-    }
-    if (jb.to_vt) {
+    // E bf16 per lane in words of two: one 4-byte load at D = 128, else
+    // 8-byte loads (the rows are only 8-byte aligned)
+    const uint16_t* sp = jb.src + t * jb.ss_t + (int64_t)h * jb.ss_h + E * lane;
+    uint32_t r[E / 2];
+    if constexpr (E == 2) {
+      r[0] = *reinterpret_cast<const uint32_t*>(sp);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a.vt[vt_offset(jb.vt_key0 + t, h, 4 * lane + i, a.vt_tiles)] =
-            (uint16_t)((i < 2 ? res.x : res.y) >> (16 * (i & 1)));
-      return;
+      for (int i = 0; i < E / 4; ++i) {
+        const uint2 x = *reinterpret_cast<const uint2*>(sp + 4 * i);
+        r[2 * i] = x.x;
+        r[2 * i + 1] = x.y;
+      }
     }
-    *reinterpret_cast<uint2*>(jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + 4 * lane) = res;
+    if (jb.rotate) {
+      double v[E];
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = bf16_to_f64((r[i >> 1] >> (16 * (i & 1))) & 0xFFFF);
+      if constexpr (D == kHeadDim)
+        fwht256_wave(v, lane);
+      else
+        fwht_wave<E>(v, lane);
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i)
+        r[i] = bf16_bits_rne(v[2 * i] * rot_scale<D>()) | (bf16_bits_rne(v[2 * i + 1] * rot_scale<D>()) << 16);
+    }
+    if constexpr (D == kHeadDim) {
+      if (jb.to_vt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a.vt[vt_offset(jb.vt_key0 + t, h, 4 * lane + i, a.vt_tiles)] = (uint16_t)(r[i >> 1] >> (16 * (i & 1)));
+        return;
+      }
+    }
+    uint16_t* dp = jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + E * lane;
+    if constexpr (E == 2) {
+      *reinterpret_cast<uint32_t*>(dp) = r[0];
+    } else {
+#pragma unroll
+      for (int i = 0; i < E / 4; ++i) *reinterpret_cast<uint2*>(dp + 4 * i) = make_uint2(r[2 * i], r[2 * i + 1]);
+    }
     return;
   }
 }
@@ -512,7 +561,16 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   const int64_t waves = (int64_t)a.n_tok * a.Hk + a.vt_pad * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
   if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_gather_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  // the tiled value layout is built for head dim 256 only
+  if (a.D != kHeadDim && (a.vt || a.vt_pad || a.job[0].to_vt || a.job[1].to_vt || a.job[2].to_vt))
+    return hipErrorInvalidValue;
+  switch (a.D) {
+    case 128: hipLaunchKernelGGL(prefill_gather_kernel<128>, grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(prefill_gather_kernel<256>, grid, block, 0, stream, a); break;
+    case 512: hipLaunchKernelGGL(prefill_gather_kernel<512>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

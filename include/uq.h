@@ -40,9 +40,8 @@
  * The rotation of head dim D is the Sylvester Hadamard matrix with entries
  * (-1)**popcount(i & j) times one float64 scale, the nearest double to
  * 1/sqrt(D) (exactly 1/16 for D = 256).
- * Store and decode take D in {128, 256, 512}; the continuation-prefill entry
- * points (uq_rotate, uq_dequant_kv, uq_prefill_attention,
- * uq_continuation_prefill) take D = 256.
+ * Store, decode, uq_rotate and uq_dequant_kv take D in {128, 256, 512};
+ * uq_prefill_attention and uq_continuation_prefill take D = 256.
  */
 #ifndef UQ_H
 #define UQ_H
@@ -231,12 +230,13 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
 /*
  * out[n, h, :] = bf16(x[n, h, :] H) for n < N, h < H: the rotation the page
  * applies to the chunk's keys and queries ((x.float() @ PiT).to(bf16)). The
- * product is computed exactly (float64 butterfly) and rounded once to bf16,
- * nearest-even; the sign of an exactly-zero result is not defined.
+ * +-1 sums are computed exactly (float64 butterfly), multiplied by the
+ * float64 nearest 1/sqrt(D) (exactly 1/16 at D = 256) and rounded once to
+ * bf16, nearest-even; the sign of an exactly-zero result is not defined.
  *   x, out:   (device) bf16, last dim contiguous, 8-byte aligned; strides in
  *             elements, non-negative multiples of 4. out may equal x (with
  *             the same strides); other overlaps are undefined.
- *   D:        256 only (UQ_EUNSUPPORTED otherwise).
+ *   D:        128, 256 or 512 (UQ_EUNSUPPORTED otherwise).
  * Errors: UQ_EINVAL for N < 0, H < 1, a null pointer (N > 0), bad strides
  * or alignment; UQ_EHIP for a launch failure.
  */
@@ -252,10 +252,12 @@ int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t
  *   block_row: (device) int32, at least ceil(n_tokens / block_size) entries:
  *              physical block of logical block j. An entry outside
  *              [0, num_blocks) reads as zeros.
+ *   D:         128, 256 or 512, the head dim of the cache (slot 17*D/16
+ *              bytes); UQ_EUNSUPPORTED otherwise.
  *   k_out, v_out: (device) bf16, 16-byte aligned; element [t, h, d] at
  *              t * out_stride_t + h * out_stride_h + d, strides non-negative
- *              multiples of 8 (e.g. Hk*256 and 256 for (n, Hk, 256), or 256
- *              and n*256 for the page's (Hk, n, 256) buffers).
+ *              multiples of 8 (e.g. Hk*D and D for (n, Hk, D), or D and n*D
+ *              for the page's (Hk, n, D) buffers).
  * Errors: UQ_EINVAL / UQ_EUNSUPPORTED for bad shapes, pointers, strides or
  * block sizes; UQ_EHIP for a launch failure.
  */

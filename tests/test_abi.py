@@ -148,7 +148,7 @@ def rotate_args(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(N=-1), -1), (dict(H=0), -1), (dict(D=128), -2), (dict(x=None), -1),
+    (dict(N=-1), -1), (dict(H=0), -1), (dict(D=64), -2), (dict(D=384), -2), (dict(x=None), -1),
     (dict(xsh=6), -1), (dict(osn=-4), -1), (dict(out=FAKE + 4), -1),
 ])
 def test_rotate_rejects(libuq, kw, code):
@@ -168,7 +168,7 @@ def dequant_args(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(n=-1), -1), (dict(Hk=0), -1), (dict(num_blocks=0), -1), (dict(D=512), -2),
+    (dict(n=-1), -1), (dict(Hk=0), -1), (dict(num_blocks=0), -1), (dict(D=64), -2), (dict(D=1024), -2),
     (dict(block_size=8), -2), (dict(block_row=None), -1), (dict(ost=4), -1),
     (dict(k_out=FAKE + 8), -1), (dict(kv_cache=FAKE + 4), -1),
 ])

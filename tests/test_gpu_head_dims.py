@@ -1,5 +1,6 @@
 """Head dims 128 and 512 (the pages' other head sizes): the slot format
-scales with D (17 D / 16 bytes), the store is bit-exact against the oracle
+scales with D (17 D / 16 bytes), the store and the continuation-prefill
+operands (rotation, dequantised prefix) are bit-exact against the oracle,
 and decode is within max-abs 1e-2 / rel-L2 5e-3. Through the C ABI."""
 import numpy as np
 import pytest
@@ -174,3 +175,88 @@ def test_decode_ex_window_and_sinks(d):
                        sinks=torch.from_numpy(sinks).to(DEV), sliding_window=50)
     ref = O.decode(bits(q), ref_cache, table, np.array(lens), 0.1, sinks=sinks, sliding_window=50)
     check_close(to_np(out), ref, f"decode_ex d={d}")
+
+
+# --------------------------------------------- continuation-prefill operands
+def value_bits(x):
+    """bf16 bit patterns of float64 values that bf16 represents exactly
+    (values past bf16's range become infinities)."""
+    with np.errstate(over="ignore"):
+        return inputs.bf16_bits(torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16))
+
+
+def same_bf16(got_bits, want_values, what):
+    """Bit-equal, except that the sign of an exact zero is not compared."""
+    want = value_bits(want_values)
+    zero = np.asarray(want_values) == 0
+    bad = (got_bits != want) & ~(zero & ((got_bits & 0x7FFF) == 0))
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} differ, first at {np.argwhere(bad)[:3].tolist()}"
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_rotate_bit_exact(d):
+    """bf16(x H) at head dim d: the exact +-1 sums times the float64 nearest
+    1/sqrt(d), rounded once. Gaussian rows, rows over 24 binades, one-hot
+    rows (every output is +-1/sqrt(d) rounded), bf16 subnormals, zeros,
+    huge values; then a strided view rotated in place."""
+    say(f"rotate d={d}")
+    rng = np.random.default_rng(d + 7)
+    x = rng.standard_normal((33, 3, d))
+    x[0] = 0.0
+    x[1, 0] = np.ldexp(rng.uniform(0.5, 1, d), -130)
+    for i in range(2, 8):
+        x[i] = rng.choice([-1, 1], (3, d)) * (1 + rng.random((3, d))) * np.exp2(rng.integers(-12, 12, (3, d)))
+    x[8] = np.eye(d)[rng.integers(d, size=3)]
+    x[9] = rng.standard_normal((3, d)) * 1e30
+    xb = bf16(x)
+    want = O.rotate_to_bf16(bits(xb))
+    out = uq.rotate(xb.to(DEV))
+    same_bf16(bits(out), want, "rotate")
+    big = torch.zeros((33, 3, 2 * d), dtype=torch.bfloat16, device=DEV)
+    big[:, :, d // 2:d // 2 + d] = xb.to(DEV)
+    view = big[:, :, d // 2:d // 2 + d]
+    uq.rotate(view, out=view)
+    same_bf16(bits(view), want, "rotate in place")
+    assert torch.all(big[:, :, :d // 2] == 0) and torch.all(big[:, :, d // 2 + d:] == 0)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_dequant_bit_exact(d):
+    """Dequantised prefix at head dim d equals the oracle's values bit for
+    bit, token-major and in the page's (Hk, n, d) layout; one slot holds
+    every code and extreme scale bytes (bf16 subnormals and infinities); a
+    block entry outside the cache reads as zeros."""
+    say(f"dequant d={d}")
+    rng = np.random.default_rng(d + 9)
+    n, hk, bs, extra = 3 * 16 + 5, 3, 16, 3
+    nblk = -(-n // bs)
+    row = rng.permutation(nblk + extra)[:nblk].astype(np.int32)
+    cache = torch.zeros((nblk + extra, bs, hk, slot(d)), dtype=torch.uint8, device=DEV)
+    ref = np.zeros(tuple(cache.shape), dtype=np.uint8)
+    kb = bf16(rng.standard_normal((n, hk, d)))
+    vb = bf16(rng.standard_t(4, (n, hk, d)))
+    t = np.arange(n)
+    slots = row[t // bs].astype(np.int64) * bs + t % bs
+    uq.store(kb.to(DEV), vb.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+    O.store(bits(kb), bits(vb), ref, slots)
+    s = ref[row[0], 1, 0].copy()
+    s[:d] = (np.arange(d) * 37 + 1) % 256
+    s[d:] = np.resize(np.array([0, 1, 2, 3, 127, 200, 252, 254, 0, 5, 60, 126, 128, 130, 160, 250]), d // 16)
+    ref[row[0], 1, 0] = s
+    cache[int(row[0]), 1, 0] = torch.from_numpy(s).to(DEV)
+    K, V = O.dequant_prefix(ref, row, n)
+    brow = torch.from_numpy(row).to(DEV)
+    k, v = uq.dequant_kv(cache, brow, n)
+    assert tuple(k.shape) == (n, hk, d)
+    same_bf16(bits(k), K, "K")
+    same_bf16(bits(v), V, "V")
+    assert np.signbit(to_np(v))[V == 0].tolist() == np.signbit(V)[V == 0].tolist()
+    kh = torch.empty((hk, n, d), dtype=torch.bfloat16, device=DEV)
+    vh = torch.empty((hk, n, d), dtype=torch.bfloat16, device=DEV)
+    uq.dequant_kv(cache, brow, n, k_out=kh.transpose(0, 1), v_out=vh.transpose(0, 1))
+    assert torch.equal(kh.transpose(0, 1), k) and torch.equal(vh.transpose(0, 1), v)
+    bad = brow.clone()
+    bad[1] = cache.shape[0]
+    k2, v2 = uq.dequant_kv(cache, bad, n)
+    assert torch.all(k2[bs:2 * bs] == 0) and torch.all(v2[bs:2 * bs] == 0)
+    assert torch.equal(k2[:bs], k[:bs]) and torch.equal(k2[2 * bs:], k[2 * bs:])
