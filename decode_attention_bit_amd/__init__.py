@@ -165,8 +165,12 @@ _WS_POOL: dict = {}
 
 
 def _workspace(device, nbytes: int) -> torch.Tensor:
-    """Per-device cached workspace, grown when a bigger one is needed."""
-    key = str(device)
+    """Cached workspace per (device, current stream), grown when a bigger one
+    is needed. Calls on one stream run in order, so they can share it; calls
+    on different streams get different buffers, and a replaced buffer is
+    freed on the stream that used it. Code captured into a graph should pass
+    its own workspace, so that replays do not share it with eager calls."""
+    key = (str(torch.device(device)), _stream(device))
     ws = _WS_POOL.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)

@@ -373,6 +373,38 @@ def test_decode_query_strides_and_reuse_of_outputs():
     assert torch.equal(o, out)
 
 
+def test_decode_default_workspace_per_stream():
+    """Calls without a workspace on two streams at once get separate cached
+    buffers and give the results of the same calls on one stream."""
+    say("decode two streams")
+    out1, ref1, c1 = _decode_case([300, 77, 512], Hk=2, qg=8, splits=4, seed=31)
+    out2, ref2, c2 = _decode_case([1000, 5], Hk=4, qg=6, splits=8, seed=32)
+    check_close(to_np(out1), ref1, "stream case 1")
+    check_close(to_np(out2), ref2, "stream case 2")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    s1.wait_stream(main)
+    s2.wait_stream(main)
+    got1, got2 = [], []
+    for _ in range(8):
+        with torch.cuda.stream(s1):
+            got1.append(uq.decode(c1["q"].to(DEV), c1["cache"], c1["table"], c1["lens"], c1["scale"], 4))
+        with torch.cuda.stream(s2):
+            got2.append(uq.decode(c2["q"].to(DEV), c2["cache"], c2["table"], c2["lens"], c2["scale"], 8))
+    torch.cuda.synchronize()
+    for o in got1:
+        assert torch.equal(o, out1)
+    for o in got2:
+        assert torch.equal(o, out2)
+    with torch.cuda.stream(s1):
+        w1 = uq._workspace(DEV, 256)
+    with torch.cuda.stream(s2):
+        w2 = uq._workspace(DEV, 256)
+    assert w1.data_ptr() != w2.data_ptr()
+    with torch.cuda.stream(s1):
+        assert uq._workspace(DEV, 256).data_ptr() == w1.data_ptr()
+
+
 def test_decode_stage_masks_compose():
     say("decode stages")
     out, ref, ctx = _decode_case([90, 33], Hk=2, qg=8, splits=4, seed=10)
