@@ -156,6 +156,18 @@ __device__ __forceinline__ uint32_t e2m1_code(double x, double inv_scale) {
   return c | (signbit(x) ? 8u : 0u);
 }
 
+// The same code from float32 operands. Exact for values: a bf16 value and a
+// power-of-two scale are float32 values, and their product is exact wherever
+// it can reach a threshold (0.25 .. 5, far above float32's subnormals); NaN
+// and infinity compare as in float64.
+__device__ __forceinline__ uint32_t e2m1_code_f32(float x, float inv_scale) {
+  const float r = fabsf(x) * inv_scale;
+  uint32_t c = (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) +
+               (uint32_t)(r >= 1.75f) + (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) +
+               (uint32_t)(r > 5.0f);
+  return c | (signbit(x) ? 8u : 0u);
+}
+
 // OCP FP8 E4M3 (fn) code of x, round to nearest even, magnitudes above 448
 // saturate to 448. Exact: every step is a power-of-two scaling and one
 // rint() of a value below 2**5.

@@ -11,7 +11,8 @@ namespace uq {
 // One wave per (token, KV head): lane l owns elements E l .. E l + E - 1
 // (E = D / 64), so a 32-element scale block is 32 / E consecutive lanes and
 // the D/2 code bytes of a region are written as 64 contiguous stores of E/2
-// bytes.
+// bytes. K is rotated in float64; V is quantised in float32, which holds
+// bf16 values exactly (the codes and scales come out the same).
 template <int D>
 __global__ __launch_bounds__(256) void store_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
@@ -28,13 +29,14 @@ __global__ __launch_bounds__(256) void store_kernel(
   const int64_t slot = slot_mapping[n];
   if (slot < 0 || slot >= num_slots) return;
 
-  double k[E], v[E];
+  double k[E];
+  float v[E];
   const uint16_t* kp = key + n * ksn + h * ksh + E * lane;
   const uint16_t* vp = value + n * vsn + h * vsh + E * lane;
   if constexpr (E == 2) {
     const uint32_t kr = *reinterpret_cast<const uint32_t*>(kp), vr = *reinterpret_cast<const uint32_t*>(vp);
     k[0] = bf16_to_f64(kr & 0xFFFF); k[1] = bf16_to_f64(kr >> 16);
-    v[0] = bf16_to_f64(vr & 0xFFFF); v[1] = bf16_to_f64(vr >> 16);
+    v[0] = bf16_to_f32(vr & 0xFFFF); v[1] = bf16_to_f32(vr >> 16);
   } else {
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) {
@@ -42,8 +44,8 @@ __global__ __launch_bounds__(256) void store_kernel(
       const uint2 vr = *reinterpret_cast<const uint2*>(vp + 4 * c);
       k[4 * c] = bf16_to_f64(kr.x & 0xFFFF); k[4 * c + 1] = bf16_to_f64(kr.x >> 16);
       k[4 * c + 2] = bf16_to_f64(kr.y & 0xFFFF); k[4 * c + 3] = bf16_to_f64(kr.y >> 16);
-      v[4 * c] = bf16_to_f64(vr.x & 0xFFFF); v[4 * c + 1] = bf16_to_f64(vr.x >> 16);
-      v[4 * c + 2] = bf16_to_f64(vr.y & 0xFFFF); v[4 * c + 3] = bf16_to_f64(vr.y >> 16);
+      v[4 * c] = bf16_to_f32(vr.x & 0xFFFF); v[4 * c + 1] = bf16_to_f32(vr.x >> 16);
+      v[4 * c + 2] = bf16_to_f32(vr.y & 0xFFFF); v[4 * c + 3] = bf16_to_f32(vr.y >> 16);
     }
   }
 
@@ -54,26 +56,28 @@ __global__ __launch_bounds__(256) void store_kernel(
     if (k[i] == 0.0) k[i] = 0.0;       // an exact zero carries no sign: +0
   }
 
-  double ka = 0.0, va = 0.0;
+  double ka = 0.0;
+  float va = 0.f;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     ka = fmax(ka, fabs(k[i]));
-    va = fmax(va, fabs(v[i]));
+    va = fmaxf(va, fabsf(v[i]));
   }
 #pragma unroll
   for (int m = 1; m < LPB; m <<= 1) {
     ka = fmax(ka, __shfl_xor(ka, m));
-    va = fmax(va, __shfl_xor(va, m));
+    va = fmaxf(va, __shfl_xor(va, m));
   }
   const int ke = mx_block_exponent(ka);
-  const int ve = mx_block_exponent(va);
-  const double kinv = pow2(-ke), vinv = pow2(-ve);
+  const int ve = mx_block_exponent((double)va);
+  const double kinv = pow2(-ke);
+  const float vinv = (float)pow2(-ve);     // 2**-127 .. 2**127: a float32 value
 
   uint32_t kc = 0, vc = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     kc |= e2m1_code(k[i], kinv) << (4 * i);
-    vc |= e2m1_code(v[i], vinv) << (4 * i);
+    vc |= e2m1_code_f32(v[i], vinv) << (4 * i);
   }
   uint8_t* dst = cache + ((size_t)slot * Hk + h) * F::kSlot;
   if constexpr (E == 2) {
