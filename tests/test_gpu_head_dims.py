@@ -116,7 +116,7 @@ def _decode_case(d, seq_lens, hk, qg, bs=16, splits=3, seed=0, scale=None):
 
 @pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("qg", [6, 8, 16])
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 64, 256])
 def test_decode_ragged(d, qg, bs):
     say(f"decode d={d} qg={qg} bs={bs}")
     lens = [1, 15, 16, 17, 100, 257, 300, 0, 33]
@@ -128,7 +128,7 @@ def test_decode_ragged(d, qg, bs):
 @pytest.mark.parametrize("hk", [1, 3, 8])
 def test_decode_head_counts(d, hk):
     """KV head counts that give stage 1 one head per workgroup (1, and the
-    odd 3) or two heads per workgroup (8)."""
+    odd 3) or four heads per workgroup (8)."""
     say(f"decode d={d} hk={hk}")
     lens = [700, 5, 16, 129]
     for qg in (6, 8):
@@ -139,10 +139,11 @@ def test_decode_head_counts(d, hk):
 @pytest.mark.parametrize("d", DIMS)
 def test_decode_long_split_invariance(d):
     """One long sequence per KV head group at several split counts, against
-    the single-softmax oracle."""
+    the single-softmax oracle; 512 splits (the maximum) leave most partials
+    empty and give the merge four waves per row."""
     say(f"decode long d={d}")
     lens = [3000, 1234]
-    for splits in (1, 8, 32):
+    for splits in (1, 8, 32, 512):
         out, ref = _decode_case(d, lens, hk=4, qg=8, splits=splits, seed=d + 7)
         check_close(to_np(out), ref, f"d={d} splits={splits}")
 
