@@ -230,9 +230,11 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
 /*
  * out[n, h, :] = bf16(x[n, h, :] H) for n < N, h < H: the rotation the page
  * applies to the chunk's keys and queries ((x.float() @ PiT).to(bf16)). The
- * +-1 sums are computed exactly (float64 butterfly), multiplied by the
- * float64 nearest 1/sqrt(D) (exactly 1/16 at D = 256) and rounded once to
- * bf16, nearest-even; the sign of an exactly-zero result is not defined.
+ * +-1 sums are computed in a float64 butterfly (exact when the vector's
+ * non-zero magnitudes span at most 44 - log2(D) binades, as for uq_store),
+ * multiplied by the float64 nearest 1/sqrt(D) (exactly 1/16 at D = 256) and
+ * rounded once to bf16, nearest-even; the sign of an exactly-zero result is
+ * not defined.
  *   x, out:   (device) bf16, last dim contiguous, 8-byte aligned; strides in
  *             elements, non-negative multiples of 4. out may equal x (with
  *             the same strides); other overlaps are undefined.
