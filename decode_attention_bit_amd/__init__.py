@@ -15,12 +15,13 @@ Entry points mirror include/uq.h:
             query_row=None, sinks=None, sliding_window=0,
             out=None, workspace=None)               -> (B, Hq, D) bf16
 Store, decode, rotate and dequant_kv take head dims D in {128, 256, 512}
-(slot 17*D/16 bytes); prefill_attention and continuation_prefill take D = 256.
+(slot 17*D/16 bytes); continuation_prefill takes D in {128, 256} and
+prefill_attention D = 256.
   rotate(x, out=None)                               -> bf16(x H), same shape
   dequant_kv(kv_cache, block_row, n_tokens)         -> (K, V) (n_tokens, Hk, D) bf16
   prefill_attention(q, k, v, scale, out=None)       -> (q_len, Hq, 256) bf16
   continuation_prefill(query, key, value, kv_cache, block_row, cached_len, scale,
-                       out=None, workspace=None)    -> (q_len, Hq, 256) bf16
+                       out=None, workspace=None)    -> (q_len, Hq, D) bf16
 """
 from __future__ import annotations
 
@@ -351,9 +352,10 @@ def continuation_prefill(query: torch.Tensor, key: torch.Tensor, value: torch.Te
                          kv_cache: torch.Tensor, block_row: torch.Tensor | None, cached_len: int,
                          scale: float, out: torch.Tensor | None = None,
                          workspace: torch.Tensor | None = None, stages: int = 3) -> torch.Tensor:
-    """uq_continuation_prefill: a chunk of q_len tokens (query (q_len, Hq, 256),
-    key / value (q_len, Hk, 256), bf16, unrotated) after cached_len cached
-    tokens reached through block_row; returns (q_len, Hq, 256) bf16.
+    """uq_continuation_prefill: a chunk of q_len tokens (query (q_len, Hq, D),
+    key / value (q_len, Hk, D), bf16, unrotated, D in {128, 256}) after
+    cached_len cached tokens reached through block_row (a cache of head dim
+    D); returns (q_len, Hq, D) bf16.
     ``stages`` selects the gather and/or the attention launch
     (uq_continuation_prefill_stages); the default runs both."""
     for t, name in ((query, "query"), (key, "key"), (value, "value")):
@@ -365,7 +367,9 @@ def continuation_prefill(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     q_len, Hq, D = query.shape
     nb, bs, Hk, ss = kv_cache.shape
     if key.shape != (q_len, Hk, D) or value.shape != (q_len, Hk, D):
-        raise ValueError("key and value must be (q_len, Hk, 256)")
+        raise ValueError("key and value must be (q_len, Hk, D) like the query")
+    if ss != slot_bytes(D):
+        raise ValueError(f"kv_cache slot size {ss} does not match head dim {D} (17*D/16)")
     if cached_len > 0 and (block_row is None or block_row.numel() * bs < cached_len):
         raise ValueError("block_row holds fewer blocks than cached_len needs")
     if out is None:

@@ -222,11 +222,14 @@ int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_token
   return hip_status(uq::launch_gather(a, (hipStream_t)stream), "uq_dequant_kv launch");
 }
 
-static int check_attention_shape(const char* who, int q_len, int seq_len, int Hq, int Hk, int D, float scale) {
+// with128: head dim 128 is accepted beside 256
+static int check_attention_shape(const char* who, int q_len, int seq_len, int Hq, int Hk, int D, float scale,
+                                 bool with128) {
   if (q_len < 0 || seq_len < q_len || Hq < 1 || Hk < 1)
     return fail(UQ_EINVAL, "%s: q_len=%d seq_len=%d Hq=%d Hk=%d", who, q_len, seq_len, Hq, Hk);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(UQ_EINVAL, "%s: scale must be finite and > 0", who);
-  if (D != UQ_HEAD_DIM) return fail(UQ_EUNSUPPORTED, "%s: head_dim %d unsupported (only 256)", who, D);
+  if (D != UQ_HEAD_DIM && !(with128 && D == UQ_HEAD_DIM / 2))
+    return fail(UQ_EUNSUPPORTED, "%s: head_dim %d unsupported (%s)", who, D, with128 ? "128, 256" : "only 256");
   if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "%s: Hq=%d is not a multiple of Hk=%d", who, Hq, Hk);
   if (uq::prefill_positions_per_wg(Hq / Hk) < 1)
     return fail(UQ_EUNSUPPORTED, "%s: GQA group %d above 128", who, Hq / Hk);
@@ -239,7 +242,7 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int64_t q_stride_t, int64_t q_stride_h, int64_t kv_stride_t,
                          int64_t kv_stride_h, int64_t out_stride_t, int64_t out_stride_h,
                          void* stream) {
-  const int rc = check_attention_shape("uq_prefill_attention", q_len, seq_len, Hq, Hk, D, scale);
+  const int rc = check_attention_shape("uq_prefill_attention", q_len, seq_len, Hq, Hk, D, scale, false);
   if (rc != UQ_OK) return rc;
   if (q_len == 0) return ok();
   if (!q || !k || !v || !out) return fail(UQ_EINVAL, "uq_prefill_attention: null pointer argument");
@@ -253,7 +256,7 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
   if (kv_stride_t < UQ_HEAD_DIM || kv_stride_t >= (1LL << 25))
     return fail(UQ_EUNSUPPORTED, "uq_prefill_attention: kv_stride_t %lld outside [256, 2^25)", (long long)kv_stride_t);
   uq::PrefillAttnArgs a{q, k, v, out, q_stride_t, q_stride_h, kv_stride_t, kv_stride_h,
-                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale, 0};
+                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale, 0, UQ_HEAD_DIM};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_prefill_attention launch");
 }
 
@@ -278,7 +281,8 @@ static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, 
 }
 
 size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int Hq, int Hk, int D) {
-  if (q_len < 0 || max_seq_len < q_len || Hq < 1 || Hk < 1 || Hq % Hk || D != UQ_HEAD_DIM) return 0;
+  if (q_len < 0 || max_seq_len < q_len || Hq < 1 || Hk < 1 || Hq % Hk || (D != UQ_HEAD_DIM && D != UQ_HEAD_DIM / 2))
+    return 0;
   const size_t t = prefill_layout(q_len, max_seq_len, Hq, Hk).total;
   return t > 0 ? t : 256;
 }
@@ -298,7 +302,7 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   if (cached_len < 0 || (long long)cached_len + q_len > 0x7FFFFFFFLL)
     return fail(UQ_EINVAL, "%s: cached_len=%d", who, cached_len);
   const int seq_len = cached_len + q_len;
-  int rc = check_attention_shape(who, q_len, seq_len, Hq, Hk, D, scale);
+  int rc = check_attention_shape(who, q_len, seq_len, Hq, Hk, D, scale, true);
   if (rc != UQ_OK) return rc;
   if (num_blocks < 1) return fail(UQ_EINVAL, "%s: num_blocks=%lld < 1", who, (long long)num_blocks);
   if (!pow2_in(block_size, 16, 256))
@@ -328,7 +332,8 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   int log2_bs = 0;
   while ((1 << log2_bs) < block_size) ++log2_bs;
   uq::GatherArgs g{};
-  g.D = UQ_HEAD_DIM;
+  g.D = D;
+  g.pad = D != UQ_HEAD_DIM;        // head dim 128: zero-padded 256-wide operands
   g.cache = kv_cache;
   g.block_row = block_row;
   g.n_tok = cached_len;
@@ -355,7 +360,7 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   }
   if (!(stage_mask & UQ_PREFILL_ATTEND)) return ok();
   uq::PrefillAttnArgs a{qr, kf, vf, out, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM, row, UQ_HEAD_DIM,
-                        out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale, lay.vt_tiles};
+                        out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale, lay.vt_tiles, D};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_continuation_prefill attention launch");
 }
 

@@ -68,7 +68,8 @@ struct VecJob {
 // 32 keys in the order the attention's P operand uses, its 16-byte chunks
 // permuted by chunk ^ ((d >> 2) & 3).
 struct GatherArgs {
-  int D;                     // head dim: 128, 256 or 512 (vt and to_vt: 256 only)
+  int D;                     // head dim: 128, 256 or 512 (vt and to_vt: 256, or 128 with pad)
+  int pad;                   // D = 128 only: write 256-wide rows, elements 128 .. 255 zero
   // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])
   const uint8_t* cache;
   const int32_t* block_row;
@@ -94,6 +95,7 @@ struct PrefillAttnArgs {
   int q_len, cached_len, Hk, QG;
   float scale;
   int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head
+  int d_out;                 // output dims written: 256, or 128 for zero-padded 128-dim operands
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,

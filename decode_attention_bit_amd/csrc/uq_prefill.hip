@@ -70,10 +70,15 @@ __device__ __forceinline__ int64_t vt_offset(int64_t key, int h, int dim, int64_
 // 32-element block).
 // Rotate: lane l holds x[D/64 l .. D/64 l + D/64 - 1] through the float64
 // butterfly, then the float64 nearest 1/sqrt(D) and one rounding to bf16.
-// The tiled value layout (vt, vt_pad, to_vt) exists for D = 256 only.
+// PAD (D = 128 only): the rows go to buffers 256 elements wide, the
+// attention's operands, with elements D .. 255 written as zeros; the tiled
+// value layout (vt, vt_pad, to_vt) is 256 dims wide and exists with PAD or
+// at D = 256.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
+  static_assert(!PAD || 2 * D == kHeadDim, "padding doubles a 128-element row");
+  constexpr bool TILED = PAD || D == kHeadDim;
   using F = Fmt<D>;
   constexpr int EPL = D / 32;              // dequantised elements per lane
   constexpr int NCB = EPL / 2;             // code bytes per lane: 2, 4 or 8
@@ -109,17 +114,20 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
       o[i] = ok ? (e2m1_bf16_bits((uint32_t)(codes >> (8 * i)) & 0xF, e) |
                    (e2m1_bf16_bits((uint32_t)(codes >> (8 * i + 4)) & 0xF, e) << 16))
                 : 0u;
-    if constexpr (D == kHeadDim) {
+    if constexpr (TILED) {
       if (is_v && a.vt) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          a.vt[vt_offset(t, h, 8 * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+        for (int i = 0; i < EPL; ++i) {
+          a.vt[vt_offset(t, h, EPL * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+          if constexpr (PAD) a.vt[vt_offset(t, h, D + EPL * l + i, a.vt_tiles)] = 0;
+        }
         return;
       }
     }
     uint16_t* dst = (is_v ? a.vout : a.kout) + t * a.os_t + (int64_t)h * a.os_h + EPL * l;
     if constexpr (NCB == 2) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+      if constexpr (PAD) *reinterpret_cast<uint2*>(dst + D) = make_uint2(0u, 0u);
     } else {
 #pragma unroll
       for (int i = 0; i < NCB / 4; ++i)
@@ -130,7 +138,7 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
   w -= n_slots;
   const int64_t n_pad = a.vt_pad * a.Hk;
   if (w < n_pad) {                          // zero the keys past the sequence in its last tile
-    if constexpr (D == kHeadDim) {
+    if constexpr (TILED) {
       const int64_t key = a.vt_pad0 + w / a.Hk;
       const int h = (int)(w % a.Hk);
 #pragma unroll
@@ -174,17 +182,20 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
       for (int i = 0; i < E / 2; ++i)
         r[i] = bf16_bits_rne(v[2 * i] * rot_scale<D>()) | (bf16_bits_rne(v[2 * i + 1] * rot_scale<D>()) << 16);
     }
-    if constexpr (D == kHeadDim) {
+    if constexpr (TILED) {
       if (jb.to_vt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a.vt[vt_offset(jb.vt_key0 + t, h, 4 * lane + i, a.vt_tiles)] = (uint16_t)(r[i >> 1] >> (16 * (i & 1)));
+        for (int i = 0; i < E; ++i) {
+          a.vt[vt_offset(jb.vt_key0 + t, h, E * lane + i, a.vt_tiles)] = (uint16_t)(r[i >> 1] >> (16 * (i & 1)));
+          if constexpr (PAD) a.vt[vt_offset(jb.vt_key0 + t, h, D + E * lane + i, a.vt_tiles)] = 0;
+        }
         return;
       }
     }
     uint16_t* dp = jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + E * lane;
     if constexpr (E == 2) {
       *reinterpret_cast<uint32_t*>(dp) = r[0];
+      if constexpr (PAD) *reinterpret_cast<uint32_t*>(dp + D) = 0u;
     } else {
 #pragma unroll
       for (int i = 0; i < E / 4; ++i) *reinterpret_cast<uint2*>(dp + 4 * i) = make_uint2(r[2 * i], r[2 * i + 1]);
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
     int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2,
-    int64_t vt_tiles) {
+    int64_t vt_tiles, int d_out) {
   // one array per stage and operand, so that the compiler can tell the slot
   // being read from the slots being filled
   __shared__ uint4 kr0[kTileU4], kr1[kTileU4], kr2[kTileU4], kr3[kTileU4];
@@ -542,14 +553,16 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
       const int pos = p0 + c / QG;
       if (!(c < ppw * QG && pos < q_len)) continue;
       uint16_t* op = out + (int64_t)pos * os_t + (int64_t)(hk * QG + c % QG) * os_h;
+      // dims d_out .. 255 (zero-padded operands of a narrower head) are not written
       if constexpr (VT) {
 #pragma unroll
         for (int n = 0; n < 16; ++n)
-          op[16 * n + r16] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][n][i] * inv));
+          if (16 * n < d_out) op[16 * n + r16] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][n][i] * inv));
       } else {
 #pragma unroll
         for (int b = 0; b < 8; ++b)
-          *reinterpret_cast<uint32_t*>(op + 32 * b + 2 * r16) = __builtin_bit_cast(
+          if (32 * b < d_out)
+            *reinterpret_cast<uint32_t*>(op + 32 * b + 2 * r16) = __builtin_bit_cast(
               uint32_t, __builtin_convertvector((v2f){acc[cb][2 * b][i] * inv, acc[cb][2 * b + 1][i] * inv}, v2bf));
       }
     }
@@ -562,13 +575,18 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   const int64_t waves = (int64_t)a.n_tok * a.Hk + a.vt_pad * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
   if (waves == 0) return hipSuccess;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  // the tiled value layout is built for head dim 256 only
-  if (a.D != kHeadDim && (a.vt || a.vt_pad || a.job[0].to_vt || a.job[1].to_vt || a.job[2].to_vt))
+  // the tiled value layout is 256 dims wide: head dim 256, or 128 padded
+  if (a.pad && a.D != kHeadDim / 2) return hipErrorInvalidValue;
+  if (!a.pad && a.D != kHeadDim && (a.vt || a.vt_pad || a.job[0].to_vt || a.job[1].to_vt || a.job[2].to_vt))
     return hipErrorInvalidValue;
+  if (a.pad) {
+    hipLaunchKernelGGL((prefill_gather_kernel<128, true>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   switch (a.D) {
-    case 128: hipLaunchKernelGGL(prefill_gather_kernel<128>, grid, block, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(prefill_gather_kernel<256>, grid, block, 0, stream, a); break;
-    case 512: hipLaunchKernelGGL(prefill_gather_kernel<512>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((prefill_gather_kernel<128, false>), grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL((prefill_gather_kernel<256, false>), grid, block, 0, stream, a); break;
+    case 512: hipLaunchKernelGGL((prefill_gather_kernel<512, false>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -578,17 +596,18 @@ int prefill_positions_per_wg(int QG) { return QG <= kColsPerWg ? kColsPerWg / QG
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
   if (a.q_len == 0) return hipSuccess;
+  if (a.d_out != kHeadDim && a.d_out != kHeadDim / 2) return hipErrorInvalidValue;
   const int ppw = prefill_positions_per_wg(a.QG);
   const int n_ptiles = (a.q_len + ppw - 1) / ppw;
   const dim3 grid((unsigned)n_ptiles, (unsigned)a.Hk), block(64 * (8 / CB));
   if (a.vt_tiles > 0)
     hipLaunchKernelGGL(prefill_attn_kernel<true>, grid, block, 0, stream,
                        a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len,
-                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, a.vt_tiles);
+                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, a.vt_tiles, a.d_out);
   else
     hipLaunchKernelGGL(prefill_attn_kernel<false>, grid, block, 0, stream,
                        a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len,
-                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, (int64_t)0);
+                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, (int64_t)0, a.d_out);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@
  * (-1)**popcount(i & j) times one float64 scale, the nearest double to
  * 1/sqrt(D) (exactly 1/16 for D = 256).
  * Store, decode, uq_rotate and uq_dequant_kv take D in {128, 256, 512};
- * uq_prefill_attention and uq_continuation_prefill take D = 256.
+ * uq_continuation_prefill takes D in {128, 256}; uq_prefill_attention D = 256.
  */
 #ifndef UQ_H
 #define UQ_H
@@ -287,7 +287,8 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          void* stream);
 
 /* Workspace bytes of uq_continuation_prefill for chunks of up to q_len
- * tokens and sequences of up to max_seq_len tokens (0 on invalid shapes). */
+ * tokens and sequences of up to max_seq_len tokens, D in {128, 256} (the same
+ * for both: the operands are 256 wide); 0 on invalid shapes. */
 size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int Hq, int Hk, int D);
 
 /*
@@ -296,13 +297,17 @@ size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int H
  * attend (the steps of uq_dequant_kv, uq_rotate and uq_prefill_attention on
  * buffers in the workspace, the values kept there in 32-key tiles laid out
  * for the attention; two launches on `stream`).
- *   query:  (device) bf16 (q_len, Hq, 256) before rotation; key, value:
- *           (q_len, Hk, 256) of the chunk (key before rotation). 8-byte
+ *   D:      128 or 256 (UQ_EUNSUPPORTED otherwise). At 128 the operands
+ *           are built zero-padded to 256 elements in the workspace and the
+ *           head-dim-256 attention runs over them (the zeros add nothing to
+ *           any score; the output's 128 dims are written).
+ *   query:  (device) bf16 (q_len, Hq, D) before rotation; key, value:
+ *           (q_len, Hk, D) of the chunk (key before rotation). 8-byte
  *           aligned, strides non-negative multiples of 4 elements.
  *   kv_cache, block_row, num_blocks, block_size: as uq_dequant_kv, for the
- *           cached_len tokens already stored (block_row may be NULL when
- *           cached_len is 0).
- *   out:    (device) bf16 (q_len, Hq, 256), 16-byte aligned, strides
+ *           cached_len tokens already stored (a cache of head dim D, slots
+ *           of 17*D/16 bytes; block_row may be NULL when cached_len is 0).
+ *   out:    (device) bf16 (q_len, Hq, D), 16-byte aligned, strides
  *           multiples of 8.
  *   workspace: (device) 256-byte aligned, at least
  *           uq_continuation_prefill_workspace_bytes(q_len, cached_len + q_len,

@@ -208,6 +208,7 @@ def continuation_args(**kw):
     (dict(cached_len=-1), -1), (dict(block_row=None), -1), (dict(workspace=FAKE + 16), -1),
     (dict(ws_bytes=4096), -3), (dict(block_size=48), -2), (dict(Hq=17), -2),
     (dict(ost=4), -1), (dict(kst=2), -1), (dict(query=FAKE + 2), -1),
+    (dict(D=512), -2), (dict(D=64), -2),
 ])
 def test_continuation_prefill_rejects(libuq, kw, code):
     assert libuq.uq_continuation_prefill(*continuation_args(**kw)) == code
@@ -218,11 +219,20 @@ def test_continuation_prefill_workspace_bytes(libuq):
     f = libuq.uq_continuation_prefill_workspace_bytes
     assert f(8, 7, 16, 2, 256) == 0
     assert f(8, 100, 15, 2, 256) == 0
-    assert f(8, 100, 16, 2, 128) == 0
+    assert f(8, 100, 16, 2, 512) == 0
     n = f(8, 100, 16, 2, 256)
     # rotated queries, keys of the whole sequence, then values in tiles of 32 keys, as bf16
     assert n == 8 * 16 * 512 + 100 * 2 * 512 + 2 * 4 * 32 * 512
     assert f(8, 101, 16, 2, 256) > n
+    # head dim 128 builds the same 256-wide (zero-padded) operands
+    assert f(8, 100, 16, 2, 128) == n
+
+
+def test_continuation_prefill_head_dim_128_accepted(libuq):
+    """D = 128 passes every host check (q_len = 0 then returns before any HIP
+    call); uq_prefill_attention on caller operands still takes 256 only."""
+    assert libuq.uq_continuation_prefill(*continuation_args(D=128, q_len=0)) == 0
+    assert libuq.uq_prefill_attention(*prefill_attention_args(D=128)) == -2
 
 
 @pytest.mark.parametrize("mask", [0, 4, -1, 7])

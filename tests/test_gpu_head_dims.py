@@ -261,3 +261,36 @@ def test_dequant_bit_exact(d):
     k2, v2 = uq.dequant_kv(cache, bad, n)
     assert torch.all(k2[bs:2 * bs] == 0) and torch.all(v2[bs:2 * bs] == 0)
     assert torch.equal(k2[:bs], k[:bs]) and torch.equal(k2[2 * bs:], k[2 * bs:])
+
+
+@pytest.mark.parametrize("cached_len,q_len", [(0, 37), (100, 64), (333, 129)])
+@pytest.mark.parametrize("qg", [6, 8, 16])
+def test_continuation_prefill_d128(cached_len, q_len, qg):
+    """Continuation prefill at head dim 128 (the operands zero-padded to 256
+    for the attention) against the oracle, written into a strided output
+    whose extra columns must stay untouched."""
+    d, hk, bs = 128, 2, 16
+    say(f"prefill d=128 qg={qg} cached={cached_len} q_len={q_len}")
+    rng = np.random.default_rng(qg * 100 + cached_len + q_len)
+    nblk = max(1, -(-cached_len // bs))
+    row = rng.permutation(nblk + 3)[:nblk].astype(np.int32)
+    cache = torch.zeros((nblk + 3, bs, hk, slot(d)), dtype=torch.uint8, device=DEV)
+    ref = np.zeros(tuple(cache.shape), dtype=np.uint8)
+    if cached_len:
+        kb = bf16(rng.standard_normal((cached_len, hk, d)))
+        vb = bf16(rng.standard_t(4, (cached_len, hk, d)))
+        t = np.arange(cached_len)
+        slots = row[t // bs].astype(np.int64) * bs + t % bs
+        uq.store(kb.to(DEV), vb.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+        O.store(bits(kb), bits(vb), ref, slots)
+    q = bf16(rng.standard_normal((q_len, hk * qg, d)))
+    kc = bf16(rng.standard_normal((q_len, hk, d)))
+    vc = bf16(rng.standard_t(4, (q_len, hk, d)))
+    scale = 1 / np.sqrt(d)
+    big = torch.full((q_len, hk * qg, d + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = uq.continuation_prefill(q.to(DEV), kc.to(DEV), vc.to(DEV), cache, torch.from_numpy(row).to(DEV),
+                                  cached_len, scale, out=big[:, :, :d])
+    assert torch.isnan(big[:, :, d:]).all()
+    want = O.continuation_prefill(bits(q), bits(kc), bits(vc), ref, row, cached_len, scale)
+    check_close(to_np(out), want, f"prefill d=128 qg={qg} cached={cached_len} q_len={q_len}",
+                allow_output_rounding=True)
