@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--sinks", action="store_true",
                     help="add seeded per-head sink logits (uq_decode_ex)")
     ap.add_argument("--head-dim", type=int, default=256, choices=(128, 256, 512),
-                    help="head dim of the decode workloads (slot 17*D/16 bytes, scale 1/sqrt(D))")
+                    help="head dim of the workload (slot 17*D/16 bytes, scale 1/sqrt(D)); "
+                         "prefill takes 128 or 256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -269,15 +270,17 @@ def cpu_baseline(w, lay, seconds, wall_cap=150.0):
 
 
 # Continuation prefill: one sequence of the decode workload's shape (Hq 32,
-# Hk 4, D 256) holding 4096 cached tokens receives a 2048-token chunk.
-PREFILL = dict(cached=4096, q_len=2048, Hq=32, Hk=4, block_size=16, scale=1 / 16, seed=7)
+# Hk 4, D 256 unless --head-dim 128) holding 4096 cached tokens receives a
+# 2048-token chunk.
+PREFILL = dict(cached=4096, q_len=2048, Hq=32, Hk=4, block_size=16, seed=7)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def prefill_flops(cached, q_len, Hq):
+def prefill_flops(cached, q_len, Hq, D=256):
     """QK and PV multiply-adds over the visible (query, key) pairs:
-    4 * D * Hq * sum_i (cached + i + 1)."""
-    return 4 * 256 * Hq * (q_len * cached + q_len * (q_len + 1) // 2)
+    4 * D * Hq * sum_i (cached + i + 1) (at D = 128 the operands run
+    zero-padded to 256; only the 128-dim work counts)."""
+    return 4 * D * Hq * (q_len * cached + q_len * (q_len + 1) // 2)
 
 
 def time_events(fn, steps, warmup):
@@ -297,7 +300,7 @@ def time_events(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds):
+def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds, D=256):
     """The oracle, untuned, on sampled chunk positions (every key still
     dequantised and rotated), one BLAS thread."""
     import numpy as np
@@ -307,6 +310,7 @@ def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds):
     from oracle import uq_oracle as O
 
     qb, kb, vb = (inputs.bf16_bits(t.cpu()) for t in (q, kc, vc))
+    scale = 1.0 / math.sqrt(D)
     cache_np, row_np = cache.cpu().numpy(), row.cpu().numpy()
     rng = np.random.default_rng(0)
     done, flops, elapsed = 0, 0, 0.0
@@ -314,10 +318,10 @@ def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds):
         while elapsed < seconds and done < P["q_len"]:
             rows = rng.integers(0, P["q_len"], 4)
             t = time.perf_counter()
-            O.continuation_prefill(qb, kb, vb, cache_np, row_np, P["cached"], P["scale"], rows=rows)
+            O.continuation_prefill(qb, kb, vb, cache_np, row_np, P["cached"], scale, rows=rows)
             elapsed += time.perf_counter() - t
             done += len(rows)
-            flops += sum(4 * 256 * P["Hq"] * (P["cached"] + int(i) + 1) for i in rows)
+            flops += sum(4 * D * P["Hq"] * (P["cached"] + int(i) + 1) for i in rows)
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} chunk positions of this workload, each call dequantising the whole "
                       f"prefix and rotating the whole chunk, {elapsed:.1f} s"}
@@ -330,39 +334,44 @@ def prefill_main(args):
     import decode_attention_bit_amd as uq
 
     P = PREFILL
+    D = args.head_dim
+    if D not in (128, 256):
+        print(json.dumps({"error": f"continuation prefill runs at head dims 128 and 256, not {D}"}))
+        sys.exit(2)
+    scale = 1.0 / math.sqrt(D)
     dev = torch.device("cuda:0")
     g = torch.Generator(device="cpu").manual_seed(P["seed"])
     bs, Hk, Hq, cached, q_len = P["block_size"], P["Hk"], P["Hq"], P["cached"], P["q_len"]
     nblk = cached // bs
     log(f"setup prefill: {cached} cached + {q_len} chunk tokens")
-    cache = torch.zeros((nblk + 64, bs, Hk, 272), dtype=torch.uint8, device=dev)
+    cache = torch.zeros((nblk + 64, bs, Hk, D * 17 // 16), dtype=torch.uint8, device=dev)
     row = torch.randperm(nblk + 64, generator=g)[:nblk].to(torch.int32).to(dev)
     randn = lambda *shape: torch.randn(shape, generator=g).to(torch.bfloat16).to(dev)
-    k, v = randn(cached, Hk, 256), randn(cached, Hk, 256)
+    k, v = randn(cached, Hk, D), randn(cached, Hk, D)
     t = torch.arange(cached, device=dev)
     uq.store(k, v, cache, row[t // bs].long() * bs + t % bs)
-    q, kc, vc = randn(q_len, Hq, 256), randn(q_len, Hk, 256), randn(q_len, Hk, 256)
-    out = torch.empty((q_len, Hq, 256), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(uq.continuation_prefill_workspace_bytes(q_len, cached + q_len, Hq, Hk),
+    q, kc, vc = randn(q_len, Hq, D), randn(q_len, Hk, D), randn(q_len, Hk, D)
+    out = torch.empty((q_len, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(uq.continuation_prefill_workspace_bytes(q_len, cached + q_len, Hq, Hk, D),
                      dtype=torch.uint8, device=dev)
     steps = max(1, args.steps // 4)
     warmup = max(1, args.warmup // 4)
     log(f"timing {steps} calls")
-    call = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, P["scale"], out=out, workspace=ws)
+    call = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, scale, out=out, workspace=ws)
     ms = time_events(call, steps, warmup)
     # each launch of the call alone, on the workspace the whole call left
-    gather = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, P["scale"], out=out,
+    gather = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, scale, out=out,
                                              workspace=ws, stages=uq.PREFILL_GATHER)
-    attn = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, P["scale"], out=out,
+    attn = lambda: uq.continuation_prefill(q, kc, vc, cache, row, cached, scale, out=out,
                                            workspace=ws, stages=uq.PREFILL_ATTEND)
     gather_ms = time_events(gather, steps, warmup)
     attn_ms = time_events(attn, steps, warmup)
-    fl = prefill_flops(cached, q_len, Hq)
+    fl = prefill_flops(cached, q_len, Hq, D)
     tf = fl / (ms * 1e-3) / 1e12
     attn_tf = fl / (attn_ms * 1e-3) / 1e12
     res = {
         "metric": f"continuation prefill TFLOP/s (bf16 MFMA), {q_len}-token chunk after {cached} cached "
-                  f"tokens, GQA-8 D=256",
+                  f"tokens, GQA-8 D={D}",
         "value": round(tf, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -374,7 +383,7 @@ def prefill_main(args):
         "vs_baseline": None,
         "dtype": "bf16-mfma",
         "data": "synthetic",
-        "config": {"workload": f"prefill: cached_len={cached} q_len={q_len} Hq={Hq} Hk={Hk} D=256 "
+        "config": {"workload": f"prefill: cached_len={cached} q_len={q_len} Hq={Hq} Hk={Hk} D={D} "
                                f"block_size={bs} (step = one uq_continuation_prefill)",
                    "flops_per_step": fl},
         "tokens_per_s": round(q_len / (ms * 1e-3), 1),
@@ -386,7 +395,7 @@ def prefill_main(args):
     }
     if not args.no_cpu_baseline:
         log("cpu baseline")
-        res["cpu_baseline"] = prefill_cpu_baseline(P, q, kc, vc, cache, row, args.cpu_seconds)
+        res["cpu_baseline"] = prefill_cpu_baseline(P, q, kc, vc, cache, row, args.cpu_seconds, D)
     print(json.dumps(res), flush=True)
 
 
