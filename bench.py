@@ -278,8 +278,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 def prefill_flops(cached, q_len, Hq, D=256):
     """QK and PV multiply-adds over the visible (query, key) pairs:
-    4 * D * Hq * sum_i (cached + i + 1) (at D = 128 the operands run
-    zero-padded to 256; only the 128-dim work counts)."""
+    4 * D * Hq * sum_i (cached + i + 1)."""
     return 4 * D * Hq * (q_len * cached + q_len * (q_len + 1) // 2)
 
 

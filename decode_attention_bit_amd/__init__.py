@@ -15,11 +15,11 @@ Entry points mirror include/uq.h:
             query_row=None, sinks=None, sliding_window=0,
             out=None, workspace=None)               -> (B, Hq, D) bf16
 Store, decode, rotate and dequant_kv take head dims D in {128, 256, 512}
-(slot 17*D/16 bytes); continuation_prefill takes D in {128, 256} and
-prefill_attention D = 256.
+(slot 17*D/16 bytes); prefill_attention and continuation_prefill take
+D in {128, 256}.
   rotate(x, out=None)                               -> bf16(x H), same shape
   dequant_kv(kv_cache, block_row, n_tokens)         -> (K, V) (n_tokens, Hk, D) bf16
-  prefill_attention(q, k, v, scale, out=None)       -> (q_len, Hq, 256) bf16
+  prefill_attention(q, k, v, scale, out=None)       -> (q_len, Hq, D) bf16
   continuation_prefill(query, key, value, kv_cache, block_row, cached_len, scale,
                        out=None, workspace=None)    -> (q_len, Hq, D) bf16
 """
@@ -318,9 +318,9 @@ def dequant_kv(kv_cache: torch.Tensor, block_row: torch.Tensor, n_tokens: int,
 
 def prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
                       out: torch.Tensor | None = None) -> torch.Tensor:
-    """uq_prefill_attention: causal attention of (q_len, Hq, 256) bf16 queries
-    over (seq_len, Hk, 256) bf16 keys/values, query i at position
-    seq_len - q_len + i; returns (q_len, Hq, 256) bf16."""
+    """uq_prefill_attention: causal attention of (q_len, Hq, D) bf16 queries
+    over (seq_len, Hk, D) bf16 keys/values, D in {128, 256}, query i at
+    position seq_len - q_len + i; returns (q_len, Hq, D) bf16."""
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _bf16_3d(t, name)
     if k.shape != v.shape or k.stride() != v.stride():

@@ -222,14 +222,12 @@ int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_token
   return hip_status(uq::launch_gather(a, (hipStream_t)stream), "uq_dequant_kv launch");
 }
 
-// with128: head dim 128 is accepted beside 256
-static int check_attention_shape(const char* who, int q_len, int seq_len, int Hq, int Hk, int D, float scale,
-                                 bool with128) {
+static int check_attention_shape(const char* who, int q_len, int seq_len, int Hq, int Hk, int D, float scale) {
   if (q_len < 0 || seq_len < q_len || Hq < 1 || Hk < 1)
     return fail(UQ_EINVAL, "%s: q_len=%d seq_len=%d Hq=%d Hk=%d", who, q_len, seq_len, Hq, Hk);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(UQ_EINVAL, "%s: scale must be finite and > 0", who);
-  if (D != UQ_HEAD_DIM && !(with128 && D == UQ_HEAD_DIM / 2))
-    return fail(UQ_EUNSUPPORTED, "%s: head_dim %d unsupported (%s)", who, D, with128 ? "128, 256" : "only 256");
+  if (D != UQ_HEAD_DIM && D != UQ_HEAD_DIM / 2)
+    return fail(UQ_EUNSUPPORTED, "%s: head_dim %d unsupported (128, 256)", who, D);
   if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "%s: Hq=%d is not a multiple of Hk=%d", who, Hq, Hk);
   if (uq::prefill_positions_per_wg(Hq / Hk) < 1)
     return fail(UQ_EUNSUPPORTED, "%s: GQA group %d above 128", who, Hq / Hk);
@@ -242,7 +240,7 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int64_t q_stride_t, int64_t q_stride_h, int64_t kv_stride_t,
                          int64_t kv_stride_h, int64_t out_stride_t, int64_t out_stride_h,
                          void* stream) {
-  const int rc = check_attention_shape("uq_prefill_attention", q_len, seq_len, Hq, Hk, D, scale, false);
+  const int rc = check_attention_shape("uq_prefill_attention", q_len, seq_len, Hq, Hk, D, scale);
   if (rc != UQ_OK) return rc;
   if (q_len == 0) return ok();
   if (!q || !k || !v || !out) return fail(UQ_EINVAL, "uq_prefill_attention: null pointer argument");
@@ -253,37 +251,37 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return fail(UQ_EINVAL, "uq_prefill_attention: q, k, v and out must be 16-byte aligned");
   // key rows are staged 32 at a time through one buffer descriptor each
-  if (kv_stride_t < UQ_HEAD_DIM || kv_stride_t >= (1LL << 25))
-    return fail(UQ_EUNSUPPORTED, "uq_prefill_attention: kv_stride_t %lld outside [256, 2^25)", (long long)kv_stride_t);
+  if (kv_stride_t < D || kv_stride_t >= (1LL << 25))
+    return fail(UQ_EUNSUPPORTED, "uq_prefill_attention: kv_stride_t %lld outside [D, 2^25)", (long long)kv_stride_t);
   uq::PrefillAttnArgs a{q, k, v, out, q_stride_t, q_stride_h, kv_stride_t, kv_stride_h,
-                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale, 0, UQ_HEAD_DIM};
+                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale, 0, D};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_prefill_attention launch");
 }
 
 // Workspace of uq_continuation_prefill: rotated queries, keys of prefix +
 // chunk (token-major), then the values in the tiled layout of the attention
-// kernel (per KV head, ceil(seq_len / 32) tiles of 16 KB), each section
+// kernel (per KV head, ceil(seq_len / 32) tiles of 64 D bytes), each section
 // 256-byte aligned.
 struct PrefillLayout {
   size_t q_off, k_off, v_off, total;
   long long vt_tiles;
 };
 
-static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, int Hk) {
+static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, int Hk, int D) {
   auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   PrefillLayout l{};
   l.vt_tiles = (seq_len + 31) / 32;
   l.q_off = 0;
-  l.k_off = a256((size_t)q_len * Hq * UQ_HEAD_DIM * 2);
-  l.v_off = l.k_off + a256((size_t)seq_len * Hk * UQ_HEAD_DIM * 2);
-  l.total = l.v_off + (size_t)Hk * l.vt_tiles * 32 * UQ_HEAD_DIM * 2;
+  l.k_off = a256((size_t)q_len * Hq * D * 2);
+  l.v_off = l.k_off + a256((size_t)seq_len * Hk * D * 2);
+  l.total = l.v_off + (size_t)Hk * l.vt_tiles * 32 * D * 2;
   return l;
 }
 
 size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int Hq, int Hk, int D) {
   if (q_len < 0 || max_seq_len < q_len || Hq < 1 || Hk < 1 || Hq % Hk || (D != UQ_HEAD_DIM && D != UQ_HEAD_DIM / 2))
     return 0;
-  const size_t t = prefill_layout(q_len, max_seq_len, Hq, Hk).total;
+  const size_t t = prefill_layout(q_len, max_seq_len, Hq, Hk, D).total;
   return t > 0 ? t : 256;
 }
 
@@ -302,7 +300,7 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   if (cached_len < 0 || (long long)cached_len + q_len > 0x7FFFFFFFLL)
     return fail(UQ_EINVAL, "%s: cached_len=%d", who, cached_len);
   const int seq_len = cached_len + q_len;
-  int rc = check_attention_shape(who, q_len, seq_len, Hq, Hk, D, scale, true);
+  int rc = check_attention_shape(who, q_len, seq_len, Hq, Hk, D, scale);
   if (rc != UQ_OK) return rc;
   if (num_blocks < 1) return fail(UQ_EINVAL, "%s: num_blocks=%lld < 1", who, (long long)num_blocks);
   if (!pow2_in(block_size, 16, 256))
@@ -319,7 +317,7 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   if (!aligned(query, 8) || !aligned(key, 8) || !aligned(value, 8) || !aligned(kv_cache, 16) ||
       !aligned(block_row, 4) || !aligned(out, 16) || !aligned(workspace, 256))
     return fail(UQ_EINVAL, "%s: misaligned pointer (query/key/value 8 B, kv_cache/out 16 B, workspace 256 B)", who);
-  const PrefillLayout lay = prefill_layout(q_len, seq_len, Hq, Hk);
+  const PrefillLayout lay = prefill_layout(q_len, seq_len, Hq, Hk, D);
   if (workspace_bytes < lay.total)
     return fail(UQ_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, lay.total);
   const long long waves = (long long)(seq_len + 32) * Hk * 2 + (long long)q_len * Hq;
@@ -328,12 +326,11 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + lay.q_off);
   uint16_t* kf = reinterpret_cast<uint16_t*>(ws + lay.k_off);
   uint16_t* vf = reinterpret_cast<uint16_t*>(ws + lay.v_off);
-  const int64_t row = (int64_t)Hk * UQ_HEAD_DIM;          // token stride of the key/value buffers
+  const int64_t row = (int64_t)Hk * D;                   // token stride of the key/value buffers
   int log2_bs = 0;
   while ((1 << log2_bs) < block_size) ++log2_bs;
   uq::GatherArgs g{};
   g.D = D;
-  g.pad = D != UQ_HEAD_DIM;        // head dim 128: zero-padded 256-wide operands
   g.cache = kv_cache;
   g.block_row = block_row;
   g.n_tok = cached_len;
@@ -343,14 +340,14 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   g.kout = kf;
   g.vout = nullptr;
   g.os_t = row;
-  g.os_h = UQ_HEAD_DIM;
+  g.os_h = D;
   g.vt = vf;
   g.vt_tiles = lay.vt_tiles;
   g.vt_pad0 = seq_len;
   g.vt_pad = lay.vt_tiles * 32 - seq_len;
-  g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM,
+  g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * D, D,
                         (int64_t)q_len * Hq, Hq, 1, 0, 0};
-  g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, UQ_HEAD_DIM,
+  g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, D,
                         (int64_t)q_len * Hk, Hk, 1, 0, 0};
   g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, nullptr, 0, 0, (int64_t)q_len * Hk, Hk, 0, 1,
                         (int64_t)cached_len};
@@ -359,7 +356,7 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
     if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");
   }
   if (!(stage_mask & UQ_PREFILL_ATTEND)) return ok();
-  uq::PrefillAttnArgs a{qr, kf, vf, out, (int64_t)Hq * UQ_HEAD_DIM, UQ_HEAD_DIM, row, UQ_HEAD_DIM,
+  uq::PrefillAttnArgs a{qr, kf, vf, out, (int64_t)Hq * D, D, row, D,
                         out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale, lay.vt_tiles, D};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_continuation_prefill attention launch");
 }

@@ -64,12 +64,11 @@ struct VecJob {
 };
 
 // Tiled value layout of the continuation prefill (vt != null): per KV head,
-// tiles of 32 keys, each 256 dim rows of 64 bytes; row d of tile j holds the
+// tiles of 32 keys, each D dim rows of 64 bytes; row d of tile j holds the
 // 32 keys in the order the attention's P operand uses, its 16-byte chunks
 // permuted by chunk ^ ((d >> 2) & 3).
 struct GatherArgs {
-  int D;                     // head dim: 128, 256 or 512 (vt and to_vt: 256, or 128 with pad)
-  int pad;                   // D = 128 only: write 256-wide rows, elements 128 .. 255 zero
+  int D;                     // head dim: 128, 256 or 512 (vt and to_vt: 128 and 256)
   // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])
   const uint8_t* cache;
   const int32_t* block_row;
@@ -87,15 +86,15 @@ struct GatherArgs {
 };
 
 struct PrefillAttnArgs {
-  const uint16_t* q;         // (q_len, Hq, 256) rotated queries, bf16
-  const uint16_t* k;         // (cached_len + q_len, Hk, 256) rotated keys, bf16
+  const uint16_t* q;         // (q_len, Hq, D) rotated queries, bf16
+  const uint16_t* k;         // (cached_len + q_len, Hk, D) rotated keys, bf16
   const uint16_t* v;         // same shape, values
-  uint16_t* out;             // (q_len, Hq, 256)
+  uint16_t* out;             // (q_len, Hq, D)
   int64_t qs_t, qs_h, kvs_t, kvs_h, os_t, os_h;
   int q_len, cached_len, Hk, QG;
   float scale;
   int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head
-  int d_out;                 // output dims written: 256, or 128 for zero-padded 128-dim operands
+  int D;                     // head dim: 128 or 256
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,

@@ -52,12 +52,14 @@ __device__ __forceinline__ uint32_t e2m1_bf16_bits(uint32_t code, int e) {
   return sign | ((2u + half) << (E + 132));                 // value / 2**-133
 }
 
-// Element offset of (key, head h, dim) in the tiled value layout: key
-// 16kb + 4g + i of a tile sits at slot s = i + 4kb of chunk g of its dim row.
+// Element offset of (key, head h, dim) in the tiled value layout of head
+// dim DV: key 16kb + 4g + i of a tile sits at slot s = i + 4kb of chunk g of
+// its dim row.
+template <int DV>
 __device__ __forceinline__ int64_t vt_offset(int64_t key, int h, int dim, int64_t tiles) {
   const int kk = (int)(key & 31);
   const int g = (kk & 15) >> 2, s = (kk & 3) + ((kk >> 4) << 2);
-  return (((int64_t)h * tiles + (key >> 5)) * kHeadDim + dim) * 32 + 8 * (g ^ ((dim >> 2) & 3)) + s;
+  return (((int64_t)h * tiles + (key >> 5)) * DV + dim) * 32 + 8 * (g ^ ((dim >> 2) & 3)) + s;
 }
 
 // ---------------------------------------------------------------------------
@@ -70,15 +72,12 @@ __device__ __forceinline__ int64_t vt_offset(int64_t key, int h, int dim, int64_
 // 32-element block).
 // Rotate: lane l holds x[D/64 l .. D/64 l + D/64 - 1] through the float64
 // butterfly, then the float64 nearest 1/sqrt(D) and one rounding to bf16.
-// PAD (D = 128 only): the rows go to buffers 256 elements wide, the
-// attention's operands, with elements D .. 255 written as zeros; the tiled
-// value layout (vt, vt_pad, to_vt) is 256 dims wide and exists with PAD or
-// at D = 256.
+// The tiled value layout (vt, vt_pad, to_vt) exists at D = 128 and 256,
+// the head dims of the attention.
 // ---------------------------------------------------------------------------
-template <int D, bool PAD>
+template <int D>
 __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
-  static_assert(!PAD || 2 * D == kHeadDim, "padding doubles a 128-element row");
-  constexpr bool TILED = PAD || D == kHeadDim;
+  constexpr bool TILED = D <= kHeadDim;
   using F = Fmt<D>;
   constexpr int EPL = D / 32;              // dequantised elements per lane
   constexpr int NCB = EPL / 2;             // code bytes per lane: 2, 4 or 8
@@ -117,17 +116,14 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
     if constexpr (TILED) {
       if (is_v && a.vt) {
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          a.vt[vt_offset(t, h, EPL * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
-          if constexpr (PAD) a.vt[vt_offset(t, h, D + EPL * l + i, a.vt_tiles)] = 0;
-        }
+        for (int i = 0; i < EPL; ++i)
+          a.vt[vt_offset<D>(t, h, EPL * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
         return;
       }
     }
     uint16_t* dst = (is_v ? a.vout : a.kout) + t * a.os_t + (int64_t)h * a.os_h + EPL * l;
     if constexpr (NCB == 2) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
-      if constexpr (PAD) *reinterpret_cast<uint2*>(dst + D) = make_uint2(0u, 0u);
     } else {
 #pragma unroll
       for (int i = 0; i < NCB / 4; ++i)
@@ -142,7 +138,7 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
       const int64_t key = a.vt_pad0 + w / a.Hk;
       const int h = (int)(w % a.Hk);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.vt[vt_offset(key, h, 4 * lane + i, a.vt_tiles)] = 0;
+      for (int i = 0; i < E; ++i) a.vt[vt_offset<D>(key, h, E * lane + i, a.vt_tiles)] = 0;
     }
     return;
   }
@@ -185,17 +181,14 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
     if constexpr (TILED) {
       if (jb.to_vt) {
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-          a.vt[vt_offset(jb.vt_key0 + t, h, E * lane + i, a.vt_tiles)] = (uint16_t)(r[i >> 1] >> (16 * (i & 1)));
-          if constexpr (PAD) a.vt[vt_offset(jb.vt_key0 + t, h, D + E * lane + i, a.vt_tiles)] = 0;
-        }
+        for (int i = 0; i < E; ++i)
+          a.vt[vt_offset<D>(jb.vt_key0 + t, h, E * lane + i, a.vt_tiles)] = (uint16_t)(r[i >> 1] >> (16 * (i & 1)));
         return;
       }
     }
     uint16_t* dp = jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + E * lane;
     if constexpr (E == 2) {
       *reinterpret_cast<uint32_t*>(dp) = r[0];
-      if constexpr (PAD) *reinterpret_cast<uint32_t*>(dp + D) = 0u;
     } else {
 #pragma unroll
       for (int i = 0; i < E / 4; ++i) *reinterpret_cast<uint2*>(dp + 4 * i) = make_uint2(r[2 * i], r[2 * i + 1]);
@@ -232,13 +225,29 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
 // raised when a tile exceeds it by more than 8 (weights stay <= 2^8 in bf16);
 // the denominator sums the same bf16 weights the product uses.
 // ---------------------------------------------------------------------------
+// Matrix-core and buffer builtins behind plain functions: the attention
+// kernel is a template over the head dim, and a builtin call whose operands
+// depend on a template parameter keeps the host pass from emitting the
+// kernel's launch stub.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int nrec) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, nrec, 0x00020000);
+}
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+
 constexpr int kKeyTile = 32;
-constexpr int kRowBytes = 2 * kHeadDim;
-constexpr int kTileU4 = kKeyTile * kRowBytes / 16;      // 1024 chunks of 16 bytes
 constexpr int kColsPerWg = 128;
 constexpr int kStages = 4;
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt on vector memory only (gfx9 encoding; expcnt and lgkmcnt left free)
 #define UQP_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
@@ -274,12 +283,18 @@ __device__ __forceinline__ float rowgroup_max(float x) {
 #endif
 constexpr int CB = UQ_PREFILL_CB;           // 16-column blocks per wave: 1 or 2
 
-template <bool VT>
+// DV: head dim, 256 or 128 (rows of 2 DV bytes, NCH chunks of 16 bytes; one
+// 1 KB load moves RPL rows).
+template <bool VT, int DV>
 __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
     int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2,
-    int64_t vt_tiles, int d_out) {
+    int64_t vt_tiles) {
+  static_assert(DV == 128 || DV == 256, "head dim");
+  constexpr int kRowBytes = 2 * DV, NCH = kRowBytes / 16, RPL = 64 / NCH;
+  constexpr int kTileU4 = kKeyTile * kRowBytes / 16;      // 16-byte chunks per tile
+  constexpr int NJ = DV / 32, NACC = DV / 16;              // query registers, accumulators
   // one array per stage and operand, so that the compiler can tell the slot
   // being read from the slots being filled
   __shared__ uint4 kr0[kTileU4], kr1[kTileU4], kr2[kTileU4], kr3[kTileU4];
@@ -287,7 +302,8 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
 
   // CB column blocks of 16 per wave, 128 / (16 CB) waves; each wave moves
   // ROWS of the 32 rows of every K and V tile, NDMA loads of 1 KB each
-  constexpr int WAVES = 8 / CB, ROWS = kKeyTile / WAVES, NDMA = 16 / WAVES;
+  constexpr int WAVES = 8 / CB, ROWS = kKeyTile / WAVES, NDMA = ROWS / RPL;
+  static_assert(NDMA * RPL == ROWS && NDMA * WAVES * 1024 == kKeyTile * kRowBytes, "tile loads");
   const int n_ptiles = (q_len + ppw - 1) / ppw;
   const int p0 = (n_ptiles - 1 - (int)blockIdx.x) * ppw;    // latest positions (most keys) first
   const int hk = blockIdx.y;
@@ -309,26 +325,26 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
   }
   // the query first, so that waiting for it never waits for a tile; the
   // addresses stay inside the tensor even for columns past the chunk
-  v8bf qb[CB][8];
+  v8bf qb[CB][NJ];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int pos = cval[cb] ? cpos[cb] : 0;
     const int head = cval[cb] ? chead[cb] : 0;
     const uint16_t* qp = q + (int64_t)pos * qs_t + (int64_t)head * qs_h + 8 * g;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (cval[cb]) x = ld16(qp + 32 * j);
       qb[cb][j] = __builtin_bit_cast(v8bf, x);
     }
   }
 
-  // Load i of this wave moves rows ROWS*w + 2i + l/32 of the tile, LDS chunk l%32.
+  // Load i of this wave moves rows ROWS*w + RPL i + l/NCH of the tile, LDS chunk l%NCH.
   const uint32_t row_bytes = (uint32_t)(kvs_t * 2);
   uint32_t koff[NDMA], voff[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int r = ROWS * wave + 2 * i + (lane >> 5), c = lane & 31;
+    const int r = ROWS * wave + RPL * i + lane / NCH, c = lane % NCH;
     koff[i] = r * row_bytes + 16 * (c ^ (r & 15));
     voff[i] = VT ? 1024 * (NDMA * wave + i) + 16 * lane : r * row_bytes + 16 * (c ^ (((r >> 2) & 3) << 2));
   }
@@ -339,24 +355,23 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
     // the descriptors end at the last key the workgroup needs: rows past it land as zeros
     const int nrec = (nv - 1) * (int)row_bytes + kRowBytes;
     const int64_t base = (int64_t)key0 * kvs_t + (int64_t)hk * kvs_h;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((void*)(k + base), nrec);
     const __amdgpu_buffer_rsrc_t rv =
-        VT ? __builtin_amdgcn_make_buffer_rsrc((void*)(v + ((int64_t)hk * vt_tiles + t) * (kKeyTile * kHeadDim)),
-                                               (short)0, kKeyTile * kRowBytes, 0x00020000)
-           : __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, nrec, 0x00020000);
+        VT ? buffer_rsrc((void*)(v + ((int64_t)hk * vt_tiles + t) * (kKeyTile * DV)), kKeyTile * kRowBytes)
+           : buffer_rsrc((void*)(v + base), nrec);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(ks + 64 * (NDMA * wave + i)), 16, koff[i], 0, 0, 0);
+      load_lds16(rk, ks + 64 * (NDMA * wave + i), koff[i]);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vs + 64 * (NDMA * wave + i)), 16, voff[i], 0, 0, 0);
+      load_lds16(rv, vs + 64 * (NDMA * wave + i), voff[i]);
   };
 
-  v4f acc[CB][16];
+  v4f acc[CB][NACC];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[cb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NACC; ++j) acc[cb][j] = (v4f){0.f, 0.f, 0.f, 0.f};
   v4f lsum[CB];                                            // row sums of the weights
   float m_ref[CB];
 #pragma unroll
@@ -378,7 +393,7 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) r.s[kb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < DV / 128; ++h) {
       v8bf ka[2][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
-            r.s[kb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][j], qb[cb][4 * h + j], r.s[kb][cb], 0, 0, 0);
+            r.s[kb][cb] = mfma_bf16(ka[kb][j], qb[cb][4 * h + j], r.s[kb][cb]);
     }
     return r;
   };
@@ -446,11 +461,11 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) fsel[i] = r16 == 4 * g + i ? f : 0.f;
 #pragma unroll
-        for (int j = 0; j < 17; ++j) {
-          v4f& a = j < 16 ? acc[cb][j] : lsum[cb];
+        for (int j = 0; j < NACC + 1; ++j) {
+          v4f& a = j < NACC ? acc[cb][j] : lsum[cb];
           v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_mfma_f32_16x16x4f32(fsel[i], a[i], d, 0, 0, 0);
+          for (int i = 0; i < 4; ++i) d = mfma_f32x4(fsel[i], a[i], d);
           a = d;
         }
         m_ref[cb] = m_new;
@@ -470,22 +485,22 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
         pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pa, pc}, v2bf));
       }
       pb[cb] = __builtin_bit_cast(v8bf, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      lsum[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ones, lsum[cb], 0, 0, 0);
+      lsum[cb] = mfma_bf16(pb[cb], ones, lsum[cb]);
     }
 
     if constexpr (VT) {
 #pragma unroll
-      for (int n = 0; n < 16; ++n) {
+      for (int n = 0; n < NACC; ++n) {
         const int dim = 16 * n + r16;
         const v8bf vb = __builtin_bit_cast(v8bf, ld16(vb_ + dim * 64 + 16 * (g ^ ((r16 >> 2) & 3))));
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          acc[cb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], vb, acc[cb][n], 0, 0, 0);
+          acc[cb][n] = mfma_bf16(pb[cb], vb, acc[cb][n]);
       }
       return;
     }
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < NJ; ++b) {
       uint32_t w[8];
 #pragma unroll
       for (int s_ = 0; s_ < 8; ++s_) {
@@ -504,8 +519,8 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
       const v8bf ae = __builtin_bit_cast(v8bf, ev), ao = __builtin_bit_cast(v8bf, od);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        acc[cb][2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ae, acc[cb][2 * b], 0, 0, 0);
-        acc[cb][2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb[cb], ao, acc[cb][2 * b + 1], 0, 0, 0);
+        acc[cb][2 * b] = mfma_bf16(pb[cb], ae, acc[cb][2 * b]);
+        acc[cb][2 * b + 1] = mfma_bf16(pb[cb], ao, acc[cb][2 * b + 1]);
       }
     }
   };
@@ -553,16 +568,14 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
       const int pos = p0 + c / QG;
       if (!(c < ppw * QG && pos < q_len)) continue;
       uint16_t* op = out + (int64_t)pos * os_t + (int64_t)(hk * QG + c % QG) * os_h;
-      // dims d_out .. 255 (zero-padded operands of a narrower head) are not written
       if constexpr (VT) {
 #pragma unroll
-        for (int n = 0; n < 16; ++n)
-          if (16 * n < d_out) op[16 * n + r16] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][n][i] * inv));
+        for (int n = 0; n < NACC; ++n)
+          op[16 * n + r16] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][n][i] * inv));
       } else {
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
-          if (32 * b < d_out)
-            *reinterpret_cast<uint32_t*>(op + 32 * b + 2 * r16) = __builtin_bit_cast(
+        for (int b = 0; b < NJ; ++b)
+          *reinterpret_cast<uint32_t*>(op + 32 * b + 2 * r16) = __builtin_bit_cast(
               uint32_t, __builtin_convertvector((v2f){acc[cb][2 * b][i] * inv, acc[cb][2 * b + 1][i] * inv}, v2bf));
       }
     }
@@ -575,18 +588,13 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   const int64_t waves = (int64_t)a.n_tok * a.Hk + a.vt_pad * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
   if (waves == 0) return hipSuccess;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  // the tiled value layout is 256 dims wide: head dim 256, or 128 padded
-  if (a.pad && a.D != kHeadDim / 2) return hipErrorInvalidValue;
-  if (!a.pad && a.D != kHeadDim && (a.vt || a.vt_pad || a.job[0].to_vt || a.job[1].to_vt || a.job[2].to_vt))
+  // the tiled value layout exists at head dims 128 and 256
+  if (a.D > kHeadDim && (a.vt || a.vt_pad || a.job[0].to_vt || a.job[1].to_vt || a.job[2].to_vt))
     return hipErrorInvalidValue;
-  if (a.pad) {
-    hipLaunchKernelGGL((prefill_gather_kernel<128, true>), grid, block, 0, stream, a);
-    return hipGetLastError();
-  }
   switch (a.D) {
-    case 128: hipLaunchKernelGGL((prefill_gather_kernel<128, false>), grid, block, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL((prefill_gather_kernel<256, false>), grid, block, 0, stream, a); break;
-    case 512: hipLaunchKernelGGL((prefill_gather_kernel<512, false>), grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(prefill_gather_kernel<128>, grid, block, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(prefill_gather_kernel<256>, grid, block, 0, stream, a); break;
+    case 512: hipLaunchKernelGGL(prefill_gather_kernel<512>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -596,18 +604,21 @@ int prefill_positions_per_wg(int QG) { return QG <= kColsPerWg ? kColsPerWg / QG
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
   if (a.q_len == 0) return hipSuccess;
-  if (a.d_out != kHeadDim && a.d_out != kHeadDim / 2) return hipErrorInvalidValue;
+  if (a.D != kHeadDim && a.D != kHeadDim / 2) return hipErrorInvalidValue;
   const int ppw = prefill_positions_per_wg(a.QG);
   const int n_ptiles = (a.q_len + ppw - 1) / ppw;
   const dim3 grid((unsigned)n_ptiles, (unsigned)a.Hk), block(64 * (8 / CB));
-  if (a.vt_tiles > 0)
-    hipLaunchKernelGGL(prefill_attn_kernel<true>, grid, block, 0, stream,
-                       a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len,
-                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, a.vt_tiles, a.d_out);
-  else
-    hipLaunchKernelGGL(prefill_attn_kernel<false>, grid, block, 0, stream,
-                       a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len,
-                       a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f, (int64_t)0, a.d_out);
+  const float sl2 = a.scale * 1.4426950408889634f;
+#define UQP_LAUNCH(VTV, DVV, TILES)                                                                      \
+  hipLaunchKernelGGL((prefill_attn_kernel<VTV, DVV>), grid, block, 0, stream, a.q, a.qs_t, a.qs_h, a.k, \
+                     a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len, a.cached_len, a.QG, ppw, sl2, \
+                     (int64_t)(TILES))
+  if (a.vt_tiles > 0) {
+    if (a.D == kHeadDim) UQP_LAUNCH(true, 256, a.vt_tiles); else UQP_LAUNCH(true, 128, a.vt_tiles);
+  } else {
+    if (a.D == kHeadDim) UQP_LAUNCH(false, 256, 0); else UQP_LAUNCH(false, 128, 0);
+  }
+#undef UQP_LAUNCH
   return hipGetLastError();
 }
 

@@ -186,7 +186,7 @@ def prefill_attention_args(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q_len=-1), -1), (dict(seq_len=7), -1), (dict(scale=0.0), -1),
-    (dict(scale=float("inf")), -1), (dict(D=128), -2), (dict(Hq=15), -2),
+    (dict(scale=float("inf")), -1), (dict(D=512), -2), (dict(D=64), -2), (dict(Hq=15), -2),
     (dict(Hq=258, Hk=2), -2), (dict(v=None), -1), (dict(kvst=508), -1), (dict(out=FAKE + 8), -1),
     (dict(kvst=248), -2), (dict(kvst=1 << 25), -2),
 ])
@@ -224,15 +224,16 @@ def test_continuation_prefill_workspace_bytes(libuq):
     # rotated queries, keys of the whole sequence, then values in tiles of 32 keys, as bf16
     assert n == 8 * 16 * 512 + 100 * 2 * 512 + 2 * 4 * 32 * 512
     assert f(8, 101, 16, 2, 256) > n
-    # head dim 128 builds the same 256-wide (zero-padded) operands
-    assert f(8, 100, 16, 2, 128) == n
+    # head dim 128: the same sections with 128-element rows
+    assert f(8, 100, 16, 2, 128) == 8 * 16 * 256 + 100 * 2 * 256 + 2 * 4 * 32 * 256
 
 
 def test_continuation_prefill_head_dim_128_accepted(libuq):
-    """D = 128 passes every host check (q_len = 0 then returns before any HIP
-    call); uq_prefill_attention on caller operands still takes 256 only."""
+    """D = 128 passes every host check of both attention calls (q_len = 0
+    then returns before any HIP call); D = 512 does not."""
     assert libuq.uq_continuation_prefill(*continuation_args(D=128, q_len=0)) == 0
-    assert libuq.uq_prefill_attention(*prefill_attention_args(D=128)) == -2
+    assert libuq.uq_prefill_attention(*prefill_attention_args(D=128, q_len=0, kvst=128, kvsh=128)) == 0
+    assert libuq.uq_prefill_attention(*prefill_attention_args(D=512, q_len=0)) == -2
 
 
 @pytest.mark.parametrize("mask", [0, 4, -1, 7])
