@@ -169,8 +169,14 @@ def _workspace(device, nbytes: int) -> torch.Tensor:
     """Cached workspace per (device, current stream), grown when a bigger one
     is needed. Calls on one stream run in order, so they can share it; calls
     on different streams get different buffers, and a replaced buffer is
-    freed on the stream that used it. Code captured into a graph should pass
-    its own workspace, so that replays do not share it with eager calls."""
+    freed on the stream that used it. A call captured into a graph must pass
+    its own workspace: replays would otherwise share this buffer with eager
+    calls and with other graphs, and a later call that grows it would free
+    memory a graph still writes on replay."""
+    if torch.cuda.is_current_stream_capturing():
+        raise ValueError("a call captured into a graph must pass its own workspace (workspace=...): "
+                         "the cached workspace is shared with eager calls and can be replaced while "
+                         "the graph still uses it")
     key = (str(torch.device(device)), _stream(device))
     ws = _WS_POOL.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -13,6 +13,7 @@ namespace uq {
 namespace {
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -224,9 +225,12 @@ __device__ __forceinline__ void read_tile(Tile<D>& T, const uint4* __restrict__ 
 
 // Byte M of each token's 8 V-code bytes holds d = 16*(l%16) + 2M (low nibble)
 // and 2M + 1 (high nibble). Convert them for the lane's 4 tokens, regroup the
-// bf16 halves by d, and accumulate two MFMAs (d even / odd).
+// bf16 halves by d, and accumulate two MFMAs (d even / odd). Each MFMA runs
+// over k = 32: the lane's 4 tokens twice, against the high and the low bf16
+// parts of their weights (pb), so a weight enters the product with 16
+// significant bits, not 8.
 template <int D, int M>
-__device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4], const v4s& pb,
+__device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4], const v8bf& pb,
                                         v4f acc[D / 16]) {
   uint32_t w[4];
 #pragma unroll
@@ -239,10 +243,10 @@ __device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4],
   const uint32_t e1 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
   const uint32_t o0 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
   const uint32_t o1 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-  const v4s ae = __builtin_bit_cast(v4s, make_uint2(e0, e1));
-  const v4s ao = __builtin_bit_cast(v4s, make_uint2(o0, o1));
-  acc[2 * M] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ae, pb, acc[2 * M], 0, 0, 0);
-  acc[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ao, pb, acc[2 * M + 1], 0, 0, 0);
+  const v8bf ae = __builtin_bit_cast(v8bf, make_uint4(e0, e1, e0, e1));
+  const v8bf ao = __builtin_bit_cast(v8bf, make_uint4(o0, o1, o0, o1));
+  acc[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, pb, acc[2 * M], 0, 0, 0);
+  acc[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, pb, acc[2 * M + 1], 0, 0, 0);
 }
 
 // Maximum over the four 16-lane row groups (lanes l, l^16, l^32, l^48), with
@@ -286,13 +290,21 @@ __device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], flo
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
-  const uint32_t p01 = pack_bf16(p[0], p[1]);
-  const uint32_t p23 = pack_bf16(p[2], p[3]);
-  // the denominator sums the same bf16 weights the product uses, so a
+  // Each weight as the sum of two bf16 values: hi = bf16(p) and
+  // lo = bf16(p - hi) (p - hi is exact in float32), within 2^-17 of p. A
+  // single bf16 weight (2^-9) put up to 2^-9 |v - o| into the output where a
+  // few tokens dominate.
+  const uint32_t h01 = pack_bf16(p[0], p[1]);
+  const uint32_t h23 = pack_bf16(p[2], p[3]);
+  const float q0 = __uint_as_float(h01 << 16), q1 = __uint_as_float(h01 & 0xFFFF0000u);
+  const float q2 = __uint_as_float(h23 << 16), q3 = __uint_as_float(h23 & 0xFFFF0000u);
+  const uint32_t l01 = pack_bf16(p[0] - q0, p[1] - q1);
+  const uint32_t l23 = pack_bf16(p[2] - q2, p[3] - q3);
+  // the denominator sums the weights the product uses (hi + lo), so a
   // dominant token passes through with weight exactly 1
-  l_part += (__uint_as_float(p01 << 16) + __uint_as_float(p01 & 0xFFFF0000u)) +
-            (__uint_as_float(p23 << 16) + __uint_as_float(p23 & 0xFFFF0000u));
-  const v4s pb = __builtin_bit_cast(v4s, make_uint2(p01, p23));
+  l_part += ((q0 + __uint_as_float(l01 << 16)) + (q1 + __uint_as_float(l01 & 0xFFFF0000u))) +
+            ((q2 + __uint_as_float(l23 << 16)) + (q3 + __uint_as_float(l23 & 0xFFFF0000u)));
+  const v8bf pb = __builtin_bit_cast(v8bf, make_uint4(h01, h23, l01, l23));
   float vscale[4];
   const int vsh = 8 * (((D * n16) / 512) & 3);
 #pragma unroll

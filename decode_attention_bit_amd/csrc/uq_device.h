@@ -6,9 +6,7 @@
 
 namespace uq {
 
-constexpr int kHeadDim = 256;
-constexpr int kSlotBytes = 272;
-constexpr int kKCodeOff = 0, kVCodeOff = 128, kKScaleOff = 256, kVScaleOff = 264;
+constexpr int kHeadDim = 256;   // the decode path's head dim (128 and 512 are templates too)
 constexpr int kTile = 16;        // tokens per decode tile
 
 // Slot format for head dim D (128, 256 or 512): D/2 bytes of K codes, D/2 of
@@ -91,7 +89,8 @@ __device__ __forceinline__ double xor_lane(double v, int m, int lane) {
 // holds x[4l .. 4l+3] in v[0..3]. Index bits 0-1 live inside a lane, bits 2-7
 // are lane bits 0-5. Each stage maps (a, b) -> (a + b, a - b). In float64 the
 // result is exact whenever every +-sum of the inputs fits 53 bits, which
-// holds for bf16 inputs whose non-zero magnitudes span at most 36 binades.
+// holds for bf16 inputs whose non-zero magnitudes span at most 45 - log2(D)
+// binades (37 at D = 256).
 // REG: lane exchanges in registers (xor_lane), which shortens a wave's
 // latency (the query prologue: 2.81 -> 2.68 us); otherwise through the LDS
 // pipe (__shfl_xor), which runs beside the VALU and keeps the store's

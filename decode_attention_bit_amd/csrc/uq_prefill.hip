@@ -222,8 +222,9 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
 //     for the even dims (col r -> dim 32b + 2r) and one for the odd ones.
 //     Rows of O are query columns, so a rescale is diag(f) O (see below).
 // Online softmax in the log2 domain with a reference maximum that is only
-// raised when a tile exceeds it by more than 8 (weights stay <= 2^8 in bf16);
-// the denominator sums the same bf16 weights the product uses.
+// raised when a tile exceeds it by more than 8 (weights stay <= 2^8); each
+// weight enters P.V as a high and a low bf16 part (two MFMAs), and the
+// denominator sums the same parts.
 // ---------------------------------------------------------------------------
 // Matrix-core and buffer builtins behind plain functions: the attention
 // kernel is a template over the head dim, and a builtin call whose operands
@@ -471,21 +472,29 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
         m_ref[cb] = m_new;
       }
     }
-    // weights p = 2^(s * scale_log2 - m_ref) in bf16; their row sums come
-    // from one more MFMA against ones, so they are the sums of exactly the
-    // bf16 weights the product uses and land in O's row layout
-    v8bf pb[CB];
+    // weights p = 2^(s * scale_log2 - m_ref), each as two bf16 parts,
+    // hi = bf16(p) and lo = bf16(p - hi) (p - hi is exact in float32), so a
+    // weight enters the product with 16 significant bits (a single bf16
+    // weight put up to 2^-9 |v - o| into the output where a few keys
+    // dominate). Their row sums come from MFMAs against ones, so they are
+    // the sums of exactly the weights the product uses and land in O's row
+    // layout.
+    v8bf pb[CB], pl[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      uint32_t pw[4];
+      uint32_t pw[4], lw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[cb][2 * i], scale_log2, -m_ref[cb]));
         const float pc = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[cb][2 * i + 1], scale_log2, -m_ref[cb]));
         pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pa, pc}, v2bf));
+        const float ha = __uint_as_float(pw[i] << 16), hc = __uint_as_float(pw[i] & 0xFFFF0000u);
+        lw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pa - ha, pc - hc}, v2bf));
       }
       pb[cb] = __builtin_bit_cast(v8bf, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      pl[cb] = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       lsum[cb] = mfma_bf16(pb[cb], ones, lsum[cb]);
+      lsum[cb] = mfma_bf16(pl[cb], ones, lsum[cb]);
     }
 
     if constexpr (VT) {
@@ -494,8 +503,10 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
         const int dim = 16 * n + r16;
         const v8bf vb = __builtin_bit_cast(v8bf, ld16(vb_ + dim * 64 + 16 * (g ^ ((r16 >> 2) & 3))));
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb) {
           acc[cb][n] = mfma_bf16(pb[cb], vb, acc[cb][n]);
+          acc[cb][n] = mfma_bf16(pl[cb], vb, acc[cb][n]);
+        }
       }
       return;
     }
@@ -520,7 +531,9 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         acc[cb][2 * b] = mfma_bf16(pb[cb], ae, acc[cb][2 * b]);
+        acc[cb][2 * b] = mfma_bf16(pl[cb], ae, acc[cb][2 * b]);
         acc[cb][2 * b + 1] = mfma_bf16(pb[cb], ao, acc[cb][2 * b + 1]);
+        acc[cb][2 * b + 1] = mfma_bf16(pl[cb], ao, acc[cb][2 * b + 1]);
       }
     }
   };

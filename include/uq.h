@@ -91,7 +91,7 @@ int uq_build_hadamard(int D, float* H, void* stream);
  *   D in {128, 256, 512}, slot_size 17*D/16, block_size a power of two in
  *   [16, 256]. N == 0 is a no-op.
  * Exactness: the rotation is exact when the non-zero magnitudes of a key
- * vector span at most 44 - log2(D) binades (36 for D = 256) (always true for bf16 data of ordinary
+ * vector span at most 45 - log2(D) binades (37 for D = 256) (always true for bf16 data of ordinary
  * range); the cache bytes are then a function of the inputs alone.
  * Errors: UQ_EINVAL, UQ_EUNSUPPORTED, UQ_EHIP.
  */
@@ -231,7 +231,7 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
  * out[n, h, :] = bf16(x[n, h, :] H) for n < N, h < H: the rotation the page
  * applies to the chunk's keys and queries ((x.float() @ PiT).to(bf16)). The
  * +-1 sums are computed in a float64 butterfly (exact when the vector's
- * non-zero magnitudes span at most 44 - log2(D) binades, as for uq_store),
+ * non-zero magnitudes span at most 45 - log2(D) binades, as for uq_store),
  * multiplied by the float64 nearest 1/sqrt(D) (exactly 1/16 at D = 256) and
  * rounded once to bf16, nearest-even; the sign of an exactly-zero result is
  * not defined.

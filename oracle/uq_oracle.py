@@ -66,20 +66,6 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float64 to bf16 (nearest, ties to even) via float32.
-
-    Only used to state what a bf16 output of an exact value is; values passed
-    here are exactly representable in float32 or the double rounding is
-    irrelevant to the caller.
-    """
-    f = np.asarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = (u + 0x7FFF + lsb) >> 16
-    return r.astype(np.uint16)
-
-
 # --------------------------------------------------------------------------
 # Rotation ([UQ-impl] _ensure_on_device: the rotation is a pure Hadamard,
 # orthonormal and symmetric, so PiT = Pi = H; _store_kv rotates K by it;
@@ -113,16 +99,21 @@ def sylvester(n: int) -> np.ndarray:
     return _SYLVESTER[n]
 
 
-# A +-subset sum of 256 bf16 values (8 significant bits each) fits in float64's
-# 53 bits when the exponents of the non-zero inputs span at most 36 binades:
-# 53 >= span + 8 (significand) + 9 (carry of 256 terms). Then x @ H is exact
-# in any summation order and the GPU butterfly sees the same value. For n
-# terms the carry is log2(n) + 1 bits.
-MAX_EXACT_SPAN = 36
-
-
+# Exactness of the rotation. Let the non-zero magnitudes of a bf16 vector of n
+# values have exponents (floor log2) from emin to emax, span = emax - emin.
+# Every value is an integer multiple of u = 2**(emin - 7) (8 significant bits)
+# and at most 255 * 2**span units, so every +-sum of the n values is an
+# integer number of units of magnitude at most n * 255 * 2**span. That
+# integer is exact in float64 (53 bits) whenever n * 255 * 2**span < 2**53,
+# i.e. span <= 45 - log2(n) (37 binades at n = 256, 38 at 128, 36 at 512), and
+# then x @ sylvester(n) is exact in any summation order. One binade more and
+# n - 1 values of 255 units plus one of 129 units sum to an odd integer above
+# 2**53, which no float64 holds.
 def max_exact_span(n: int) -> int:
-    return 44 - int(np.log2(n))
+    return 45 - int(np.log2(n))
+
+
+MAX_EXACT_SPAN = max_exact_span(D)
 
 
 def exact_span_ok(x: np.ndarray) -> np.ndarray:

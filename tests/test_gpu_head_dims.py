@@ -45,6 +45,7 @@ def test_store_bit_exact(d):
     k[2, :, :] = 0
     k[2, 0, :2] = [1.0, 1.0]                               # rotated: exact zeros on odd indices
     v[3] = np.ldexp(rng.uniform(0.5, 1, (hk, d)), -130)    # bf16 subnormals, scale clamps
+    v[25] = np.ldexp(rng.uniform(1, 4, (hk, d)) * rng.choice([-1, 1], (hk, d)), -128)  # codes 1 to 4, byte 0
     k[4] = rng.standard_normal((hk, d)) * 1e30
     for i in range(5, 15):                                  # magnitudes over 24 binades
         k[i] = np.ldexp(rng.uniform(0.5, 1, (hk, d)) * rng.choice([-1, 1], (hk, d)),

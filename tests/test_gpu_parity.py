@@ -97,6 +97,8 @@ def test_store_edge_values():
     k[2, 0, 0], k[2, 0, 1] = 1.0, 1.0                   # rotated: exact zeros on odd d
     k[3, 0, :2] = [5.0, 4.0]                             # rotated lands on ties
     v[4] = np.ldexp(rng.uniform(0.5, 1, (2, 256)), -130)  # bf16 subnormals, scale clamps
+    v[10] = np.ldexp(rng.uniform(1, 4, (2, 256)), -128)  # subnormals under byte 0: codes 1 to 4
+    v[10, 1, :32] = np.ldexp(rng.uniform(1, 4, 32), -129) * rng.choice([-1, 1], 32)
     v[5] = rng.standard_normal((2, 256)) * 1e37          # near the top of the range
     k[6] = rng.standard_normal((2, 256)) * 1e30
     k[7] = np.ldexp(rng.uniform(0.5, 1, (2, 256)), -110)
@@ -587,3 +589,36 @@ def test_store_and_decode_replay_in_hip_graph():
         torch.cuda.synchronize()
         assert torch.equal(cache, ref_cache), f"replay {i}: cache differs"
         assert torch.equal(out, ref_out), f"replay {i}: output differs"
+
+
+def test_capture_without_workspace_is_refused():
+    """A captured call must bring its own workspace: the binding's cached one
+    is shared with eager calls and can be replaced (freed) while a graph still
+    writes into it on replay, so under capture the binding refuses to use it.
+    Eager calls keep using the cached workspace afterwards."""
+    say("graph capture without a workspace")
+    rng = np.random.default_rng(78)
+    B, Hk, qg, bs, width = 2, 1, 8, 16, 4
+    Hq = Hk * qg
+    table = torch.from_numpy(rng.permutation(B * width).reshape(B, width).astype(np.int32)).to(DEV)
+    lens = torch.tensor([40, 17], dtype=torch.int32, device=DEV)
+    cache = torch.zeros((B * width, bs, Hk, 272), dtype=torch.uint8, device=DEV)
+    for b in range(B):
+        L = int(lens[b])
+        t = torch.arange(L, device=DEV)
+        uq.store(bf16(rng.standard_normal((L, Hk, 256))).to(DEV), bf16(rng.standard_normal((L, Hk, 256))).to(DEV),
+                 cache, table[b, t // bs].long() * bs + t % bs)
+    q = bf16(rng.standard_normal((B, Hq, 256))).to(DEV)
+    out = torch.empty((B, Hq, 256), dtype=torch.bfloat16, device=DEV)
+    eager = uq.decode(q, cache, table, lens, 1 / 16, 4).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with pytest.raises(ValueError, match="own workspace"):
+            with torch.cuda.graph(g):
+                uq.decode(q, cache, table, lens, 1 / 16, 4, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    again = uq.decode(q, cache, table, lens, 1 / 16, 4)
+    assert torch.equal(again, eager)

@@ -2,9 +2,12 @@
 GQA 6, 8, 16, 1 to 8 KV heads (odd counts included), block sizes 16 to
 256, 1 to 512 splits, ragged lengths with empty sequences and spare table
 width, sliding windows, sinks, a few outlier key channels. Cache bytes
-bit-exact; outputs within the tolerance plus half a bf16 ulp of the
-reference (these inputs reach |o| of 2 to 3, where rounding the exact
-answer to bf16 alone takes up to 0.0078 of the 0.01 bound)."""
+bit-exact; outputs within max-abs 1e-2 (plus half a bf16 ulp of the
+reference only where |o| >= 4, where rounding the exact answer to bf16
+alone can exceed 1e-2) and rel-L2 5e-3. UQ_RANDOM_CASES sets the number of
+shapes (24 by default; a sweep of 180 was run as well)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -40,7 +43,7 @@ def _case(rng):
                 scale=float(rng.choice([1 / 16, 0.1, 0.3])))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(int(os.environ.get("UQ_RANDOM_CASES", "24"))))
 def test_decode_random_shape(seed):
     rng = np.random.default_rng(5000 + seed)
     c = _case(rng)

@@ -85,6 +85,43 @@ def test_rotation_rejects_inexact_span():
         O.rotate(x)
 
 
+def _span_vector(n, span):
+    """n - 1 copies of the largest bf16 significand at exponent 0 (255/128)
+    and one value of 129 units of 2**(-span - 7): the +-sum of largest
+    magnitude with an odd number of units."""
+    x = np.full(n, 255.0 / 128.0)
+    x[-1] = 129.0 * 2.0 ** (-span - 7)
+    assert np.array_equal(O.bf16_to_f64(bf16(x)), x)     # bf16 values
+    return x
+
+
+@pytest.mark.parametrize("n,span", [(128, 38), (256, 37), (512, 36)])
+def test_exact_span_boundary(n, span):
+    """The guard sits exactly at the bound: at `span` binades the all-plus sum
+    (coordinate 0) of the worst vector is exact, checked against Fractions,
+    and the oracle computes it; one binade more, that sum is no float64 at
+    all, so the oracle must refuse the vector."""
+    x = _span_vector(n, span)
+    exact = sum(fractions.Fraction(v) for v in x)
+    assert fractions.Fraction(float(exact)) == exact
+    assert O.exact_span_ok(x)
+    y = O.rotate(x)
+    scale = fractions.Fraction(O.rot_scale(n))
+    assert fractions.Fraction(y[0]) == fractions.Fraction(float(exact * scale))
+    # a coordinate with mixed signs too
+    j = n // 2 + 3
+    sj = sum((fractions.Fraction(x[i]) if bin(i & j).count("1") % 2 == 0 else -fractions.Fraction(x[i]))
+             for i in range(n))
+    assert fractions.Fraction(y[j]) == fractions.Fraction(float(sj * scale))
+
+    x1 = _span_vector(n, span + 1)
+    exact1 = sum(fractions.Fraction(v) for v in x1)
+    assert fractions.Fraction(float(exact1)) != exact1        # not representable in float64
+    assert not O.exact_span_ok(x1)
+    with pytest.raises(ValueError):
+        O.rotate(x1)
+
+
 # ------------------------------------------------------- E2M1 and UE8M0
 def test_e2m1_value_table_matches_ocp_table():
     table = golden_io.e2m1_table()
