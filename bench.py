@@ -187,6 +187,22 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
 
+    # pass 1b: the spread of single steps, with an event recorded between
+    # consecutive steps (the events add a little to each step, so the mean of
+    # this pass is not the value; its percentiles show the step's spread)
+    import numpy as np
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    busy(steps + PREROLL)
+    for i in range(PREROLL):
+        step(i)
+    evs[0].record()
+    for i in range(steps):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    spread = {f"p{p}": round(float(np.percentile(per_step, p)), 5) for p in (10, 50, 90)}
+
     # pass 2: each kernel on its own, `steps` back-to-back launches between two
     # events on the decode stream, so that the average is the kernel's own
     # duration (what a kernel trace reports). Stage 1 reads the prologue's
@@ -205,11 +221,25 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
         return a.elapsed_time(b) / steps
 
     if multi is not None or sinks is not None or window:
-        return step_ms, None, None, None      # the per-kernel entry points take no options
-    pro = alone(uq.STAGE_PROLOGUE)
-    st1 = alone(uq.STAGE_SPLIT)
-    st2 = alone(uq.STAGE_MERGE)
-    return step_ms, pro, st1, st2
+        return step_ms, spread, None      # the per-kernel entry points take no options
+    st = {"prologue": alone(uq.STAGE_PROLOGUE), "split_kv": alone(uq.STAGE_SPLIT),
+          "merge": alone(uq.STAGE_MERGE)}
+
+    # the streaming ceiling: a plain read of exactly the blocks the step
+    # reads (all KV heads of every block of every sequence, in table order),
+    # back to back over the same cache copies
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    busy(steps + PREROLL)
+    for i in range(PREROLL):
+        uq.stream_blocks(caches[i % R], bt, sl, sink)
+    a.record()
+    for i in range(steps):
+        uq.stream_blocks(caches[i % R], bt, sl, sink)
+    b.record()
+    torch.cuda.synchronize()
+    st["stream_read"] = a.elapsed_time(b) / steps
+    return step_ms, spread, st
 
 
 STAGE1_SOURCE = os.path.join(ROOT, "decode_attention_bit_amd", "csrc", "uq_decode.hip")
@@ -236,37 +266,46 @@ def recorded_traffic(workload):
 
 def cpu_baseline(w, lay, seconds, wall_cap=150.0):
     """The oracle, untuned, on a bounded sample: whole (sequence, KV head)
-    decodes of this workload, one BLAS thread. Sequences are drawn at random;
-    each is encoded once (untimed) and decoded for all its KV heads, until
-    the timed decodes reach `seconds` or the whole loop reaches `wall_cap`."""
+    decodes of this workload, on every core this process may run on, one
+    (sequence, KV head) pair per thread with one BLAS thread each. Sequences
+    are drawn at random; each is encoded once (untimed), then all its KV
+    heads are decoded concurrently with other sequences' heads, until the
+    timed decodes reach `seconds` of wall time or the whole loop `wall_cap`."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
 
     from decode_attention_bit_amd import inputs
     from oracle import uq_oracle as O
 
+    cores = len(os.sched_getaffinity(0))
     q_bits = inputs.bf16_bits(inputs.make_query(w))
-    order = np.random.default_rng(0).permutation(w.B)
+    order = np.random.default_rng(0).permutation(w.B).tolist()
     start = time.perf_counter()
-    pairs, done_bytes, elapsed = [], 0, 0.0
-    for b in order.tolist():
-        if elapsed >= seconds or time.perf_counter() - start >= wall_cap:
-            break
-        L = int(lay.seq_lens[b])
-        cache = np.zeros((lay.num_blocks, w.block_size, w.Hk, w.slot_bytes), dtype=np.uint8)
-        k, v = inputs.make_kv(w, lay, b)
-        O.store(inputs.bf16_bits(k), inputs.bf16_bits(v), cache, inputs.slots_for(lay, b, 0, L))
-        todo = [(b, h) for h in range(w.Hk)]
-        with threadpool_limits(limits=1):
+    pairs, done_bytes, elapsed = 0, 0, 0.0
+    with threadpool_limits(limits=1), ThreadPoolExecutor(cores) as pool:
+        while order and elapsed < seconds and time.perf_counter() - start < wall_cap:
+            # encode a batch of sequences (untimed), then decode all their heads at once
+            batch, order = order[:max(1, cores // max(1, w.Hk))], order[max(1, cores // max(1, w.Hk)):]
+            caches = {}
+            for b in batch:
+                L = int(lay.seq_lens[b])
+                cache = np.zeros((lay.num_blocks, w.block_size, w.Hk, w.slot_bytes), dtype=np.uint8)
+                k, v = inputs.make_kv(w, lay, b)
+                O.store(inputs.bf16_bits(k), inputs.bf16_bits(v), cache, inputs.slots_for(lay, b, 0, L))
+                caches[b] = cache
+            todo = [(b, h) for b in batch for h in range(w.Hk)]
             t = time.perf_counter()
-            O.decode(q_bits, cache, lay.block_table, lay.seq_lens, w.scale, pairs=todo)
+            list(pool.map(lambda bh: O.decode(q_bits, caches[bh[0]], lay.block_table, lay.seq_lens,
+                                              w.scale, pairs=[bh]), todo))
             elapsed += time.perf_counter() - t
-        done_bytes += L * w.Hk * w.slot_bytes
-        pairs += todo
-        log(f"cpu baseline: sequence {b} decoded, {elapsed:.1f} s timed")
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(pairs)} whole (sequence, KV head) decodes of this workload "
-                      f"({done_bytes / 1e6:.1f} MB of cache), {elapsed:.1f} s, cache encoding untimed"}
+            done_bytes += sum(int(lay.seq_lens[b]) for b in batch) * w.Hk * w.slot_bytes
+            pairs += len(todo)
+            log(f"cpu baseline: {pairs} pairs decoded, {elapsed:.1f} s timed")
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{pairs} whole (sequence, KV head) decodes of this workload "
+                      f"({done_bytes / 1e6:.1f} MB of cache), {elapsed:.1f} s wall on {cores} threads "
+                      f"(one pair per thread, one BLAS thread each), cache encoding untimed"}
 
 
 # Continuation prefill: one sequence of the decode workload's shape (Hq 32,
@@ -301,7 +340,7 @@ def time_events(fn, steps, warmup):
 
 def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds, D=256):
     """The oracle, untuned, on sampled chunk positions (every key still
-    dequantised and rotated), one BLAS thread."""
+    dequantised and rotated), BLAS threads on every core of this process."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -312,8 +351,9 @@ def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds, D=256):
     scale = 1.0 / math.sqrt(D)
     cache_np, row_np = cache.cpu().numpy(), row.cpu().numpy()
     rng = np.random.default_rng(0)
+    cores = len(os.sched_getaffinity(0))
     done, flops, elapsed = 0, 0, 0.0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
         while elapsed < seconds and done < P["q_len"]:
             rows = rng.integers(0, P["q_len"], 4)
             t = time.perf_counter()
@@ -321,9 +361,9 @@ def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds, D=256):
             elapsed += time.perf_counter() - t
             done += len(rows)
             flops += sum(4 * D * P["Hq"] * (P["cached"] + int(i) + 1) for i in rows)
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} chunk positions of this workload, each call dequantising the whole "
-                      f"prefix and rotating the whole chunk, {elapsed:.1f} s"}
+                      f"prefix and rotating the whole chunk, {elapsed:.1f} s, BLAS on {cores} threads"}
 
 
 def prefill_main(args):
@@ -410,6 +450,7 @@ def main():
         return prefill_main(args)
     import torch
 
+    import decode_attention_bit_amd as uq
     from decode_attention_bit_amd import inputs
 
     w = inputs.WORKLOADS[args.workload]
@@ -443,11 +484,13 @@ def main():
         import numpy as np
         kv_bytes = int(np.minimum(lay.seq_lens.astype(np.int64), args.sliding_window).sum()) * w.Hk * w.slot_bytes
         logical_bytes = kv_bytes
-    step_ms, pro_ms, st1_ms, st2_ms = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup,
-                                               store_args, multi, sinks, args.sliding_window)
+    step_ms, spread, st = gpu_time(w, lay, q, caches, bt, sl, args.steps, args.warmup,
+                                   store_args, multi, sinks, args.sliding_window)
     gbs = kv_bytes / (step_ms * 1e-3) / 1e9
-    plain = st1_ms is not None               # no option: stage 1 timed on its own
+    plain = st is not None                   # no option: stage 1 timed on its own
+    st1_ms = st["split_kv"] if plain else None
     st1_gbs = kv_bytes / ((st1_ms if plain else step_ms) * 1e-3) / 1e9
+    parts = uq.decode_partials(w.B, w.Hq, w.Hk, w.num_kv_splits, bt.shape[1], w.block_size, w.D)
     res = {
         "metric": METRIC.format(D=w.D),
         "value": round(gbs, 2),
@@ -471,13 +514,20 @@ def main():
                                + (f" (sliding window {args.sliding_window})" if args.sliding_window > 0 else "")
                                + (" (with sinks)" if sinks is not None else ""),
                    "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "D": w.D, "block_size": w.block_size,
-                   "num_kv_splits": w.num_kv_splits, "kv_bytes_per_step": kv_bytes,
-                   "logical_kv_bytes_per_step": logical_bytes},
+                   "num_kv_splits": w.num_kv_splits, "partials_per_row": parts,
+                   "kv_bytes_per_step": kv_bytes, "logical_kv_bytes_per_step": logical_bytes},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.B * max(1, args.queries_per_seq) / (step_ms * 1e-3), 1),
-        "stage_ms": ({"prologue": round(pro_ms, 5), "split_kv": round(st1_ms, 5), "merge": round(st2_ms, 5)}
-                     if plain else None),
+        "step_ms_spread": spread,
+        "timing": "HIP events around back-to-back steps queued ahead of the GPU behind a spin kernel: "
+                  "device time per step, host launch cost excluded",
+        "stage_ms": ({k: round(v, 5) for k, v in st.items() if k != "stream_read"} if plain else None),
         "cache_copies": len(caches),
+        "stream_ceiling": ({"value": round(kv_bytes / (st["stream_read"] * 1e-3) / 1e9, 2), "unit": "GB/s",
+                            "ms": round(st["stream_read"], 5),
+                            "what": "uq_stream_blocks: plain 16-byte reads of exactly the blocks the step "
+                                    "reads, in table order, same run"} if plain else None),
+        "pct_of_stream": (round(100 * st["stream_read"] / step_ms, 2) if plain else None),
         "roofline": {"bound": "hbm", "achieved": round(st1_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(st1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(w.name) if plain and store_args is None and w.D == 256 else None,

@@ -30,7 +30,8 @@ import os
 
 import torch
 
-__all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_workspace_bytes", "rotate",
+__all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_workspace_bytes",
+           "decode_partials", "stream_blocks", "rotate",
            "dequant_kv", "prefill_attention", "continuation_prefill",
            "continuation_prefill_workspace_bytes", "library_path",
            "UQError", "HEAD_DIM", "HEAD_DIMS", "SLOT_BYTES", "slot_bytes"]
@@ -100,6 +101,10 @@ def _load():
     lib.uq_continuation_prefill.restype = i32
     lib.uq_continuation_prefill_stages.argtypes = [i32] + lib.uq_continuation_prefill.argtypes
     lib.uq_continuation_prefill_stages.restype = i32
+    lib.uq_decode_partials.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.uq_decode_partials.restype = i32
+    lib.uq_stream_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i64, i32, i32, vp, i32, vp]
+    lib.uq_stream_blocks.restype = i32
     lib.uq_last_error.argtypes = []
     lib.uq_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -160,6 +165,39 @@ def decode_workspace_bytes(B: int, Hq: int, Hk: int, num_kv_splits: int, max_blo
     if n == 0:
         raise ValueError("invalid decode shape")
     return int(n)
+
+
+def decode_partials(B: int, Hq: int, Hk: int, num_kv_splits: int, max_blocks_per_seq: int,
+                    block_size: int = 16, D: int = HEAD_DIM) -> int:
+    """Partial results per (sequence, query head) that uq_decode writes for
+    this shape (uq_decode_partials)."""
+    n = _load().uq_decode_partials(int(B), int(Hq), int(Hk), int(D), int(num_kv_splits),
+                                   int(max_blocks_per_seq), int(block_size))
+    if n == 0:
+        raise ValueError("invalid decode shape")
+    return int(n)
+
+
+def stream_blocks(kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                  sink: torch.Tensor) -> None:
+    """uq_stream_blocks: read every cache byte a decode of these sequences
+    reads, and nothing else (a measurement aid); sink is an int32/uint32
+    device tensor of scratch words."""
+    if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
+        raise TypeError("kv_cache must be a contiguous 4-d uint8 tensor")
+    if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise TypeError("block_table must be a contiguous (B, max_blocks) int32 tensor")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("seq_lens must be a contiguous int32 tensor")
+    if sink.element_size() != 4 or not sink.is_contiguous():
+        raise TypeError("sink must be a contiguous tensor of 4-byte words")
+    nb, bs, Hk, ss = kv_cache.shape
+    B = block_table.shape[0]
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have one entry per table row")
+    _check(_load().uq_stream_blocks(_ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), B, Hk,
+                                    ss * 16 // 17, nb, bs, block_table.shape[1], _ptr(sink),
+                                    sink.numel(), _stream(kv_cache.device)))
 
 
 _WS_POOL: dict = {}

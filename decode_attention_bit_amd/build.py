@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["uq_store.hip", "uq_decode.hip", "uq_prefill.hip", "uq_api.hip"]
+SOURCES = ["uq_store.hip", "uq_decode.hip", "uq_prefill.hip", "uq_probe.hip", "uq_api.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-FP32 instructions anywhere in the library

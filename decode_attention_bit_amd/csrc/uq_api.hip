@@ -43,7 +43,7 @@ extern "C" {
 
 int uq_build_hadamard(int D, float* H, void* stream) {
   if (!H) return fail(UQ_EINVAL, "uq_build_hadamard: H is null");
-  if (!pow2_in(D, 1, 256)) return fail(UQ_EINVAL, "uq_build_hadamard: D=%d is not a power of two in [1, 256]", D);
+  if (!pow2_in(D, 1, 512)) return fail(UQ_EINVAL, "uq_build_hadamard: D=%d is not a power of two in [1, 512]", D);
   return hip_status(uq::launch_hadamard(D, H, (hipStream_t)stream), "uq_build_hadamard launch");
 }
 
@@ -141,6 +141,32 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
                      num_kv_splits, nullptr, 0, out, B, Hq, Hk, D, num_blocks, block_size,
                      max_blocks_per_seq, q_stride_b, q_stride_h, workspace, workspace_bytes,
                      stream);
+}
+
+int uq_decode_partials(int B, int Hq, int Hk, int D, int num_kv_splits, int max_blocks_per_seq,
+                       int block_size) {
+  if (uq_decode_workspace_bytes(B, Hq, Hk, D, num_kv_splits, max_blocks_per_seq, block_size) == 0) return 0;
+  return uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).parts;
+}
+
+int uq_stream_blocks(const uint8_t* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     int B, int Hk, int D, int64_t num_blocks, int block_size, int max_blocks_per_seq,
+                     uint32_t* sink, int sink_words, void* stream) {
+  if (B < 1 || Hk < 1 || num_blocks < 1 || max_blocks_per_seq < 1 || sink_words < 1)
+    return fail(UQ_EINVAL, "uq_stream_blocks: B=%d Hk=%d num_blocks=%lld max_blocks=%d sink_words=%d", B, Hk,
+                (long long)num_blocks, max_blocks_per_seq, sink_words);
+  if (D != 128 && D != 256 && D != 512)
+    return fail(UQ_EUNSUPPORTED, "uq_stream_blocks: head_dim %d unsupported (128, 256, 512)", D);
+  if (!pow2_in(block_size, 16, 256))
+    return fail(UQ_EUNSUPPORTED, "uq_stream_blocks: block_size %d unsupported (16, 32, 64, 128, 256)", block_size);
+  if ((long long)block_size * Hk * (D * 17 / 16) > 0x7FFFFFFFLL || (long long)B * max_blocks_per_seq > 0x7FFFFFFFLL)
+    return fail(UQ_EUNSUPPORTED, "uq_stream_blocks: shape too large");
+  if (!kv_cache || !block_table || !seq_lens || !sink) return fail(UQ_EINVAL, "uq_stream_blocks: null pointer argument");
+  if (!aligned(kv_cache, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(sink, 4))
+    return fail(UQ_EINVAL, "uq_stream_blocks: misaligned pointer (kv_cache 16 B)");
+  uq::StreamArgs a{kv_cache, block_table, seq_lens, B, max_blocks_per_seq, block_size, Hk, D * 17 / 16,
+                   num_blocks, sink, sink_words};
+  return hip_status(uq::launch_stream_blocks(a, (hipStream_t)stream), "uq_stream_blocks launch");
 }
 
 int uq_decode_ex(const uint16_t* query, const uint8_t* kv_cache, const int32_t* block_table,

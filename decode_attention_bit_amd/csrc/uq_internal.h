@@ -97,6 +97,17 @@ struct PrefillAttnArgs {
   int D;                     // head dim: 128 or 256
 };
 
+// Streaming-read probe over the blocks a decode reads.
+struct StreamArgs {
+  const uint8_t* cache;
+  const int32_t* block_table;   // (B, max_blocks)
+  const int32_t* seq_lens;      // (B,)
+  int B, max_blocks, block_size, Hk, slot_bytes;
+  int64_t num_blocks;
+  uint32_t* sink;               // sink_words words, overwritten
+  int sink_words;
+};
+
 DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
                        int block_size, int D);
 
@@ -105,6 +116,7 @@ hipError_t launch_hadamard(int D, float* H, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream);
 int prefill_positions_per_wg(int QG);
+hipError_t launch_stream_blocks(const StreamArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mask, hipStream_t stream);
 
 }  // namespace uq

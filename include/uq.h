@@ -69,7 +69,8 @@ extern "C" {
  * H[i][j] = (-1)**popcount(i & j) / sqrt(D) as D x D float32, row-major.
  * Follows _ensure_on_device on the UltraQuantAttentionImpl page: one matrix
  * serves as both Pi and PiT because it is orthonormal and symmetric.
- *   D: power of two, 1 <= D <= 256.
+ *   D: power of two, 1 <= D <= 512 (512: the rotation of the head-dim-512
+ *      cache; entries are the float32 nearest the float64 1/sqrt(D)).
  *   H: (device) D*D floats, written.
  * Errors: UQ_EINVAL for a null H or D not a power of two in range.
  */
@@ -114,6 +115,15 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
  */
 size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits,
                                  int max_blocks_per_seq, int block_size);
+
+/*
+ * Number of partial results stage 1 writes per (sequence, query head) for
+ * this shape (0 on invalid arguments): one per run of whole splits, or per
+ * piece of a split, as uq_decode cuts them. The workspace holds that many
+ * rows per (sequence, query head).
+ */
+int uq_decode_partials(int B, int Hq, int Hk, int D, int num_kv_splits, int max_blocks_per_seq,
+                       int block_size);
 
 /*
  * Decode one query token per sequence against the paged 4-bit cache and
@@ -344,6 +354,22 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
 
 /* Message describing the last non-zero return on the calling thread
  * ("" if none). The pointer stays valid until the thread's next call. */
+/*
+ * Streaming-read probe (a measurement aid, not a step of the method): reads
+ * every cache byte a decode of these sequences reads (each physical block a
+ * sequence's tokens live in, all Hk heads, up to the sequence's last token,
+ * in block-table order) with plain 16-byte loads and does nothing with them
+ * but an XOR, so its rate is the ceiling for streaming those blocks on the
+ * device. Arguments as for uq_decode (kv_cache (num_blocks, block_size, Hk,
+ * 17*D/16) read only, block_table (B, max_blocks_per_seq), seq_lens (B,),
+ * clamped like uq_decode's); sink: (device) sink_words >= 1 uint32 words,
+ * overwritten with values of no meaning. Errors: UQ_EINVAL, UQ_EUNSUPPORTED,
+ * UQ_EHIP.
+ */
+int uq_stream_blocks(const uint8_t* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     int B, int Hk, int D, int64_t num_blocks, int block_size, int max_blocks_per_seq,
+                     uint32_t* sink, int sink_words, void* stream);
+
 const char* uq_last_error(void);
 
 #ifdef __cplusplus

@@ -21,7 +21,8 @@ def test_header_declares_entry_points():
     for n in ("uq_build_hadamard", "uq_store", "uq_decode", "uq_decode_ex", "uq_decode_stages",
               "uq_decode_workspace_bytes", "uq_rotate", "uq_dequant_kv", "uq_prefill_attention",
               "uq_continuation_prefill", "uq_continuation_prefill_stages",
-              "uq_continuation_prefill_workspace_bytes", "uq_last_error"):
+              "uq_continuation_prefill_workspace_bytes", "uq_decode_partials", "uq_stream_blocks",
+              "uq_last_error"):
         assert n in names
 
 
@@ -46,7 +47,7 @@ def test_build_hadamard_rejects(libuq):
     buf = ctypes.c_void_p(0x1000)   # never dereferenced: the size check fails first
     assert libuq.uq_build_hadamard(0, buf, None) == -1
     assert libuq.uq_build_hadamard(384, buf, None) == -1
-    assert libuq.uq_build_hadamard(512, buf, None) == -1
+    assert libuq.uq_build_hadamard(1024, buf, None) == -1
 
 
 FAKE = 0x10000   # 256-byte aligned host address used only for argument checks

@@ -30,7 +30,7 @@ def say(msg):
 
 
 # ------------------------------------------------------------------ Hadamard
-@pytest.mark.parametrize("D", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("D", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512])
 def test_build_hadamard(D):
     say(f"hadamard D={D}")
     H = uq.build_hadamard(D, DEV).cpu().numpy()
