@@ -84,21 +84,23 @@ __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restri
 // read by one CU. A wave walks its token range in 16-token tiles:
 //   scores^T (16 tokens x 16 q-heads) = K (FP4, UE8M0 scales) x q8 (E4M3) on
 //     two V_MFMA_SCALE_F32_16X16X128_F8F6F4 (d = 0..127, 128..255);
-//   online softmax in the log2 domain; the running max is only raised when a
-//     tile exceeds it by more than 8 (p stays <= 256, exact softmax);
-//   O^T (256 d x 16 q-heads) += V^T (bf16, converted with its scale) x P^T
-//     (bf16) on 16 V_MFMA_F32_16X16X16_BF16.
+//   online softmax in the log2 domain; the reference maximum is only raised
+//     when a tile exceeds it by more than 8 (p stays <= 256, exact softmax);
+//   O (16 q-heads x 256 d) += P (bf16 high and low parts of each weight) x V
+//     (bf16, converted with its scale) on 16 V_MFMA_F32_16X16X32_BF16.
 // Lane layouts (gfx950):
 //   scaled MFMA A (FP4, 4 VGPRs): lane l -> row l%16, k = 32*(l/16) + j for
 //     nibble j; its scale byte covers those 32 k.
 //   scaled MFMA B (FP8, 8 VGPRs): lane l -> col l%16, byte j -> k = 16*(l/16)+j
 //     for j < 16 and 64 + 16*(l/16) + (j-16) above.
-//   16x16x16 bf16 A/B: lane l -> row/col l%16, k = 4*(l/16) + i.
+//   16x16x32 bf16 A/B: lane l -> row/col l%16, eight k slots.
 //   Result: lane l -> col l%16, rows 4*(l/16) + i.
 // So the score tile leaves lane (g = l%16, grp = l/16) holding tokens
-// 4*grp .. 4*grp+3 of q-head g, which is exactly the P^T operand of the
-// P.V product, and the O^T accumulator of lane l holds q-head l%16,
-// d = 64*grp + 16*i + j (i = element, j = MFMA index).
+// 4*grp .. 4*grp+3 of q-head g, which is the P operand of the value product
+// as it stands (A: row = q-head, k slots = those four tokens, high parts,
+// then the same four tokens, low parts); the V operand (B) of lane l holds
+// dims (D/16)*(l%16) + j of the same four tokens, twice. The accumulator
+// O[j] of lane l then holds q-heads 4*(l/16) + i at dim (D/16)*(l%16) + j.
 // ---------------------------------------------------------------------------
 template <int D>
 struct Tile {
@@ -223,14 +225,14 @@ __device__ __forceinline__ void read_tile(Tile<D>& T, const uint4* __restrict__ 
   T.nvalid = nvalid;
 }
 
-// Byte M of each token's 8 V-code bytes holds d = 16*(l%16) + 2M (low nibble)
-// and 2M + 1 (high nibble). Convert them for the lane's 4 tokens, regroup the
-// bf16 halves by d, and accumulate two MFMAs (d even / odd). Each MFMA runs
-// over k = 32: the lane's 4 tokens twice, against the high and the low bf16
-// parts of their weights (pb), so a weight enters the product with 16
-// significant bits, not 8.
+// Byte M of each token's D/32 V-code bytes holds dims (D/16)*(l%16) + 2M
+// (low nibble) and 2M + 1 (high nibble). Convert them for the lane's 4
+// tokens, regroup the bf16 halves by dim, and accumulate two MFMAs (dim even
+// / odd). Each MFMA runs over k = 32: the lane's 4 tokens twice, against the
+// high and the low bf16 parts of their weights (pa), so a weight enters the
+// product with 16 significant bits, not 8.
 template <int D, int M>
-__device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4], const v8bf& pb,
+__device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4], const v8bf& pa,
                                         v4f acc[D / 16]) {
   uint32_t w[4];
 #pragma unroll
@@ -243,10 +245,10 @@ __device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4],
   const uint32_t e1 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
   const uint32_t o0 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
   const uint32_t o1 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-  const v8bf ae = __builtin_bit_cast(v8bf, make_uint4(e0, e1, e0, e1));
-  const v8bf ao = __builtin_bit_cast(v8bf, make_uint4(o0, o1, o0, o1));
-  acc[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, pb, acc[2 * M], 0, 0, 0);
-  acc[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, pb, acc[2 * M + 1], 0, 0, 0);
+  const v8bf be = __builtin_bit_cast(v8bf, make_uint4(e0, e1, e0, e1));
+  const v8bf bo = __builtin_bit_cast(v8bf, make_uint4(o0, o1, o0, o1));
+  acc[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, be, acc[2 * M], 0, 0, 0);
+  acc[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bo, acc[2 * M + 1], 0, 0, 0);
 }
 
 // Maximum over the four 16-lane row groups (lanes l, l^16, l^32, l^48), with
@@ -283,7 +285,7 @@ __device__ __forceinline__ void qk_tile(const Tile<D>& T, const v8i qb[D / 128],
 }
 
 // Softmax weights p = 2^(s - m_ref) (<= 2^8 by the re-basing rule), then
-// O^T += V^T P^T. Touches the accumulators only through MFMAs.
+// O += P V. Touches the accumulators only through MFMAs.
 template <int D>
 __device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], float m_ref, int n16,
                                         v4f acc[D / 16], float& l_part) {
@@ -329,6 +331,49 @@ __device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], flo
     pv_step<D, 14>(T, vscale, pb, acc);
     pv_step<D, 15>(T, vscale, pb, acc);
   }
+}
+
+// Maximum over the 16 lanes of a row (lanes 16*grp .. 16*grp + 15), by DPP
+// row exchanges.
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const int lane = __lane_id();
+    x = fmaxf(x, __uint_as_float(xor_lane_u32(__float_as_uint(x), m, lane)));
+  }
+  return x;
+}
+
+// Raise the softmax reference of every query head to cover a tile whose
+// maximum mt exceeds it by more than 8 (never lowering it, so each factor
+// f = 2^(m_ref - m_new) is <= 1), and rescale that head's row of O and its
+// weight sum by f. Row r of O sits in register i of lanes 16*g + c with
+// 4g + i = r, so O <- diag(f) O is four V_MFMA_F32_16X16X4_F32 per
+// accumulator: MFMA i takes register i of the accumulator as B (k slot g ->
+// row 4g + i) and, as A, f_r in lane (row r, k slot g) when r = 4g + i, zero
+// otherwise (f_r is lane r's own factor: lane l%16 holds head l%16's
+// statistics).
+__device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void rebase(v4f acc[D / 16], float& m_ref, float mt, float& l_part, int n16,
+                                       int grp) {
+  const float m_new = fmaxf(m_ref, mt);
+  const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
+  float fsel[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fsel[i] = n16 == 4 * grp + i ? f : 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d = mfma_f32x4(fsel[i], acc[j][i], d);
+    acc[j] = d;
+  }
+  l_part *= f;
+  m_ref = m_new;
 }
 
 template <int D, int QG, int HPW, int NSLOT>
@@ -461,15 +506,16 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 
   // Softmax reference: the first tile's maximum. The weights 2^(s - m_ref)
   // are exact for any reference; keeping them <= 2^8 bounds their range. A
-  // tile that exceeds the reference by more than that ends the current
-  // segment: outside the tile loop its sums are folded into `hold`, rescaled
-  // to the raised reference, and the tile loop restarts at that tile. The
-  // running accumulators are only ever written by MFMAs inside the loop, so
-  // they stay in the accumulator registers.
-  v4f acc[NA], hold[NA];
+  // tile that exceeds the reference by more than that ends the tile loop:
+  // outside it, the rows of O (one per query head) are rescaled in place to
+  // the raised reference by diag(f) O on float32 MFMAs, and the loop resumes
+  // at that tile. The accumulators are only ever touched by MFMAs, so they
+  // stay in the accumulator registers, and the rare rescale stays out of the
+  // loop body.
+  v4f acc[NA];
 #pragma unroll
-  for (int j = 0; j < NA; ++j) hold[j] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_part = 0.f, l_hold = 0.f;
+  for (int j = 0; j < NA; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_part = 0.f;
   int t0 = u0;
   // valid-token count of the tile in each slot, known when it is issued
   int nv_ring0 = 0, nv_ring1 = 0, nv_ring2 = 0, nv_ring3 = 0;
@@ -483,12 +529,9 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   for (;;) {
     Tile<D> T;
     float sv[4], mt;
-#pragma unroll
-    for (int j = 0; j < NA; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
-    l_part = 0.f;
     bool rebased = false;
     int t_stop = 0;
-    if (!filled) {              // a segment after a re-base refills the ring at t0
+    if (!filled) {              // after a re-base the ring is refilled at t0
       nv_ring0 = issue(ring0[wave], t0);
       UQ_PRE(1, UQ_PHYS_B) UQ_PRE(2, UQ_PHYS_B) UQ_PRE(3, UQ_PHYS_B) UQ_PRE(4, UQ_PHYS_B) UQ_PRE(5, UQ_PHYS_B)
       UQ_PRE(6, UQ_PHYS_B)
@@ -543,15 +586,10 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     }
 #undef UQ_STEP
     if (!rebased) break;
-    // Raise the reference to cover tile t_stop (never below the old one, so
-    // the factor is <= 1) and fold the segment into `hold`. Drain the ring;
-    // the loop restarts at t_stop, which is then within 2^8 of the reference.
-    const float m_new = fmaxf(m_ref, mt);
-    const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
-#pragma unroll
-    for (int j = 0; j < NA; ++j) hold[j] = (hold[j] + acc[j]) * f;
-    l_hold = (l_hold + l_part) * f;
-    m_ref = m_new;
+    // Raise the reference to cover tile t_stop and rescale O and the sums in
+    // place; drain the ring; the loop resumes at t_stop, which is then within
+    // 2^8 of the reference.
+    rebase<D>(acc, m_ref, mt, l_part, n16, grp);
     UQ_WAIT_VMCNT(0);
     t0 = t_stop;
   }
@@ -560,19 +598,24 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 #undef issue_at
 #undef UQ_PHYS_S
 #undef UQ_PHYS_B
-#pragma unroll
-  for (int j = 0; j < NA; ++j) acc[j] += hold[j];
-  l_part += l_hold;
 
+  // Lane (head l%16, any grp) holds that head's weight sum after the reduction.
   const float l1 = l_part + __shfl_xor(l_part, 16);
   const float l_tot = l1 + __shfl_xor(l1, 32);
+  // a non-empty range has l >= 1 (its largest weight is exactly 1)
+  const float inv = 1.f / l_tot;
+  if (qlane && grp == 0) {
+    part_m[stat] = m_ref;
+    part_l[stat] = l_tot;
+  }
   // The partial O / l of each query head is stored as an fp16 row times
   // 2^ex, with ex chosen from the row's largest magnitude so that it lands in
-  // [2^14, 2^15): the rounding error is at most 2^-11 of the row maximum. The
+  // [2^14, 2^15): the rounding error is at most 2^-11 of each element. The
   // row leaves as one contiguous store: the lanes first place their dims in
   // the wave's own ring, free now that every tile it issued has been
   // consumed (row stride 2 D + 16 bytes, RPS rows per slot), then each row is
-  // read back across the wave.
+  // read back across the wave. Lane (n16, grp) holds heads 4*grp + i at dims
+  // (D/16)*n16 + j.
   constexpr int RS = D * 2 + 16;
   constexpr int RPS = S::kTileU4 * 16 / RS;
   static_assert((QG + RPS - 1) / RPS <= NSLOT, "the ring cannot stage the partial rows");
@@ -580,33 +623,26 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   uint4* const own[8] = {UQ_OWN_PTR(0), UQ_OWN_PTR(1), UQ_OWN_PTR(2), UQ_OWN_PTR(3),
                          UQ_OWN_PTR(4), UQ_OWN_PTR(5), UQ_OWN_PTR(6), UQ_OWN_PTR(7)};
 #undef UQ_OWN_PTR
-  // a non-empty range has l >= 1 (its largest weight is exactly 1)
-  const float inv = 1.f / l_tot;
-  float amax = 0.f;
 #pragma unroll
-  for (int j = 0; j < NA; ++j)
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * grp + i;                               // query head of the row
+    const float inv_r = __shfl(inv, r);
+    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[j][i]));
-  amax = rowgroup_max(amax * inv);
-  const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14 : 0;
-  if (qlane && grp == 0) {
-    part_m[stat] = m_ref;
-    part_l[stat] = l_tot;
-    part_e[stat] = ex;
-  }
-  if (qlane) {
-    // lane (head l%16, grp) holds dims NA*(4*grp + i) + j
-    uint8_t* rowp = reinterpret_cast<uint8_t*>(own[n16 / RPS]) + (n16 % RPS) * RS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < NA; ++j) amax = fmaxf(amax, fabsf(acc[j][i]));
+    amax = row16_max(amax) * inv_r;
+    const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14 : 0;
+    if (r < QG) {
+      if (n16 == 0) part_e[((size_t)b * Hq + (size_t)h * QG + r) * P + part] = ex;
+      uint8_t* rowp = reinterpret_cast<uint8_t*>(own[r / RPS]) + (r % RPS) * RS + 2 * NA * n16;
 #pragma unroll
       for (int j = 0; j < NA; j += 8) {
         uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          w[k] = pack_f16(__builtin_amdgcn_ldexpf(acc[j + 2 * k][i] * inv, -ex),
-                          __builtin_amdgcn_ldexpf(acc[j + 2 * k + 1][i] * inv, -ex));
-        *reinterpret_cast<uint4*>(rowp + 2 * (NA * (4 * grp + i) + j)) = make_uint4(w[0], w[1], w[2], w[3]);
+          w[k] = pack_f16(__builtin_amdgcn_ldexpf(acc[j + 2 * k][i] * inv_r, -ex),
+                          __builtin_amdgcn_ldexpf(acc[j + 2 * k + 1][i] * inv_r, -ex));
+        *reinterpret_cast<uint4*>(rowp + 2 * j) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   }

@@ -90,3 +90,13 @@ def decode_two_token():
         elif tag == "seq_len":
             d["seq_len"] = int(rest[0])
     return d
+
+
+def cache_digests():
+    """{workload: (cache bytes, sha256)} from cache_digests.txt (written by
+    make_cache_digests.py from the oracle and the seeded inputs only)."""
+    out = {}
+    for l in _lines("cache_digests.txt"):
+        name, nbytes, digest = l.split()
+        out[name] = (int(nbytes), digest)
+    return out

@@ -58,38 +58,47 @@ class Instance:
                          splits or self.w.num_kv_splits, **kw)
 
     # ----------------------------------------------------------- oracle side
-    def oracle_slots(self, b: int, tokens: np.ndarray) -> np.ndarray:
-        """Oracle slot bytes (n, Hk, 272) of the given tokens of sequence b."""
-        k, v = inputs.make_kv_tokens(self.w, self.layout, b, tokens)
-        kb, vb = inputs.bf16_bits(k), inputs.bf16_bits(v)
-        out = []
-        for i in range(0, len(tokens), 4096):
-            out.append(O.encode_slots(kb[i:i + 4096], vb[i:i + 4096]))
-        return np.concatenate(out) if out else np.zeros((0, self.w.Hk, self.w.slot_bytes), np.uint8)
-
-    def gpu_slots(self, b: int, tokens: np.ndarray) -> np.ndarray:
-        slots = inputs.slots_for(self.layout, b, 0, int(self.layout.seq_lens[b]))[tokens]
-        flat = self.cache.view(-1, self.w.Hk, self.w.slot_bytes)
-        return flat[torch.from_numpy(slots).to(self.dev)].cpu().numpy()
-
-    def oracle_output(self, b: int, h: int) -> np.ndarray:
-        """Oracle output rows (QG, 256) of KV head h of sequence b, from the
-        oracle's own encoding of that sequence."""
-        L = int(self.layout.seq_lens[b])
-        k, v = inputs.make_kv(self.w, self.layout, b)      # uses the thread pool itself
-        kb, vb = inputs.bf16_bits(k)[:, h], inputs.bf16_bits(v)[:, h]
-
-        def enc(i):
-            return O.decode_slots(O.encode_slots(kb[i:i + 8192], vb[i:i + 8192]))
-
+    def oracle_pairs(self, pairs_by_seq: dict, chunk: int = 2048) -> dict:
+        """Oracle output rows {(b, h): (QG, D)} for the given {b: [KV heads]},
+        every sequence encoded by the oracle itself. The (sequence, chunk)
+        encodes run on a thread pool (numpy releases the GIL in them)."""
+        import os
         from concurrent.futures import ThreadPoolExecutor
-        with ThreadPoolExecutor(8) as ex:                   # not the generator's pool: no nesting
-            parts = list(ex.map(enc, range(0, L, 8192)))
-        K = np.concatenate([p[0] for p in parts])
-        V = np.concatenate([p[1] for p in parts])
-        qg = self.w.QG
-        q8 = O.query_haircut(inputs.bf16_bits(self.query)[b, h * qg:(h + 1) * qg])
-        return O.attention(q8, K, V, self.w.scale)
+        w = self.w
+        seqs = {}
+        for b, heads in pairs_by_seq.items():
+            k, v = inputs.make_kv(w, self.layout, b)
+            seqs[b] = (inputs.bf16_bits(k)[:, heads], inputs.bf16_bits(v)[:, heads])
+        jobs = [(b, i) for b in seqs for i in range(0, int(self.layout.seq_lens[b]), chunk)]
+
+        def enc(job):
+            b, i = job
+            kb, vb = seqs[b]
+            return O.decode_slots(O.encode_slots(kb[i:i + chunk], vb[i:i + chunk]))
+
+        with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+            done = dict(zip(jobs, ex.map(enc, jobs)))
+        qg = w.QG
+        qb = inputs.bf16_bits(self.query)
+        out = {}
+        for b, heads in pairs_by_seq.items():
+            parts = [done[(b2, i)] for (b2, i) in jobs if b2 == b]
+            K = np.concatenate([p[0] for p in parts])
+            V = np.concatenate([p[1] for p in parts])
+            for j, h in enumerate(heads):
+                q8 = O.query_haircut(qb[b, h * qg:(h + 1) * qg])
+                out[(b, h)] = O.attention(q8, K[:, j], V[:, j], w.scale)
+        return out
+
+    def gpu_cache_digest(self) -> str:
+        """SHA-256 of the whole device cache (copied to the host in pieces)."""
+        import hashlib
+        h = hashlib.sha256()
+        flat = self.cache.view(-1)
+        step = 256 << 20
+        for i in range(0, flat.numel(), step):
+            h.update(flat[i:i + step].cpu().numpy().tobytes())
+        return h.hexdigest()
 
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
