@@ -3,8 +3,10 @@
 
 Workload: B=32 sequences of 4096 tokens, Hq=32, Hk=4 (GQA-8), D=256,
 block_size 16 with a shuffled block table, 32 KV splits, bf16 q/k/v ~ N(0,1)
-(seeded, synthetic). One step = one full uq_decode (query prologue, split-KV
-stage 1, stage-2 merge) over the resident cache.
+(seeded, synthetic). One step = one full uq_decode over the resident cache:
+split-KV stage 1 with the query rotation and E4M3 haircut inside it, then
+the stage-2 merge (at head dims 128 and 512 a separate query prologue
+first).
 
 Metric: cache bytes streamed per step (sum_b L_b * Hk * 17 D / 16; 272 bytes
 per token and KV head at D = 256) / step time, in GB/s, with the fraction of
@@ -17,9 +19,9 @@ last >= 768 MB of traffic.
 Timing: HIP events on the stream the kernels run on. The host first queues a
 spin kernel, then a few untimed steps (the first launches after the idle spin
 run slower than the steady state), then all timed steps, so the GPU runs them
-back to back without waiting on Python. A second pass times each of the three kernels alone, as
-back-to-back launches, which gives the dominant kernel's duration for the
-roofline.
+back to back without waiting on Python. A second pass times each kernel
+alone, as back-to-back launches, which gives the dominant kernel's duration
+for the roofline.
 """
 import argparse
 import json
@@ -224,6 +226,9 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
         return step_ms, spread, None      # the per-kernel entry points take no options
     st = {"prologue": alone(uq.STAGE_PROLOGUE), "split_kv": alone(uq.STAGE_SPLIT),
           "merge": alone(uq.STAGE_MERGE)}
+    if w.D == 256:
+        # the two-launch form's stage 1, which computes the query codes itself
+        st["split_kv_with_query_prologue_inside"] = alone(uq.STAGE_SPLIT | uq.STAGE_FUSED_QUERY)
 
     # the streaming ceiling: a plain read of exactly the blocks the step
     # reads (all KV heads of every block of every sequence, in table order),

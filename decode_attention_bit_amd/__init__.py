@@ -223,17 +223,19 @@ def _workspace(device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-STAGE_PROLOGUE, STAGE_SPLIT, STAGE_MERGE = 1, 2, 4
+STAGE_PROLOGUE, STAGE_SPLIT, STAGE_MERGE, STAGE_FUSED_QUERY = 1, 2, 4, 8
 
 
 def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
            seq_lens: torch.Tensor, scale: float, num_kv_splits: int,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-           stages: int = 7) -> torch.Tensor:
+           stages: int | None = None) -> torch.Tensor:
     """Split-KV decode over the 4-bit cache; returns (B, Hq, D) bf16.
 
-    ``stages`` selects a subset of the three kernels (uq_decode_stages); the
-    default runs all of them (uq_decode)."""
+    ``stages`` (STAGE_PROLOGUE | STAGE_SPLIT | STAGE_MERGE, and
+    STAGE_FUSED_QUERY with STAGE_SPLIT for stage 1 computing the query codes
+    itself) runs a subset of the kernels through uq_decode_stages; None runs
+    uq_decode."""
     if query.dtype != torch.bfloat16 or query.dim() != 3 or query.stride(2) != 1:
         raise TypeError("query must be (B, Hq, D) bfloat16 with a contiguous last dim")
     if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
@@ -254,7 +256,7 @@ def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     if workspace is None:
         workspace = _workspace(query.device, max(int(need), 256))
     lib = _load()
-    fn = lib.uq_decode if stages == 7 else (lambda *a: lib.uq_decode_stages(int(stages), *a))
+    fn = lib.uq_decode if stages is None else (lambda *a: lib.uq_decode_stages(int(stages), *a))
     _check(fn(_ptr(query), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
                              float(scale), int(num_kv_splits), _ptr(out), B, Hq, Hk, D, nb, bs,
                              block_table.shape[1], query.stride(0), query.stride(1),

@@ -89,8 +89,10 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
                        int B, int Hq, int Hk, int D, int64_t num_blocks, int block_size,
                        int max_blocks_per_seq, int64_t q_stride_b, int64_t q_stride_h,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (stage_mask <= 0 || (stage_mask & ~7))
-    return fail(UQ_EINVAL, "uq_decode: stage_mask %d is not a non-empty subset of 1|2|4", stage_mask);
+  if (stage_mask <= 0 || (stage_mask & ~15) || stage_mask == UQ_STAGE_FUSED_QUERY)
+    return fail(UQ_EINVAL, "uq_decode: stage_mask %d is not a non-empty subset of 1|2|4 (| 8)", stage_mask);
+  if ((stage_mask & UQ_STAGE_FUSED_QUERY) && !(stage_mask & UQ_STAGE_SPLIT))
+    return fail(UQ_EINVAL, "uq_decode: UQ_STAGE_FUSED_QUERY needs UQ_STAGE_SPLIT");
   if (B < 1 || Hq < 1 || Hk < 1) return fail(UQ_EINVAL, "uq_decode: B=%d Hq=%d Hk=%d must be >= 1", B, Hq, Hk);
   if (num_blocks < 1 || max_blocks_per_seq < 1 || n_table_rows < 1)
     return fail(UQ_EINVAL, "uq_decode: num_blocks, max_blocks_per_seq and the table rows must be >= 1");
@@ -98,6 +100,8 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
   if (sliding_window < 0) return fail(UQ_EINVAL, "uq_decode: sliding_window %d < 0", sliding_window);
   if (D != 128 && D != 256 && D != 512)
     return fail(UQ_EUNSUPPORTED, "uq_decode: head_dim %d unsupported (128, 256, 512)", D);
+  if ((stage_mask & UQ_STAGE_FUSED_QUERY) && D != 256)
+    return fail(UQ_EUNSUPPORTED, "uq_decode: the query prologue inside stage 1 is built for head dim 256, not %d", D);
   if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "uq_decode: Hq=%d is not a multiple of Hk=%d", Hq, Hk);
   const int qg = Hq / Hk;
   if (qg != 6 && qg != 8 && qg != 16)

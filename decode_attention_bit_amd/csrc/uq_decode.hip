@@ -376,9 +376,99 @@ __device__ __forceinline__ void rebase(v4f acc[D / 16], float& m_ref, float mt, 
   m_ref = m_new;
 }
 
-template <int D, int QG, int HPW, int NSLOT>
+// In-kernel query prologue at head dim 256: q8 = E4M3(q H) for the wave's
+// QG query rows, computed while the first tiles are in flight. The 256-point
+// Hadamard is the Kronecker square of the 16-point one (H256[16a+b][16a'+b']
+// = H16[a][a'] H16[b][b'], popcounts add), so per row, with Q[a][b] =
+// q[16a + b], Y = H16 Q H16 is two 16 x 16 x 16 products on
+// V_MFMA_F64_16X16X4F64 (four each). Every product is q times +-1 and every
+// partial sum a +-subset sum of the row, so float64 keeps them exact (the
+// same exactness condition as the butterfly) and the E4M3 rounding sees the
+// exact y = Y / 16.
+//   Z = Q H16: MFMA kb takes, in lane (c, g), A = q[16c + 4g + kb] (row c,
+//     k slot g -> b = 4g + kb) and B = H16[4g + kb][c]; Z[4g + i][c] lands in
+//     register i of lane (c, g).
+//   Y = H16 Z: MFMA kb takes A = H16[c][4g + kb] (= H16[4g + kb][c]) and, as
+//     B, register kb of the lane's own Z (k slot g -> a = 4g + kb).
+//   Y[4g + i][c] = y[16 (4g + i) + c] lands in register i of lane (c, g).
+// The codes go through the wave's free LDS slot (QG rows of 256 bytes) into
+// the scaled MFMA's B layout (lane (head c, g): bytes 16g .. 16g + 15 and
+// 64 + 16g .. 64 + 16g + 15 of each 128-byte half of row c).
+typedef double v4d __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4d mfma_f64(double a, double b, v4d c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// float32 rounding of x to odd: the float32 next to x whose last bit is 1
+// when x is not a float32 (exact otherwise); rounding that to fewer bits
+// (here E4M3) then gives the same result as rounding x itself.
+__device__ __forceinline__ float to_f32_odd(double x) {
+  const float f = (float)x;                        // nearest
+  const double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  if (back != x && !(u & 1u)) u += fabs(back) < fabs(x) ? 1u : 0xFFFFFFFFu;   // the odd neighbour toward x
+  return __uint_as_float(u);
+}
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+// E4M3 (fn) codes of two float32 values, nearest even, saturating at 448: the
+// gfx950 conversion rounds to nearest even and is exact below 464 but gives
+// NaN above, so the inputs are clamped to [-448, 448] first.
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+  b = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+  const v2s16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s16){0, 0}, a, b, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0];
+}
+
+template <int QG>
+__device__ __forceinline__ void load_query_rows(const uint16_t* __restrict__ query, int64_t qsb, int64_t qsh,
+                                                int b, int h, int lane, uint2 qraw[QG]) {
+  const int n16 = lane & 15, grp = lane >> 4;
+  const uint16_t* qp = query + (int64_t)b * qsb + (int64_t)h * QG * qsh + 16 * n16 + 4 * grp;
+#pragma unroll
+  for (int r = 0; r < QG; ++r) qraw[r] = *reinterpret_cast<const uint2*>(qp + (int64_t)r * qsh);
+}
+
+template <int QG>
+__device__ __forceinline__ void rotate_queries_d256(const uint2 qraw[QG], int lane, uint8_t* __restrict__ rows,
+                                                    v8i qb[2]) {
+  const int n16 = lane & 15, grp = lane >> 4;
+  double hs[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) hs[kb] = (__popc((4 * grp + kb) & n16) & 1) ? -1.0 : 1.0;
+#pragma unroll
+  for (int r = 0; r < QG; ++r) {
+    const double q[4] = {bf16_to_f64(qraw[r].x & 0xFFFF), bf16_to_f64(qraw[r].x >> 16),
+                         bf16_to_f64(qraw[r].y & 0xFFFF), bf16_to_f64(qraw[r].y >> 16)};
+    v4d z = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) z = mfma_f64(q[kb], hs[kb], z);
+    v4d y = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) y = mfma_f64(hs[kb], z[kb], y);
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const uint32_t c = e4m3_pair(to_f32_odd(y[i] * 0.0625), to_f32_odd(y[i + 1] * 0.0625));
+      rows[r * 256 + 16 * (4 * grp + i) + n16] = (uint8_t)c;
+      rows[r * 256 + 16 * (4 * grp + i + 1) + n16] = (uint8_t)(c >> 8);
+    }
+  }
+  // the wave's own LDS writes are seen by its later reads in program order
+  if (n16 < QG) {
+    const uint8_t* rp = rows + n16 * 256;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(rp + 128 * m + 16 * grp);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(rp + 128 * m + 64 + 16 * grp);
+      qb[m] = (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    }
+  }
+}
+
+template <int D, int QG, int HPW, int NSLOT, bool FUSEQ>
 __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
-    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ cache,
+    const uint8_t* __restrict__ q8, const uint16_t* __restrict__ query, int64_t qsb, int64_t qsh,
+    const uint8_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ query_row, int n_rows,
     const int32_t* __restrict__ seq_lens,
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
@@ -423,10 +513,16 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int n16 = lane & 15, grp = lane >> 4;
   const bool qlane = n16 < QG;
   const int hq = h * QG + (qlane ? n16 : 0);
+  static_assert(!FUSEQ || D == 256, "the in-kernel query prologue is built for head dim 256");
   v8i qb[C];
 #pragma unroll
   for (int m = 0; m < C; ++m) qb[m] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
-  if (qlane) {
+  // the query rows (FUSEQ: bf16, rotated below) or their codes, requested
+  // first so that they are not queued behind the tiles
+  uint2 qraw[FUSEQ ? QG : 1];
+  if constexpr (FUSEQ) {
+    load_query_rows<QG>(query, qsb, qsh, b, h, lane, qraw);
+  } else if (qlane) {
     const uint8_t* qp = q8 + ((size_t)b * Hq + hq) * D;
 #pragma unroll
     for (int m = 0; m < C; ++m) {
@@ -525,6 +621,19 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   nv_ring0 = issue_at(ring0[wave], t0, UQ_PHYS_S(t0));
   UQ_PRE(1, UQ_PHYS_S) UQ_PRE(2, UQ_PHYS_S) UQ_PRE(3, UQ_PHYS_S) UQ_PRE(4, UQ_PHYS_S) UQ_PRE(5, UQ_PHYS_S)
   UQ_PRE(6, UQ_PHYS_S)
+  if constexpr (FUSEQ) {
+    // The ring's last slot is not filled before the first step: it holds the
+    // code rows of the transpose, read back (and waited for) before that
+    // step issues a tile into it.
+#define UQ_SLOT_PTR(K) (NSLOT > K ? &ring##K[NSLOT > K ? wave : 0][0] : &ring0[0][0])
+    uint4* const last = NSLOT == 2 ? UQ_SLOT_PTR(1) : NSLOT == 3 ? UQ_SLOT_PTR(2) : NSLOT == 4 ? UQ_SLOT_PTR(3)
+                      : NSLOT == 5 ? UQ_SLOT_PTR(4) : NSLOT == 6 ? UQ_SLOT_PTR(5) : NSLOT == 7 ? UQ_SLOT_PTR(6)
+                                                                                    : UQ_SLOT_PTR(7);
+#undef UQ_SLOT_PTR
+    static_assert(QG * 256 <= S::kTileU4 * 16, "a ring slot holds the code rows");
+    rotate_queries_d256<QG>(qraw, lane, reinterpret_cast<uint8_t*>(last), qb);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the code rows are read before the slot refills
+  }
   bool filled = true;
   for (;;) {
     Tile<D> T;
@@ -923,16 +1032,28 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   // with three slots; a grid of one round keeps three (decode 36.0 against
   // 39.9 us with two).
   const bool two_slots = p.D == 256 && n_wg * hpw > 2 * 1024;
-#define UQ_STAGE1S(DV, QGV, HPWV, NS)                                                             \
-  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, NS>), grid1, block1, 0, stream, q8,              \
-                     a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens, scale_log2,    \
-                     p.Hq, p.Hk, hgroups,                                                      \
-                     cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,            \
+#define UQ_STAGE1S(DV, QGV, HPWV, NS, FQ)                                                         \
+  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, NS, FQ>), grid1, block1, 0, stream, q8, a.query,  \
+                     a.qsb, a.qsh, a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens,     \
+                     scale_log2, p.Hq, p.Hk, hgroups,                                             \
+                     cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,                   \
                      a.num_blocks, a.window, part_o, part_m, part_l, part_e)
+  // Stage 1 reads the query codes from the workspace, or (the two-launch
+  // form, head dim 256) computes them itself.
+  const bool fuse_q = p.D == 256 && (stage_mask & 8);
+#define UQ_STAGE1F(DV, QGV, HPWV, NS)                                 \
+  do {                                                                \
+    if constexpr (DV == 256) {                                        \
+      if (fuse_q) UQ_STAGE1S(DV, QGV, HPWV, NS, true);                \
+      else UQ_STAGE1S(DV, QGV, HPWV, NS, false);                      \
+    } else {                                                          \
+      UQ_STAGE1S(DV, QGV, HPWV, NS, false);                           \
+    }                                                                 \
+  } while (0)
 #define UQ_STAGE1(DV, QGV, HPWV)                                      \
   do {                                                                \
-    if (DV == 256 && two_slots) UQ_STAGE1S(DV, QGV, HPWV, 2);         \
-    else UQ_STAGE1S(DV, QGV, HPWV, ring_slots<DV>(HPWV));             \
+    if (DV == 256 && two_slots) UQ_STAGE1F(DV, QGV, HPWV, 2);         \
+    else UQ_STAGE1F(DV, QGV, HPWV, ring_slots<DV>(HPWV));             \
   } while (0)
 #define UQ_STAGE1_HPW(DV, QGV)                  \
   do {                                          \
@@ -962,6 +1083,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
 #undef UQ_STAGE1_QG
 #undef UQ_STAGE1_HPW
 #undef UQ_STAGE1
+#undef UQ_STAGE1F
 #undef UQ_STAGE1S
   if (stage_mask & 4) {
     // waves per row: one up to 16 partials, then two, then four

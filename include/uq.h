@@ -135,6 +135,9 @@ int uq_decode_partials(int B, int Hq, int Hk, int D, int num_kv_splits, int max_
  * structure of triton_turboquant_decode_attention_v2. Enqueues three kernels
  * (query prologue, split-KV stage 1, log-sum-exp merge) on `stream`; no host
  * synchronisation and no allocation, so it can be captured in a HIP graph.
+ * (The page rotates the query inside its decode kernel; that two-launch form
+ * is uq_decode_stages(UQ_STAGE_SPLIT | UQ_STAGE_FUSED_QUERY | UQ_STAGE_MERGE)
+ * at D = 256, bit for bit the same output.)
  *   query:       (device) bf16, element (b, hq, d) at b*q_stride_b + hq*q_stride_h + d.
  *   kv_cache:    (device) uint8 (num_blocks, block_size, Hk, 17*D/16), read only.
  *   block_table: (device) int32 (B, max_blocks_per_seq): logical block j of
@@ -213,11 +216,22 @@ int uq_decode_ex(const uint16_t* query, const uint8_t* kv_cache,
  * (stage 2, reads stage 1's output). Running the three masks in that order on
  * one stream, with the same arguments and workspace, is exactly uq_decode;
  * it exists so a caller can time or capture each kernel on its own.
- * Errors: as uq_decode, plus UQ_EINVAL for an empty or unknown mask.
+ * UQ_STAGE_FUSED_QUERY, with UQ_STAGE_SPLIT, makes stage 1 compute the query
+ * codes itself (D = 256 only: the in-kernel Walsh-Hadamard rotation of the
+ * flydsl_ultraquant_decode page, here a 16 x 16 Kronecker product on float64
+ * matrix cores, exact, then E4M3); UQ_STAGE_SPLIT | UQ_STAGE_FUSED_QUERY |
+ * UQ_STAGE_MERGE is then a two-launch decode, bit for bit uq_decode's output.
+ * Every partial's workgroup repeats its rows' rotation, which measured slower
+ * than the separate prologue launch on every workload, so uq_decode keeps
+ * three launches.
+ * Errors: as uq_decode, plus UQ_EINVAL for an empty or unknown mask (or
+ * UQ_STAGE_FUSED_QUERY without UQ_STAGE_SPLIT) and UQ_EUNSUPPORTED for
+ * UQ_STAGE_FUSED_QUERY at D != 256.
  */
 #define UQ_STAGE_PROLOGUE 1
 #define UQ_STAGE_SPLIT    2
 #define UQ_STAGE_MERGE    4
+#define UQ_STAGE_FUSED_QUERY 8
 int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_cache,
                      const int32_t* block_table, const int32_t* seq_lens, float scale,
                      int num_kv_splits, uint16_t* out, int B, int Hq, int Hk, int D,

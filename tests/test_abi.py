@@ -99,9 +99,14 @@ def test_decode_rejects(libuq, kw, code):
     assert _err(libuq)
 
 
-@pytest.mark.parametrize("mask", [0, 8, -1, 15])
+@pytest.mark.parametrize("mask", [0, 8, -1, 16, 12, 9, 13])
 def test_decode_stages_rejects_mask(libuq, mask):
     assert libuq.uq_decode_stages(mask, *decode_args()) == -1
+
+
+def test_decode_stages_fused_query_only_at_256(libuq):
+    assert libuq.uq_decode_stages(2 | 8, *decode_args(D=128)) == -2
+    assert "head dim 256" in _err(libuq)
 
 
 def test_workspace_bytes(libuq):

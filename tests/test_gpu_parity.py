@@ -442,17 +442,21 @@ def _extreme_queries(rng, B, Hq):
 def test_decode_extreme_queries(qg):
     """Query rows of every kind the haircut distinguishes (flushed, subnormal,
     saturated, wide-range, one-hot) through a whole decode: the output
-    matches the oracle, and bit for bit the output of the prologue run on
-    its own followed by stages 1 and 2."""
+    matches the oracle, bit for bit the output of the prologue run on its own
+    followed by stages 1 and 2, and bit for bit the two-launch form whose
+    stage 1 computes the query codes itself."""
     say(f"decode extreme queries qg={qg}")
     Hk = 2
     _, _, ctx = _decode_case([37, 20, 64], Hk=Hk, qg=qg, splits=2, seed=11 + qg)
     q = _extreme_queries(np.random.default_rng(qg), 3, Hk * qg).to(DEV)
     full = uq.decode(q, ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 2)
+    args = (q, ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 2)
     o = torch.empty_like(full)
     for st in (uq.STAGE_PROLOGUE, uq.STAGE_SPLIT | uq.STAGE_MERGE):
-        uq.decode(q, ctx["cache"], ctx["table"], ctx["lens"], ctx["scale"], 2, out=o, stages=st)
+        uq.decode(*args, out=o, stages=st)
     assert torch.equal(o, full)
+    fused = uq.decode(*args, stages=uq.STAGE_SPLIT | uq.STAGE_FUSED_QUERY | uq.STAGE_MERGE)
+    assert torch.equal(fused, full), "in-kernel query codes differ from the prologue kernel's"
     ref = O.decode(bits(q.cpu()), ctx["ref_cache"], ctx["table"].cpu().numpy(),
                    ctx["lens"].cpu().numpy(), ctx["scale"])
     check_close(to_np(full), ref, f"extreme queries qg={qg}", allow_output_rounding=True)
