@@ -30,7 +30,7 @@ import os
 
 import torch
 
-__all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_workspace_bytes",
+__all__ = ["build_hadamard", "store", "decode", "decode_ex", "decode_no_alloc", "decode_workspace_bytes",
            "decode_partials", "stream_blocks", "rotate",
            "dequant_kv", "prefill_attention", "continuation_prefill",
            "continuation_prefill_workspace_bytes", "library_path",
@@ -101,6 +101,9 @@ def _load():
     lib.uq_continuation_prefill.restype = i32
     lib.uq_continuation_prefill_stages.argtypes = [i32] + lib.uq_continuation_prefill.argtypes
     lib.uq_continuation_prefill_stages.restype = i32
+    lib.uq_decode_no_alloc.argtypes = [vp, vp, vp, vp, ctypes.c_float, i32, vp, i32, i32, i32, i32, i64,
+                                       i32, i32, i64, i64, vp]
+    lib.uq_decode_no_alloc.restype = i32
     lib.uq_decode_partials.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.uq_decode_partials.restype = i32
     lib.uq_stream_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i64, i32, i32, vp, i32, vp]
@@ -262,6 +265,33 @@ def decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
                              block_table.shape[1], query.stride(0), query.stride(1),
                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(query.device)))
+    return out
+
+
+def decode_no_alloc(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                    seq_lens: torch.Tensor, scale: float, num_kv_splits: int,
+                    out: torch.Tensor) -> torch.Tensor:
+    """uq_decode_no_alloc: uq_decode with the workspace in the library's
+    device scratch (no allocation at all: ``out`` is the caller's). Calls that
+    may overlap on one device share that scratch and must be serialised."""
+    if query.dtype != torch.bfloat16 or query.dim() != 3 or query.stride(2) != 1:
+        raise TypeError("query must be (B, Hq, D) bfloat16 with a contiguous last dim")
+    if kv_cache.dtype != torch.uint8 or not kv_cache.is_contiguous() or kv_cache.dim() != 4:
+        raise TypeError("kv_cache must be a contiguous 4-d uint8 tensor")
+    if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise TypeError("block_table must be a contiguous (B, max_blocks) int32 tensor")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("seq_lens must be a contiguous int32 tensor")
+    B, Hq, D = query.shape
+    nb, bs, Hk, ss = kv_cache.shape
+    if block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table / seq_lens batch mismatch")
+    if out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
+        raise TypeError("out must be a contiguous (B, Hq, D) bfloat16 tensor")
+    _check(_load().uq_decode_no_alloc(_ptr(query), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+                                      float(scale), int(num_kv_splits), _ptr(out), B, Hq, Hk, D, nb, bs,
+                                      block_table.shape[1], query.stride(0), query.stride(1),
+                                      _stream(query.device)))
     return out
 
 

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/uq.h"
@@ -82,13 +83,58 @@ size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits
   return uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).total;
 }
 
+// Device scratch of uq_decode_no_alloc: the decode's workspace (query codes,
+// partial rows and their statistics) for callers that cannot allocate. One
+// copy per device, held from the library's load on that device until the
+// process ends. Host code never uses the array's name as an address: each
+// device's copy is at the address hipGetSymbolAddress gives with that device
+// current, taken once per device and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[UQ_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The scratch address on the device of `stream` (which must be the current
+// device: the symbol's address is per device).
+int scratch_address(void* stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(UQ_EHIP, "uq_decode_no_alloc: hipGetDevice: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice((hipStream_t)stream, &dev);
+    if (e != hipSuccess) return fail(UQ_EHIP, "uq_decode_no_alloc: hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev != cur)
+    return fail(UQ_EINVAL, "uq_decode_no_alloc: the stream belongs to device %d, not the current device %d", dev, cur);
+  if (dev < 0 || dev >= kMaxDevices) return fail(UQ_EUNSUPPORTED, "uq_decode_no_alloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(UQ_EHIP, "uq_decode_no_alloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ok();
+}
+
+}  // namespace
+
+// use_scratch: the workspace is the device scratch (uq_decode_no_alloc);
+// workspace and workspace_bytes are then ignored.
 static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_cache,
                        const int32_t* block_table, int n_table_rows, const int32_t* query_row,
                        const int32_t* seq_lens, float scale, int num_kv_splits,
                        const float* sinks, int sliding_window, uint16_t* out,
                        int B, int Hq, int Hk, int D, int64_t num_blocks, int block_size,
                        int max_blocks_per_seq, int64_t q_stride_b, int64_t q_stride_h,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       bool use_scratch = false) {
   if (stage_mask <= 0 || (stage_mask & ~15) || stage_mask == UQ_STAGE_FUSED_QUERY)
     return fail(UQ_EINVAL, "uq_decode: stage_mask %d is not a non-empty subset of 1|2|4 (| 8)", stage_mask);
   if ((stage_mask & UQ_STAGE_FUSED_QUERY) && !(stage_mask & UQ_STAGE_SPLIT))
@@ -112,20 +158,27 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
     return fail(UQ_EUNSUPPORTED, "uq_decode: num_kv_splits %d outside [1, %d]", num_kv_splits, UQ_MAX_SPLITS);
   if ((long long)max_blocks_per_seq * block_size > 0x7FFFFFFFLL)
     return fail(UQ_EUNSUPPORTED, "uq_decode: max_blocks_per_seq * block_size exceeds 2^31");
-  if (!query || !kv_cache || !block_table || !seq_lens || !out || !workspace)
+  if (!query || !kv_cache || !block_table || !seq_lens || !out || (!workspace && !use_scratch))
     return fail(UQ_EINVAL, "uq_decode: null pointer argument");
   if (q_stride_b < 0 || q_stride_h < 0 || q_stride_b % 4 || q_stride_h % 4)
     return fail(UQ_EINVAL, "uq_decode: query strides must be non-negative multiples of 4 elements");
-  if (!aligned(query, 8) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
+  if (!aligned(query, 8) || !aligned(kv_cache, 16) || !aligned(out, 16) || (!use_scratch && !aligned(workspace, 256)) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_row, 4) ||
       !aligned(sinks, 4))
     return fail(UQ_EINVAL, "uq_decode: misaligned pointer (query 8 B, kv_cache/out 16 B, workspace 256 B)");
   const uq::DecodePlan plan =
       uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D);
-  if (workspace_bytes < plan.total)
+  if (use_scratch && plan.total > (size_t)UQ_NO_ALLOC_SCRATCH_BYTES)
+    return fail(UQ_EWORKSPACE, "uq_decode_no_alloc: this shape needs %zu bytes of scratch, above the %zu-byte "
+                "static buffer; use uq_decode with a workspace", plan.total, (size_t)UQ_NO_ALLOC_SCRATCH_BYTES);
+  if (!use_scratch && workspace_bytes < plan.total)
     return fail(UQ_EWORKSPACE, "uq_decode: workspace %zu bytes < required %zu", workspace_bytes, plan.total);
   if ((long long)B * plan.parts * Hk > 0x7FFFFFFFLL || (long long)B * Hq > 0x7FFFFFFFLL)
     return fail(UQ_EUNSUPPORTED, "uq_decode: grid too large");
+  if (use_scratch) {                       // every argument checked: now the first HIP call
+    const int rc = scratch_address(stream, &workspace);
+    if (rc != UQ_OK) return rc;
+  }
   uq::DecodeArgs a{query, kv_cache, block_table, query_row, n_table_rows, seq_lens, sinks,
                    sliding_window, scale, out,
                    num_blocks, block_size,
@@ -198,6 +251,15 @@ int uq_decode(const uint16_t* query, const uint8_t* kv_cache, const int32_t* blo
                           block_table, seq_lens, scale, num_kv_splits, out, B, Hq, Hk, D,
                           num_blocks, block_size, max_blocks_per_seq, q_stride_b, q_stride_h,
                           workspace, workspace_bytes, stream);
+}
+
+int uq_decode_no_alloc(const uint16_t* query, const uint8_t* kv_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, float scale, int num_kv_splits, uint16_t* out, int B,
+                       int Hq, int Hk, int D, int64_t num_blocks, int block_size, int max_blocks_per_seq,
+                       int64_t q_stride_b, int64_t q_stride_h, void* stream) {
+  return decode_impl(UQ_STAGE_PROLOGUE | UQ_STAGE_SPLIT | UQ_STAGE_MERGE, query, kv_cache, block_table, B,
+                     nullptr, seq_lens, scale, num_kv_splits, nullptr, 0, out, B, Hq, Hk, D, num_blocks,
+                     block_size, max_blocks_per_seq, q_stride_b, q_stride_h, nullptr, 0, stream, true);
 }
 
 int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t x_stride_n,

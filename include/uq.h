@@ -170,6 +170,34 @@ int uq_decode(const uint16_t* query, const uint8_t* kv_cache,
               size_t workspace_bytes, void* stream);
 
 /*
+ * uq_decode for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * the same output bit for bit, with the workspace taken from a device array
+ * inside the library instead of the caller's memory. The array,
+ * UQ_NO_ALLOC_SCRATCH_BYTES (64 MiB) per device, is held from the library's
+ * load on a device until the process ends; its address is looked up once per
+ * device (hipGetSymbolAddress) on the first call there. The call allocates
+ * nothing and does not synchronise.
+ *   Arguments as for uq_decode, without workspace and workspace_bytes.
+ *   `stream` must belong to the current device (NULL: the current device's
+ *   null stream).
+ * Every call on a device shares that device's array: calls whose work may
+ * overlap on one device (several streams, or several threads) race and must
+ * be serialised by the caller. The array needs no initialisation: every byte
+ * a call reads was written by that call.
+ * Errors: as uq_decode; UQ_EWORKSPACE when the shape needs more than
+ * UQ_NO_ALLOC_SCRATCH_BYTES (checked on the host before any HIP call, like
+ * every argument; uq_decode_workspace_bytes gives the need), UQ_EINVAL for a
+ * stream of another device.
+ */
+#define UQ_NO_ALLOC_SCRATCH_BYTES (64 << 20)
+int uq_decode_no_alloc(const uint16_t* query, const uint8_t* kv_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, float scale,
+                       int num_kv_splits, uint16_t* out, int B, int Hq, int Hk, int D,
+                       int64_t num_blocks, int block_size, int max_blocks_per_seq,
+                       int64_t q_stride_b, int64_t q_stride_h, void* stream);
+
+/*
  * uq_decode with three options; uq_decode is this call with none of them.
  *
  * Multi-query rows (query_row). Several query rows may read the same

@@ -22,6 +22,7 @@ def test_header_declares_entry_points():
               "uq_decode_workspace_bytes", "uq_rotate", "uq_dequant_kv", "uq_prefill_attention",
               "uq_continuation_prefill", "uq_continuation_prefill_stages",
               "uq_continuation_prefill_workspace_bytes", "uq_decode_partials", "uq_stream_blocks",
+              "uq_decode_no_alloc",
               "uq_last_error"):
         assert n in names
 
@@ -258,3 +259,20 @@ def test_other_head_dims_accepted(libuq, d):
     n = f(2, 16, 2, d, 1, 1, 16)
     assert n == 2 * 16 * d + 2 * 16 * d * 2 + 3 * 256
     assert f(2, 16, 2, d, 1, 1, 16) < f(2, 16, 2, 2 * d, 1, 1, 16) if d < 512 else True
+
+
+def test_decode_no_alloc_rejects_on_the_host(libuq):
+    """Checked before any HIP call, like every entry point: bad arguments,
+    and a shape whose workspace exceeds the static scratch (64 MiB)."""
+    args = decode_args()
+    del args[-3:-1]                      # no workspace, no workspace bytes
+    big = decode_args(B=4096)
+    del big[-3:-1]
+    assert libuq.uq_decode_no_alloc(*big) == -3
+    assert "scratch" in _err(libuq)
+    bad = decode_args(D=64)
+    del bad[-3:-1]
+    assert libuq.uq_decode_no_alloc(*bad) == -2
+    nul = decode_args(query=None)
+    del nul[-3:-1]
+    assert libuq.uq_decode_no_alloc(*nul) == -1
