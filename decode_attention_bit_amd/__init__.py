@@ -14,9 +14,7 @@ Entry points mirror include/uq.h:
   decode_ex(query, kv_cache, block_table, seq_lens, scale, num_kv_splits,
             query_row=None, sinks=None, sliding_window=0,
             out=None, workspace=None)               -> (B, Hq, D) bf16
-Store, decode, rotate and dequant_kv take head dims D in {128, 256, 512}
-(slot 17*D/16 bytes); prefill_attention and continuation_prefill take
-D in {128, 256}.
+Every call takes head dims D in {128, 256, 512} (slot 17*D/16 bytes).
   rotate(x, out=None)                               -> bf16(x H), same shape
   dequant_kv(kv_cache, block_row, n_tokens)         -> (K, V) (n_tokens, Hk, D) bf16
   prefill_attention(q, k, v, scale, out=None)       -> (q_len, Hq, D) bf16
@@ -395,7 +393,7 @@ def dequant_kv(kv_cache: torch.Tensor, block_row: torch.Tensor, n_tokens: int,
 def prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
                       out: torch.Tensor | None = None) -> torch.Tensor:
     """uq_prefill_attention: causal attention of (q_len, Hq, D) bf16 queries
-    over (seq_len, Hk, D) bf16 keys/values, D in {128, 256}, query i at
+    over (seq_len, Hk, D) bf16 keys/values, D in {128, 256, 512}, query i at
     position seq_len - q_len + i; returns (q_len, Hq, D) bf16."""
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _bf16_3d(t, name)
@@ -429,7 +427,7 @@ def continuation_prefill(query: torch.Tensor, key: torch.Tensor, value: torch.Te
                          scale: float, out: torch.Tensor | None = None,
                          workspace: torch.Tensor | None = None, stages: int = 3) -> torch.Tensor:
     """uq_continuation_prefill: a chunk of q_len tokens (query (q_len, Hq, D),
-    key / value (q_len, Hk, D), bf16, unrotated, D in {128, 256}) after
+    key / value (q_len, Hk, D), bf16, unrotated, D in {128, 256, 512}) after
     cached_len cached tokens reached through block_row (a cache of head dim
     D); returns (q_len, Hq, D) bf16.
     ``stages`` selects the gather and/or the attention launch

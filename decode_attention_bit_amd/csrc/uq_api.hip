@@ -318,11 +318,11 @@ static int check_attention_shape(const char* who, int q_len, int seq_len, int Hq
   if (q_len < 0 || seq_len < q_len || Hq < 1 || Hk < 1)
     return fail(UQ_EINVAL, "%s: q_len=%d seq_len=%d Hq=%d Hk=%d", who, q_len, seq_len, Hq, Hk);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(UQ_EINVAL, "%s: scale must be finite and > 0", who);
-  if (D != UQ_HEAD_DIM && D != UQ_HEAD_DIM / 2)
-    return fail(UQ_EUNSUPPORTED, "%s: head_dim %d unsupported (128, 256)", who, D);
+  if (D != UQ_HEAD_DIM && D != UQ_HEAD_DIM / 2 && D != 2 * UQ_HEAD_DIM)
+    return fail(UQ_EUNSUPPORTED, "%s: head_dim %d unsupported (128, 256, 512)", who, D);
   if (Hq % Hk) return fail(UQ_EUNSUPPORTED, "%s: Hq=%d is not a multiple of Hk=%d", who, Hq, Hk);
-  if (uq::prefill_positions_per_wg(Hq / Hk) < 1)
-    return fail(UQ_EUNSUPPORTED, "%s: GQA group %d above 128", who, Hq / Hk);
+  if (uq::prefill_positions_per_wg(Hq / Hk, D) < 1)
+    return fail(UQ_EUNSUPPORTED, "%s: GQA group %d above %d", who, Hq / Hk, D > UQ_HEAD_DIM ? 64 : 128);
   if (Hk > 65535) return fail(UQ_EUNSUPPORTED, "%s: Hk=%d above 65535", who, Hk);
   return ok();
 }
@@ -351,8 +351,9 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
 }
 
 // Workspace of uq_continuation_prefill: rotated queries, keys of prefix +
-// chunk (token-major), then the values in the tiled layout of the attention
-// kernel (per KV head, ceil(seq_len / 32) tiles of 64 D bytes), each section
+// chunk (token-major), then the values: at head dims 128 and 256 in the tiled
+// layout of the attention kernel (per KV head, ceil(seq_len / 32) tiles of
+// 64 D bytes), at 512 token-major like the keys (vt_tiles = 0); each section
 // 256-byte aligned.
 struct PrefillLayout {
   size_t q_off, k_off, v_off, total;
@@ -362,16 +363,18 @@ struct PrefillLayout {
 static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, int Hk, int D) {
   auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   PrefillLayout l{};
-  l.vt_tiles = (seq_len + 31) / 32;
+  l.vt_tiles = D <= UQ_HEAD_DIM ? (seq_len + 31) / 32 : 0;
   l.q_off = 0;
   l.k_off = a256((size_t)q_len * Hq * D * 2);
   l.v_off = l.k_off + a256((size_t)seq_len * Hk * D * 2);
-  l.total = l.v_off + (size_t)Hk * l.vt_tiles * 32 * D * 2;
+  l.total = l.v_off + (l.vt_tiles > 0 ? (size_t)Hk * l.vt_tiles * 32 * D * 2 : (size_t)seq_len * Hk * D * 2);
   return l;
 }
 
 size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int Hq, int Hk, int D) {
-  if (q_len < 0 || max_seq_len < q_len || Hq < 1 || Hk < 1 || Hq % Hk || (D != UQ_HEAD_DIM && D != UQ_HEAD_DIM / 2))
+  if (q_len < 0 || max_seq_len < q_len || Hq < 1 || Hk < 1 || Hq % Hk ||
+      (D != UQ_HEAD_DIM && D != UQ_HEAD_DIM / 2 && D != 2 * UQ_HEAD_DIM) ||
+      uq::prefill_positions_per_wg(Hq / Hk, D) < 1)
     return 0;
   const size_t t = prefill_layout(q_len, max_seq_len, Hq, Hk, D).total;
   return t > 0 ? t : 256;
@@ -429,20 +432,23 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   g.Hk = Hk;
   g.num_blocks = num_blocks;
   g.log2_bs = log2_bs;
+  const bool tiled = lay.vt_tiles > 0;
   g.kout = kf;
-  g.vout = nullptr;
+  g.vout = tiled ? nullptr : vf;
   g.os_t = row;
   g.os_h = D;
-  g.vt = vf;
+  g.vt = tiled ? vf : nullptr;
   g.vt_tiles = lay.vt_tiles;
   g.vt_pad0 = seq_len;
-  g.vt_pad = lay.vt_tiles * 32 - seq_len;
+  g.vt_pad = tiled ? lay.vt_tiles * 32 - seq_len : 0;
   g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * D, D,
                         (int64_t)q_len * Hq, Hq, 1, 0, 0};
   g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, D,
                         (int64_t)q_len * Hk, Hk, 1, 0, 0};
-  g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, nullptr, 0, 0, (int64_t)q_len * Hk, Hk, 0, 1,
-                        (int64_t)cached_len};
+  g.job[2] = tiled ? uq::VecJob{value, val_stride_t, val_stride_h, nullptr, 0, 0, (int64_t)q_len * Hk, Hk, 0, 1,
+                                (int64_t)cached_len}
+                   : uq::VecJob{value, val_stride_t, val_stride_h, vf + (int64_t)cached_len * row, row, D,
+                                (int64_t)q_len * Hk, Hk, 0, 0, 0};
   if (stage_mask & UQ_PREFILL_GATHER) {
     hipError_t e = uq::launch_gather(g, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");

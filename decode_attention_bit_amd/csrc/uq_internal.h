@@ -93,8 +93,8 @@ struct PrefillAttnArgs {
   int64_t qs_t, qs_h, kvs_t, kvs_h, os_t, os_h;
   int q_len, cached_len, Hk, QG;
   float scale;
-  int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head
-  int D;                     // head dim: 128 or 256
+  int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head (D <= 256)
+  int D;                     // head dim: 128, 256 or 512
 };
 
 // Streaming-read probe over the blocks a decode reads.
@@ -115,7 +115,7 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_hadamard(int D, float* H, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream);
-int prefill_positions_per_wg(int QG);
+int prefill_positions_per_wg(int QG, int D);
 hipError_t launch_stream_blocks(const StreamArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mask, hipStream_t stream);
 

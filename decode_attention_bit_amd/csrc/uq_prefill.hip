@@ -595,6 +595,212 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head dim 512: rows of 1 KB, so keys stream in tiles of 16 (four stages of
+// K and V still fit in 128 KB of LDS) and values stay token-major. Four
+// waves of 16 columns each (64 columns of one KV head; a wave's 128
+// accumulator and 64 query registers need the register file of a SIMD to
+// itself) and the same pipeline as above; what changes with the tile:
+//   S^T (16 keys x 16 cols) = K Q^T takes D/32 MFMAs; lane (col, g) is left
+//     with keys 4g + i of its column.
+//   O += P V: a 16-key tile fills only half of the 32 k-slots, so the high
+//     and low bf16 parts of each weight share one MFMA: slot (g, s) stands
+//     for key 4g + (s & 3), the high part for s < 4 and the low one for
+//     s >= 4, and B repeats that key's value in both halves. Lane (r, g)
+//     reads 8 bytes (dims 64b + 4r .. 64b + 4r + 3) of each of its 4 keys;
+//     byte permutes sort them by dim mod 4 into four B operands, one per
+//     accumulator 4b + (dim mod 4).
+// Chunk c of LDS row r holds chunk c ^ f(r) of the key's row: f(r) = r & 15
+// for K (the 16 rows of a score read hit distinct banks), ((r >> 2) & 3) << 3
+// for V (the four key groups of a value read sit 128 bytes apart).
+// ---------------------------------------------------------------------------
+constexpr int kColsPerWg16 = 64;
+
+template <int DV>
+__global__ __launch_bounds__(256) void prefill_attn16_kernel(
+    const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
+    int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2) {
+  constexpr int KT = 16, kRowBytes = 2 * DV, NCH = kRowBytes / 16;
+  static_assert(NCH == 64, "one 1 KB load per row");
+  constexpr int kTileU4 = KT * NCH;
+  constexpr int NJ = DV / 32, NB = DV / 64, NACC = DV / 16;
+  constexpr int WAVES = kColsPerWg16 / 16, ROWS = KT / WAVES;   // rows of K and of V each wave moves
+  __shared__ uint4 kr0[kTileU4], kr1[kTileU4], kr2[kTileU4], kr3[kTileU4];
+  __shared__ uint4 vr0[kTileU4], vr1[kTileU4], vr2[kTileU4], vr3[kTileU4];
+
+  const int n_ptiles = (q_len + ppw - 1) / ppw;
+  const int p0 = (n_ptiles - 1 - (int)blockIdx.x) * ppw;
+  const int hk = blockIdx.y;
+  const int p_end = min(p0 + ppw, q_len);
+  const int kend = cached_len + p_end;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+
+  const int c0 = 16 * wave + r16;
+  const int cpos = p0 + c0 / QG;
+  const bool cval = c0 < ppw * QG && cpos < q_len;
+  const int klim = cached_len + cpos + 1;
+  v8bf qb[NJ];
+  {
+    const uint16_t* qp = q + (int64_t)(cval ? cpos : 0) * qs_t + (int64_t)(cval ? hk * QG + c0 % QG : 0) * qs_h + 8 * g;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (cval) x = ld16(qp + 32 * j);
+      qb[j] = __builtin_bit_cast(v8bf, x);
+    }
+  }
+
+  const uint32_t row_bytes = (uint32_t)(kvs_t * 2);
+  uint32_t koff[ROWS], voff[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int r = ROWS * wave + i;
+    koff[i] = r * row_bytes + 16 * (lane ^ (r & 15));
+    voff[i] = r * row_bytes + 16 * (lane ^ (((r >> 2) & 3) << 3));
+  }
+  const int n_kt = (kend + KT - 1) / KT;
+  auto issue = [&](uint4* ks, uint4* vs, int t) {
+    const int key0 = t * KT;
+    const int nv = min(KT, kend - key0);
+    const int nrec = (nv - 1) * (int)row_bytes + kRowBytes;
+    const int64_t base = (int64_t)key0 * kvs_t + (int64_t)hk * kvs_h;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((void*)(k + base), nrec);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((void*)(v + base), nrec);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) load_lds16(rk, ks + 64 * (ROWS * wave + i), koff[i]);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) load_lds16(rv, vs + 64 * (ROWS * wave + i), voff[i]);
+  };
+
+  v4f acc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  v4f lsum = {0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;
+  const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
+  auto scores = [&](const uint4* ks) {
+    const uint8_t* kb_ = reinterpret_cast<const uint8_t*>(ks);
+    // two independent accumulation chains, added at the end
+    v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int h = 0; h < NJ / 4; ++h) {
+      v8bf ka[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ka[j] = __builtin_bit_cast(v8bf, ld16(kb_ + r16 * kRowBytes + 16 * ((4 * (4 * h + j) + g) ^ r16)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j & 1] = mfma_bf16(ka[j], qb[4 * h + j], s[j & 1]);
+    }
+    return s[0] + s[1];
+  };
+
+  auto weigh = [&](const v4f& s, const uint4* vs, int t) {
+    const uint8_t* vb_ = reinterpret_cast<const uint8_t*>(vs);
+    const int key0 = t * KT;
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = s[i];
+    if (key0 + KT > cached_len + p0 + 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key0 + 4 * g + i >= klim) sv[i] = -INFINITY;
+    }
+    const float mt = rowgroup_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * scale_log2;
+    if (t == 0) m_ref = mt;
+    if (__any(mt > m_ref + 8.0f)) {
+      // raise the reference, O <- diag(f) O on float32 MFMAs (as above)
+      const float m_new = fmaxf(m_ref, mt);
+      const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
+      float fsel[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fsel[i] = r16 == 4 * g + i ? f : 0.f;
+#pragma unroll
+      for (int j = 0; j < NACC + 1; ++j) {
+        v4f& a = j < NACC ? acc[j] : lsum;
+        v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d = mfma_f32x4(fsel[i], a[i], d);
+        a = d;
+      }
+      m_ref = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -m_ref));
+    const uint32_t h01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p[0], p[1]}, v2bf));
+    const uint32_t h23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p[2], p[3]}, v2bf));
+    const uint32_t l01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+        (v2f){p[0] - __uint_as_float(h01 << 16), p[1] - __uint_as_float(h01 & 0xFFFF0000u)}, v2bf));
+    const uint32_t l23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+        (v2f){p[2] - __uint_as_float(h23 << 16), p[3] - __uint_as_float(h23 & 0xFFFF0000u)}, v2bf));
+    const v8bf pb = __builtin_bit_cast(v8bf, make_uint4(h01, h23, l01, l23));
+    lsum = mfma_bf16(pb, ones, lsum);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      uint2 w[4];
+#pragma unroll
+      for (int s_ = 0; s_ < 4; ++s_)
+        w[s_] = *reinterpret_cast<const uint2*>(vb_ + (4 * g + s_) * kRowBytes + 128 * (b ^ g) + 8 * r16);
+      const uint32_t x0 = __builtin_amdgcn_perm(w[1].x, w[0].x, 0x05040100u);
+      const uint32_t y0 = __builtin_amdgcn_perm(w[3].x, w[2].x, 0x05040100u);
+      const uint32_t x1 = __builtin_amdgcn_perm(w[1].x, w[0].x, 0x07060302u);
+      const uint32_t y1 = __builtin_amdgcn_perm(w[3].x, w[2].x, 0x07060302u);
+      const uint32_t x2 = __builtin_amdgcn_perm(w[1].y, w[0].y, 0x05040100u);
+      const uint32_t y2 = __builtin_amdgcn_perm(w[3].y, w[2].y, 0x05040100u);
+      const uint32_t x3 = __builtin_amdgcn_perm(w[1].y, w[0].y, 0x07060302u);
+      const uint32_t y3 = __builtin_amdgcn_perm(w[3].y, w[2].y, 0x07060302u);
+      acc[4 * b] = mfma_bf16(pb, __builtin_bit_cast(v8bf, make_uint4(x0, y0, x0, y0)), acc[4 * b]);
+      acc[4 * b + 1] = mfma_bf16(pb, __builtin_bit_cast(v8bf, make_uint4(x1, y1, x1, y1)), acc[4 * b + 1]);
+      acc[4 * b + 2] = mfma_bf16(pb, __builtin_bit_cast(v8bf, make_uint4(x2, y2, x2, y2)), acc[4 * b + 2]);
+      acc[4 * b + 3] = mfma_bf16(pb, __builtin_bit_cast(v8bf, make_uint4(x3, y3, x3, y3)), acc[4 * b + 3]);
+    }
+  };
+
+  issue(kr0, vr0, 0);
+  if (1 < n_kt) issue(kr1, vr1, 1);
+  if (2 < n_kt) issue(kr2, vr2, 2);
+  wait_tiles<kStages - 2, 2 * ROWS>(n_kt - 1);
+  __syncthreads();
+  v4f cur = scores(kr0);
+#define UQP_STEP16(KC, VC, KN, KF, VF)                               \
+  {                                                                  \
+    wait_tiles<kStages - 3, 2 * ROWS>(n_kt - 2 - t);                 \
+    __syncthreads();                                                 \
+    if (t + kStages - 1 < n_kt) issue(KF, VF, t + kStages - 1);      \
+    const v4f nxt = scores(KN);                                      \
+    weigh(cur, VC, t);                                               \
+    cur = nxt;                                                       \
+    if (++t >= n_kt) break;                                          \
+  }
+  for (int t = 0;;) {
+    UQP_STEP16(kr0, vr0, kr1, kr3, vr3)
+    UQP_STEP16(kr1, vr1, kr2, kr0, vr0)
+    UQP_STEP16(kr2, vr2, kr3, kr1, vr1)
+    UQP_STEP16(kr3, vr3, kr0, kr2, vr2)
+  }
+#undef UQP_STEP16
+
+  // lane (r, g) holds, for column 4g + i, O at dims 64b + 4r + m in
+  // accumulator 4b + m, and that column's weight sum
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 16 * wave + 4 * g + i;
+    const float inv = 1.f / lsum[i];
+    const int pos = p0 + c / QG;
+    if (!(c < ppw * QG && pos < q_len)) continue;
+    uint16_t* op = out + (int64_t)pos * os_t + (int64_t)(hk * QG + c % QG) * os_h + 4 * r16;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      *reinterpret_cast<uint2*>(op + 64 * b) = make_uint2(
+          __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){acc[4 * b][i] * inv, acc[4 * b + 1][i] * inv}, v2bf)),
+          __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){acc[4 * b + 2][i] * inv, acc[4 * b + 3][i] * inv}, v2bf)));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
@@ -613,13 +819,24 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int prefill_positions_per_wg(int QG) { return QG <= kColsPerWg ? kColsPerWg / QG : 0; }
+int prefill_positions_per_wg(int QG, int D) {
+  const int cols = D > kHeadDim ? kColsPerWg16 : kColsPerWg;
+  return QG <= cols ? cols / QG : 0;
+}
 
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
   if (a.q_len == 0) return hipSuccess;
-  if (a.D != kHeadDim && a.D != kHeadDim / 2) return hipErrorInvalidValue;
-  const int ppw = prefill_positions_per_wg(a.QG);
+  if (a.D != kHeadDim && a.D != kHeadDim / 2 && a.D != 2 * kHeadDim) return hipErrorInvalidValue;
+  const int ppw = prefill_positions_per_wg(a.QG, a.D);
   const int n_ptiles = (a.q_len + ppw - 1) / ppw;
+  if (a.D == 2 * kHeadDim) {                 // token-major values only
+    if (a.vt_tiles > 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_attn16_kernel<512>), dim3((unsigned)n_ptiles, (unsigned)a.Hk),
+                       dim3(64 * (kColsPerWg16 / 16)), 0,
+                       stream, a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h,
+                       a.q_len, a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)n_ptiles, (unsigned)a.Hk), block(64 * (8 / CB));
   const float sl2 = a.scale * 1.4426950408889634f;
 #define UQP_LAUNCH(VTV, DVV, TILES)                                                                      \

@@ -40,8 +40,7 @@
  * The rotation of head dim D is the Sylvester Hadamard matrix with entries
  * (-1)**popcount(i & j) times one float64 scale, the nearest double to
  * 1/sqrt(D) (exactly 1/16 for D = 256).
- * Store, decode, uq_rotate and uq_dequant_kv take D in {128, 256, 512};
- * uq_prefill_attention and uq_continuation_prefill take D in {128, 256}.
+ * Every call takes D in {128, 256, 512}.
  */
 #ifndef UQ_H
 #define UQ_H
@@ -325,11 +324,12 @@ int uq_dequant_kv(const uint8_t* kv_cache, const int32_t* block_row, int n_token
  * j <= seq_len - q_len + i, with hk = hq / (Hq / Hk) (the flash-attention
  * step of the page's path, causal=True with q_len <= seq_len).
  *   q:    (device) bf16 (q_len, Hq, D); k, v: (seq_len, Hk, D) sharing
- *         strides; out: (q_len, Hq, D) bf16, D = 128 or 256. All 16-byte aligned, strides
+ *         strides; out: (q_len, Hq, D) bf16, D = 128, 256 or 512. All 16-byte aligned, strides
  *         in elements, non-negative multiples of 8.
- *   scale: finite, > 0. Hq / Hk at most 128. kv_stride_t in [D, 2^25).
+ *   scale: finite, > 0. Hq / Hk at most 128 (64 at D = 512). kv_stride_t in
+ *   [D, 2^25).
  * Errors: UQ_EINVAL for q_len < 0, seq_len < q_len, a null pointer, bad
- * strides or alignment; UQ_EUNSUPPORTED for D not 128 or 256, Hq % Hk or a key
+ * strides or alignment; UQ_EUNSUPPORTED for D not 128, 256 or 512, Hq % Hk or a key
  * stride outside that range; UQ_EHIP.
  */
 int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
@@ -339,7 +339,7 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          void* stream);
 
 /* Workspace bytes of uq_continuation_prefill for chunks of up to q_len
- * tokens and sequences of up to max_seq_len tokens, D in {128, 256}; 0 on
+ * tokens and sequences of up to max_seq_len tokens, D in {128, 256, 512}; 0 on
  * invalid shapes. */
 size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int Hq, int Hk, int D);
 
@@ -348,8 +348,9 @@ size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int H
  * rotate the chunk's keys and the queries, append the chunk's values, then
  * attend (the steps of uq_dequant_kv, uq_rotate and uq_prefill_attention on
  * buffers in the workspace, the values kept there in 32-key tiles laid out
- * for the attention; two launches on `stream`).
- *   D:      128 or 256 (UQ_EUNSUPPORTED otherwise).
+ * for the attention at D = 128 and 256, token-major at 512; two launches on
+ * `stream`).
+ *   D:      128, 256 or 512 (UQ_EUNSUPPORTED otherwise).
  *   query:  (device) bf16 (q_len, Hq, D) before rotation; key, value:
  *           (q_len, Hk, D) of the chunk (key before rotation). 8-byte
  *           aligned, strides non-negative multiples of 4 elements.

@@ -193,7 +193,8 @@ def prefill_attention_args(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q_len=-1), -1), (dict(seq_len=7), -1), (dict(scale=0.0), -1),
-    (dict(scale=float("inf")), -1), (dict(D=512), -2), (dict(D=64), -2), (dict(Hq=15), -2),
+    (dict(scale=float("inf")), -1), (dict(D=1024), -2), (dict(D=64), -2), (dict(Hq=15), -2),
+    (dict(D=512, Hq=130, Hk=1, kvst=512, kvsh=512), -2),
     (dict(Hq=258, Hk=2), -2), (dict(v=None), -1), (dict(kvst=508), -1), (dict(out=FAKE + 8), -1),
     (dict(kvst=248), -2), (dict(kvst=1 << 25), -2),
 ])
@@ -215,7 +216,7 @@ def continuation_args(**kw):
     (dict(cached_len=-1), -1), (dict(block_row=None), -1), (dict(workspace=FAKE + 16), -1),
     (dict(ws_bytes=4096), -3), (dict(block_size=48), -2), (dict(Hq=17), -2),
     (dict(ost=4), -1), (dict(kst=2), -1), (dict(query=FAKE + 2), -1),
-    (dict(D=512), -2), (dict(D=64), -2),
+    (dict(D=1024), -2), (dict(D=64), -2), (dict(D=512, Hq=65 * 2), -2),
 ])
 def test_continuation_prefill_rejects(libuq, kw, code):
     assert libuq.uq_continuation_prefill(*continuation_args(**kw)) == code
@@ -226,21 +227,25 @@ def test_continuation_prefill_workspace_bytes(libuq):
     f = libuq.uq_continuation_prefill_workspace_bytes
     assert f(8, 7, 16, 2, 256) == 0
     assert f(8, 100, 15, 2, 256) == 0
-    assert f(8, 100, 16, 2, 512) == 0
+    assert f(8, 100, 16, 2, 1024) == 0
     n = f(8, 100, 16, 2, 256)
     # rotated queries, keys of the whole sequence, then values in tiles of 32 keys, as bf16
     assert n == 8 * 16 * 512 + 100 * 2 * 512 + 2 * 4 * 32 * 512
     assert f(8, 101, 16, 2, 256) > n
     # head dim 128: the same sections with 128-element rows
     assert f(8, 100, 16, 2, 128) == 8 * 16 * 256 + 100 * 2 * 256 + 2 * 4 * 32 * 256
+    # head dim 512: values token-major like the keys
+    assert f(8, 100, 16, 2, 512) == 8 * 16 * 1024 + 100 * 2 * 1024 + 100 * 2 * 1024
+    assert f(8, 100, 130, 2, 512) == 0        # GQA group 64 at most at D = 512
+    assert f(8, 100, 128, 2, 512) > 0 and f(8, 100, 130, 2, 256) > 0
 
 
-def test_continuation_prefill_head_dim_128_accepted(libuq):
-    """D = 128 passes every host check of both attention calls (q_len = 0
-    then returns before any HIP call); D = 512 does not."""
-    assert libuq.uq_continuation_prefill(*continuation_args(D=128, q_len=0)) == 0
-    assert libuq.uq_prefill_attention(*prefill_attention_args(D=128, q_len=0, kvst=128, kvsh=128)) == 0
-    assert libuq.uq_prefill_attention(*prefill_attention_args(D=512, q_len=0)) == -2
+@pytest.mark.parametrize("d", [128, 512])
+def test_continuation_prefill_other_head_dims_accepted(libuq, d):
+    """D = 128 and 512 pass every host check of both attention calls
+    (q_len = 0 then returns before any HIP call)."""
+    assert libuq.uq_continuation_prefill(*continuation_args(D=d, q_len=0)) == 0
+    assert libuq.uq_prefill_attention(*prefill_attention_args(D=d, q_len=0, kvst=d, kvsh=d)) == 0
 
 
 @pytest.mark.parametrize("mask", [0, 4, -1, 7])

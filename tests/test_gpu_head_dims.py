@@ -1,7 +1,8 @@
 """Head dims 128 and 512 (the pages' other head sizes): the slot format
 scales with D (17 D / 16 bytes), the store and the continuation-prefill
 operands (rotation, dequantised prefix) are bit-exact against the oracle,
-and decode is within max-abs 1e-2 / rel-L2 5e-3. Through the C ABI."""
+and decode and the continuation-prefill attention are within max-abs 1e-2 /
+rel-L2 5e-3. Through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -266,12 +267,14 @@ def test_dequant_bit_exact(d):
 
 @pytest.mark.parametrize("cached_len,q_len", [(0, 37), (100, 64), (333, 129)])
 @pytest.mark.parametrize("qg", [6, 8, 16])
-def test_continuation_prefill_d128(cached_len, q_len, qg):
-    """Continuation prefill at head dim 128 (the attention kernel's 128-dim
-    instance, values tiled) against the oracle, written into a strided
-    output whose extra columns must stay untouched."""
-    d, hk, bs = 128, 2, 16
-    say(f"prefill d=128 qg={qg} cached={cached_len} q_len={q_len}")
+@pytest.mark.parametrize("d", DIMS)
+def test_continuation_prefill(d, cached_len, q_len, qg):
+    """Continuation prefill at head dim d (at 128 the attention kernel's
+    128-dim instance with values tiled; at 512 the 16-key-tile kernel with
+    values token-major) against the oracle, written into a strided output
+    whose extra columns must stay untouched."""
+    hk, bs = 2, 16
+    say(f"prefill d={d} qg={qg} cached={cached_len} q_len={q_len}")
     rng = np.random.default_rng(qg * 100 + cached_len + q_len)
     nblk = max(1, -(-cached_len // bs))
     row = rng.permutation(nblk + 3)[:nblk].astype(np.int32)
@@ -293,18 +296,19 @@ def test_continuation_prefill_d128(cached_len, q_len, qg):
                                   cached_len, scale, out=big[:, :, :d])
     assert torch.isnan(big[:, :, d:]).all()
     want = O.continuation_prefill(bits(q), bits(kc), bits(vc), ref, row, cached_len, scale)
-    check_close(to_np(out), want, f"prefill d=128 qg={qg} cached={cached_len} q_len={q_len}",
+    check_close(to_np(out), want, f"prefill d={d} qg={qg} cached={cached_len} q_len={q_len}",
                 allow_output_rounding=True)
 
 
 @pytest.mark.parametrize("qg", [8, 16])
-def test_prefill_attention_d128_strided_and_peaked(qg):
-    """uq_prefill_attention at head dim 128 on strided views (values
+@pytest.mark.parametrize("d", DIMS)
+def test_prefill_attention_strided_and_peaked(d, qg):
+    """uq_prefill_attention at head dim d on strided views (values
     token-major), 300 keys (a ragged last tile) and a large scale that
     raises the running maximum along the keys, against a float64 softmax."""
-    say(f"prefill attention d=128 qg={qg}")
-    rng = np.random.default_rng(17 + qg)
-    d, q_len, seq, hk = 128, 50, 300, 2
+    say(f"prefill attention d={d} qg={qg}")
+    rng = np.random.default_rng(17 + qg + d)
+    q_len, seq, hk = 50, 300, 2
     grow = np.linspace(0.2, 4.0, seq)[:, None, None]
     k = bf16(rng.standard_normal((seq, hk, d)) * grow)
     v = bf16(rng.standard_normal((seq, hk, d)))
@@ -315,13 +319,14 @@ def test_prefill_attention_d128_strided_and_peaked(qg):
     qq = torch.zeros((q_len, hk * qg, d + 64), dtype=torch.bfloat16, device=DEV)
     qq[:, :, 64:] = q.to(DEV)
     o = torch.full((q_len, hk * qg, d + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
-    uq.prefill_attention(qq[:, :, 64:], kv[:, 0, :, :d], kv[:, 1, :, :d], 0.5, out=o[:, :, :d])
+    sc = 0.5 * np.sqrt(128 / d)                  # the same score spread at every d
+    uq.prefill_attention(qq[:, :, 64:], kv[:, 0, :, :d], kv[:, 1, :, :d], sc, out=o[:, :, :d])
     K, V, Q = O.bf16_to_f64(bits(k)), O.bf16_to_f64(bits(v)), O.bf16_to_f64(bits(q))
     want = np.zeros((q_len, hk * qg, d))
     for hq in range(hk * qg):
-        s = 0.5 * Q[:, hq] @ K[:, hq // qg].T
+        s = sc * Q[:, hq] @ K[:, hq // qg].T
         s = np.where(np.arange(seq)[None, :] <= seq - q_len + np.arange(q_len)[:, None], s, -np.inf)
         p = np.exp(s - s.max(-1, keepdims=True))
         want[:, hq] = p @ V[:, hq // qg] / p.sum(-1, keepdims=True)
-    check_close(to_np(o[:, :, :d]), want, f"d=128 strided peaked qg={qg}", allow_output_rounding=True)
+    check_close(to_np(o[:, :, :d]), want, f"d={d} strided peaked qg={qg}", allow_output_rounding=True)
     assert torch.isnan(o[:, :, d:]).all()
