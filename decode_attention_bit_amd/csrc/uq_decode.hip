@@ -36,7 +36,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 // Query prologue: q8 = E4M3(q H), one wave per (sequence, query head), for
 // head dims 128, 256 and 512.
 // The rotation runs in float64 and is exact, so the E4M3 rounding decision is
-// taken on the exact product.
+// taken on the exact product (scaled by the float64 1/sqrt(D)).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restrict__ query,
@@ -65,9 +65,12 @@ __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restri
     }
   }
   fwht_wave<E, true>(v, lane);
+  // codes of the float64 products, through float32 rounded to odd
   uint32_t w[(E + 3) / 4] = {};
 #pragma unroll
-  for (int i = 0; i < E; ++i) w[i / 4] |= e4m3_code(v[i] * rot_scale<D>()) << (8 * (i % 4));
+  for (int i = 0; i < E; i += 2)
+    w[i / 4] |= e4m3_pair(to_f32_odd(v[i] * rot_scale<D>()), to_f32_odd(v[i + 1] * rot_scale<D>()))
+                << (8 * (i % 4));
   uint8_t* dst = q8 + vec * D + E * lane;
   if constexpr (E == 2) {
     *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
@@ -397,27 +400,6 @@ __device__ __forceinline__ void rebase(v4f acc[D / 16], float& m_ref, float mt, 
 typedef double v4d __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v4d mfma_f64(double a, double b, v4d c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
-}
-
-// float32 rounding of x to odd: the float32 next to x whose last bit is 1
-// when x is not a float32 (exact otherwise); rounding that to fewer bits
-// (here E4M3) then gives the same result as rounding x itself.
-__device__ __forceinline__ float to_f32_odd(double x) {
-  const float f = (float)x;                        // nearest
-  const double back = (double)f;
-  uint32_t u = __float_as_uint(f);
-  if (back != x && !(u & 1u)) u += fabs(back) < fabs(x) ? 1u : 0xFFFFFFFFu;   // the odd neighbour toward x
-  return __uint_as_float(u);
-}
-typedef short v2s16 __attribute__((ext_vector_type(2)));
-// E4M3 (fn) codes of two float32 values, nearest even, saturating at 448: the
-// gfx950 conversion rounds to nearest even and is exact below 464 but gives
-// NaN above, so the inputs are clamped to [-448, 448] first.
-__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
-  a = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
-  b = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
-  const v2s16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s16){0, 0}, a, b, 1.0f, false);
-  return (uint32_t)(uint16_t)r[0];
 }
 
 template <int QG>

@@ -96,6 +96,14 @@ __device__ __forceinline__ double xor_lane(double v, int m, int lane) {
 // pipe (__shfl_xor), which runs beside the VALU and keeps the store's
 // throughput when many waves are resident (the store of 16384 x 4 vectors
 // took 51 us this way and 60 us with register exchanges).
+// x with its sign bit XORed with flip (0 or the sign bit): -x or x, exactly;
+// IEEE subtraction o - x is by definition the sum (-x) + o, so a butterfly's
+// upper output needs no separate subtraction.
+__device__ __forceinline__ double negate_if(double x, uint32_t flip) {
+  const uint64_t u = __double_as_longlong(x) ^ ((uint64_t)flip << 32);
+  return __longlong_as_double(u);
+}
+
 template <int E, bool REG = false>
 __device__ __forceinline__ void fwht_wave(double v[E], int lane) {
   // D-point butterfly, D = 64 E: index bits below log2(E) inside a lane, the
@@ -112,11 +120,11 @@ __device__ __forceinline__ void fwht_wave(double v[E], int lane) {
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+    const uint32_t flip = (lane & m) ? 0x80000000u : 0u;   // upper lane: o - v = (-v) + o
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const double o = REG ? xor_lane(v[i], m, lane) : __shfl_xor(v[i], m);
-      v[i] = upper ? (o - v[i]) : (v[i] + o);
+      v[i] = negate_if(v[i], flip) + o;
     }
   }
 }
@@ -127,11 +135,11 @@ __device__ __forceinline__ void fwht256_wave(double v[4], int lane) {
   v[0] = a0 + a2; v[1] = a1 + a3; v[2] = a0 - a2; v[3] = a1 - a3;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+    const uint32_t flip = (lane & m) ? 0x80000000u : 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const double o = __shfl_xor(v[i], m);
-      v[i] = upper ? (o - v[i]) : (v[i] + o);
+      v[i] = negate_if(v[i], flip) + o;
     }
   }
 }
@@ -144,46 +152,42 @@ __device__ __forceinline__ int mx_block_exponent(double amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// 4-bit E2M1 code of x under block exponent e: magnitude |x| * 2**-e rounded
-// to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code,
-// saturating at 6; bit 3 carries the sign of x.
-__device__ __forceinline__ uint32_t e2m1_code(double x, double inv_scale) {
-  const double r = fabs(x) * inv_scale;
-  uint32_t c = (uint32_t)(r > 0.25) + (uint32_t)(r >= 0.75) + (uint32_t)(r > 1.25) +
-               (uint32_t)(r >= 1.75) + (uint32_t)(r > 2.5) + (uint32_t)(r >= 3.5) +
-               (uint32_t)(r > 5.0);
-  return c | (signbit(x) ? 8u : 0u);
+// float32 rounding of x to odd: the float32 next to x whose last bit is 1
+// when x is not a float32 (exact otherwise). Rounding that to a format of at
+// most 11 significand bits (E2M1, E4M3) then gives the same result as
+// rounding x itself (Boldo and Melquiond, round-to-odd), and no threshold
+// decision can flip: a value strictly between two float32 values never
+// lands on one whose last bit is 0, which every rounding boundary of those
+// formats is. Beyond float32's range the result is the largest finite
+// float32 of x's sign.
+__device__ __forceinline__ float to_f32_odd(double x) {
+  const float f = (float)x;                        // nearest
+  const double back = (double)f;
+  uint32_t u = __float_as_uint(f);
+  if (back != x && !(u & 1u)) u += fabs(back) < fabs(x) ? 1u : 0xFFFFFFFFu;   // the odd neighbour toward x
+  return __uint_as_float(u);
 }
 
-// The same code from float32 operands. Exact for values: a bf16 value and a
-// power-of-two scale are float32 values, and their product is exact wherever
-// it can reach a threshold (0.25 .. 5, far above float32's subnormals); NaN
-// and infinity compare as in float64.
-__device__ __forceinline__ uint32_t e2m1_code_f32(float x, float inv_scale) {
-  const float r = fabsf(x) * inv_scale;
-  uint32_t c = (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) +
-               (uint32_t)(r >= 1.75f) + (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) +
-               (uint32_t)(r > 5.0f);
-  return c | (signbit(x) ? 8u : 0u);
+// 4-bit E2M1 codes of two float32 values, a in bits 0-3 and b in bits 4-7:
+// magnitude rounded to the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to
+// the even code, saturating at 6, bit 3 the sign (also of a zero result).
+// The gfx950 conversion at scale 1 follows exactly this rule (checked on
+// every rounding boundary and tie, one float32 step either side, signed
+// zeros, subnormals and values past 6).
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
 }
 
-// OCP FP8 E4M3 (fn) code of x, round to nearest even, magnitudes above 448
-// saturate to 448. Exact: every step is a power-of-two scaling and one
-// rint() of a value below 2**5.
-__device__ __forceinline__ uint32_t e4m3_code(double x) {
-  const double a = fabs(x);
-  uint32_t c;
-  if (a >= 448.0) {
-    c = 0x7E;
-  } else if (a < 0.015625) {                       // below 2**-6: grid k * 2**-9
-    c = (uint32_t)rint(a * 512.0);                 // k = 8 is the first normal, code 8
-  } else {
-    const int E = floor_log2(a);                   // -6 .. 8
-    const uint32_t m = (uint32_t)rint(a * pow2(3 - E));   // 8 .. 16
-    c = ((uint32_t)(E + 7) << 3) + (m - 8);        // m = 16 carries into the exponent
-    if (c > 0x7E) c = 0x7E;
-  }
-  return c | (signbit(x) ? 0x80u : 0u);
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+// E4M3 (fn) codes of two float32 values, a in bits 0-7, nearest even,
+// saturating at 448: the gfx950 conversion rounds to nearest even and is
+// exact below 464 but gives NaN above, so the inputs are clamped to
+// [-448, 448] first.
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+  b = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+  const v2s16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s16){0, 0}, a, b, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0];
 }
 
 }  // namespace uq

@@ -11,8 +11,10 @@ namespace uq {
 // One wave per (token, KV head): lane l owns elements E l .. E l + E - 1
 // (E = D / 64), so a 32-element scale block is 32 / E consecutive lanes and
 // the D/2 code bytes of a region are written as 64 contiguous stores of E/2
-// bytes. K is rotated in float64; V is quantised in float32, which holds
-// bf16 values exactly (the codes and scales come out the same).
+// bytes. K is rotated in float64, scaled by its power of two there and
+// rounded to odd in float32; V is scaled in float32, which holds bf16 values
+// and their power-of-two multiples exactly. Both are encoded by the E2M1
+// conversion, so the codes are those of the exact scaled values.
 template <int D>
 __global__ __launch_bounds__(256) void store_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
@@ -75,9 +77,9 @@ __global__ __launch_bounds__(256) void store_kernel(
 
   uint32_t kc = 0, vc = 0;
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    kc |= e2m1_code(k[i], kinv) << (4 * i);
-    vc |= e2m1_code_f32(v[i], vinv) << (4 * i);
+  for (int i = 0; i < E; i += 2) {
+    kc |= e2m1_pair(to_f32_odd(k[i] * kinv), to_f32_odd(k[i + 1] * kinv)) << (4 * i);
+    vc |= e2m1_pair(v[i] * vinv, v[i + 1] * vinv) << (4 * i);
   }
   uint8_t* dst = cache + ((size_t)slot * Hk + h) * F::kSlot;
   if constexpr (E == 2) {
