@@ -66,7 +66,7 @@ struct VecJob {
 // Tiled value layout of the continuation prefill (vt != null): per KV head,
 // tiles of 32 keys, each D dim rows of 64 bytes; row d of tile j holds the
 // 32 keys in the order the attention's P operand uses, its 16-byte chunks
-// permuted by chunk ^ ((d >> 2) & 3).
+// permuted by chunk ^ (((d >> 2) ^ (d >> 1)) & 3).
 struct GatherArgs {
   int D;                     // head dim: 128, 256 or 512 (vt and to_vt: 128 and 256)
   // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])

@@ -52,6 +52,13 @@ __device__ __forceinline__ uint32_t e2m1_bf16_bits(uint32_t code, int e) {
   return sign | ((2u + half) << (E + 132));                 // value / 2**-133
 }
 
+// Chunk permutation of dim row `dim` in the tiled value layout. The P.V read
+// of 16 consecutive dim rows (64 bytes apart), chunk g of each, then hits
+// distinct banks both within each aligned group of 8 rows (128 bytes of
+// banks) and across all 16 (256 bytes): the pairs (dim mod 2, swizzle) and
+// (dim mod 4, swizzle) are distinct there.
+__device__ __forceinline__ int vt_swizzle(int dim) { return ((dim >> 2) ^ (dim >> 1)) & 3; }
+
 // Element offset of (key, head h, dim) in the tiled value layout of head
 // dim DV: key 16kb + 4g + i of a tile sits at slot s = i + 4kb of chunk g of
 // its dim row.
@@ -59,7 +66,7 @@ template <int DV>
 __device__ __forceinline__ int64_t vt_offset(int64_t key, int h, int dim, int64_t tiles) {
   const int kk = (int)(key & 31);
   const int g = (kk & 15) >> 2, s = (kk & 3) + ((kk >> 4) << 2);
-  return (((int64_t)h * tiles + (key >> 5)) * DV + dim) * 32 + 8 * (g ^ ((dim >> 2) & 3)) + s;
+  return (((int64_t)h * tiles + (key >> 5)) * DV + dim) * 32 + 8 * (g ^ vt_swizzle(dim)) + s;
 }
 
 // ---------------------------------------------------------------------------
@@ -501,7 +508,7 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
 #pragma unroll
       for (int n = 0; n < NACC; ++n) {
         const int dim = 16 * n + r16;
-        const v8bf vb = __builtin_bit_cast(v8bf, ld16(vb_ + dim * 64 + 16 * (g ^ ((r16 >> 2) & 3))));
+        const v8bf vb = __builtin_bit_cast(v8bf, ld16(vb_ + dim * 64 + 16 * (g ^ vt_swizzle(dim))));
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           acc[cb][n] = mfma_bf16(pb[cb], vb, acc[cb][n]);
