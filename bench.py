@@ -57,8 +57,7 @@ def parse():
     ap.add_argument("--sinks", action="store_true",
                     help="add seeded per-head sink logits (uq_decode_ex)")
     ap.add_argument("--head-dim", type=int, default=256, choices=(128, 256, 512),
-                    help="head dim of the workload (slot 17*D/16 bytes, scale 1/sqrt(D)); "
-                         "prefill takes 128 or 256")
+                    help="head dim of the workload (slot 17*D/16 bytes, scale 1/sqrt(D))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
@@ -249,24 +248,25 @@ def gpu_time(w, lay, q, caches, bt, sl, steps, warmup, store_args=None, multi=No
 
 STAGE1_SOURCE = os.path.join(ROOT, "decode_attention_bit_amd", "csrc", "uq_decode.hip")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "stage1_decode_traffic.md")
+PREFILL_SOURCE = os.path.join(ROOT, "decode_attention_bit_amd", "csrc", "uq_prefill.hip")
+PREFILL_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "prefill_attention_traffic.md")
 
 
-def recorded_traffic(workload):
-    """HBM bytes per stage-1 launch from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by the reference kernel), or None when
-    there is none for this workload or the kernel source has changed since."""
+def recorded_traffic(workload, record=TRAFFIC_RECORD, source=STAGE1_SOURCE):
+    """HBM bytes per launch of the dominant kernel from a committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the reference kernel), or None
+    when it holds no record for this workload or the kernel source has
+    changed since the counters were taken."""
     import hashlib
     import re
-    if not os.path.exists(TRAFFIC_RECORD):
+    if not os.path.exists(record):
         return None
-    text = open(TRAFFIC_RECORD).read()
-    m = re.search(r"^record: workload=(\S+) source_sha256=([0-9a-f]{64}) fetch_bytes=(\d+) "
-                  r"write_bytes=(\d+)$", text, re.M)
-    if not m or m.group(1) != workload:
-        return None
-    if hashlib.sha256(open(STAGE1_SOURCE, "rb").read()).hexdigest() != m.group(2):
-        return None
-    return int(m.group(3)) + int(m.group(4))
+    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    for m in re.finditer(r"^record: workload=(\S+) source_sha256=([0-9a-f]{64}) fetch_bytes=(\d+) "
+                         r"write_bytes=(\d+)$", open(record).read(), re.M):
+        if m.group(1) == workload and m.group(2) == sha:
+            return int(m.group(3)) + int(m.group(4))
+    return None
 
 
 def cpu_baseline(w, lay, seconds, wall_cap=150.0):
@@ -371,6 +371,22 @@ def prefill_cpu_baseline(P, q, kc, vc, cache, row, seconds, D=256):
                       f"prefix and rotating the whole chunk, {elapsed:.1f} s, BLAS on {cores} threads"}
 
 
+def copy_reference(mib, dev):
+    """One int32 bitwise_not over mib MiB (reads and writes mib MiB): the kernel
+    of known size that HBM byte counters are scaled by."""
+    import torch
+    if mib <= 0:
+        return
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"reference kernel bitwise_not: {n} bytes read, {n} bytes written")
+    del src, dst
+
+
 def prefill_main(args):
     import numpy as np
     import torch
@@ -395,6 +411,7 @@ def prefill_main(args):
     out = torch.empty((q_len, Hq, D), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(uq.continuation_prefill_workspace_bytes(q_len, cached + q_len, Hq, Hk, D),
                      dtype=torch.uint8, device=dev)
+    copy_reference(args.copy_ref_mib, dev)
     steps = max(1, args.steps // 4)
     warmup = max(1, args.warmup // 4)
     log(f"timing {steps} calls")
@@ -431,7 +448,8 @@ def prefill_main(args):
         "stage_ms": {"whole_call": round(ms, 5), "gather_alone": round(gather_ms, 5),
                      "attention_alone": round(attn_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic(f"prefill-D{D}", PREFILL_TRAFFIC_RECORD, PREFILL_SOURCE),
                      "kernel": "prefill_attn16_kernel" if D == 512 else "prefill_attn_kernel",
                      "flops_per_launch": fl},
     }
@@ -464,15 +482,7 @@ def main():
     log(f"setup {w.name}")
     lay, q, caches, bt, sl = setup(w, dev)
     kv_bytes = inputs.kv_bytes(w, lay)
-    if args.copy_ref_mib > 0:
-        n = args.copy_ref_mib << 20
-        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
-        log(f"reference kernel bitwise_not: {n} bytes read, {n} bytes written")
-        del src, dst
+    copy_reference(args.copy_ref_mib, dev)
     log(f"timing {args.steps} steps ({len(caches)} cache copies)")
     store_args = serving_store(w, lay, dev) if w.name == "mixed" else None
     multi = multi_query(w, lay, args.queries_per_seq, dev) if args.queries_per_seq > 1 else None

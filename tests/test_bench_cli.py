@@ -1,5 +1,5 @@
-"""bench.py's host-side refusals: both end with status 2 and one JSON line
-naming the reason, before any GPU work."""
+"""bench.py's host-side refusal of more than one GPU: it ends with status 2
+and one JSON line naming the reason, before any GPU work."""
 import json
 import os
 import subprocess
@@ -18,7 +18,3 @@ def test_more_than_one_gpu_is_refused():
     code, line = _run("--gpus", "2")
     assert code == 2 and line["n_gpus"] == 2 and "one GPU" in line["error"]
 
-
-def test_prefill_head_dim_512_is_refused():
-    code, line = _run("--workload", "prefill", "--head-dim", "512")
-    assert code == 2 and "128 and 256" in line["error"]
