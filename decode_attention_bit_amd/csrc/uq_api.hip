@@ -276,7 +276,7 @@ int uq_rotate(const uint16_t* x, uint16_t* out, int64_t N, int H, int D, int64_t
   if ((N * H + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "uq_rotate: N*H too large for one launch");
   uq::GatherArgs a{};
   a.D = D;
-  a.job[0] = uq::VecJob{x, x_stride_n, x_stride_h, out, out_stride_n, out_stride_h, N * H, H, 1, 0, 0};
+  a.job[0] = uq::VecJob{x, x_stride_n, x_stride_h, out, out_stride_n, out_stride_h, N * H, H, 1};
   return hip_status(uq::launch_gather(a, (hipStream_t)stream), "uq_rotate launch");
 }
 
@@ -415,7 +415,7 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   const PrefillLayout lay = prefill_layout(q_len, seq_len, Hq, Hk, D);
   if (workspace_bytes < lay.total)
     return fail(UQ_EWORKSPACE, "%s: workspace %zu bytes < required %zu", who, workspace_bytes, lay.total);
-  const long long waves = (long long)(seq_len + 32) * Hk * 2 + (long long)q_len * Hq;
+  const long long waves = (long long)(seq_len + 32) * Hk * 3 + (long long)q_len * Hq;
   if ((waves + 3) / 4 > 0x7FFFFFFFLL) return fail(UQ_EUNSUPPORTED, "%s: too large for one launch", who);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + lay.q_off);
@@ -432,23 +432,25 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   g.Hk = Hk;
   g.num_blocks = num_blocks;
   g.log2_bs = log2_bs;
-  const bool tiled = lay.vt_tiles > 0;
+  const bool tiled = lay.vt_tiles > 0;      // head dims 128 and 256
   g.kout = kf;
   g.vout = tiled ? nullptr : vf;
   g.os_t = row;
   g.os_h = D;
   g.vt = tiled ? vf : nullptr;
   g.vt_tiles = lay.vt_tiles;
-  g.vt_pad0 = seq_len;
-  g.vt_pad = tiled ? lay.vt_tiles * 32 - seq_len : 0;
+  g.vsrc = value;
+  g.vs_t = val_stride_t;
+  g.vs_h = val_stride_h;
+  g.v_keys = seq_len;
   g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * D, D,
-                        (int64_t)q_len * Hq, Hq, 1, 0, 0};
+                        (int64_t)q_len * Hq, Hq, 1};
   g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, D,
-                        (int64_t)q_len * Hk, Hk, 1, 0, 0};
-  g.job[2] = tiled ? uq::VecJob{value, val_stride_t, val_stride_h, nullptr, 0, 0, (int64_t)q_len * Hk, Hk, 0, 1,
-                                (int64_t)cached_len}
-                   : uq::VecJob{value, val_stride_t, val_stride_h, vf + (int64_t)cached_len * row, row, D,
-                                (int64_t)q_len * Hk, Hk, 0, 0, 0};
+                        (int64_t)q_len * Hk, Hk, 1};
+  // token-major values (head dim 512): the chunk's values are copied after the prefix's
+  if (!tiled)
+    g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, vf + (int64_t)cached_len * row, row, D,
+                          (int64_t)q_len * Hk, Hk, 0};
   if (stage_mask & UQ_PREFILL_GATHER) {
     hipError_t e = uq::launch_gather(g, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");

@@ -59,8 +59,6 @@ struct VecJob {
   int64_t n;
   int H;
   int rotate;
-  int to_vt;                 // write row t as key vt_key0 + t of the tiled value layout instead
-  int64_t vt_key0;
 };
 
 // Tiled value layout of the continuation prefill (vt != null): per KV head,
@@ -68,7 +66,7 @@ struct VecJob {
 // 32 keys in the order the attention's P operand uses, its 16-byte chunks
 // permuted by chunk ^ (((d >> 2) ^ (d >> 1)) & 3).
 struct GatherArgs {
-  int D;                     // head dim: 128, 256 or 512 (vt and to_vt: 128 and 256)
+  int D;                     // head dim: 128, 256 or 512 (vt: 128 and 256)
   // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])
   const uint8_t* cache;
   const int32_t* block_row;
@@ -79,9 +77,15 @@ struct GatherArgs {
   uint16_t* kout;
   uint16_t* vout;
   int64_t os_t, os_h;
-  uint16_t* vt;              // values go here (tiled) instead of vout when set
+  // Tiled values (vt != null, D = 128 or 256): one workgroup per (KV head,
+  // tile) builds the whole tile: keys below n_tok dequantised from the cache
+  // (their V is then not written to vout), keys n_tok .. v_keys - 1 copied
+  // from vsrc row key - n_tok, the rest of the last tile zero.
+  uint16_t* vt;
   int64_t vt_tiles;          // tiles per KV head
-  int64_t vt_pad0, vt_pad;   // keys vt_pad0 .. vt_pad0 + vt_pad - 1 are zero padding
+  const uint16_t* vsrc;
+  int64_t vs_t, vs_h;
+  int64_t v_keys;
   VecJob job[3];
 };
 

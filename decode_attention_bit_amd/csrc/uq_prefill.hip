@@ -59,38 +59,94 @@ __device__ __forceinline__ uint32_t e2m1_bf16_bits(uint32_t code, int e) {
 // (dim mod 4, swizzle) are distinct there.
 __device__ __forceinline__ int vt_swizzle(int dim) { return ((dim >> 2) ^ (dim >> 1)) & 3; }
 
-// Element offset of (key, head h, dim) in the tiled value layout of head
-// dim DV: key 16kb + 4g + i of a tile sits at slot s = i + 4kb of chunk g of
-// its dim row.
-template <int DV>
-__device__ __forceinline__ int64_t vt_offset(int64_t key, int h, int dim, int64_t tiles) {
-  const int kk = (int)(key & 31);
+// Element offset of (key kk, dim) within one tile of the tiled value layout:
+// key 16kb + 4g + i of a tile sits at slot s = i + 4kb of chunk g of its dim
+// row (64 bytes per dim row, 32 keys).
+__device__ __forceinline__ int vt_tile_offset(int kk, int dim) {
   const int g = (kk & 15) >> 2, s = (kk & 3) + ((kk >> 4) << 2);
-  return (((int64_t)h * tiles + (key >> 5)) * DV + dim) * 32 + 8 * (g ^ vt_swizzle(dim)) + s;
+  return dim * 32 + 8 * (g ^ vt_swizzle(dim)) + s;
+}
+
+// One 32-key tile of the tiled values of KV head h, built by a whole
+// workgroup (4 waves, 8 keys each) in LDS and written out as contiguous
+// 16-byte stores, so that each dim row reaches memory whole. Lane l holds
+// dims D/64 l .. D/64 l + D/64 - 1 of a key: from the cache for keys below
+// n_tok (codes and scale byte of those dims, exact bf16 bits), from vsrc
+// for the chunk's keys up to v_keys, zero past them.
+template <int D>
+__device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j) {
+  using F = Fmt<D>;
+  constexpr int DL = D / 64;                 // dims per lane: 2 or 4
+  __shared__ uint16_t img[32 * D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int kk0 = 0; kk0 < 8; ++kk0) {
+    const int kk = 8 * wave + kk0;
+    const int64_t key = 32 * j + kk;
+    uint32_t v[DL / 2] = {};
+    if (key < a.n_tok) {
+      const int phys = a.block_row[key >> a.log2_bs];
+      if (phys >= 0 && (int64_t)phys < a.num_blocks) {
+        const uint8_t* slot =
+            a.cache + ((((int64_t)phys << a.log2_bs) + (key & ((1 << a.log2_bs) - 1))) * a.Hk + h) * F::kSlot;
+        const uint32_t codes = DL == 4 ? *reinterpret_cast<const uint16_t*>(slot + F::kVCode + 2 * lane)
+                                       : slot[F::kVCode + lane];
+        const int e = (int)slot[F::kVScale + (DL * lane) / 32] - 127;
+#pragma unroll
+        for (int i = 0; i < DL / 2; ++i)
+          v[i] = e2m1_bf16_bits((codes >> (8 * i)) & 0xF, e) | (e2m1_bf16_bits((codes >> (8 * i + 4)) & 0xF, e) << 16);
+      }
+    } else if (key < a.v_keys) {
+      const uint16_t* src = a.vsrc + (key - a.n_tok) * a.vs_t + (int64_t)h * a.vs_h + DL * lane;
+      if constexpr (DL == 4) {
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        v[0] = x.x;
+        v[1] = x.y;
+      } else {
+        v[0] = *reinterpret_cast<const uint32_t*>(src);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < DL; ++i) img[vt_tile_offset(kk, DL * lane + i)] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+  }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(a.vt + ((int64_t)h * a.vt_tiles + j) * 32 * D);
+  const uint4* srcl = reinterpret_cast<const uint4*>(img);
+#pragma unroll
+  for (int i = 0; i < 4 * D / 256; ++i) dst[256 * i + threadIdx.x] = srcl[256 * i + threadIdx.x];
 }
 
 // ---------------------------------------------------------------------------
-// Gather: one wave per unit of work, the role chosen by the wave's index
-// (wave-uniform): first the prefix slots (token, KV head) to dequantise, then
-// up to three jobs over vectors of D bf16 (rotate or copy).
+// Gather. With tiled values (D = 128, 256) the first Hk * vt_tiles
+// workgroups each build one value tile (value_tile). After them, one wave
+// per unit of work, the role chosen by the wave's index (wave-uniform):
+// first the prefix slots (token, KV head) to dequantise, then up to three
+// jobs over vectors of D bf16 (rotate or copy).
 // Dequant: lanes 0-31 write K elements D/32 l .. D/32 l + D/32 - 1, lanes
-// 32-63 the same V elements; each reads the code bytes and the one scale
-// byte that cover them (D/32 <= 16 consecutive elements never straddle a
-// 32-element block).
+// 32-63 the same V elements (token-major values only); each reads the code
+// bytes and the one scale byte that cover them (D/32 <= 16 consecutive
+// elements never straddle a 32-element block).
 // Rotate: lane l holds x[D/64 l .. D/64 l + D/64 - 1] through the float64
 // butterfly, then the float64 nearest 1/sqrt(D) and one rounding to bf16.
-// The tiled value layout (vt, vt_pad, to_vt) exists at D = 128 and 256,
-// the head dims of the attention.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
-  constexpr bool TILED = D <= kHeadDim;
   using F = Fmt<D>;
   constexpr int EPL = D / 32;              // dequantised elements per lane
   constexpr int NCB = EPL / 2;             // code bytes per lane: 2, 4 or 8
   constexpr int E = F::kPerLane;           // rotated elements per lane: 2, 4 or 8
   int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  if constexpr (D <= kHeadDim) {
+    if (a.vt) {                              // workgroup-uniform
+      const int64_t n_vt = (int64_t)a.Hk * a.vt_tiles;
+      if ((int64_t)blockIdx.x < n_vt) {
+        value_tile<D>(a, (int)(blockIdx.x / a.vt_tiles), (int64_t)blockIdx.x % a.vt_tiles);
+        return;
+      }
+      w -= 4 * n_vt;
+    }
+  }
   const int64_t n_slots = (int64_t)a.n_tok * a.Hk;
   if (w < n_slots) {
     const int64_t t = w / a.Hk;
@@ -120,14 +176,7 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
       o[i] = ok ? (e2m1_bf16_bits((uint32_t)(codes >> (8 * i)) & 0xF, e) |
                    (e2m1_bf16_bits((uint32_t)(codes >> (8 * i + 4)) & 0xF, e) << 16))
                 : 0u;
-    if constexpr (TILED) {
-      if (is_v && a.vt) {
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          a.vt[vt_offset<D>(t, h, EPL * l + i, a.vt_tiles)] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
-        return;
-      }
-    }
+    if (is_v && a.vt) return;                // the value tiles hold V
     uint16_t* dst = (is_v ? a.vout : a.kout) + t * a.os_t + (int64_t)h * a.os_h + EPL * l;
     if constexpr (NCB == 2) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
@@ -139,17 +188,6 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
     return;
   }
   w -= n_slots;
-  const int64_t n_pad = a.vt_pad * a.Hk;
-  if (w < n_pad) {                          // zero the keys past the sequence in its last tile
-    if constexpr (TILED) {
-      const int64_t key = a.vt_pad0 + w / a.Hk;
-      const int h = (int)(w % a.Hk);
-#pragma unroll
-      for (int i = 0; i < E; ++i) a.vt[vt_offset<D>(key, h, E * lane + i, a.vt_tiles)] = 0;
-    }
-    return;
-  }
-  w -= n_pad;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const VecJob& jb = a.job[j];
@@ -184,14 +222,6 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
 #pragma unroll
       for (int i = 0; i < E / 2; ++i)
         r[i] = bf16_bits_rne(v[2 * i] * rot_scale<D>()) | (bf16_bits_rne(v[2 * i + 1] * rot_scale<D>()) << 16);
-    }
-    if constexpr (TILED) {
-      if (jb.to_vt) {
-#pragma unroll
-        for (int i = 0; i < E; ++i)
-          a.vt[vt_offset<D>(jb.vt_key0 + t, h, E * lane + i, a.vt_tiles)] = (uint16_t)(r[i >> 1] >> (16 * (i & 1)));
-        return;
-      }
     }
     uint16_t* dp = jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + E * lane;
     if constexpr (E == 2) {
@@ -811,12 +841,12 @@ __global__ __launch_bounds__(256) void prefill_attn16_kernel(
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
-  const int64_t waves = (int64_t)a.n_tok * a.Hk + a.vt_pad * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
+  // the tiled value layout exists at head dims 128 and 256
+  if (a.D > kHeadDim && a.vt) return hipErrorInvalidValue;
+  const int64_t tile_waves = a.vt ? 4 * (int64_t)a.Hk * a.vt_tiles : 0;
+  const int64_t waves = tile_waves + (int64_t)a.n_tok * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
   if (waves == 0) return hipSuccess;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  // the tiled value layout exists at head dims 128 and 256
-  if (a.D > kHeadDim && (a.vt || a.vt_pad || a.job[0].to_vt || a.job[1].to_vt || a.job[2].to_vt))
-    return hipErrorInvalidValue;
   switch (a.D) {
     case 128: hipLaunchKernelGGL(prefill_gather_kernel<128>, grid, block, 0, stream, a); break;
     case 256: hipLaunchKernelGGL(prefill_gather_kernel<256>, grid, block, 0, stream, a); break;
