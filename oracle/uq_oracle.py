@@ -139,9 +139,9 @@ def rotate(x: np.ndarray) -> np.ndarray:
     """y = x @ H over the last axis ([UQ-impl] _store_kv; key_chunk @ PiT).
 
     Computed as the exact +-1 sums x @ sylvester(n) times rot_scale(n) (the
-    float64 nearest 1/sqrt(n)), one rounding (this build's reading where
-    sqrt(n) is not a power of two, n = 128 or 512; for n = 256 the scale
-    1/16 is exact and so is y)."""
+    float64 nearest 1/sqrt(n)), one rounding (a reading: the pages leave the
+    rounding open where sqrt(n) is not a power of two, n = 128 or 512; for
+    n = 256 the scale 1/16 is exact and so is y)."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[-1]
     if not np.all(exact_span_ok(x)):
@@ -316,7 +316,7 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
 
     Magnitudes above 448 saturate to 448. The pages' cast is not specified
     beyond the format; above 464 round-to-nearest would produce NaN in this
-    format, so saturation is this build's reading.
+    format, so saturation is the reading taken here.
     """
     x = np.asarray(x, dtype=np.float64)
     a = np.abs(x)
@@ -358,7 +358,7 @@ def attention(q8: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, sinks=
     unchanged).
 
     ``sinks`` (G,) are per-head sink logits ([UQ-impl] passes ``self.sinks``
-    to the unified attention kernel; this build's reading, as in attention
+    to the unified attention kernel; the reading taken here, as in attention
     with sinks: one more logit per head in the softmax normaliser, with no
     value behind it, in the units of the scaled scores).
     """
@@ -392,8 +392,8 @@ def decode(query_bits, kv_cache, block_table, seq_lens, scale, pairs=None, sinks
     for b, h in todo:
         L = int(seq_lens[b])
         if L <= 0:
-            # no key to attend to: the empty weighted sum, zero (this build's
-            # reading; the pages only decode sequences holding the new token)
+            # no key to attend to: the empty weighted sum, zero (a reading;
+            # the pages only decode sequences holding the new token)
             out[b, h * qg:(h + 1) * qg] = 0.0
             continue
         K, V = gather_sequence(kv_cache, block_table[b], L, h)
@@ -460,9 +460,9 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 def rotate_to_bf16(x_bits: np.ndarray) -> np.ndarray:
     """bf16 value of x @ H per vector ([UQ-impl] (x.to(float32) @ PiT).to(dtype)).
 
-    This build's reading: the exact product rounded once to bf16 (the pages'
-    float32 product differs from it only where its own rounding error moves a
-    value across a bf16 rounding boundary)."""
+    The reading taken here: the exact product rounded once to bf16 (the
+    pages' float32 product differs from it only where its own rounding error
+    moves a value across a bf16 rounding boundary)."""
     return bf16_round(rotate(bf16_to_f64(x_bits)))
 
 
