@@ -265,7 +265,7 @@ def test_dequant_bit_exact(d):
     assert torch.equal(k2[:bs], k[:bs]) and torch.equal(k2[2 * bs:], k[2 * bs:])
 
 
-@pytest.mark.parametrize("cached_len,q_len", [(0, 37), (100, 64), (333, 129)])
+@pytest.mark.parametrize("cached_len,q_len", [(0, 37), (100, 64), (333, 129), (32, 32)])
 @pytest.mark.parametrize("qg", [6, 8, 16])
 @pytest.mark.parametrize("d", DIMS)
 def test_continuation_prefill(d, cached_len, q_len, qg):

@@ -148,6 +148,41 @@ def test_continuation_prefill_vs_oracle(qg, cached_len, q_len):
                 allow_output_rounding=True)
 
 
+@pytest.mark.parametrize("cached_len,q_len", [(64, 32), (31, 1), (32, 32), (96, 64)])
+def test_continuation_prefill_whole_tiles(cached_len, q_len):
+    """Sequences that end exactly on a 32-key value tile (no zero keys pad
+    the last tile), including a one-token chunk after a 31-token prefix."""
+    say(f"prefill whole tiles cached={cached_len} q_len={q_len}")
+    rng = np.random.default_rng(5000 + cached_len + q_len)
+    out, c = _prefill_case(rng, cached_len, q_len, 2, 8)
+    want = O.continuation_prefill(bits(c["q"]), bits(c["kc"]), bits(c["vc"]), c["ref"], c["row"],
+                                  cached_len, c["scale"])
+    check_close(to_np(out), want, f"whole tiles cached={cached_len} q_len={q_len}",
+                allow_output_rounding=True)
+
+
+def test_continuation_prefill_block_outside_cache_reads_zeros():
+    """A prefix block entry past the cache reads as zero keys and values (as
+    in uq_dequant_kv): the same as the oracle over an all-zero block."""
+    say("prefill block outside the cache")
+    rng = np.random.default_rng(17)
+    cached_len, q_len, hk, qg = 70, 20, 2, 8
+    cache, ref, row = stored_sequence(rng, cached_len, hk)
+    spare = int(np.setdiff1d(np.arange(cache.shape[0]), row)[0])   # never written: all zero
+    assert not ref[spare].any()
+    bad = row.copy()
+    bad[1] = cache.shape[0]
+    q = bf16(rng.standard_normal((q_len, hk * qg, 256)))
+    kc = bf16(rng.standard_normal((q_len, hk, 256)))
+    vc = bf16(rng.standard_t(4, (q_len, hk, 256)))
+    out = uq.continuation_prefill(q.to(DEV), kc.to(DEV), vc.to(DEV), cache, torch.from_numpy(bad).to(DEV),
+                                  cached_len, 1 / 16)
+    zrow = row.copy()
+    zrow[1] = spare
+    want = O.continuation_prefill(bits(q), bits(kc), bits(vc), ref, zrow, cached_len, 1 / 16)
+    check_close(to_np(out), want, "block outside the cache", allow_output_rounding=True)
+
+
 def test_prefill_attention_strided_and_peaked():
     """The attention call on its own over strided views, with a large scale
     (peaked weights that raise the running maximum along the keys)."""
