@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restri
 //     two V_MFMA_SCALE_F32_16X16X128_F8F6F4 (d = 0..127, 128..255);
 //   online softmax in the log2 domain; the reference maximum is only raised
 //     when a tile exceeds it by more than 8 (p stays <= 256, exact softmax);
-//   O (16 q-heads x 256 d) += P (bf16 high and low parts of each weight) x V
-//     (bf16, converted with its scale) on 16 V_MFMA_F32_16X16X32_BF16.
+//   O^T (256 d x 16 q-heads) += V^T (bf16, converted with its scale) x P^T
+//     (bf16 high and low parts of each weight) on 16 V_MFMA_F32_16X16X32_BF16.
 // Lane layouts (gfx950):
 //   scaled MFMA A (FP4, 4 VGPRs): lane l -> row l%16, k = 32*(l/16) + j for
 //     nibble j; its scale byte covers those 32 k.
@@ -99,11 +99,13 @@ __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restri
 //   16x16x32 bf16 A/B: lane l -> row/col l%16, eight k slots.
 //   Result: lane l -> col l%16, rows 4*(l/16) + i.
 // So the score tile leaves lane (g = l%16, grp = l/16) holding tokens
-// 4*grp .. 4*grp+3 of q-head g, which is the P operand of the value product
-// as it stands (A: row = q-head, k slots = those four tokens, high parts,
-// then the same four tokens, low parts); the V operand (B) of lane l holds
-// dims (D/16)*(l%16) + j of the same four tokens, twice. The accumulator
-// O[j] of lane l then holds q-heads 4*(l/16) + i at dim (D/16)*(l%16) + j.
+// 4*grp .. 4*grp+3 of q-head g, which is the P^T operand of the value
+// product as it stands (B: col = q-head, k slots = those four tokens, high
+// parts, then the same four tokens, low parts); the V^T operand (A) of lane
+// l holds dims (D/16)*(l%16) + j of the same four tokens, twice. The
+// accumulator O[j] of lane l then holds q-head l%16 at dims
+// (D/16)*(4*(l/16) + i) + j: every value a lane accumulates belongs to its
+// own head, whose softmax statistics the lane also holds.
 // ---------------------------------------------------------------------------
 template <int D>
 struct Tile {
@@ -231,11 +233,13 @@ __device__ __forceinline__ void read_tile(Tile<D>& T, const uint4* __restrict__ 
 // Byte M of each token's D/32 V-code bytes holds dims (D/16)*(l%16) + 2M
 // (low nibble) and 2M + 1 (high nibble). Convert them for the lane's 4
 // tokens, regroup the bf16 halves by dim, and accumulate two MFMAs (dim even
-// / odd). Each MFMA runs over k = 32: the lane's 4 tokens twice, against the
-// high and the low bf16 parts of their weights (pa), so a weight enters the
-// product with 16 significant bits, not 8.
+// / odd) into O^T: the values are the A operand (row = dim), the weights the
+// B operand (column = query head), so each lane's accumulators belong to one
+// query head. Each MFMA runs over k = 32: the lane's 4 tokens twice, against
+// the high and the low bf16 parts of their weights (pb), so a weight enters
+// the product with 16 significant bits, not 8.
 template <int D, int M>
-__device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4], const v8bf& pa,
+__device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4], const v8bf& pb,
                                         v4f acc[D / 16]) {
   uint32_t w[4];
 #pragma unroll
@@ -248,10 +252,10 @@ __device__ __forceinline__ void pv_step(const Tile<D>& T, const float vscale[4],
   const uint32_t e1 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
   const uint32_t o0 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
   const uint32_t o1 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-  const v8bf be = __builtin_bit_cast(v8bf, make_uint4(e0, e1, e0, e1));
-  const v8bf bo = __builtin_bit_cast(v8bf, make_uint4(o0, o1, o0, o1));
-  acc[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, be, acc[2 * M], 0, 0, 0);
-  acc[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bo, acc[2 * M + 1], 0, 0, 0);
+  const v8bf ae = __builtin_bit_cast(v8bf, make_uint4(e0, e1, e0, e1));
+  const v8bf ao = __builtin_bit_cast(v8bf, make_uint4(o0, o1, o0, o1));
+  acc[2 * M] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, pb, acc[2 * M], 0, 0, 0);
+  acc[2 * M + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, pb, acc[2 * M + 1], 0, 0, 0);
 }
 
 // Maximum over the four 16-lane row groups (lanes l, l^16, l^32, l^48), with
@@ -288,7 +292,7 @@ __device__ __forceinline__ void qk_tile(const Tile<D>& T, const v8i qb[D / 128],
 }
 
 // Softmax weights p = 2^(s - m_ref) (<= 2^8 by the re-basing rule), then
-// O += P V. Touches the accumulators only through MFMAs.
+// O^T += V^T P^T. Touches the accumulators only through MFMAs.
 template <int D>
 __device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], float m_ref, int n16,
                                         v4f acc[D / 16], float& l_part) {
@@ -334,49 +338,6 @@ __device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], flo
     pv_step<D, 14>(T, vscale, pb, acc);
     pv_step<D, 15>(T, vscale, pb, acc);
   }
-}
-
-// Maximum over the 16 lanes of a row (lanes 16*grp .. 16*grp + 15), by DPP
-// row exchanges.
-__device__ __forceinline__ float row16_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
-    const int lane = __lane_id();
-    x = fmaxf(x, __uint_as_float(xor_lane_u32(__float_as_uint(x), m, lane)));
-  }
-  return x;
-}
-
-// Raise the softmax reference of every query head to cover a tile whose
-// maximum mt exceeds it by more than 8 (never lowering it, so each factor
-// f = 2^(m_ref - m_new) is <= 1), and rescale that head's row of O and its
-// weight sum by f. Row r of O sits in register i of lanes 16*g + c with
-// 4g + i = r, so O <- diag(f) O is four V_MFMA_F32_16X16X4_F32 per
-// accumulator: MFMA i takes register i of the accumulator as B (k slot g ->
-// row 4g + i) and, as A, f_r in lane (row r, k slot g) when r = 4g + i, zero
-// otherwise (f_r is lane r's own factor: lane l%16 holds head l%16's
-// statistics).
-__device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <int D>
-__device__ __forceinline__ void rebase(v4f acc[D / 16], float& m_ref, float mt, float& l_part, int n16,
-                                       int grp) {
-  const float m_new = fmaxf(m_ref, mt);
-  const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
-  float fsel[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fsel[i] = n16 == 4 * grp + i ? f : 0.f;
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) {
-    v4f d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d = mfma_f32x4(fsel[i], acc[j][i], d);
-    acc[j] = d;
-  }
-  l_part *= f;
-  m_ref = m_new;
 }
 
 // In-kernel query prologue at head dim 256: q8 = E4M3(q H) for the wave's
@@ -585,11 +546,11 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   // Softmax reference: the first tile's maximum. The weights 2^(s - m_ref)
   // are exact for any reference; keeping them <= 2^8 bounds their range. A
   // tile that exceeds the reference by more than that ends the tile loop:
-  // outside it, the rows of O (one per query head) are rescaled in place to
-  // the raised reference by diag(f) O on float32 MFMAs, and the loop resumes
-  // at that tile. The accumulators are only ever touched by MFMAs, so they
-  // stay in the accumulator registers, and the rare rescale stays out of the
-  // loop body.
+  // outside it, each lane scales its accumulators and weight sum (all of its
+  // own head) to the raised reference, and the loop resumes at that tile.
+  // Inside the loop the accumulators are only touched by MFMAs, so they stay
+  // in the accumulator registers and the rare rescale stays out of the loop
+  // body.
   v4f acc[NA];
 #pragma unroll
   for (int j = 0; j < NA; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -677,10 +638,16 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     }
 #undef UQ_STEP
     if (!rebased) break;
-    // Raise the reference to cover tile t_stop and rescale O and the sums in
-    // place; drain the ring; the loop resumes at t_stop, which is then within
-    // 2^8 of the reference.
-    rebase<D>(acc, m_ref, mt, l_part, n16, grp);
+    // Raise the reference to cover tile t_stop (never below the old one, so
+    // the factor is <= 1) and rescale the lane's sums in place. Drain the
+    // ring; the loop resumes at t_stop, which is then within 2^8 of the
+    // reference.
+    const float m_new = fmaxf(m_ref, mt);
+    const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) acc[j] *= f;
+    l_part *= f;
+    m_ref = m_new;
     UQ_WAIT_VMCNT(0);
     t0 = t_stop;
   }
@@ -695,18 +662,15 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const float l_tot = l1 + __shfl_xor(l1, 32);
   // a non-empty range has l >= 1 (its largest weight is exactly 1)
   const float inv = 1.f / l_tot;
-  if (qlane && grp == 0) {
-    part_m[stat] = m_ref;
-    part_l[stat] = l_tot;
-  }
   // The partial O / l of each query head is stored as an fp16 row times
   // 2^ex, with ex chosen from the row's largest magnitude so that it lands in
-  // [2^14, 2^15): the rounding error is at most 2^-11 of each element. The
+  // [2^14, 2^15): the rounding error is at most 2^-11 of the row maximum. The
   // row leaves as one contiguous store: the lanes first place their dims in
   // the wave's own ring, free now that every tile it issued has been
   // consumed (row stride 2 D + 16 bytes, RPS rows per slot), then each row is
-  // read back across the wave. Lane (n16, grp) holds heads 4*grp + i at dims
-  // (D/16)*n16 + j.
+  // read back across the wave. Lane (head l%16, grp) holds dims
+  // (D/16)*(4*grp + i) + j of its head, so the head's maximum is one
+  // reduction over the four row groups.
   constexpr int RS = D * 2 + 16;
   constexpr int RPS = S::kTileU4 * 16 / RS;
   static_assert((QG + RPS - 1) / RPS <= NSLOT, "the ring cannot stage the partial rows");
@@ -714,26 +678,30 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   uint4* const own[8] = {UQ_OWN_PTR(0), UQ_OWN_PTR(1), UQ_OWN_PTR(2), UQ_OWN_PTR(3),
                          UQ_OWN_PTR(4), UQ_OWN_PTR(5), UQ_OWN_PTR(6), UQ_OWN_PTR(7)};
 #undef UQ_OWN_PTR
+  float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * grp + i;                               // query head of the row
-    const float inv_r = __shfl(inv, r);
-    float amax = 0.f;
+  for (int j = 0; j < NA; ++j)
 #pragma unroll
-    for (int j = 0; j < NA; ++j) amax = fmaxf(amax, fabsf(acc[j][i]));
-    amax = row16_max(amax) * inv_r;
-    const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14 : 0;
-    if (r < QG) {
-      if (n16 == 0) part_e[((size_t)b * Hq + (size_t)h * QG + r) * P + part] = ex;
-      uint8_t* rowp = reinterpret_cast<uint8_t*>(own[r / RPS]) + (r % RPS) * RS + 2 * NA * n16;
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[j][i]));
+  amax = rowgroup_max(amax * inv);
+  const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14 : 0;
+  if (qlane && grp == 0) {
+    part_m[stat] = m_ref;
+    part_l[stat] = l_tot;
+    part_e[stat] = ex;
+  }
+  if (qlane) {
+    uint8_t* rowp = reinterpret_cast<uint8_t*>(own[n16 / RPS]) + (n16 % RPS) * RS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < NA; j += 8) {
         uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          w[k] = pack_f16(__builtin_amdgcn_ldexpf(acc[j + 2 * k][i] * inv_r, -ex),
-                          __builtin_amdgcn_ldexpf(acc[j + 2 * k + 1][i] * inv_r, -ex));
-        *reinterpret_cast<uint4*>(rowp + 2 * j) = make_uint4(w[0], w[1], w[2], w[3]);
+          w[k] = pack_f16(__builtin_amdgcn_ldexpf(acc[j + 2 * k][i] * inv, -ex),
+                          __builtin_amdgcn_ldexpf(acc[j + 2 * k + 1][i] * inv, -ex));
+        *reinterpret_cast<uint4*>(rowp + 2 * (NA * (4 * grp + i) + j)) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   }
