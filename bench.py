@@ -428,7 +428,7 @@ def prefill_main(args):
     tf = fl / (ms * 1e-3) / 1e12
     attn_tf = fl / (attn_ms * 1e-3) / 1e12
     res = {
-        "metric": f"continuation prefill TFLOP/s (bf16 MFMA), {q_len}-token chunk after {cached} cached "
+        "metric": f"continuation prefill TFLOP/s (16-bit MFMA), {q_len}-token chunk after {cached} cached "
                   f"tokens, GQA-8 D={D}",
         "value": round(tf, 2),
         "unit": "TFLOP/s",
@@ -439,7 +439,9 @@ def prefill_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16-mfma",
+        # scores on bf16 MFMAs; P.V on fp16 MFMAs over the scaled fp16 value
+        # tiles at D = 128 and 256, on bf16 high/low pairs at 512
+        "dtype": "bf16+fp16-mfma" if D <= 256 else "bf16-mfma",
         "data": "synthetic",
         "config": {"workload": f"prefill: cached_len={cached} q_len={q_len} Hq={Hq} Hk={Hk} D={D} "
                                f"block_size={bs} (step = one uq_continuation_prefill)",

@@ -346,17 +346,18 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
   if (kv_stride_t < D || kv_stride_t >= (1LL << 25))
     return fail(UQ_EUNSUPPORTED, "uq_prefill_attention: kv_stride_t %lld outside [D, 2^25)", (long long)kv_stride_t);
   uq::PrefillAttnArgs a{q, k, v, out, q_stride_t, q_stride_h, kv_stride_t, kv_stride_h,
-                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale, 0, D};
+                        out_stride_t, out_stride_h, q_len, seq_len - q_len, Hk, Hq / Hk, scale, 0, D, nullptr};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_prefill_attention launch");
 }
 
 // Workspace of uq_continuation_prefill: rotated queries, keys of prefix +
 // chunk (token-major), then the values: at head dims 128 and 256 in the tiled
 // layout of the attention kernel (per KV head, ceil(seq_len / 32) tiles of
-// 64 D bytes), at 512 token-major like the keys (vt_tiles = 0); each section
-// 256-byte aligned.
+// 64 D bytes, fp16 scaled per 32-dim block) followed by the blocks' exponent
+// parts and shifts (int32), at 512 token-major like the keys (vt_tiles = 0);
+// each section 256-byte aligned.
 struct PrefillLayout {
-  size_t q_off, k_off, v_off, total;
+  size_t q_off, k_off, v_off, e_off, s_off, total;
   long long vt_tiles;
 };
 
@@ -367,7 +368,13 @@ static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, 
   l.q_off = 0;
   l.k_off = a256((size_t)q_len * Hq * D * 2);
   l.v_off = l.k_off + a256((size_t)seq_len * Hk * D * 2);
-  l.total = l.v_off + (l.vt_tiles > 0 ? (size_t)Hk * l.vt_tiles * 32 * D * 2 : (size_t)seq_len * Hk * D * 2);
+  if (l.vt_tiles > 0) {
+    l.e_off = l.v_off + a256((size_t)Hk * l.vt_tiles * 32 * D * 2);
+    l.s_off = l.e_off + a256((size_t)Hk * uq::kVexpParts * (D / 32) * 4);
+    l.total = l.s_off + (size_t)Hk * (D / 32) * 4;
+  } else {
+    l.total = l.v_off + (size_t)seq_len * Hk * D * 2;
+  }
   return l;
 }
 
@@ -443,6 +450,8 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   g.vs_t = val_stride_t;
   g.vs_h = val_stride_h;
   g.v_keys = seq_len;
+  g.vexp_part = tiled ? reinterpret_cast<int32_t*>(ws + lay.e_off) : nullptr;
+  g.vshift = tiled ? reinterpret_cast<int32_t*>(ws + lay.s_off) : nullptr;
   g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * D, D,
                         (int64_t)q_len * Hq, Hq, 1};
   g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, D,
@@ -457,7 +466,8 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   }
   if (!(stage_mask & UQ_PREFILL_ATTEND)) return ok();
   uq::PrefillAttnArgs a{qr, kf, vf, out, (int64_t)Hq * D, D, row, D,
-                        out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale, lay.vt_tiles, D};
+                        out_stride_t, out_stride_h, q_len, cached_len, Hk, Hq / Hk, scale, lay.vt_tiles, D,
+                        g.vshift};
   return hip_status(uq::launch_prefill_attn(a, (hipStream_t)stream), "uq_continuation_prefill attention launch");
 }
 

@@ -300,9 +300,9 @@ __device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], flo
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sv[i] - m_ref);
   // Each weight as the sum of two bf16 values: hi = bf16(p) and
-  // lo = bf16(p - hi) (p - hi is exact in float32), within 2^-17 of p. A
-  // single bf16 weight (2^-9) put up to 2^-9 |v - o| into the output where a
-  // few tokens dominate.
+  // lo = bf16(p - hi) (p - hi is exact in float32), within 2^-16 p of p. A
+  // single bf16 weight (relative error up to 2^-8) put up to 2^-8 |v - o|
+  // into the output where a few tokens dominate.
   const uint32_t h01 = pack_bf16(p[0], p[1]);
   const uint32_t h23 = pack_bf16(p[2], p[3]);
   const float q0 = __uint_as_float(h01 << 16), q1 = __uint_as_float(h01 & 0xFFFF0000u);

@@ -80,14 +80,23 @@ struct GatherArgs {
   // Tiled values (vt != null, D = 128 or 256): one workgroup per (KV head,
   // tile) builds the whole tile: keys below n_tok dequantised from the cache
   // (their V is then not written to vout), keys n_tok .. v_keys - 1 copied
-  // from vsrc row key - n_tok, the rest of the last tile zero.
+  // from vsrc row key - n_tok, the rest of the last tile zero. The tiles hold
+  // fp16 values times 2^-vshift[h][d / 32]: a first kernel writes, per
+  // (KV head, part of the keys), the largest exponent of each 32-dim block
+  // (vexp_part, Hk x kVexpParts x D / 32), and the tile workgroups take the
+  // shift from it (the ones of tile 0 also store it in vshift, Hk x D / 32).
   uint16_t* vt;
   int64_t vt_tiles;          // tiles per KV head
   const uint16_t* vsrc;
   int64_t vs_t, vs_h;
   int64_t v_keys;
+  int32_t* vexp_part;
+  int32_t* vshift;
   VecJob job[3];
 };
+
+// Parts of the keys the value-exponent kernel splits each KV head into.
+constexpr int kVexpParts = 256;
 
 struct PrefillAttnArgs {
   const uint16_t* q;         // (q_len, Hq, D) rotated queries, bf16
@@ -99,6 +108,7 @@ struct PrefillAttnArgs {
   float scale;
   int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head (D <= 256)
   int D;                     // head dim: 128, 256 or 512
+  const int32_t* vshift;     // vt_tiles > 0: the tiles hold v * 2^-vshift[h][d / 32] in fp16
 };
 
 // Streaming-read probe over the blocks a decode reads.

@@ -6,11 +6,16 @@
 // and a dense causal attention over prefix + chunk aligns query i to absolute
 // position cached_len + i.)
 //
-// Two kernels:
-//   prefill_gather_kernel  builds the bf16 operands: dequantised prefix K/V,
-//                          rotated queries and chunk keys (float64 butterfly,
-//                          one rounding to bf16), copied chunk values;
-//   prefill_attn_kernel    flash attention over them on bf16 matrix cores.
+// Kernels:
+//   prefill_vexp_kernel    (values tiled, D = 128 and 256) the largest
+//                          exponent of each 32-dim block of V, by parts;
+//   prefill_gather_kernel  builds the operands: dequantised prefix K (and V
+//                          at D = 512), rotated queries and chunk keys
+//                          (float64 butterfly, one rounding to bf16), the
+//                          value tiles (fp16, scaled per block) or copied
+//                          chunk values;
+//   prefill_attn_kernel    flash attention over them on matrix cores
+//   prefill_attn16_kernel  (D = 512).
 #include "uq_internal.h"
 
 namespace uq {
@@ -19,6 +24,8 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -52,6 +59,16 @@ __device__ __forceinline__ uint32_t e2m1_bf16_bits(uint32_t code, int e) {
   return sign | ((2u + half) << (E + 132));                 // value / 2**-133
 }
 
+// The FP4 E2M1 code's value times 2**e as float32 (exact while the result is
+// a normal float32; ldexp rounds below that).
+__device__ __forceinline__ float e2m1_scaled(uint32_t code, int e) {
+  const uint32_t m = code & 7u;
+  // magnitudes 0, 0.5 (m < 2: m / 2), then (2 + (m & 1)) * 2^(m/2 - 2): 1, 1.5, 2, 3, 4, 6
+  const float mag = m < 2u ? 0.5f * (float)m : (float)(2u + (m & 1u)) * (float)(1u << ((m >> 1) - 1)) * 0.5f;
+  const float x = __builtin_amdgcn_ldexpf(mag, e);
+  return (code & 8u) ? -x : x;
+}
+
 // Chunk permutation of dim row `dim` in the tiled value layout. The P.V read
 // of 16 consecutive dim rows (64 bytes apart), chunk g of each, then hits
 // distinct banks both within each aligned group of 8 rows (128 bytes of
@@ -67,47 +84,165 @@ __device__ __forceinline__ int vt_tile_offset(int kk, int dim) {
   return dim * 32 + 8 * (g ^ vt_swizzle(dim)) + s;
 }
 
+// Largest exponent (floor(log2 |v|), or above) of each 32-dim block of the
+// values of KV head blockIdx.y over part blockIdx.x of the keys (kVexpParts
+// equal parts of 0 .. v_keys - 1): for a cached key the block's scale byte
+// bounds it (the largest E2M1 magnitude is 6 = 1.5 * 2^2), for a chunk key
+// the bf16 exponent fields of the block's values. -1000 where the part has
+// no key. One workgroup per (part, KV head); the value tiles read the parts.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_vexp_kernel(GatherArgs a) {
+  using F = Fmt<D>;
+  constexpr int NB = D / 32, PPK = D / 4;    // value blocks; 8-byte pieces per chunk key
+  __shared__ int red[NB];
+  const int part = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid < NB) red[tid] = -1000;
+  const int64_t per = (a.v_keys + kVexpParts - 1) / kVexpParts;
+  const int64_t k0 = (int64_t)part * per, k1 = min(k0 + per, a.v_keys);
+  int em[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) em[b] = -1000;
+  // cached keys, one per thread: the block's scale bytes
+  for (int64_t key = k0 + tid; key < min(k1, (int64_t)a.n_tok); key += 256) {
+    const int phys = a.block_row[key >> a.log2_bs];
+    if (phys < 0 || (int64_t)phys >= a.num_blocks) continue;     // read as zeros
+    const uint8_t* sp = a.cache + ((((int64_t)phys << a.log2_bs) + (key & ((1 << a.log2_bs) - 1))) * a.Hk + h) *
+                                      F::kSlot + F::kVScale;
+    uint32_t w[NB / 4];
+    if constexpr (NB == 4) {
+      w[0] = *reinterpret_cast<const uint32_t*>(sp);
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(sp);
+      w[0] = x.x;
+      w[1] = x.y;
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) em[b] = max(em[b], (int)((w[b >> 2] >> (8 * (b & 3))) & 0xFF) - 127 + 2);
+  }
+  // chunk keys: thread t takes 8-byte pieces t, t + 256, ... of the part's
+  // rows (PPK pieces per key, so its 4 dims 4 (t % PPK) .. stay the same),
+  // eight pieces in flight at a time
+  const int64_t c0 = max(k0, (int64_t)a.n_tok);
+  const int64_t n_pieces = max(k1 - c0, (int64_t)0) * PPK;
+  int ec = -1000;
+  for (int64_t base = 0; base < n_pieces; base += 8 * 256) {
+    uint2 x[8];
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t piece = base + 256 * u + tid;
+      ok[u] = piece < n_pieces;
+      x[u] = make_uint2(0, 0);
+      if (ok[u])
+        x[u] = *reinterpret_cast<const uint2*>(a.vsrc + (c0 + piece / PPK - a.n_tok) * a.vs_t +
+                                               (int64_t)h * a.vs_h + 4 * (piece % PPK));
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!ok[u]) continue;
+      const uint32_t m = max(max((x[u].x >> 7) & 0xFF, (x[u].x >> 23) & 0xFF),
+                             max((x[u].y >> 7) & 0xFF, (x[u].y >> 23) & 0xFF));
+      ec = max(ec, (int)m - 127);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (em[b] > -1000) atomicMax(&red[b], em[b]);
+  if (ec > -1000) atomicMax(&red[(4 * (tid % PPK)) / 32], ec);
+  __syncthreads();
+  if (tid < NB) a.vexp_part[((int64_t)h * kVexpParts + part) * NB + tid] = red[tid];
+}
+
+// fp16 bits of x (float32) rounded to nearest-even.
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
 // One 32-key tile of the tiled values of KV head h, built by a whole
 // workgroup (4 waves, 8 keys each) in LDS and written out as contiguous
 // 16-byte stores, so that each dim row reaches memory whole. Lane l holds
 // dims D/64 l .. D/64 l + D/64 - 1 of a key: from the cache for keys below
-// n_tok (codes and scale byte of those dims, exact bf16 bits), from vsrc
-// for the chunk's keys up to v_keys, zero past them.
+// n_tok (codes and scale byte of those dims), from vsrc for the chunk's keys
+// up to v_keys, zero past them. Each value v of 32-dim block b is stored as
+// fp16(v * 2^-shift_b), shift_b = (largest exponent of the block over all
+// keys) - 14, so the block's largest magnitude lands below 2^15: exact for
+// every value whose last significant bit is at least 2^(shift_b - 24), i.e.
+// within about 2^38 (cached) or 2^31 (chunk) of the block's largest; smaller
+// ones round to fp16's subnormals (absolute error at most 2^(shift_b - 25)).
 template <int D>
 __device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j) {
   using F = Fmt<D>;
   constexpr int DL = D / 64;                 // dims per lane: 2 or 4
+  constexpr int NB = D / 32;
   __shared__ uint16_t img[32 * D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ int sh[NB];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < NB) sh[tid] = -1000;
+  __syncthreads();
+  // the blocks' exponents over the kVexpParts parts are requested first,
+  // then the lane's raw values of its 8 keys (codes and exponent of a cached
+  // key, bf16 bits of a chunk key), so that both round trips overlap
+  constexpr int NPT = kVexpParts * NB / 256;   // part entries per thread
+  static_assert(NPT * 256 == kVexpParts * NB, "part entries");
+  int pe[NPT];
+  const int32_t* pp = a.vexp_part + (int64_t)h * kVexpParts * NB;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) pe[i] = pp[tid + 256 * i];
+  uint32_t raw[8][DL / 2];
+  int ek[8], kind[8];                        // kind: 0 zero, 1 cached, 2 chunk
 #pragma unroll
   for (int kk0 = 0; kk0 < 8; ++kk0) {
-    const int kk = 8 * wave + kk0;
-    const int64_t key = 32 * j + kk;
-    uint32_t v[DL / 2] = {};
+    const int64_t key = 32 * j + 8 * wave + kk0;
+    kind[kk0] = 0;
+    ek[kk0] = 0;
+#pragma unroll
+    for (int i = 0; i < DL / 2; ++i) raw[kk0][i] = 0;
     if (key < a.n_tok) {
       const int phys = a.block_row[key >> a.log2_bs];
       if (phys >= 0 && (int64_t)phys < a.num_blocks) {
         const uint8_t* slot =
             a.cache + ((((int64_t)phys << a.log2_bs) + (key & ((1 << a.log2_bs) - 1))) * a.Hk + h) * F::kSlot;
-        const uint32_t codes = DL == 4 ? *reinterpret_cast<const uint16_t*>(slot + F::kVCode + 2 * lane)
-                                       : slot[F::kVCode + lane];
-        const int e = (int)slot[F::kVScale + (DL * lane) / 32] - 127;
-#pragma unroll
-        for (int i = 0; i < DL / 2; ++i)
-          v[i] = e2m1_bf16_bits((codes >> (8 * i)) & 0xF, e) | (e2m1_bf16_bits((codes >> (8 * i + 4)) & 0xF, e) << 16);
+        raw[kk0][0] = DL == 4 ? *reinterpret_cast<const uint16_t*>(slot + F::kVCode + 2 * lane)
+                              : slot[F::kVCode + lane];
+        ek[kk0] = (int)slot[F::kVScale + (DL * lane) / 32] - 127;
+        kind[kk0] = 1;
       }
     } else if (key < a.v_keys) {
       const uint16_t* src = a.vsrc + (key - a.n_tok) * a.vs_t + (int64_t)h * a.vs_h + DL * lane;
       if constexpr (DL == 4) {
-        const uint2 x = *reinterpret_cast<const uint2*>(src);
-        v[0] = x.x;
-        v[1] = x.y;
+        const uint2 y = *reinterpret_cast<const uint2*>(src);
+        raw[kk0][0] = y.x;
+        raw[kk0][1] = y.y;
       } else {
-        v[0] = *reinterpret_cast<const uint32_t*>(src);
+        raw[kk0][0] = *reinterpret_cast<const uint32_t*>(src);
       }
+      kind[kk0] = 2;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NPT; ++i)
+    if (pe[i] > -1000) atomicMax(&sh[(tid + 256 * i) % NB], pe[i]);
+  __syncthreads();
+  if (j == 0 && tid < NB) a.vshift[h * NB + tid] = sh[tid] > -1000 ? sh[tid] - 14 : 0;
+  const int shift = sh[(DL * lane) / 32] > -1000 ? sh[(DL * lane) / 32] - 14 : 0;
+#pragma unroll
+  for (int kk0 = 0; kk0 < 8; ++kk0) {
+    const int kk = 8 * wave + kk0;
+    float v[DL];
+#pragma unroll
+    for (int i = 0; i < DL; ++i) {
+      if (kind[kk0] == 1)        // code value times 2^(e - shift), see e2m1_scaled
+        v[i] = e2m1_scaled((raw[kk0][0] >> (4 * i)) & 0xF, ek[kk0] - shift);
+      else if (kind[kk0] == 2)
+        v[i] = __builtin_amdgcn_ldexpf(__uint_as_float(((raw[kk0][i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16),
+                                       -shift);
+      else
+        v[i] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < DL; ++i) img[vt_tile_offset(kk, DL * lane + i)] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+    for (int i = 0; i < DL; ++i) img[vt_tile_offset(kk, DL * lane + i)] = (uint16_t)f16_bits(v[i]);
   }
   __syncthreads();
   uint4* dst = reinterpret_cast<uint4*>(a.vt + ((int64_t)h * a.vt_tiles + j) * 32 * D);
@@ -259,9 +394,11 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
 //     for the even dims (col r -> dim 32b + 2r) and one for the odd ones.
 //     Rows of O are query columns, so a rescale is diag(f) O (see below).
 // Online softmax in the log2 domain with a reference maximum that is only
-// raised when a tile exceeds it by more than 8 (weights stay <= 2^8); each
-// weight enters P.V as a high and a low bf16 part (two MFMAs), and the
-// denominator sums the same parts.
+// raised when a tile exceeds it by more than 8 (weights stay <= 2^8). With
+// tiled values the weights enter P.V as fp16 against the fp16 value tiles
+// (V_MFMA_F32_16X16X32_F16, same lane layouts); with token-major values each
+// weight enters as a high and a low bf16 part (two MFMAs). The denominator
+// sums exactly the weights the product uses.
 // ---------------------------------------------------------------------------
 // Matrix-core and buffer builtins behind plain functions: the attention
 // kernel is a template over the head dim, and a builtin call whose operands
@@ -271,6 +408,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_f16(v8h a, v8h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -328,7 +468,7 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
     int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2,
-    int64_t vt_tiles) {
+    int64_t vt_tiles, const int32_t* __restrict__ vshift) {
   static_assert(DV == 128 || DV == 256, "head dim");
   constexpr int kRowBytes = 2 * DV, NCH = kRowBytes / 16, RPL = 64 / NCH;
   constexpr int kTileU4 = kKeyTile * kRowBytes / 16;      // 16-byte chunks per tile
@@ -418,6 +558,7 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
     m_ref[cb] = -INFINITY;
   }
   const v8bf ones = __builtin_bit_cast(v8bf, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  const v8h ones16 = __builtin_bit_cast(v8h, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
 
   // Scores of one tile, S^T = K Q^T (K operands read four steps ahead).
   struct Scores {
@@ -509,13 +650,39 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
         m_ref[cb] = m_new;
       }
     }
-    // weights p = 2^(s * scale_log2 - m_ref), each as two bf16 parts,
-    // hi = bf16(p) and lo = bf16(p - hi) (p - hi is exact in float32), so a
-    // weight enters the product with 16 significant bits (a single bf16
-    // weight put up to 2^-9 |v - o| into the output where a few keys
-    // dominate). Their row sums come from MFMAs against ones, so they are
-    // the sums of exactly the weights the product uses and land in O's row
-    // layout.
+    // weights p = 2^(s * scale_log2 - m_ref). Their row sums come from MFMAs
+    // against ones, so they are the sums of exactly the weights the product
+    // uses and land in O's row layout.
+    if constexpr (VT) {
+      // fp16 weights (11 significant bits, relative error at most 2^-11, so
+      // at most 2^-11 |v - o| in the output) against the fp16 value tiles,
+      // one MFMA per product
+      v8h ph[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        uint32_t pw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[cb][2 * i], scale_log2, -m_ref[cb]));
+          const float pc = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[cb][2 * i + 1], scale_log2, -m_ref[cb]));
+          pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pa, pc}, v2h));
+        }
+        ph[cb] = __builtin_bit_cast(v8h, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        lsum[cb] = mfma_f16(ph[cb], ones16, lsum[cb]);
+      }
+#pragma unroll
+      for (int n = 0; n < NACC; ++n) {
+        const int dim = 16 * n + r16;
+        const v8h vh = __builtin_bit_cast(v8h, ld16(vb_ + dim * 64 + 16 * (g ^ vt_swizzle(dim))));
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[cb][n] = mfma_f16(ph[cb], vh, acc[cb][n]);
+      }
+      return;
+    }
+    // token-major bf16 values: each weight as two bf16 parts, hi = bf16(p)
+    // and lo = bf16(p - hi) (p - hi is exact in float32), so a weight enters
+    // the product with 16 significant bits (a single bf16 weight put up to
+    // 2^-8 |v - o| into the output where a few keys dominate)
     v8bf pb[CB], pl[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -532,20 +699,6 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
       pl[cb] = __builtin_bit_cast(v8bf, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       lsum[cb] = mfma_bf16(pb[cb], ones, lsum[cb]);
       lsum[cb] = mfma_bf16(pl[cb], ones, lsum[cb]);
-    }
-
-    if constexpr (VT) {
-#pragma unroll
-      for (int n = 0; n < NACC; ++n) {
-        const int dim = 16 * n + r16;
-        const v8bf vb = __builtin_bit_cast(v8bf, ld16(vb_ + dim * 64 + 16 * (g ^ vt_swizzle(dim))));
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          acc[cb][n] = mfma_bf16(pb[cb], vb, acc[cb][n]);
-          acc[cb][n] = mfma_bf16(pl[cb], vb, acc[cb][n]);
-        }
-      }
-      return;
     }
 #pragma unroll
     for (int b = 0; b < NJ; ++b) {
@@ -605,9 +758,12 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
   }
 #undef UQP_STEP
 
-  // Epilogue: lane (r, g) holds, for column 4g + i, O at dims 16n + r (VT)
-  // or at dims 32b + 2r, 2r + 1 (even / odd accumulators), and that
-  // column's weight sum.
+  // Epilogue: lane (r, g) holds, for column 4g + i, O at dims 16n + r (VT,
+  // in units of 2^vshift of the dims' 32-block) or at dims 32b + 2r, 2r + 1
+  // (even / odd accumulators), and that column's weight sum.
+  int vsh[VT ? DV / 32 : 1];
+#pragma unroll
+  for (int b = 0; b < (VT ? DV / 32 : 1); ++b) vsh[b] = VT ? vshift[hk * (DV / 32) + b] : 0;
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -621,7 +777,8 @@ __global__ __launch_bounds__(64 * (8 / CB)) void prefill_attn_kernel(
       if constexpr (VT) {
 #pragma unroll
         for (int n = 0; n < NACC; ++n)
-          op[16 * n + r16] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][n][i] * inv));
+          op[16 * n + r16] =
+              __builtin_bit_cast(uint16_t, (__bf16)__builtin_amdgcn_ldexpf(acc[cb][n][i] * inv, vsh[n / 2]));
       } else {
 #pragma unroll
         for (int b = 0; b < NJ; ++b)
@@ -846,6 +1003,13 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   const int64_t tile_waves = a.vt ? 4 * (int64_t)a.Hk * a.vt_tiles : 0;
   const int64_t waves = tile_waves + (int64_t)a.n_tok * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
   if (waves == 0) return hipSuccess;
+  if (a.vt) {                                 // the value tiles' exponent shifts first
+    const dim3 vgrid(kVexpParts, (unsigned)a.Hk);
+    if (a.D == kHeadDim)
+      hipLaunchKernelGGL(prefill_vexp_kernel<256>, vgrid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(prefill_vexp_kernel<128>, vgrid, dim3(256), 0, stream, a);
+  }
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   switch (a.D) {
     case 128: hipLaunchKernelGGL(prefill_gather_kernel<128>, grid, block, 0, stream, a); break;
@@ -879,8 +1043,9 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
 #define UQP_LAUNCH(VTV, DVV, TILES)                                                                      \
   hipLaunchKernelGGL((prefill_attn_kernel<VTV, DVV>), grid, block, 0, stream, a.q, a.qs_t, a.qs_h, a.k, \
                      a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len, a.cached_len, a.QG, ppw, sl2, \
-                     (int64_t)(TILES))
+                     (int64_t)(TILES), a.vshift)
   if (a.vt_tiles > 0) {
+    if (!a.vshift) return hipErrorInvalidValue;
     if (a.D == kHeadDim) UQP_LAUNCH(true, 256, a.vt_tiles); else UQP_LAUNCH(true, 128, a.vt_tiles);
   } else {
     if (a.D == kHeadDim) UQP_LAUNCH(false, 256, 0); else UQP_LAUNCH(false, 128, 0);

@@ -229,11 +229,13 @@ def test_continuation_prefill_workspace_bytes(libuq):
     assert f(8, 100, 15, 2, 256) == 0
     assert f(8, 100, 16, 2, 1024) == 0
     n = f(8, 100, 16, 2, 256)
-    # rotated queries, keys of the whole sequence, then values in tiles of 32 keys, as bf16
-    assert n == 8 * 16 * 512 + 100 * 2 * 512 + 2 * 4 * 32 * 512
+    # rotated queries, keys of the whole sequence, values in tiles of 32 keys
+    # (2-byte elements), then per KV head 256 parts and one shift for each of
+    # the D / 32 value blocks (int32), every section 256-byte aligned
+    assert n == 8 * 16 * 512 + 100 * 2 * 512 + 2 * 4 * 32 * 512 + 2 * 256 * 8 * 4 + 2 * 8 * 4
     assert f(8, 101, 16, 2, 256) > n
-    # head dim 128: the same sections with 128-element rows
-    assert f(8, 100, 16, 2, 128) == 8 * 16 * 256 + 100 * 2 * 256 + 2 * 4 * 32 * 256
+    # head dim 128: the same sections with 128-element rows and 4 blocks
+    assert f(8, 100, 16, 2, 128) == 8 * 16 * 256 + 100 * 2 * 256 + 2 * 4 * 32 * 256 + 2 * 256 * 4 * 4 + 2 * 4 * 4
     # head dim 512: values token-major like the keys
     assert f(8, 100, 16, 2, 512) == 8 * 16 * 1024 + 100 * 2 * 1024 + 100 * 2 * 1024
     assert f(8, 100, 130, 2, 512) == 0        # GQA group 64 at most at D = 512
