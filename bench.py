@@ -439,9 +439,8 @@ def prefill_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # scores on bf16 MFMAs; P.V on fp16 MFMAs over the scaled fp16 value
-        # tiles at D = 128 and 256, on bf16 high/low pairs at 512
-        "dtype": "bf16+fp16-mfma" if D <= 256 else "bf16-mfma",
+        # scores on bf16 MFMAs, P.V on fp16 MFMAs over the scaled fp16 value tiles
+        "dtype": "bf16+fp16-mfma",
         "data": "synthetic",
         "config": {"workload": f"prefill: cached_len={cached} q_len={q_len} Hq={Hq} Hk={Hk} D={D} "
                                f"block_size={bs} (step = one uq_continuation_prefill)",
@@ -452,7 +451,7 @@ def prefill_main(args):
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(f"prefill-D{D}", PREFILL_TRAFFIC_RECORD, PREFILL_SOURCE),
-                     "kernel": "prefill_attn16_kernel" if D == 512 else "prefill_attn_kernel",
+                     "kernel": "prefill_attn512x2_kernel" if D == 512 else "prefill_attn_kernel",
                      "flops_per_launch": fl},
     }
     if not args.no_cpu_baseline:

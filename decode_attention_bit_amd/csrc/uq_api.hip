@@ -351,10 +351,9 @@ int uq_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v
 }
 
 // Workspace of uq_continuation_prefill: rotated queries, keys of prefix +
-// chunk (token-major), then the values: at head dims 128 and 256 in the tiled
-// layout of the attention kernel (per KV head, ceil(seq_len / 32) tiles of
-// 64 D bytes, fp16 scaled per 32-dim block) followed by the blocks' exponent
-// parts and shifts (int32), at 512 token-major like the keys (vt_tiles = 0);
+// chunk (token-major), the values in the tiled layout of the attention
+// kernels (per KV head, ceil(seq_len / 32) tiles of 64 D bytes, fp16 scaled
+// per 32-dim block), then the blocks' exponent parts and shifts (int32);
 // each section 256-byte aligned.
 struct PrefillLayout {
   size_t q_off, k_off, v_off, e_off, s_off, total;
@@ -364,17 +363,13 @@ struct PrefillLayout {
 static PrefillLayout prefill_layout(long long q_len, long long seq_len, int Hq, int Hk, int D) {
   auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
   PrefillLayout l{};
-  l.vt_tiles = D <= UQ_HEAD_DIM ? (seq_len + 31) / 32 : 0;
+  l.vt_tiles = (seq_len + 31) / 32;
   l.q_off = 0;
   l.k_off = a256((size_t)q_len * Hq * D * 2);
   l.v_off = l.k_off + a256((size_t)seq_len * Hk * D * 2);
-  if (l.vt_tiles > 0) {
-    l.e_off = l.v_off + a256((size_t)Hk * l.vt_tiles * 32 * D * 2);
-    l.s_off = l.e_off + a256((size_t)Hk * uq::kVexpParts * (D / 32) * 4);
-    l.total = l.s_off + (size_t)Hk * (D / 32) * 4;
-  } else {
-    l.total = l.v_off + (size_t)seq_len * Hk * D * 2;
-  }
+  l.e_off = l.v_off + a256((size_t)Hk * l.vt_tiles * 32 * D * 2);
+  l.s_off = l.e_off + a256((size_t)Hk * uq::kVexpParts * (D / 32) * 4);
+  l.total = l.s_off + (size_t)Hk * (D / 32) * 4;
   return l;
 }
 
@@ -439,27 +434,22 @@ int uq_continuation_prefill_stages(int stage_mask, const uint16_t* query, const 
   g.Hk = Hk;
   g.num_blocks = num_blocks;
   g.log2_bs = log2_bs;
-  const bool tiled = lay.vt_tiles > 0;      // head dims 128 and 256
   g.kout = kf;
-  g.vout = tiled ? nullptr : vf;
+  g.vout = nullptr;                         // the value tiles hold V
   g.os_t = row;
   g.os_h = D;
-  g.vt = tiled ? vf : nullptr;
+  g.vt = vf;
   g.vt_tiles = lay.vt_tiles;
   g.vsrc = value;
   g.vs_t = val_stride_t;
   g.vs_h = val_stride_h;
   g.v_keys = seq_len;
-  g.vexp_part = tiled ? reinterpret_cast<int32_t*>(ws + lay.e_off) : nullptr;
-  g.vshift = tiled ? reinterpret_cast<int32_t*>(ws + lay.s_off) : nullptr;
+  g.vexp_part = reinterpret_cast<int32_t*>(ws + lay.e_off);
+  g.vshift = reinterpret_cast<int32_t*>(ws + lay.s_off);
   g.job[0] = uq::VecJob{query, q_stride_t, q_stride_h, qr, (int64_t)Hq * D, D,
                         (int64_t)q_len * Hq, Hq, 1};
   g.job[1] = uq::VecJob{key, key_stride_t, key_stride_h, kf + (int64_t)cached_len * row, row, D,
                         (int64_t)q_len * Hk, Hk, 1};
-  // token-major values (head dim 512): the chunk's values are copied after the prefix's
-  if (!tiled)
-    g.job[2] = uq::VecJob{value, val_stride_t, val_stride_h, vf + (int64_t)cached_len * row, row, D,
-                          (int64_t)q_len * Hk, Hk, 0};
   if (stage_mask & UQ_PREFILL_GATHER) {
     hipError_t e = uq::launch_gather(g, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "uq_continuation_prefill gather launch");

@@ -66,7 +66,7 @@ struct VecJob {
 // 32 keys in the order the attention's P operand uses, its 16-byte chunks
 // permuted by chunk ^ (((d >> 2) ^ (d >> 1)) & 3).
 struct GatherArgs {
-  int D;                     // head dim: 128, 256 or 512 (vt: 128 and 256)
+  int D;                     // head dim: 128, 256 or 512
   // dequantise tokens 0 .. n_tok-1 of a sequence (block_row[t / block_size])
   const uint8_t* cache;
   const int32_t* block_row;
@@ -77,8 +77,8 @@ struct GatherArgs {
   uint16_t* kout;
   uint16_t* vout;
   int64_t os_t, os_h;
-  // Tiled values (vt != null, D = 128 or 256): one workgroup per (KV head,
-  // tile) builds the whole tile: keys below n_tok dequantised from the cache
+  // Tiled values (vt != null): one workgroup per (KV head, 32-key tile)
+  // builds the whole tile (at D = 512 two 16-key sub-tiles): keys below n_tok dequantised from the cache
   // (their V is then not written to vout), keys n_tok .. v_keys - 1 copied
   // from vsrc row key - n_tok, the rest of the last tile zero. The tiles hold
   // fp16 values times 2^-vshift[h][d / 32]: a first kernel writes, per

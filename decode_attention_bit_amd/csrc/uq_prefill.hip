@@ -7,15 +7,16 @@
 // position cached_len + i.)
 //
 // Kernels:
-//   prefill_vexp_kernel    (values tiled, D = 128 and 256) the largest
-//                          exponent of each 32-dim block of V, by parts;
+//   prefill_vexp_kernel    the largest exponent of each 32-dim block of V,
+//                          by parts of the keys;
 //   prefill_gather_kernel  builds the operands: dequantised prefix K (and V
-//                          at D = 512), rotated queries and chunk keys
-//                          (float64 butterfly, one rounding to bf16), the
-//                          value tiles (fp16, scaled per block) or copied
-//                          chunk values;
+//                          for uq_dequant_kv), rotated queries and chunk
+//                          keys (float64 butterfly, one rounding to bf16),
+//                          the value tiles (fp16, scaled per block);
 //   prefill_attn_kernel    flash attention over them on matrix cores
-//   prefill_attn16_kernel  (D = 512).
+//                          (D = 128, 256), prefill_attn512x2_kernel at
+//                          D = 512, prefill_attn16_kernel at D = 512 over
+//                          token-major bf16 values (uq_prefill_attention).
 #include "uq_internal.h"
 
 namespace uq {
@@ -26,6 +27,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -84,6 +86,20 @@ __device__ __forceinline__ int vt_tile_offset(int kk, int dim) {
   return dim * 32 + 8 * (g ^ vt_swizzle(dim)) + s;
 }
 
+// Head dim 512: a 32-key tile is two 16-key sub-tiles of 16 KB, each D dim
+// rows of 32 bytes; key 4g + i of a sub-tile sits at element i of 8-byte
+// chunk g ^ vt16_swizzle(dim) of its dim row. A 16x16x16 MFMA's B operand
+// (4 keys of one dim) is then one 8-byte read. The 16 lanes of one key group
+// read 16 consecutive dims: rows d, d + 4, d + 8, d + 12 start on the same
+// bank of a 128-byte bank row, and the swizzle sends them to its four
+// different 8-byte chunks (and the other key group of a 32-lane half to the
+// other chunk of each pair).
+__device__ __forceinline__ int vt16_swizzle(int dim) { return (dim >> 2) & 3; }
+__device__ __forceinline__ int vt16_tile_offset(int kk, int dim) {
+  const int g = (kk & 15) >> 2;
+  return (kk >> 4) * (16 * 512) + dim * 16 + 4 * (g ^ vt16_swizzle(dim)) + (kk & 3);
+}
+
 // Largest exponent (floor(log2 |v|), or above) of each 32-dim block of the
 // values of KV head blockIdx.y over part blockIdx.x of the keys (kVexpParts
 // equal parts of 0 .. v_keys - 1): for a cached key the block's scale byte
@@ -112,10 +128,16 @@ __global__ __launch_bounds__(256) void prefill_vexp_kernel(GatherArgs a) {
     uint32_t w[NB / 4];
     if constexpr (NB == 4) {
       w[0] = *reinterpret_cast<const uint32_t*>(sp);
-    } else {
+    } else if constexpr (NB == 8) {
       const uint2 x = *reinterpret_cast<const uint2*>(sp);
       w[0] = x.x;
       w[1] = x.y;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(sp);
+      w[0] = x.x;
+      w[1] = x.y;
+      w[2] = x.z;
+      w[3] = x.w;
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) em[b] = max(em[b], (int)((w[b >> 2] >> (8 * (b & 3))) & 0xFF) - 127 + 2);
@@ -174,7 +196,7 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
 template <int D>
 __device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j) {
   using F = Fmt<D>;
-  constexpr int DL = D / 64;                 // dims per lane: 2 or 4
+  constexpr int DL = D / 64;                 // dims per lane: 2, 4 or 8
   constexpr int NB = D / 32;
   __shared__ uint16_t img[32 * D];
   __shared__ int sh[NB];
@@ -204,17 +226,21 @@ __device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j
       if (phys >= 0 && (int64_t)phys < a.num_blocks) {
         const uint8_t* slot =
             a.cache + ((((int64_t)phys << a.log2_bs) + (key & ((1 << a.log2_bs) - 1))) * a.Hk + h) * F::kSlot;
-        raw[kk0][0] = DL == 4 ? *reinterpret_cast<const uint16_t*>(slot + F::kVCode + 2 * lane)
-                              : slot[F::kVCode + lane];
+        raw[kk0][0] = DL == 8   ? *reinterpret_cast<const uint32_t*>(slot + F::kVCode + 4 * lane)
+                      : DL == 4 ? *reinterpret_cast<const uint16_t*>(slot + F::kVCode + 2 * lane)
+                                : slot[F::kVCode + lane];
         ek[kk0] = (int)slot[F::kVScale + (DL * lane) / 32] - 127;
         kind[kk0] = 1;
       }
     } else if (key < a.v_keys) {
       const uint16_t* src = a.vsrc + (key - a.n_tok) * a.vs_t + (int64_t)h * a.vs_h + DL * lane;
-      if constexpr (DL == 4) {
-        const uint2 y = *reinterpret_cast<const uint2*>(src);
-        raw[kk0][0] = y.x;
-        raw[kk0][1] = y.y;
+      if constexpr (DL >= 4) {
+#pragma unroll
+        for (int c = 0; c < DL / 4; ++c) {
+          const uint2 y = *reinterpret_cast<const uint2*>(src + 4 * c);
+          raw[kk0][2 * c] = y.x;
+          raw[kk0][2 * c + 1] = y.y;
+        }
       } else {
         raw[kk0][0] = *reinterpret_cast<const uint32_t*>(src);
       }
@@ -242,7 +268,9 @@ __device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j
         v[i] = 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < DL; ++i) img[vt_tile_offset(kk, DL * lane + i)] = (uint16_t)f16_bits(v[i]);
+    for (int i = 0; i < DL; ++i)
+      img[D > kHeadDim ? vt16_tile_offset(kk, DL * lane + i) : vt_tile_offset(kk, DL * lane + i)] =
+          (uint16_t)f16_bits(v[i]);
   }
   __syncthreads();
   uint4* dst = reinterpret_cast<uint4*>(a.vt + ((int64_t)h * a.vt_tiles + j) * 32 * D);
@@ -252,7 +280,7 @@ __device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j
 }
 
 // ---------------------------------------------------------------------------
-// Gather. With tiled values (D = 128, 256) the first Hk * vt_tiles
+// Gather. With tiled values (the continuation prefill) the first Hk * vt_tiles
 // workgroups each build one value tile (value_tile). After them, one wave
 // per unit of work, the role chosen by the wave's index (wave-uniform):
 // first the prefix slots (token, KV head) to dequantise, then up to three
@@ -272,7 +300,7 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
   constexpr int E = F::kPerLane;           // rotated elements per lane: 2, 4 or 8
   int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if constexpr (D <= kHeadDim) {
+  {
     if (a.vt) {                              // workgroup-uniform
       const int64_t n_vt = (int64_t)a.Hk * a.vt_tiles;
       if ((int64_t)blockIdx.x < n_vt) {
@@ -411,6 +439,9 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
 }
 __device__ __forceinline__ v4f mfma_f16(v8h a, v8h b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_f16x16(v4h a, v4h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ v4f mfma_f32x4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -995,11 +1026,203 @@ __global__ __launch_bounds__(256) void prefill_attn16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head dim 512 over the continuation prefill's fp16 value sub-tiles, with two
+// waves per 16-column block: wave w owns columns 16 (w & 3) .. + 15 and dims
+// 256 (w >> 2) .. + 255 of O. Each wave computes the scores of its columns
+// over its half of the dims (8 MFMAs per tile); the two halves meet in LDS,
+// double-buffered by tile parity so that the one barrier per tile orders
+// them, and both waves then run the same softmax on the same full scores
+// (a + b = b + a in float32), so their weights, sums and re-bases agree.
+// Half the accumulators and query registers of prefill_attn16_kernel per
+// wave: two waves share a SIMD.
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(512) void prefill_attn512x2_kernel(
+    const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
+    int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2,
+    int64_t vt_tiles, const int32_t* __restrict__ vshift) {
+  constexpr int KT = 16, kRowBytes = 2 * DV, NCH = kRowBytes / 16;
+  static_assert(NCH == 64, "one 1 KB load per row");
+  constexpr int kTileU4 = KT * NCH;
+  constexpr int HD = DV / 2;                       // dims per wave
+  constexpr int NJ = HD / 32, NACC = HD / 16;      // query registers, accumulators
+  constexpr int WAVES = 8, ROWS = KT / WAVES;      // rows of K and of V each wave moves
+  __shared__ uint4 kr0[kTileU4], kr1[kTileU4], kr2[kTileU4], kr3[kTileU4];
+  __shared__ uint4 vr0[kTileU4], vr1[kTileU4], vr2[kTileU4], vr3[kTileU4];
+  __shared__ v4f xs[2][WAVES][64];                 // partial scores, by tile parity
+
+  const int n_ptiles = (q_len + ppw - 1) / ppw;
+  const int p0 = (n_ptiles - 1 - (int)blockIdx.x) * ppw;
+  const int hk = blockIdx.y;
+  const int p_end = min(p0 + ppw, q_len);
+  const int kend = cached_len + p_end;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cb = wave & 3, hf = wave >> 2;
+  const int r16 = lane & 15, g = lane >> 4;
+
+  const int c0 = 16 * cb + r16;
+  const int cpos = p0 + c0 / QG;
+  const bool cval = c0 < ppw * QG && cpos < q_len;
+  const int klim = cached_len + cpos + 1;
+  v8bf qb[NJ];
+  {
+    const uint16_t* qp = q + (int64_t)(cval ? cpos : 0) * qs_t + (int64_t)(cval ? hk * QG + c0 % QG : 0) * qs_h +
+                         HD * hf + 8 * g;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (cval) x = ld16(qp + 32 * j);
+      qb[j] = __builtin_bit_cast(v8bf, x);
+    }
+  }
+
+  const uint32_t row_bytes = (uint32_t)(kvs_t * 2);
+  uint32_t koff[ROWS], voff[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int r = ROWS * wave + i;
+    koff[i] = r * row_bytes + 16 * (lane ^ (r & 15));
+    voff[i] = 1024 * r + 16 * lane;                // the 16 KB sub-tile is contiguous
+  }
+  const int n_kt = (kend + KT - 1) / KT;
+  auto issue = [&](uint4* ks, uint4* vs, int t) {
+    const int key0 = t * KT;
+    const int nv = min(KT, kend - key0);
+    const int nrec = (nv - 1) * (int)row_bytes + kRowBytes;
+    const int64_t base = (int64_t)key0 * kvs_t + (int64_t)hk * kvs_h;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((void*)(k + base), nrec);
+    const __amdgpu_buffer_rsrc_t rv =
+        buffer_rsrc((void*)(v + ((int64_t)hk * vt_tiles * 2 + t) * (KT * DV)), KT * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) load_lds16(rk, ks + 64 * (ROWS * wave + i), koff[i]);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) load_lds16(rv, vs + 64 * (ROWS * wave + i), voff[i]);
+  };
+
+  v4f acc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  v4f lsum = {0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;
+  const v4h ones4 = __builtin_bit_cast(v4h, make_uint2(0x3C003C00u, 0x3C003C00u));
+
+  // S^T over this wave's dims: 32-dim steps 8 hf .. 8 hf + 7 of the key rows
+  auto pscores = [&](const uint4* ks) {
+    const uint8_t* kb_ = reinterpret_cast<const uint8_t*>(ks);
+    v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int h = 0; h < NJ / 4; ++h) {
+      v8bf ka[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ka[j] = __builtin_bit_cast(
+            v8bf, ld16(kb_ + r16 * kRowBytes + 16 * ((4 * (NJ * hf + 4 * h + j) + g) ^ r16)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j & 1] = mfma_bf16(ka[j], qb[4 * h + j], s[j & 1]);
+    }
+    return s[0] + s[1];
+  };
+
+  auto weigh = [&](const v4f& s, const uint4* vs, int t) {
+    const uint8_t* vb_ = reinterpret_cast<const uint8_t*>(vs);
+    const int key0 = t * KT;
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = s[i];
+    if (key0 + KT > cached_len + p0 + 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (key0 + 4 * g + i >= klim) sv[i] = -INFINITY;
+    }
+    const float mt = rowgroup_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * scale_log2;
+    if (t == 0) m_ref = mt;
+    if (__any(mt > m_ref + 8.0f)) {
+      // raise the reference, O <- diag(f) O on float32 MFMAs (as above)
+      const float m_new = fmaxf(m_ref, mt);
+      const float f = m_new > m_ref ? exp2f(m_ref - m_new) : 1.f;
+      float fsel[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fsel[i] = r16 == 4 * g + i ? f : 0.f;
+#pragma unroll
+      for (int j = 0; j < NACC + 1; ++j) {
+        v4f& a = j < NACC ? acc[j] : lsum;
+        v4f d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d = mfma_f32x4(fsel[i], a[i], d);
+        a = d;
+      }
+      m_ref = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -m_ref));
+    const v4h ph = __builtin_bit_cast(
+        v4h, make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p[0], p[1]}, v2h)),
+                        __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p[2], p[3]}, v2h))));
+    lsum = mfma_f16x16(ph, ones4, lsum);
+#pragma unroll
+    for (int n = 0; n < NACC; ++n) {
+      const int dim = HD * hf + 16 * n + r16;
+      const uint2 x = *reinterpret_cast<const uint2*>(vb_ + dim * 32 + 8 * (g ^ vt16_swizzle(dim)));
+      acc[n] = mfma_f16x16(ph, __builtin_bit_cast(v4h, x), acc[n]);
+    }
+  };
+
+  // Step t: tile t + 1 is made visible by the barrier, which also orders
+  // both halves' partial scores of tile t (written in step t - 1) before
+  // they are read here; tile t + 1's partial scores go to the other parity.
+  issue(kr0, vr0, 0);
+  if (1 < n_kt) issue(kr1, vr1, 1);
+  if (2 < n_kt) issue(kr2, vr2, 2);
+  wait_tiles<kStages - 2, 2 * ROWS>(n_kt - 1);
+  __syncthreads();
+  v4f mine = pscores(kr0);
+  xs[0][wave][lane] = mine;
+#define UQP_STEP2(KC, VC, KN, KF, VF)                                \
+  {                                                                  \
+    wait_tiles<kStages - 3, 2 * ROWS>(n_kt - 2 - t);                 \
+    __syncthreads();                                                 \
+    if (t + kStages - 1 < n_kt) issue(KF, VF, t + kStages - 1);      \
+    const v4f full = mine + xs[t & 1][wave ^ 4][lane];               \
+    const v4f nxt = pscores(KN);                                     \
+    xs[(t + 1) & 1][wave][lane] = nxt;                               \
+    weigh(full, VC, t);                                              \
+    mine = nxt;                                                      \
+    if (++t >= n_kt) break;                                          \
+  }
+  for (int t = 0;;) {
+    UQP_STEP2(kr0, vr0, kr1, kr3, vr3)
+    UQP_STEP2(kr1, vr1, kr2, kr0, vr0)
+    UQP_STEP2(kr2, vr2, kr3, kr1, vr1)
+    UQP_STEP2(kr3, vr3, kr0, kr2, vr2)
+  }
+#undef UQP_STEP2
+
+  // lane (r, g) holds, for column 4g + i, O at dim HD hf + 16n + r in
+  // accumulator n (in units of 2^vshift of the dim's 32-block), and that
+  // column's weight sum
+  int vsh[HD / 32];
+#pragma unroll
+  for (int b = 0; b < HD / 32; ++b) vsh[b] = vshift[hk * (DV / 32) + (HD / 32) * hf + b];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 16 * cb + 4 * g + i;
+    const float inv = 1.f / lsum[i];
+    const int pos = p0 + c / QG;
+    if (!(c < ppw * QG && pos < q_len)) continue;
+    uint16_t* op = out + (int64_t)pos * os_t + (int64_t)(hk * QG + c % QG) * os_h + HD * hf + r16;
+#pragma unroll
+    for (int n = 0; n < NACC; ++n)
+      op[16 * n] = __builtin_bit_cast(uint16_t, (__bf16)__builtin_amdgcn_ldexpf(acc[n][i] * inv, vsh[n / 2]));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
-  // the tiled value layout exists at head dims 128 and 256
-  if (a.D > kHeadDim && a.vt) return hipErrorInvalidValue;
   const int64_t tile_waves = a.vt ? 4 * (int64_t)a.Hk * a.vt_tiles : 0;
   const int64_t waves = tile_waves + (int64_t)a.n_tok * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
   if (waves == 0) return hipSuccess;
@@ -1007,8 +1230,10 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
     const dim3 vgrid(kVexpParts, (unsigned)a.Hk);
     if (a.D == kHeadDim)
       hipLaunchKernelGGL(prefill_vexp_kernel<256>, vgrid, dim3(256), 0, stream, a);
-    else
+    else if (a.D == kHeadDim / 2)
       hipLaunchKernelGGL(prefill_vexp_kernel<128>, vgrid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(prefill_vexp_kernel<512>, vgrid, dim3(256), 0, stream, a);
   }
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   switch (a.D) {
@@ -1030,12 +1255,18 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
   if (a.D != kHeadDim && a.D != kHeadDim / 2 && a.D != 2 * kHeadDim) return hipErrorInvalidValue;
   const int ppw = prefill_positions_per_wg(a.QG, a.D);
   const int n_ptiles = (a.q_len + ppw - 1) / ppw;
-  if (a.D == 2 * kHeadDim) {                 // token-major values only
-    if (a.vt_tiles > 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((prefill_attn16_kernel<512>), dim3((unsigned)n_ptiles, (unsigned)a.Hk),
-                       dim3(64 * (kColsPerWg16 / 16)), 0,
-                       stream, a.q, a.qs_t, a.qs_h, a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h,
-                       a.q_len, a.cached_len, a.QG, ppw, a.scale * 1.4426950408889634f);
+  if (a.D == 2 * kHeadDim) {
+    const dim3 grid16((unsigned)n_ptiles, (unsigned)a.Hk), block16(64 * (kColsPerWg16 / 16));
+    const float sl2_16 = a.scale * 1.4426950408889634f;
+    if (a.vt_tiles > 0) {
+      if (!a.vshift) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((prefill_attn512x2_kernel<512>), grid16, dim3(512), 0, stream, a.q, a.qs_t, a.qs_h,
+                         a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len, a.cached_len, a.QG, ppw,
+                         sl2_16, (int64_t)a.vt_tiles, a.vshift);
+    } else {
+      hipLaunchKernelGGL((prefill_attn16_kernel<512>), grid16, block16, 0, stream, a.q, a.qs_t, a.qs_h, a.k,
+                         a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len, a.cached_len, a.QG, ppw, sl2_16);
+    }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)n_ptiles, (unsigned)a.Hk), block(64 * (8 / CB));

@@ -347,14 +347,14 @@ size_t uq_continuation_prefill_workspace_bytes(int q_len, int max_seq_len, int H
  * The whole continuation prefill of one sequence: dequantise the prefix,
  * rotate the chunk's keys and the queries, append the chunk's values, then
  * attend (the steps of uq_dequant_kv, uq_rotate and uq_prefill_attention on
- * buffers in the workspace; launches on `stream`).
- * Precision of the attention: at D = 512 as uq_prefill_attention (bf16
- * values, each softmax weight as a high and a low bf16 part, relative error
- * 2^-16). At D = 128 and 256 the workspace holds the values in 32-key tiles
- * as fp16 times a power of two per (KV head, 32-dim block), chosen from the
- * block's largest exponent over prefix and chunk so that its largest
- * magnitude lands below 2^15, and the weights enter the products as fp16
- * (relative error 2^-11, so at most 2^-11 |v - o| in an output). A value
+ * buffers in the workspace; three launches on `stream`).
+ * Precision of the attention: the workspace holds the values in 32-key
+ * tiles as fp16 times a power of two per (KV head, 32-dim block), chosen
+ * from the block's largest exponent over prefix and chunk so that its
+ * largest magnitude lands below 2^15, and the weights enter the products
+ * as fp16 (relative error 2^-11, so at most 2^-11 |v - o| in an output;
+ * uq_prefill_attention on bf16 values keeps each weight as a high and a
+ * low bf16 part, 2^-16). A value
  * is exact unless it lies more than about 2^31 (a chunk value) or 2^37 (a
  * cached one) below its block's largest; such values round to fp16's
  * subnormals, an absolute error of at most about 2^-37 of that largest.

@@ -236,8 +236,8 @@ def test_continuation_prefill_workspace_bytes(libuq):
     assert f(8, 101, 16, 2, 256) > n
     # head dim 128: the same sections with 128-element rows and 4 blocks
     assert f(8, 100, 16, 2, 128) == 8 * 16 * 256 + 100 * 2 * 256 + 2 * 4 * 32 * 256 + 2 * 256 * 4 * 4 + 2 * 4 * 4
-    # head dim 512: values token-major like the keys
-    assert f(8, 100, 16, 2, 512) == 8 * 16 * 1024 + 100 * 2 * 1024 + 100 * 2 * 1024
+    # head dim 512: the same sections with 512-element rows and 16 blocks
+    assert f(8, 100, 16, 2, 512) == 8 * 16 * 1024 + 100 * 2 * 1024 + 2 * 4 * 32 * 1024 + 2 * 256 * 16 * 4 + 2 * 16 * 4
     assert f(8, 100, 130, 2, 512) == 0        # GQA group 64 at most at D = 512
     assert f(8, 100, 128, 2, 512) > 0 and f(8, 100, 130, 2, 256) > 0
 

@@ -161,49 +161,56 @@ def test_continuation_prefill_whole_tiles(cached_len, q_len):
                 allow_output_rounding=True)
 
 
-def _block_scaled_values(rng, n, hk, chunk):
+def _block_scaled_values(rng, n, hk, d, chunk):
     """Values whose 32-dim blocks differ in magnitude by up to 2^100:
     heavy-tailed t(4) values times a per-(head, block) power of two, with the
-    chunk's values 2^20 below or above the prefix's in two blocks, and two
-    blocks of constant values (+-2^40 and +-2^10 by dim), far outside fp16's
-    range, whose outputs are exact."""
-    v = rng.standard_t(4, (n, hk, 256))
-    f = np.zeros((hk, 8))
-    f[0] = [0, -20, 0, -20 if chunk else 0, 0 if chunk else -20, 0, 0, -60]
-    f[1] = [0, 0, 0, -100, 0, 0, -2, 0]
-    v = v * np.repeat(np.exp2(f), 32, axis=1)[None]
+    chunk's values 2^20 below or above the prefix's in two blocks, and
+    blocks of constant values (+-2^40, +-2^10 by dim), far outside fp16's
+    range, whose outputs are exact. Block b follows entry b % 8 of each
+    head's pattern."""
+    v = rng.standard_t(4, (n, hk, d))
+    pattern = [[0, -20, "c40", -20 if chunk else 0, 0 if chunk else -20, "c10", 0, -60],
+               [0, 0, 0, -100, 0, 0, -2, 0]]
     sign = np.where(np.arange(32) % 3 == 0, -1.0, 1.0)
-    v[:, 0, 64:96] = np.exp2(40) * sign
-    v[:, 0, 160:192] = -np.exp2(10) * sign
+    for h in range(hk):
+        for b in range(d // 32):
+            e = pattern[h % 2][b % 8]
+            if e == "c40":
+                v[:, h, 32 * b:32 * b + 32] = np.exp2(40) * sign
+            elif e == "c10":
+                v[:, h, 32 * b:32 * b + 32] = -np.exp2(10) * sign
+            else:
+                v[:, h, 32 * b:32 * b + 32] *= np.exp2(e)
     return bf16(v)
 
 
-def test_continuation_prefill_value_block_scales():
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_continuation_prefill_value_block_scales(d):
     """The value tiles hold fp16 values scaled by a power of two per (KV
     head, 32-dim block), from the largest exponent over prefix and chunk:
     blocks of very different magnitudes, blocks where the chunk's values are
     2^20 above or below the prefix's, and blocks far outside fp16's range
     all match the oracle."""
-    say("prefill value block scales")
-    rng = np.random.default_rng(23)
+    say(f"prefill value block scales d={d}")
+    rng = np.random.default_rng(23 + d)
     cached_len, q_len, hk, qg, bs = 100, 45, 2, 4, 16
     nblk = -(-cached_len // bs)
     row = rng.permutation(nblk + 2)[:nblk].astype(np.int32)
-    cache = torch.zeros((nblk + 2, bs, hk, 272), dtype=torch.uint8, device=DEV)
+    cache = torch.zeros((nblk + 2, bs, hk, d * 17 // 16), dtype=torch.uint8, device=DEV)
     ref = np.zeros(tuple(cache.shape), dtype=np.uint8)
-    kb = bf16(rng.standard_normal((cached_len, hk, 256)))
-    vb = _block_scaled_values(rng, cached_len, hk, chunk=False)
+    kb = bf16(rng.standard_normal((cached_len, hk, d)))
+    vb = _block_scaled_values(rng, cached_len, hk, d, chunk=False)
     t = np.arange(cached_len)
     slots = row[t // bs].astype(np.int64) * bs + t % bs
     uq.store(kb.to(DEV), vb.to(DEV), cache, torch.from_numpy(slots).to(DEV))
     O.store(bits(kb), bits(vb), ref, slots)
-    q = bf16(rng.standard_normal((q_len, hk * qg, 256)))
-    kc = bf16(rng.standard_normal((q_len, hk, 256)))
-    vc = _block_scaled_values(rng, q_len, hk, chunk=True)
+    q = bf16(rng.standard_normal((q_len, hk * qg, d)))
+    kc = bf16(rng.standard_normal((q_len, hk, d)))
+    vc = _block_scaled_values(rng, q_len, hk, d, chunk=True)
     out = uq.continuation_prefill(q.to(DEV), kc.to(DEV), vc.to(DEV), cache, torch.from_numpy(row).to(DEV),
                                   cached_len, 1 / 16)
     want = O.continuation_prefill(bits(q), bits(kc), bits(vc), ref, row, cached_len, 1 / 16)
-    check_close(to_np(out), want, "value block scales", allow_output_rounding=True)
+    check_close(to_np(out), want, f"value block scales d={d}", allow_output_rounding=True)
 
 
 def test_continuation_prefill_block_outside_cache_reads_zeros():
