@@ -344,17 +344,22 @@ __device__ __forceinline__ void pv_tile(const Tile<D>& T, const float sv[4], flo
 // QG query rows, computed while the first tiles are in flight. The 256-point
 // Hadamard is the Kronecker square of the 16-point one (H256[16a+b][16a'+b']
 // = H16[a][a'] H16[b][b'], popcounts add), so per row, with Q[a][b] =
-// q[16a + b], Y = H16 Q H16 is two 16 x 16 x 16 products on
-// V_MFMA_F64_16X16X4F64 (four each). Every product is q times +-1 and every
-// partial sum a +-subset sum of the row, so float64 keeps them exact (the
-// same exactness condition as the butterfly) and the E4M3 rounding sees the
-// exact y = Y / 16.
+// q[16a + b], Y = H16 Q H16 is two 16 x 16 x 16 products. Every product is q
+// times +-1 and every partial sum a +-subset sum of the row, so float64 keeps
+// them exact (the same exactness condition as the butterfly) and the E4M3
+// rounding sees the exact y = Y / 16.
+// V_MFMA_F64_16X16X4F64 reads A[m][k] from lane (m, k) and B[k][n] from lane
+// (n, k), and returns row g + 4i of D in register i of lane (n, g) (measured;
+// the 16-bit MFMAs return row 4g + i there).
 //   Z = Q H16: MFMA kb takes, in lane (c, g), A = q[16c + 4g + kb] (row c,
-//     k slot g -> b = 4g + kb) and B = H16[4g + kb][c]; Z[4g + i][c] lands in
+//     k slot g -> b = 4g + kb) and B = H16[4g + kb][c]; Z[g + 4i][c] lands in
 //     register i of lane (c, g).
-//   Y = H16 Z: MFMA kb takes A = H16[c][4g + kb] (= H16[4g + kb][c]) and, as
-//     B, register kb of the lane's own Z (k slot g -> a = 4g + kb).
-//   Y[4g + i][c] = y[16 (4g + i) + c] lands in register i of lane (c, g).
+//   Y = H16 Z: MFMA kb takes A = H16[c][4g + kb] and, as B, register kb of
+//     the lane's own Z, i.e. Z[g + 4kb][c]: k slot g of MFMA kb stands for
+//     a = g + 4kb while A carries column 4g + kb, its 2-bit halves swapped.
+//     Since H16[m][swap(a)] = H16[swap(m)][a], the product is Y with its row
+//     index swapped the same way, and the f64 layout swaps it back:
+//     Y[4g + i][c] = y[16 (4g + i) + c] lands in register i of lane (c, g).
 // The codes go through the wave's free LDS slot (QG rows of 256 bytes) into
 // the scaled MFMA's B layout (lane (head c, g): bytes 16g .. 16g + 15 and
 // 64 + 16g .. 64 + 16g + 15 of each 128-byte half of row c).
