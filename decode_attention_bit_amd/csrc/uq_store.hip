@@ -8,38 +8,47 @@
 
 namespace uq {
 
-// One wave per (token, KV head): lane l owns elements E l .. E l + E - 1
-// (E = D / 64), so a 32-element scale block is 32 / E consecutive lanes and
-// the D/2 code bytes of a region are written as 64 contiguous stores of E/2
-// bytes. K is rotated in float64, scaled by its power of two there and
+// Four (token, KV head) pairs per wave, 16 lanes each: lane s of a pair
+// owns elements E s .. E s + E - 1 (E = D / 16). K is rotated by the
+// float64 butterfly (exact under the span condition of the rotation): its
+// log2(E) low stages inside the lane, the four stages of the lane bits with
+// DPP exchanges inside the lane's row of 16, so no stage goes through the
+// LDS pipe. K is then scaled by its block's power of two in float64 and
 // rounded to odd in float32; V is scaled in float32, which holds bf16 values
 // and their power-of-two multiples exactly. Both are encoded by the E2M1
-// conversion, so the codes are those of the exact scaled values.
+// conversion, so the codes are those of the exact scaled values. The amax of
+// a 32-element block spans 32 / E lanes (one at D = 512); each lane writes
+// E/2 contiguous code bytes of K and of V.
 template <int D>
-__global__ __launch_bounds__(256) void store_kernel(
+__global__ __launch_bounds__(256) void store16_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
     int64_t n_pairs, int Hk, int64_t num_slots, int64_t ksn, int64_t ksh,
     int64_t vsn, int64_t vsh) {
   using F = Fmt<D>;
-  constexpr int E = F::kPerLane, LPB = 32 / E;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= n_pairs) return;
-  const int lane = threadIdx.x & 63;
-  const int64_t n = pair / Hk;
-  const int h = (int)(pair - n * Hk);
-  const int64_t slot = slot_mapping[n];
-  if (slot < 0 || slot >= num_slots) return;
+  constexpr int E = D / 16, LPB = E >= 32 ? 1 : 32 / E, NW = E / 8;   // NW: 32-bit code words per lane
+  const int lane = threadIdx.x & 63, s = lane & 15;
+  const int64_t pair = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  int64_t n = 0, slot = -1;
+  int h = 0;
+  if (pair < n_pairs) {
+    n = pair / Hk;
+    h = (int)(pair - n * Hk);
+    slot = slot_mapping[n];
+  }
+  const bool write = slot >= 0 && slot < num_slots;
 
+  // every lane runs the exchanges (zeros for a pair it does not write)
   double k[E];
   float v[E];
-  const uint16_t* kp = key + n * ksn + h * ksh + E * lane;
-  const uint16_t* vp = value + n * vsn + h * vsh + E * lane;
-  if constexpr (E == 2) {
-    const uint32_t kr = *reinterpret_cast<const uint32_t*>(kp), vr = *reinterpret_cast<const uint32_t*>(vp);
-    k[0] = bf16_to_f64(kr & 0xFFFF); k[1] = bf16_to_f64(kr >> 16);
-    v[0] = bf16_to_f32(vr & 0xFFFF); v[1] = bf16_to_f32(vr >> 16);
-  } else {
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    k[i] = 0.0;
+    v[i] = 0.f;
+  }
+  if (write) {
+    const uint16_t* kp = key + n * ksn + (int64_t)h * ksh + E * s;
+    const uint16_t* vp = value + n * vsn + (int64_t)h * vsh + E * s;
 #pragma unroll
     for (int c = 0; c < E / 4; ++c) {
       const uint2 kr = *reinterpret_cast<const uint2*>(kp + 4 * c);
@@ -50,8 +59,22 @@ __global__ __launch_bounds__(256) void store_kernel(
       v[4 * c + 2] = bf16_to_f32(vr.y & 0xFFFF); v[4 * c + 3] = bf16_to_f32(vr.y >> 16);
     }
   }
-
-  fwht_wave<E>(k, lane);
+#pragma unroll
+  for (int m = 1; m < E; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if (i & m) continue;
+      const double a = k[i], b = k[i + m];
+      k[i] = a + b;
+      k[i + m] = a - b;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    const uint32_t flip = (s & m) ? 0x80000000u : 0u;   // upper lane: o - v = (-v) + o
+#pragma unroll
+    for (int i = 0; i < E; ++i) k[i] = negate_if(k[i], flip) + xor_lane(k[i], m, lane);
+  }
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     k[i] *= rot_scale<D>();            // 1/16 exact at D = 256; one rounding otherwise
@@ -67,34 +90,41 @@ __global__ __launch_bounds__(256) void store_kernel(
   }
 #pragma unroll
   for (int m = 1; m < LPB; m <<= 1) {
-    ka = fmax(ka, __shfl_xor(ka, m));
-    va = fmaxf(va, __shfl_xor(va, m));
+    ka = fmax(ka, xor_lane(ka, m, lane));
+    va = fmaxf(va, __uint_as_float(xor_lane_u32(__float_as_uint(va), m, lane)));
   }
   const int ke = mx_block_exponent(ka);
   const int ve = mx_block_exponent((double)va);
   const double kinv = pow2(-ke);
   const float vinv = (float)pow2(-ve);     // 2**-127 .. 2**127: a float32 value
 
-  uint32_t kc = 0, vc = 0;
+  uint32_t kc[NW], vc[NW];
 #pragma unroll
-  for (int i = 0; i < E; i += 2) {
-    kc |= e2m1_pair(to_f32_odd(k[i] * kinv), to_f32_odd(k[i + 1] * kinv)) << (4 * i);
-    vc |= e2m1_pair(v[i] * vinv, v[i + 1] * vinv) << (4 * i);
+  for (int w = 0; w < NW; ++w) {
+    kc[w] = 0;
+    vc[w] = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const int i = 8 * w + j;
+      kc[w] |= e2m1_pair(to_f32_odd(k[i] * kinv), to_f32_odd(k[i + 1] * kinv)) << (4 * j);
+      vc[w] |= e2m1_pair(v[i] * vinv, v[i + 1] * vinv) << (4 * j);
+    }
   }
+  if (!write) return;
   uint8_t* dst = cache + ((size_t)slot * Hk + h) * F::kSlot;
-  if constexpr (E == 2) {
-    dst[F::kKCode + lane] = (uint8_t)kc;
-    dst[F::kVCode + lane] = (uint8_t)vc;
-  } else if constexpr (E == 4) {
-    reinterpret_cast<uint16_t*>(dst + F::kKCode)[lane] = (uint16_t)kc;
-    reinterpret_cast<uint16_t*>(dst + F::kVCode)[lane] = (uint16_t)vc;
+  if constexpr (NW == 1) {
+    reinterpret_cast<uint32_t*>(dst + F::kKCode)[s] = kc[0];
+    reinterpret_cast<uint32_t*>(dst + F::kVCode)[s] = vc[0];
+  } else if constexpr (NW == 2) {
+    reinterpret_cast<uint2*>(dst + F::kKCode)[s] = make_uint2(kc[0], kc[1]);
+    reinterpret_cast<uint2*>(dst + F::kVCode)[s] = make_uint2(vc[0], vc[1]);
   } else {
-    reinterpret_cast<uint32_t*>(dst + F::kKCode)[lane] = kc;
-    reinterpret_cast<uint32_t*>(dst + F::kVCode)[lane] = vc;
+    reinterpret_cast<uint4*>(dst + F::kKCode)[s] = make_uint4(kc[0], kc[1], kc[2], kc[3]);
+    reinterpret_cast<uint4*>(dst + F::kVCode)[s] = make_uint4(vc[0], vc[1], vc[2], vc[3]);
   }
-  if (lane % LPB == 0) {
-    dst[F::kKScale + lane / LPB] = (uint8_t)(ke + 127);
-    dst[F::kVScale + lane / LPB] = (uint8_t)(ve + 127);
+  if (s % LPB == 0) {
+    dst[F::kKScale + (E * s) / 32] = (uint8_t)(ke + 127);
+    dst[F::kVScale + (E * s) / 32] = (uint8_t)(ve + 127);
   }
 }
 
@@ -105,9 +135,9 @@ __global__ void hadamard_kernel(int D, float* __restrict__ H, float v) {
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t pairs = a.N * a.Hk;
-  const int64_t blocks = (pairs + 3) / 4;
+  const int64_t blocks = (pairs + 15) / 16;
 #define UQ_STORE(DV)                                                                         \
-  hipLaunchKernelGGL(store_kernel<DV>, dim3((unsigned)blocks), dim3(256), 0, stream, a.key, a.value, \
+  hipLaunchKernelGGL(store16_kernel<DV>, dim3((unsigned)blocks), dim3(256), 0, stream, a.key, a.value, \
                      a.cache, a.slot_mapping, pairs, a.Hk, a.num_blocks * (int64_t)a.block_size,   \
                      a.ksn, a.ksh, a.vsn, a.vsh)
   switch (a.D) {
