@@ -451,7 +451,7 @@ def prefill_main(args):
         "roofline": {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(f"prefill-D{D}", PREFILL_TRAFFIC_RECORD, PREFILL_SOURCE),
-                     "kernel": "prefill_attn512x2_kernel" if D == 512 else "prefill_attn_kernel",
+                     "kernel": "prefill_attn512_kernel" if D == 512 else "prefill_attn_kernel",
                      "flops_per_launch": fl},
     }
     if not args.no_cpu_baseline:

@@ -14,7 +14,7 @@
 //                          keys (float64 butterfly, one rounding to bf16),
 //                          the value tiles (fp16, scaled per block);
 //   prefill_attn_kernel    flash attention over them on matrix cores
-//                          (D = 128, 256), prefill_attn512x2_kernel at
+//                          (D = 128, 256), prefill_attn512_kernel at
 //                          D = 512, prefill_attn16_kernel at D = 512 over
 //                          token-major bf16 values (uq_prefill_attention).
 #include "uq_internal.h"
@@ -84,20 +84,6 @@ __device__ __forceinline__ int vt_swizzle(int dim) { return ((dim >> 2) ^ (dim >
 __device__ __forceinline__ int vt_tile_offset(int kk, int dim) {
   const int g = (kk & 15) >> 2, s = (kk & 3) + ((kk >> 4) << 2);
   return dim * 32 + 8 * (g ^ vt_swizzle(dim)) + s;
-}
-
-// Head dim 512: a 32-key tile is two 16-key sub-tiles of 16 KB, each D dim
-// rows of 32 bytes; key 4g + i of a sub-tile sits at element i of 8-byte
-// chunk g ^ vt16_swizzle(dim) of its dim row. A 16x16x16 MFMA's B operand
-// (4 keys of one dim) is then one 8-byte read. The 16 lanes of one key group
-// read 16 consecutive dims: rows d, d + 4, d + 8, d + 12 start on the same
-// bank of a 128-byte bank row, and the swizzle sends them to its four
-// different 8-byte chunks (and the other key group of a 32-lane half to the
-// other chunk of each pair).
-__device__ __forceinline__ int vt16_swizzle(int dim) { return (dim >> 2) & 3; }
-__device__ __forceinline__ int vt16_tile_offset(int kk, int dim) {
-  const int g = (kk & 15) >> 2;
-  return (kk >> 4) * (16 * 512) + dim * 16 + 4 * (g ^ vt16_swizzle(dim)) + (kk & 3);
 }
 
 // Largest exponent (floor(log2 |v|), or above) of each 32-dim block of the
@@ -269,8 +255,7 @@ __device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j
     }
 #pragma unroll
     for (int i = 0; i < DL; ++i)
-      img[D > kHeadDim ? vt16_tile_offset(kk, DL * lane + i) : vt_tile_offset(kk, DL * lane + i)] =
-          (uint16_t)f16_bits(v[i]);
+      img[vt_tile_offset(kk, DL * lane + i)] = (uint16_t)f16_bits(v[i]);
   }
   __syncthreads();
   uint4* dst = reinterpret_cast<uint4*>(a.vt + ((int64_t)h * a.vt_tiles + j) * 32 * D);
@@ -1027,31 +1012,35 @@ __global__ __launch_bounds__(256) void prefill_attn16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Head dim 512 over the continuation prefill's fp16 value sub-tiles, with two
+// Head dim 512 over the continuation prefill's fp16 value tiles (32 keys,
+// the tiled layout of the smaller head dims: dim rows of 64 bytes), with two
 // waves per 16-column block: wave w owns columns 16 (w & 3) .. + 15 and dims
 // 256 (w >> 2) .. + 255 of O. Each wave computes the scores of its columns
-// over its half of the dims (8 MFMAs per tile); the two halves meet in LDS,
+// over its half of the dims (16 MFMAs per tile); the two halves meet in LDS,
 // double-buffered by tile parity so that the one barrier per tile orders
 // them, and both waves then run the same softmax on the same full scores
 // (a + b = b + a in float32), so their weights, sums and re-bases agree.
+// A 32-key tile fills the k-slots of a 16x16x32 fp16 MFMA, so P.V takes one
+// MFMA per 16 dims. K and V stream through separate two-stage rings (32 KB
+// per stage): step t reads K of tile t + 1 for the scores and V of tile t
+// for P.V, and refills the stages that tiles t (K) and t - 1 (V) left.
 // Half the accumulators and query registers of prefill_attn16_kernel per
 // wave: two waves share a SIMD.
 // ---------------------------------------------------------------------------
 template <int DV>
-__global__ __launch_bounds__(512) void prefill_attn512x2_kernel(
+__global__ __launch_bounds__(512) void prefill_attn512_kernel(
     const uint16_t* __restrict__ q, int64_t qs_t, int64_t qs_h, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kvs_t, int64_t kvs_h, uint16_t* __restrict__ out,
     int64_t os_t, int64_t os_h, int q_len, int cached_len, int QG, int ppw, float scale_log2,
     int64_t vt_tiles, const int32_t* __restrict__ vshift) {
-  constexpr int KT = 16, kRowBytes = 2 * DV, NCH = kRowBytes / 16;
+  constexpr int KT = kKeyTile, kRowBytes = 2 * DV, NCH = kRowBytes / 16;
   static_assert(NCH == 64, "one 1 KB load per row");
-  constexpr int kTileU4 = KT * NCH;
+  constexpr int kTileU4 = KT * NCH;                // 32 KB per stage and operand
   constexpr int HD = DV / 2;                       // dims per wave
   constexpr int NJ = HD / 32, NACC = HD / 16;      // query registers, accumulators
-  constexpr int WAVES = 8, ROWS = KT / WAVES;      // rows of K and of V each wave moves
-  __shared__ uint4 kr0[kTileU4], kr1[kTileU4], kr2[kTileU4], kr3[kTileU4];
-  __shared__ uint4 vr0[kTileU4], vr1[kTileU4], vr2[kTileU4], vr3[kTileU4];
-  __shared__ v4f xs[2][WAVES][64];                 // partial scores, by tile parity
+  constexpr int WAVES = 8, ROWS = KT / WAVES;      // 1 KB rows of K and of V each wave moves
+  __shared__ uint4 kr0[kTileU4], kr1[kTileU4], vr0[kTileU4], vr1[kTileU4];
+  __shared__ v4f xs[2][2][WAVES][64];              // partial scores, by tile parity and key half
 
   const int n_ptiles = (q_len + ppw - 1) / ppw;
   const int p0 = (n_ptiles - 1 - (int)blockIdx.x) * ppw;
@@ -1080,26 +1069,27 @@ __global__ __launch_bounds__(512) void prefill_attn512x2_kernel(
   }
 
   const uint32_t row_bytes = (uint32_t)(kvs_t * 2);
-  uint32_t koff[ROWS], voff[ROWS];
+  uint32_t koff[ROWS];
 #pragma unroll
   for (int i = 0; i < ROWS; ++i) {
     const int r = ROWS * wave + i;
     koff[i] = r * row_bytes + 16 * (lane ^ (r & 15));
-    voff[i] = 1024 * r + 16 * lane;                // the 16 KB sub-tile is contiguous
   }
   const int n_kt = (kend + KT - 1) / KT;
-  auto issue = [&](uint4* ks, uint4* vs, int t) {
+  auto issue_k = [&](uint4* ks, int t) {
     const int key0 = t * KT;
     const int nv = min(KT, kend - key0);
+    // the descriptor ends at the last key the workgroup needs: rows past it land as zeros
     const int nrec = (nv - 1) * (int)row_bytes + kRowBytes;
-    const int64_t base = (int64_t)key0 * kvs_t + (int64_t)hk * kvs_h;
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((void*)(k + base), nrec);
-    const __amdgpu_buffer_rsrc_t rv =
-        buffer_rsrc((void*)(v + ((int64_t)hk * vt_tiles * 2 + t) * (KT * DV)), KT * kRowBytes);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((void*)(k + (int64_t)key0 * kvs_t + (int64_t)hk * kvs_h), nrec);
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) load_lds16(rk, ks + 64 * (ROWS * wave + i), koff[i]);
+  };
+  auto issue_v = [&](uint4* vs, int t) {          // the 32 KB tile is contiguous
+    const __amdgpu_buffer_rsrc_t rv =
+        buffer_rsrc((void*)(v + ((int64_t)hk * vt_tiles + t) * (KT * DV)), KT * kRowBytes);
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) load_lds16(rv, vs + 64 * (ROWS * wave + i), voff[i]);
+    for (int i = 0; i < ROWS; ++i) load_lds16(rv, vs + 64 * (ROWS * wave + i), 1024 * (ROWS * wave + i) + 16 * lane);
   };
 
   v4f acc[NACC];
@@ -1107,37 +1097,49 @@ __global__ __launch_bounds__(512) void prefill_attn512x2_kernel(
   for (int j = 0; j < NACC; ++j) acc[j] = (v4f){0.f, 0.f, 0.f, 0.f};
   v4f lsum = {0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;
-  const v4h ones4 = __builtin_bit_cast(v4h, make_uint2(0x3C003C00u, 0x3C003C00u));
+  const v8h ones16 = __builtin_bit_cast(v8h, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
 
-  // S^T over this wave's dims: 32-dim steps 8 hf .. 8 hf + 7 of the key rows
-  auto pscores = [&](const uint4* ks) {
+  // S^T over this wave's dims (32-dim steps 8 hf .. 8 hf + 7) for the key
+  // halves kb = 0, 1 of the tile: lane (col, g) gets keys 16 kb + 4 g + i
+  auto pscores = [&](const uint4* ks, v4f (&s)[2]) {
     const uint8_t* kb_ = reinterpret_cast<const uint8_t*>(ks);
-    v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    s[0] = (v4f){0.f, 0.f, 0.f, 0.f};
+    s[1] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < NJ / 4; ++h) {
-      v8bf ka[4];
+      v8bf ka[2][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        ka[j] = __builtin_bit_cast(
-            v8bf, ld16(kb_ + r16 * kRowBytes + 16 * ((4 * (NJ * hf + 4 * h + j) + g) ^ r16)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s[j & 1] = mfma_bf16(ka[j], qb[4 * h + j], s[j & 1]);
+        for (int kb = 0; kb < 2; ++kb)
+          ka[kb][j] = __builtin_bit_cast(
+              v8bf, ld16(kb_ + (16 * kb + r16) * kRowBytes + 16 * ((4 * (NJ * hf + 4 * h + j) + g) ^ r16)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16(ka[kb][j], qb[4 * h + j], s[kb]);
     }
-    return s[0] + s[1];
   };
 
-  auto weigh = [&](const v4f& s, const uint4* vs, int t) {
+  auto weigh = [&](const v4f (&s)[2], const uint4* vs, int t) {
     const uint8_t* vb_ = reinterpret_cast<const uint8_t*>(vs);
     const int key0 = t * KT;
-    float sv[4];
+    float sv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = s[i];
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[4 * kb + i] = s[kb][i];
     if (key0 + KT > cached_len + p0 + 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (key0 + 4 * g + i >= klim) sv[i] = -INFINITY;
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + 16 * kb + 4 * g + i >= klim) sv[4 * kb + i] = -INFINITY;
     }
-    const float mt = rowgroup_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))) * scale_log2;
+    float x = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) x = fmaxf(x, sv[i]);
+    const float mt = rowgroup_max(x) * scale_log2;
     if (t == 0) m_ref = mt;
     if (__any(mt > m_ref + 8.0f)) {
       // raise the reference, O <- diag(f) O on float32 MFMAs (as above)
@@ -1156,50 +1158,59 @@ __global__ __launch_bounds__(512) void prefill_attn512x2_kernel(
       }
       m_ref = m_new;
     }
-    float p[4];
+    // k-slot 8 g + s of the MFMAs stands for key 16 (s >> 2) + 4 g + (s & 3):
+    // the weights in sv order, and chunk g of a dim row in the tiled layout
+    uint32_t pw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -m_ref));
-    const v4h ph = __builtin_bit_cast(
-        v4h, make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p[0], p[1]}, v2h)),
-                        __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p[2], p[3]}, v2h))));
-    lsum = mfma_f16x16(ph, ones4, lsum);
+    for (int i = 0; i < 4; ++i) {
+      const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], scale_log2, -m_ref));
+      const float pc = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], scale_log2, -m_ref));
+      pw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){pa, pc}, v2h));
+    }
+    const v8h ph = __builtin_bit_cast(v8h, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    lsum = mfma_f16(ph, ones16, lsum);
 #pragma unroll
     for (int n = 0; n < NACC; ++n) {
       const int dim = HD * hf + 16 * n + r16;
-      const uint2 x = *reinterpret_cast<const uint2*>(vb_ + dim * 32 + 8 * (g ^ vt16_swizzle(dim)));
-      acc[n] = mfma_f16x16(ph, __builtin_bit_cast(v4h, x), acc[n]);
+      const v8h vh = __builtin_bit_cast(v8h, ld16(vb_ + dim * 64 + 16 * (g ^ vt_swizzle(dim))));
+      acc[n] = mfma_f16(ph, vh, acc[n]);
     }
   };
 
-  // Step t: tile t + 1 is made visible by the barrier, which also orders
-  // both halves' partial scores of tile t (written in step t - 1) before
-  // they are read here; tile t + 1's partial scores go to the other parity.
-  issue(kr0, vr0, 0);
-  if (1 < n_kt) issue(kr1, vr1, 1);
-  if (2 < n_kt) issue(kr2, vr2, 2);
-  wait_tiles<kStages - 2, 2 * ROWS>(n_kt - 1);
+  // Step t: the barrier makes K of tile t + 1 and V of tile t visible (both
+  // requested in step t - 1) and orders both halves' partial scores of tile
+  // t (written in step t - 1) before they are read here; it also ends every
+  // wave's use of K of tile t and V of tile t - 1, whose stages are refilled.
+  // Past the last tile the extra scores come from a stale stage and are dropped.
+  issue_k(kr0, 0);
+  if (1 < n_kt) issue_k(kr1, 1);
+  issue_v(vr0, 0);
+  UQP_WAIT_VMCNT(ROWS);                            // K of tile 0 (V of tile 0 may still fly)
   __syncthreads();
-  v4f mine = pscores(kr0);
-  xs[0][wave][lane] = mine;
-#define UQP_STEP2(KC, VC, KN, KF, VF)                                \
+  v4f mine[2];
+  pscores(kr0, mine);
+  xs[0][0][wave][lane] = mine[0];
+  xs[0][1][wave][lane] = mine[1];
+#define UQP_STEP512(KN, KF, VC, VF)                                  \
   {                                                                  \
-    wait_tiles<kStages - 3, 2 * ROWS>(n_kt - 2 - t);                 \
+    UQP_WAIT_VMCNT(0);                                               \
     __syncthreads();                                                 \
-    if (t + kStages - 1 < n_kt) issue(KF, VF, t + kStages - 1);      \
-    const v4f full = mine + xs[t & 1][wave ^ 4][lane];               \
-    const v4f nxt = pscores(KN);                                     \
-    xs[(t + 1) & 1][wave][lane] = nxt;                               \
+    if (t + 2 < n_kt) issue_k(KF, t + 2);                            \
+    if (t + 1 < n_kt) issue_v(VF, t + 1);                            \
+    v4f full[2];                                                     \
+    full[0] = mine[0] + xs[t & 1][0][wave ^ 4][lane];                \
+    full[1] = mine[1] + xs[t & 1][1][wave ^ 4][lane];                \
+    pscores(KN, mine);                                               \
+    xs[(t + 1) & 1][0][wave][lane] = mine[0];                        \
+    xs[(t + 1) & 1][1][wave][lane] = mine[1];                        \
     weigh(full, VC, t);                                              \
-    mine = nxt;                                                      \
     if (++t >= n_kt) break;                                          \
   }
   for (int t = 0;;) {
-    UQP_STEP2(kr0, vr0, kr1, kr3, vr3)
-    UQP_STEP2(kr1, vr1, kr2, kr0, vr0)
-    UQP_STEP2(kr2, vr2, kr3, kr1, vr1)
-    UQP_STEP2(kr3, vr3, kr0, kr2, vr2)
+    UQP_STEP512(kr1, kr0, vr0, vr1)
+    UQP_STEP512(kr0, kr1, vr1, vr0)
   }
-#undef UQP_STEP2
+#undef UQP_STEP512
 
   // lane (r, g) holds, for column 4g + i, O at dim HD hf + 16n + r in
   // accumulator n (in units of 2^vshift of the dim's 32-block), and that
@@ -1260,7 +1271,7 @@ hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t stream) {
     const float sl2_16 = a.scale * 1.4426950408889634f;
     if (a.vt_tiles > 0) {
       if (!a.vshift) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((prefill_attn512x2_kernel<512>), grid16, dim3(512), 0, stream, a.q, a.qs_t, a.qs_h,
+      hipLaunchKernelGGL((prefill_attn512_kernel<512>), grid16, dim3(512), 0, stream, a.q, a.qs_t, a.qs_h,
                          a.k, a.v, a.kvs_t, a.kvs_h, a.out, a.os_t, a.os_h, a.q_len, a.cached_len, a.QG, ppw,
                          sl2_16, (int64_t)a.vt_tiles, a.vshift);
     } else {
