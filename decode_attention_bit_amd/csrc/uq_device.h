@@ -93,9 +93,9 @@ __device__ __forceinline__ double xor_lane(double v, int m, int lane) {
 // binades (37 at D = 256).
 // REG: lane exchanges in registers (xor_lane), which shortens a wave's
 // latency (the query prologue: 2.81 -> 2.68 us); otherwise through the LDS
-// pipe (__shfl_xor), which runs beside the VALU and keeps the store's
-// throughput when many waves are resident (the store of 16384 x 4 vectors
-// took 51 us this way and 60 us with register exchanges).
+// pipe (__shfl_xor), which runs beside the VALU when many waves are resident
+// (a one-vector-per-wave store of 16384 x 4 vectors took 51 us this way and
+// 60 us with register exchanges).
 // x with its sign bit XORed with flip (0 or the sign bit): -x or x, exactly;
 // IEEE subtraction o - x is by definition the sum (-x) + o, so a butterfly's
 // upper output needs no separate subtraction.

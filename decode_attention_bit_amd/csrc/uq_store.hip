@@ -8,27 +8,35 @@
 
 namespace uq {
 
-// Four (token, KV head) pairs per wave, 16 lanes each: lane s of a pair
-// owns elements E s .. E s + E - 1 (E = D / 16). K is rotated by the
+// LPS lanes per (token, KV head) pair, 64 / LPS pairs per wave: lane s of a
+// pair owns elements E s .. E s + E - 1 (E = D / LPS). K is rotated by the
 // float64 butterfly (exact under the span condition of the rotation): its
-// log2(E) low stages inside the lane, the four stages of the lane bits with
-// DPP exchanges inside the lane's row of 16, so no stage goes through the
-// LDS pipe. K is then scaled by its block's power of two in float64 and
-// rounded to odd in float32; V is scaled in float32, which holds bf16 values
-// and their power-of-two multiples exactly. Both are encoded by the E2M1
-// conversion, so the codes are those of the exact scaled values. The amax of
-// a 32-element block spans 32 / E lanes (one at D = 512); each lane writes
-// E/2 contiguous code bytes of K and of V.
-template <int D>
-__global__ __launch_bounds__(256) void store16_kernel(
+// log2(E) low stages inside the lane, the stages of the lane bits with
+// register exchanges (DPP within rows of 16, the gfx950 row swaps for lane
+// xor 16 and 32), so no stage goes through the LDS pipe. K is then scaled by
+// its block's power of two in float64 and rounded to odd in float32; V is
+// scaled in float32, which holds bf16 values and their power-of-two
+// multiples exactly. Both are encoded by the E2M1 conversion, so the codes
+// are those of the exact scaled values. The amax of a 32-element block spans
+// 32 / E lanes; each lane writes E/2 contiguous code bytes of K and of V.
+// LPS = 16 (long lane chains, four pairs per wave) for large stores, where
+// throughput counts; LPS = 64 (one pair per wave, short chains spread over
+// the chip) for the few tokens of a decode step, where latency does.
+template <int D, int LPS>
+__global__ __launch_bounds__(256) void store_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     uint8_t* __restrict__ cache, const int64_t* __restrict__ slot_mapping,
     int64_t n_pairs, int Hk, int64_t num_slots, int64_t ksn, int64_t ksh,
     int64_t vsn, int64_t vsh) {
   using F = Fmt<D>;
-  constexpr int E = D / 16, LPB = E >= 32 ? 1 : 32 / E, NW = E / 8;   // NW: 32-bit code words per lane
-  const int lane = threadIdx.x & 63, s = lane & 15;
-  const int64_t pair = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  static_assert(LPS == 16 || LPS == 32 || LPS == 64, "lanes per pair");
+  constexpr int E = D / LPS, SPW = 64 / LPS;
+  constexpr int LPB = E >= 32 ? 1 : 32 / E;         // lanes per 32-element block
+  constexpr int NB = E / 2;                         // code bytes per lane and tensor
+  constexpr int NW = NB >= 4 ? NB / 4 : 1;          // 32-bit code words per lane
+  static_assert(E >= 2 && E <= 32, "elements per lane");
+  const int lane = threadIdx.x & 63, s = lane % LPS;
+  const int64_t pair = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * SPW + lane / LPS;
   int64_t n = 0, slot = -1;
   int h = 0;
   if (pair < n_pairs) {
@@ -49,14 +57,21 @@ __global__ __launch_bounds__(256) void store16_kernel(
   if (write) {
     const uint16_t* kp = key + n * ksn + (int64_t)h * ksh + E * s;
     const uint16_t* vp = value + n * vsn + (int64_t)h * vsh + E * s;
+    if constexpr (E >= 4) {
 #pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-      const uint2 kr = *reinterpret_cast<const uint2*>(kp + 4 * c);
-      const uint2 vr = *reinterpret_cast<const uint2*>(vp + 4 * c);
-      k[4 * c] = bf16_to_f64(kr.x & 0xFFFF); k[4 * c + 1] = bf16_to_f64(kr.x >> 16);
-      k[4 * c + 2] = bf16_to_f64(kr.y & 0xFFFF); k[4 * c + 3] = bf16_to_f64(kr.y >> 16);
-      v[4 * c] = bf16_to_f32(vr.x & 0xFFFF); v[4 * c + 1] = bf16_to_f32(vr.x >> 16);
-      v[4 * c + 2] = bf16_to_f32(vr.y & 0xFFFF); v[4 * c + 3] = bf16_to_f32(vr.y >> 16);
+      for (int c = 0; c < E / 4; ++c) {
+        const uint2 kr = *reinterpret_cast<const uint2*>(kp + 4 * c);
+        const uint2 vr = *reinterpret_cast<const uint2*>(vp + 4 * c);
+        k[4 * c] = bf16_to_f64(kr.x & 0xFFFF); k[4 * c + 1] = bf16_to_f64(kr.x >> 16);
+        k[4 * c + 2] = bf16_to_f64(kr.y & 0xFFFF); k[4 * c + 3] = bf16_to_f64(kr.y >> 16);
+        v[4 * c] = bf16_to_f32(vr.x & 0xFFFF); v[4 * c + 1] = bf16_to_f32(vr.x >> 16);
+        v[4 * c + 2] = bf16_to_f32(vr.y & 0xFFFF); v[4 * c + 3] = bf16_to_f32(vr.y >> 16);
+      }
+    } else {
+      const uint32_t kr = *reinterpret_cast<const uint32_t*>(kp);
+      const uint32_t vr = *reinterpret_cast<const uint32_t*>(vp);
+      k[0] = bf16_to_f64(kr & 0xFFFF); k[1] = bf16_to_f64(kr >> 16);
+      v[0] = bf16_to_f32(vr & 0xFFFF); v[1] = bf16_to_f32(vr >> 16);
     }
   }
 #pragma unroll
@@ -70,7 +85,7 @@ __global__ __launch_bounds__(256) void store16_kernel(
     }
   }
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) {
+  for (int m = 1; m < LPS; m <<= 1) {
     const uint32_t flip = (s & m) ? 0x80000000u : 0u;   // upper lane: o - v = (-v) + o
 #pragma unroll
     for (int i = 0; i < E; ++i) k[i] = negate_if(k[i], flip) + xor_lane(k[i], m, lane);
@@ -98,13 +113,14 @@ __global__ __launch_bounds__(256) void store16_kernel(
   const double kinv = pow2(-ke);
   const float vinv = (float)pow2(-ve);     // 2**-127 .. 2**127: a float32 value
 
+  // codes of elements 2j, 2j + 1 in byte j, low nibble first
   uint32_t kc[NW], vc[NW];
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     kc[w] = 0;
     vc[w] = 0;
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
+    for (int j = 0; j < (E < 8 ? E : 8); j += 2) {
       const int i = 8 * w + j;
       kc[w] |= e2m1_pair(to_f32_odd(k[i] * kinv), to_f32_odd(k[i + 1] * kinv)) << (4 * j);
       vc[w] |= e2m1_pair(v[i] * vinv, v[i + 1] * vinv) << (4 * j);
@@ -112,10 +128,16 @@ __global__ __launch_bounds__(256) void store16_kernel(
   }
   if (!write) return;
   uint8_t* dst = cache + ((size_t)slot * Hk + h) * F::kSlot;
-  if constexpr (NW == 1) {
+  if constexpr (NB == 1) {
+    dst[F::kKCode + s] = (uint8_t)kc[0];
+    dst[F::kVCode + s] = (uint8_t)vc[0];
+  } else if constexpr (NB == 2) {
+    reinterpret_cast<uint16_t*>(dst + F::kKCode)[s] = (uint16_t)kc[0];
+    reinterpret_cast<uint16_t*>(dst + F::kVCode)[s] = (uint16_t)vc[0];
+  } else if constexpr (NB == 4) {
     reinterpret_cast<uint32_t*>(dst + F::kKCode)[s] = kc[0];
     reinterpret_cast<uint32_t*>(dst + F::kVCode)[s] = vc[0];
-  } else if constexpr (NW == 2) {
+  } else if constexpr (NB == 8) {
     reinterpret_cast<uint2*>(dst + F::kKCode)[s] = make_uint2(kc[0], kc[1]);
     reinterpret_cast<uint2*>(dst + F::kVCode)[s] = make_uint2(vc[0], vc[1]);
   } else {
@@ -133,13 +155,29 @@ __global__ void hadamard_kernel(int D, float* __restrict__ H, float v) {
   H[(size_t)i * D + j] = (__popc(i & j) & 1) ? -v : v;
 }
 
+// Lanes per pair: 16, or more while that leaves fewer than about one wave
+// per SIMD (1024 waves): a lane's chain grows with its share of the D
+// elements, and a small grid leaves most of the chip idle. Measured at
+// D = 256 (us):
+//   tokens x 4 heads   32    256   512   1024  2048  4096
+//   LPS 64            2.81  2.95  3.69  5.09  8.19  14.49
+//   LPS 32            3.30  3.42  3.49  4.59  6.84  11.76
+//   LPS 16            4.19  4.29  4.36  4.52  6.41  10.21
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t pairs = a.N * a.Hk;
-  const int64_t blocks = (pairs + 15) / 16;
-#define UQ_STORE(DV)                                                                         \
-  hipLaunchKernelGGL(store16_kernel<DV>, dim3((unsigned)blocks), dim3(256), 0, stream, a.key, a.value, \
-                     a.cache, a.slot_mapping, pairs, a.Hk, a.num_blocks * (int64_t)a.block_size,   \
-                     a.ksn, a.ksh, a.vsn, a.vsh)
+  const int lps = pairs <= 1024 ? 64 : (pairs <= 2048 ? 32 : 16);
+  const int64_t per_block = 4 * (64 / lps);
+  const int64_t blocks = (pairs + per_block - 1) / per_block;
+#define UQ_STORE_L(DV, L)                                                                           \
+  hipLaunchKernelGGL((store_kernel<DV, L>), dim3((unsigned)blocks), dim3(256), 0, stream, a.key,     \
+                     a.value, a.cache, a.slot_mapping, pairs, a.Hk,                                 \
+                     a.num_blocks * (int64_t)a.block_size, a.ksn, a.ksh, a.vsn, a.vsh)
+#define UQ_STORE(DV)                                   \
+  do {                                                 \
+    if (lps == 64) UQ_STORE_L(DV, 64);                 \
+    else if (lps == 32) UQ_STORE_L(DV, 32);            \
+    else UQ_STORE_L(DV, 16);                           \
+  } while (0)
   switch (a.D) {
     case 128: UQ_STORE(128); break;
     case 256: UQ_STORE(256); break;
@@ -147,6 +185,7 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 #undef UQ_STORE
+#undef UQ_STORE_L
   return hipGetLastError();
 }
 

@@ -265,14 +265,16 @@ def test_dequant_bit_exact(d):
     assert torch.equal(k2[:bs], k[:bs]) and torch.equal(k2[2 * bs:], k[2 * bs:])
 
 
-@pytest.mark.parametrize("cached_len,q_len", [(0, 37), (100, 64), (333, 129), (32, 32)])
-@pytest.mark.parametrize("qg", [6, 8, 16])
+@pytest.mark.parametrize("cached_len,q_len,qg", [(0, 37, 6), (100, 64, 6), (333, 129, 6), (32, 32, 6),
+                                                  (0, 37, 8), (100, 64, 8), (333, 129, 8), (32, 32, 8),
+                                                  (0, 37, 16), (100, 64, 16), (333, 129, 16), (32, 32, 16),
+                                                  (45, 70, 1), (45, 70, 64)])
 @pytest.mark.parametrize("d", DIMS)
 def test_continuation_prefill(d, cached_len, q_len, qg):
     """Continuation prefill at head dim d (at 128 the attention kernel's
-    128-dim instance with values tiled; at 512 the 16-key-tile kernel with
-    values token-major) against the oracle, written into a strided output
-    whose extra columns must stay untouched."""
+    128-dim instance, at 512 the kernel with two waves per column block;
+    values tiled at every d) against the oracle, written into a strided
+    output whose extra columns must stay untouched."""
     hk, bs = 2, 16
     say(f"prefill d={d} qg={qg} cached={cached_len} q_len={q_len}")
     rng = np.random.default_rng(qg * 100 + cached_len + q_len)
