@@ -80,7 +80,11 @@ size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits
       num_kv_splits > UQ_MAX_SPLITS || max_blocks_per_seq < 1 || !pow2_in(block_size, 16, 256) ||
       (long long)max_blocks_per_seq * block_size > 0x7FFFFFFFLL)
     return 0;
-  return uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).total;
+  // enough for either plan: multi-query rows that may pair cut finer partials
+  const size_t t0 = uq::plan_decode(false, B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).total;
+  const size_t t1 =
+      Hq / Hk <= 8 ? uq::plan_decode(true, B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).total : 0;
+  return t0 > t1 ? t0 : t1;
 }
 
 // Device scratch of uq_decode_no_alloc: the decode's workspace (query codes,
@@ -166,8 +170,11 @@ static int decode_impl(int stage_mask, const uint16_t* query, const uint8_t* kv_
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_row, 4) ||
       !aligned(sinks, 4))
     return fail(UQ_EINVAL, "uq_decode: misaligned pointer (query 8 B, kv_cache/out 16 B, workspace 256 B)");
+  // query rows of one sequence may share stage-1 waves in pairs (QG <= 8, no
+  // window); the plan then counts pairs
+  const bool paired = query_row != nullptr && sliding_window == 0 && qg <= 8;
   const uq::DecodePlan plan =
-      uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D);
+      uq::plan_decode(paired, B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D);
   if (use_scratch && plan.total > (size_t)UQ_NO_ALLOC_SCRATCH_BYTES)
     return fail(UQ_EWORKSPACE, "uq_decode_no_alloc: this shape needs %zu bytes of scratch, above the %zu-byte "
                 "static buffer; use uq_decode with a workspace", plan.total, (size_t)UQ_NO_ALLOC_SCRATCH_BYTES);
@@ -203,7 +210,7 @@ int uq_decode_stages(int stage_mask, const uint16_t* query, const uint8_t* kv_ca
 int uq_decode_partials(int B, int Hq, int Hk, int D, int num_kv_splits, int max_blocks_per_seq,
                        int block_size) {
   if (uq_decode_workspace_bytes(B, Hq, Hk, D, num_kv_splits, max_blocks_per_seq, block_size) == 0) return 0;
-  return uq::plan_decode(B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).parts;
+  return uq::plan_decode(false, B, Hq, Hk, num_kv_splits, max_blocks_per_seq, block_size, D).parts;
 }
 
 int uq_stream_blocks(const uint8_t* kv_cache, const int32_t* block_table, const int32_t* seq_lens,

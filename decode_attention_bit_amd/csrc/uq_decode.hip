@@ -268,11 +268,13 @@ __device__ __forceinline__ float rowgroup_max(float x) {
 }
 
 // Scores of one tile in the log2 domain (lane: q-head l%16, tokens 4*grp+i),
-// -inf past the end of the sequence and for the tile's first `first` tokens
-// (those before a sliding window); mt = the tile maximum for the lane's head.
+// -inf from token `lc` of the tile on (the end of the lane's query row) and
+// past the tile's valid tokens, and for the tile's first `first` tokens
+// (those before a sliding window), all only when `edge`; mt = the tile
+// maximum for the lane's head.
 template <int D>
 __device__ __forceinline__ void qk_tile(const Tile<D>& T, const v8i qb[D / 128], float scale_log2,
-                                        int grp, int first, float sv[4], float& mt) {
+                                        int grp, int first, bool edge, int lc, float sv[4], float& mt) {
   v4f sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < D / 128; ++m) {
@@ -282,10 +284,13 @@ __device__ __forceinline__ void qk_tile(const Tile<D>& T, const v8i qb[D / 128],
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) sv[i] = sc[i] * scale_log2;
-  if (T.nvalid < kTile || first > 0) {     // the sequence's last tile, the window's first
+  // edge (wave-uniform): the tile holds the end of some column's row or the
+  // start of the window; lc: the lane's column's length from the tile's start
+  if (edge) {
+    const int lim = min(T.nvalid, lc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (4 * grp + i >= T.nvalid || 4 * grp + i < first) sv[i] = -INFINITY;
+      if (4 * grp + i >= lim || 4 * grp + i < first) sv[i] = -INFINITY;
   }
   mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   mt = rowgroup_max(mt);
@@ -413,15 +418,20 @@ __device__ __forceinline__ void rotate_queries_d256(const uint2 qraw[QG], int la
   }
 }
 
-template <int D, int QG, int HPW, int NSLOT, bool FUSEQ>
+// MODE 0: query codes from the workspace; 1: the query prologue inside
+// (head dim 256); 2: multi-query rows paired as described below (QG <= 8).
+template <int D, int QG, int HPW, int NSLOT, int MODE>
 __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     const uint8_t* __restrict__ q8, const uint16_t* __restrict__ query, int64_t qsb, int64_t qsh,
     const uint8_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ query_row, int n_rows,
     const int32_t* __restrict__ seq_lens,
     float scale_log2, int Hq, int Hk, int hgroups, int cs, int spw, int nsub, int P,
-    int log2_bs, int max_blocks, int64_t num_blocks, int window, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_m, float* __restrict__ part_l, int* __restrict__ part_e) {
+    int log2_bs, int max_blocks, int64_t num_blocks, int window, int n_qrows,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_m, float* __restrict__ part_l,
+    int* __restrict__ part_e) {
+  constexpr bool FUSEQ = MODE == 1, PAIR = MODE == 2;
+  static_assert(!PAIR || QG <= 8, "paired rows need half the MFMA columns free");
   static_assert(NSLOT >= 2 && NSLOT <= 8, "ring depth");
   using S = Stage<D>;
   static_assert(NSLOT * HPW * S::kTileU4 * 16 <= 160 * 1024, "ring exceeds the LDS of a CU");
@@ -440,12 +450,27 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   // the partial index, so the partials of one sequence land on different
   // XCDs: the late, often empty, partials of short sequences are then spread
   // over the chip instead of all sitting on the same XCD.
-  const int n1 = (int)(gridDim.x / (unsigned)P);
-  const int part = (int)blockIdx.x / n1;           // partial index within (b, head)
-  int j = (int)blockIdx.x - part * n1 + part % n1;
+  // With paired rows the even rows' workgroups come first and the odd rows'
+  // (which exit when their row pairs) after them, each half in that order,
+  // so the streaming workgroups are dispatched first and spread over the CUs.
+  int rows = (int)(gridDim.x / (unsigned)(P * hgroups)), x = (int)blockIdx.x, r0 = 0, rstep = 1;
+  if constexpr (PAIR) {
+    const int n_even = (rows + 1) / 2, first_odd = n_even * P * hgroups;
+    rstep = 2;
+    if (x < first_odd) {
+      rows = n_even;
+    } else {
+      x -= first_odd;
+      rows -= n_even;
+      r0 = 1;
+    }
+  }
+  const int n1 = rows * hgroups;
+  const int part = x / n1;                          // partial index within (b, head)
+  int j = x - part * n1 + part % n1;
   j = j >= n1 ? j - n1 : j;
   const int hg = j % hgroups;
-  const int b = j / hgroups;
+  const int b = r0 + rstep * (j / hgroups);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = hg * HPW + wave;
@@ -459,9 +484,27 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   const int sub_len = (spw * cs + nsub - 1) / nsub;
   const int u_rel = g_rel + (part % nsub) * sub_len;
   const int n16 = lane & 15, grp = lane >> 4;
-  const bool qlane = n16 < QG;
-  const int hq = h * QG + (qlane ? n16 : 0);
   static_assert(!FUSEQ || D == 256, "the in-kernel query prologue is built for head dim 256");
+  // Query row b reads block-table row query_row[b] (its own row when there
+  // is no mapping); a row outside the table reads as an empty sequence.
+  const int trow = query_row ? query_row[b] : b;
+  const bool row_ok = trow >= 0 && trow < n_rows;
+  // Paired rows (QG <= 8, no window): query rows 2r and 2r + 1 that read the
+  // same table row share the wave of row 2r, row 2r + 1 in MFMA columns
+  // QG .. 2 QG - 1, so their common tiles are read once; the wave of row
+  // 2r + 1 then has nothing to do. The split boundaries come from the table
+  // capacity, the same for both rows; each column masks past its own length.
+  bool paired = false;
+  if constexpr (PAIR) {
+    if (row_ok && (b ^ 1) < n_qrows && query_row[b ^ 1] == trow) {
+      if (b & 1) return;
+      paired = true;
+    }
+  }
+  const int QC = paired ? 2 * QG : QG;               // query columns in use
+  const bool qlane = n16 < QC;
+  const int crow = (PAIR && n16 >= QG && paired) ? b + 1 : b;   // the column's query row
+  const int hq = h * QG + (qlane ? (PAIR ? n16 % QG : n16) : 0);
   v8i qb[C];
 #pragma unroll
   for (int m = 0; m < C; ++m) qb[m] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
@@ -471,17 +514,13 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   if constexpr (FUSEQ) {
     load_query_rows<QG>(query, qsb, qsh, b, h, lane, qraw);
   } else if (qlane) {
-    const uint8_t* qp = q8 + ((size_t)b * Hq + hq) * D;
+    const uint8_t* qp = q8 + ((size_t)crow * Hq + hq) * D;
 #pragma unroll
     for (int m = 0; m < C; ++m) {
       const uint4 x0 = ld16(qp + 128 * m + 16 * grp), x1 = ld16(qp + 128 * m + 64 + 16 * grp);
       qb[m] = (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
   }
-  // Query row b reads block-table row query_row[b] (its own row when there
-  // is no mapping); a row outside the table reads as an empty sequence.
-  const int trow = query_row ? query_row[b] : b;
-  const bool row_ok = trow >= 0 && trow < n_rows;
   const int32_t* bt = block_table + (size_t)(row_ok ? trow : 0) * max_blocks;
   // The wave's first table entry does not depend on the length unless a
   // sliding window moves the range, so its entries are requested together
@@ -494,9 +533,19 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   int s_ent[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) s_ent[k] = bt[min(e0 + k, max_blocks - 1)];
+  const int Lcap = max_blocks << log2_bs;
   int L = row_ok ? seq_lens[b] : 0;
-  const int Lmax = max_blocks << log2_bs;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  L = L < 0 ? 0 : (L > Lcap ? Lcap : L);
+  // the column's own length (paired rows: each row's), L the longest; from
+  // tile t_edge on a tile may hold the end of the shorter row
+  int Lc = L, t_edge = 0x7FFFFFFF;
+  if (PAIR && paired) {
+    int L2 = seq_lens[b + 1];
+    L2 = L2 < 0 ? 0 : (L2 > Lcap ? Lcap : L2);
+    if (n16 >= QG) Lc = L2;
+    t_edge = (L < L2 ? L : L2) / kTile;
+    L = L > L2 ? L : L2;
+  }
   // A sliding window of W tokens starts at token lo = L - W: the splits count
   // from lo's tile, and the tokens of that tile before lo are masked.
   const int lo = (window > 0 && L > window) ? L - window : 0;
@@ -510,7 +559,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
 #pragma unroll
     for (int k = 0; k < 8; ++k) s_ent[k] = bt[min(e0 + k, max_blocks - 1)];
   }
-  const size_t stat = ((size_t)b * Hq + hq) * P + part;
+  const size_t stat = ((size_t)crow * Hq + hq) * P + part;
 
   if (u0 >= u1) {
     if (qlane && grp == 0) {
@@ -602,8 +651,10 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
       wait_tiles_ahead<NSLOT - 2, S::kLoads>(u1 - 1 - t);                        \
       read_tile<D>(T, CUR[wave], n16, grp, nv_##CUR);                            \
       if (t + NSLOT - 1 < u1) nv_##NXT = issue(NXT[wave], t + NSLOT - 1);        \
-      qk_tile<D>(T, qb, scale_log2, grp, lo - t * kTile, sv, mt);                \
-      if (t == u0) m_ref = mt;                                                   \
+      qk_tile<D>(T, qb, scale_log2, grp, lo - t * kTile,                        \
+                 T.nvalid < kTile || lo > t * kTile || (PAIR && t >= t_edge),          \
+                 PAIR ? Lc - t * kTile : kTile, sv, mt);                          \
+      if (t == u0) m_ref = (!PAIR || mt > -INFINITY) ? mt : 0.f;                 \
       if (__any(mt > m_ref + 8.0f)) { rebased = true; t_stop = t; break; }       \
       if (T.nvalid > 0) pv_tile<D>(T, sv, m_ref, n16, acc, l_part);              \
       if (++t >= u1) break;                                                      \
@@ -665,8 +716,9 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   // Lane (head l%16, any grp) holds that head's weight sum after the reduction.
   const float l1 = l_part + __shfl_xor(l_part, 16);
   const float l_tot = l1 + __shfl_xor(l1, 32);
-  // a non-empty range has l >= 1 (its largest weight is exactly 1)
-  const float inv = 1.f / l_tot;
+  // a non-empty range has l >= 1 (its largest weight is exactly 1); a
+  // paired row may have no token in it (l = 0: an empty partial)
+  const float inv = (!PAIR || l_tot > 0.f) ? 1.f / l_tot : 0.f;
   // The partial O / l of each query head is stored as an fp16 row times
   // 2^ex, with ex chosen from the row's largest magnitude so that it lands in
   // [2^14, 2^15): the rounding error is at most 2^-11 of the row maximum. The
@@ -678,7 +730,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   // reduction over the four row groups.
   constexpr int RS = D * 2 + 16;
   constexpr int RPS = S::kTileU4 * 16 / RS;
-  static_assert((QG + RPS - 1) / RPS <= NSLOT, "the ring cannot stage the partial rows");
+  static_assert(((PAIR ? 2 * QG : QG) + RPS - 1) / RPS <= NSLOT, "the ring cannot stage the partial rows");
 #define UQ_OWN_PTR(K) (NSLOT > K ? &ring##K[NSLOT > K ? wave : 0][0] : &ring0[0][0])
   uint4* const own[8] = {UQ_OWN_PTR(0), UQ_OWN_PTR(1), UQ_OWN_PTR(2), UQ_OWN_PTR(3),
                          UQ_OWN_PTR(4), UQ_OWN_PTR(5), UQ_OWN_PTR(6), UQ_OWN_PTR(7)};
@@ -691,7 +743,7 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
   amax = rowgroup_max(amax * inv);
   const int ex = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14 : 0;
   if (qlane && grp == 0) {
-    part_m[stat] = m_ref;
+    part_m[stat] = (!PAIR || l_tot > 0.f) ? m_ref : -INFINITY;
     part_l[stat] = l_tot;
     part_e[stat] = ex;
   }
@@ -711,11 +763,12 @@ __global__ __launch_bounds__(64 * HPW) void stage1_kernel(
     }
   }
   __builtin_amdgcn_wave_barrier();
-  const size_t row0 = ((size_t)b * Hq + (size_t)h * QG) * P + part;   // first query head of the group
 #pragma unroll
-  for (int r = 0; r < QG; ++r) {
+  for (int r = 0; r < (PAIR ? 2 * QG : QG); ++r) {
+    if (PAIR && r >= QC) break;
+    const size_t prow = ((size_t)(r < QG ? b : b + 1) * Hq + (size_t)h * QG + r % QG) * P + part;
     const uint8_t* rowp = reinterpret_cast<const uint8_t*>(own[r / RPS]) + (r % RPS) * RS;
-    uint8_t* dst = reinterpret_cast<uint8_t*>(part_o + (row0 + (size_t)r * P) * D);
+    uint8_t* dst = reinterpret_cast<uint8_t*>(part_o + prow * D);
     if constexpr (D == 128) {
       *reinterpret_cast<uint32_t*>(dst + 4 * lane) = *reinterpret_cast<const uint32_t*>(rowp + 4 * lane);
     } else if constexpr (D == 256) {
@@ -893,7 +946,7 @@ constexpr long kTilesPerWaveMin = 4;
 // faster; at D = 256 and 512 more waves only add partials (measured).
 static int target_waves(int D) { return D == 128 ? 2 * UQ_TARGET_WAVES : UQ_TARGET_WAVES; }
 
-DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
+DecodePlan plan_decode(bool paired, int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
                        int block_size, int D) {
   DecodePlan p{};
   p.D = D;
@@ -913,7 +966,10 @@ DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_
   // afford while the grid still offers about target_waves(D) waves when every
   // sequence is full. A partial is then a union of spw consecutive splits, or
   // one of nsub pieces of a split that is too long for one wave.
-  long budget = (long)B * Hk * max_tiles / target_waves(D);
+  // With paired query rows (multi-query rows of one sequence sharing a
+  // wave) about half the rows' waves stream, so the budget counts pairs.
+  const long rows_eff = paired ? ((long)B + 1) / 2 : (long)B;
+  long budget = rows_eff * Hk * max_tiles / target_waves(D);
   budget = budget < kTilesPerWaveMin ? kTilesPerWaveMin
                                      : (budget > UQ_TILES_PER_WAVE_MAX ? UQ_TILES_PER_WAVE_MAX : budget);
   int spw = 1, nsub = 1;
@@ -987,22 +1043,29 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   // with three slots; a grid of one round keeps three (decode 36.0 against
   // 39.9 us with two).
   const bool two_slots = p.D == 256 && n_wg * hpw > 2 * 1024;
-#define UQ_STAGE1S(DV, QGV, HPWV, NS, FQ)                                                         \
-  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, NS, FQ>), grid1, block1, 0, stream, q8, a.query,  \
+#define UQ_STAGE1S(DV, QGV, HPWV, NS, MD)                                                         \
+  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, NS, MD>), grid1, block1, 0, stream, q8, a.query,  \
                      a.qsb, a.qsh, a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens,     \
                      scale_log2, p.Hq, p.Hk, hgroups,                                             \
                      cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,                   \
-                     a.num_blocks, a.window, part_o, part_m, part_l, part_e)
+                     a.num_blocks, a.window, p.B, part_o, part_m, part_l, part_e)
   // Stage 1 reads the query codes from the workspace, or (the two-launch
   // form, head dim 256) computes them itself.
   const bool fuse_q = p.D == 256 && (stage_mask & 8);
+  // Multi-query rows of one sequence share reads in pairs (see stage1_kernel)
+  // when the group leaves half the MFMA columns free and no window moves the
+  // rows' ranges apart.
+  const bool pair_rows = a.query_row != nullptr && a.window == 0 && p.QG <= 8 && !fuse_q;
 #define UQ_STAGE1F(DV, QGV, HPWV, NS)                                 \
   do {                                                                \
+    if constexpr (QGV <= 8) {                                         \
+      if (pair_rows) { UQ_STAGE1S(DV, QGV, HPWV, NS, 2); break; }     \
+    }                                                                 \
     if constexpr (DV == 256) {                                        \
-      if (fuse_q) UQ_STAGE1S(DV, QGV, HPWV, NS, true);                \
-      else UQ_STAGE1S(DV, QGV, HPWV, NS, false);                      \
+      if (fuse_q) UQ_STAGE1S(DV, QGV, HPWV, NS, 1);                   \
+      else UQ_STAGE1S(DV, QGV, HPWV, NS, 0);                          \
     } else {                                                          \
-      UQ_STAGE1S(DV, QGV, HPWV, NS, false);                           \
+      UQ_STAGE1S(DV, QGV, HPWV, NS, 0);                               \
     }                                                                 \
   } while (0)
 #define UQ_STAGE1(DV, QGV, HPWV)                                      \

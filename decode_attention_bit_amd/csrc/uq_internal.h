@@ -106,7 +106,7 @@ struct PrefillAttnArgs {
   int64_t qs_t, qs_h, kvs_t, kvs_h, os_t, os_h;
   int q_len, cached_len, Hk, QG;
   float scale;
-  int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head (D <= 256)
+  int64_t vt_tiles;          // > 0: v is in the tiled value layout with this many tiles per head
   int D;                     // head dim: 128, 256 or 512
   const int32_t* vshift;     // vt_tiles > 0: the tiles hold v * 2^-vshift[h][d / 32] in fp16
 };
@@ -122,7 +122,7 @@ struct StreamArgs {
   int sink_words;
 };
 
-DecodePlan plan_decode(int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
+DecodePlan plan_decode(bool paired, int B, int Hq, int Hk, int num_kv_splits, int max_blocks_per_seq,
                        int block_size, int D);
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);

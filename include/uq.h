@@ -110,7 +110,8 @@ int uq_store(const uint16_t* key, const uint16_t* value, uint8_t* kv_cache,
  * query head, partial). The count of partials depends on the
  * split count and on the block-table capacity max_blocks_per_seq *
  * block_size, never on the sequence lengths, so one workspace serves every
- * step of a fixed-shape batch.
+ * step of a fixed-shape batch. The size covers uq_decode_ex too, whose
+ * multi-query rows may cut finer partials (at a GQA group of 8 or less).
  */
 size_t uq_decode_workspace_bytes(int B, int Hq, int Hk, int D, int num_kv_splits,
                                  int max_blocks_per_seq, int block_size);
@@ -205,7 +206,10 @@ int uq_decode_no_alloc(const uint16_t* query, const uint8_t* kv_cache,
  * branch): query i of a chunk whose sequence holds cached_len tokens gets
  * the length cached_len + i + 1 and the sequence's block-table row, repeated
  * for every query of the chunk. Here the rows are not repeated: query row b
- * reads block-table row query_row[b].
+ * reads block-table row query_row[b]. Query rows 2r and 2r + 1 that read
+ * the same table row (at a GQA group of 8 or less, without a window) are
+ * decoded together, each tile of their common prefix read once; put the
+ * queries of one sequence next to each other to benefit.
  *   query_row:    (device) int32 (B,), or NULL for query_row[b] = b (then
  *                 n_table_rows must be B). A value outside
  *                 [0, n_table_rows) makes that query's output zeros.

@@ -332,3 +332,48 @@ def test_prefill_attention_strided_and_peaked(d, qg):
         want[:, hq] = p @ V[:, hq // qg] / p.sum(-1, keepdims=True)
     check_close(to_np(o[:, :, :d]), want, f"d={d} strided peaked qg={qg}", allow_output_rounding=True)
     assert torch.isnan(o[:, :, d:]).all()
+
+
+@pytest.mark.parametrize("qg", [6, 8, 16])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_decode_paired_query_rows(d, qg):
+    """Multi-query rows: consecutive query rows (2r, 2r + 1) that read the
+    same block-table row share one stage-1 wave when the group leaves half
+    the MFMA columns free (QG <= 8). Pairs with the shorter row first and
+    second (so that some partials hold tokens of one row only), an empty
+    sequence, a pair over different rows, and an odd row count, against the
+    oracle and bit for bit against the same rows decoded through a table
+    with each row repeated (no pairing)."""
+    say(f"decode paired rows d={d} qg={qg}")
+    rng = np.random.default_rng(d + qg + 51)
+    hk, bs = 2, 16
+    full = [300, 77, 0, 1000]
+    nblk = [(L + bs - 1) // bs for L in full]
+    nb = sum(nblk) + 3
+    perm = rng.permutation(nb)
+    table = np.zeros((len(full), max(nblk)), dtype=np.int32)
+    off = 0
+    cache = torch.zeros((nb, bs, hk, slot(d)), dtype=torch.uint8, device=DEV)
+    ref_cache = np.zeros(tuple(cache.shape), dtype=np.uint8)
+    for b, L in enumerate(full):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+        if L == 0:
+            continue
+        k, v = bf16(rng.standard_normal((L, hk, d))), bf16(rng.standard_normal((L, hk, d)))
+        t = np.arange(L)
+        slots = table[b, t // bs].astype(np.int64) * bs + t % bs
+        uq.store(k.to(DEV), v.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+        O.store(bits(k), bits(v), ref_cache, slots)
+    rows = np.array([0, 0, 1, 1, 0, 3, 3, 3, 2, 2, 1], dtype=np.int32)
+    lens = np.array([300, 45, 77, 77, 299, 1000, 16, 1000, 0, 0, 5], dtype=np.int32)
+    q = bf16(rng.standard_normal((len(rows), hk * qg, d)))
+    scale = 1 / np.sqrt(d)
+    ref = O.decode(bits(q), ref_cache, table[rows], lens, scale)
+    q_dev, tbl = q.to(DEV), torch.from_numpy(table).to(DEV)
+    rows_dev, lens_dev = torch.from_numpy(rows).to(DEV), torch.from_numpy(lens).to(DEV)
+    for splits in (1, 8, 64):
+        out = uq.decode_ex(q_dev, cache, tbl, lens_dev, scale, splits, query_row=rows_dev)
+        check_close(to_np(out), ref, f"paired rows d={d} qg={qg} splits={splits}")
+        rep = uq.decode(q_dev, cache, tbl[rows_dev.long()].contiguous(), lens_dev, scale, splits)
+        assert torch.equal(out, rep), f"splits={splits}: differs from the repeated-row decode"
