@@ -78,7 +78,7 @@ struct GatherArgs {
   uint16_t* vout;
   int64_t os_t, os_h;
   // Tiled values (vt != null): one workgroup per (KV head, 32-key tile)
-  // builds the whole tile (at D = 512 two 16-key sub-tiles): keys below n_tok dequantised from the cache
+  // builds the whole tile: keys below n_tok dequantised from the cache
   // (their V is then not written to vout), keys n_tok .. v_keys - 1 copied
   // from vsrc row key - n_tok, the rest of the last tile zero. The tiles hold
   // fp16 values times 2^-vshift[h][d / 32]: a first kernel writes, per
