@@ -33,51 +33,65 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
-// Query prologue: q8 = E4M3(q H), one wave per (sequence, query head), for
-// head dims 128, 256 and 512.
+// Query prologue: q8 = E4M3(q H), LPR lanes per (sequence, query head) row,
+// 64 / LPR rows per wave, for head dims 128, 256 and 512. LPR = 64 (short
+// lane chains) for the rows of a small batch, where latency counts; 16
+// (more in-lane butterfly stages, fewer lane exchanges) for large batches,
+// where throughput does.
 // The rotation runs in float64 and is exact, so the E4M3 rounding decision is
 // taken on the exact product (scaled by the float64 1/sqrt(D)).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int LPR>
 __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restrict__ query,
                                                         uint8_t* __restrict__ q8, int B, int Hq,
                                                         int64_t qsb, int64_t qsh) {
-  constexpr int E = D / 64;                    // elements per lane
-  const int64_t vec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (vec >= (int64_t)B * Hq) return;
-  const int lane = threadIdx.x & 63;
+  constexpr int E = D / LPR;                   // elements per lane
+  static_assert(E >= 2 && E <= 32, "elements per lane");
+  const int lane = threadIdx.x & 63, s = lane % LPR;
+  const int64_t vec = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;
+  const bool valid = vec < (int64_t)B * Hq;
+  if (LPR == 64 && !valid) return;             // a whole wave; else every lane runs the exchanges
   const int64_t b = vec / Hq;
   const int64_t hq = vec - b * Hq;
-  const uint16_t* qp = query + b * qsb + hq * qsh + E * lane;
+  const uint16_t* qp = query + b * qsb + hq * qsh + E * s;
   double v[E];
-  if constexpr (E == 2) {
-    const uint32_t r = *reinterpret_cast<const uint32_t*>(qp);
-    v[0] = bf16_to_f64(r & 0xFFFF);
-    v[1] = bf16_to_f64(r >> 16);
-  } else {
 #pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-      const uint2 r = *reinterpret_cast<const uint2*>(qp + 4 * c);
-      v[4 * c] = bf16_to_f64(r.x & 0xFFFF);
-      v[4 * c + 1] = bf16_to_f64(r.x >> 16);
-      v[4 * c + 2] = bf16_to_f64(r.y & 0xFFFF);
-      v[4 * c + 3] = bf16_to_f64(r.y >> 16);
+  for (int i = 0; i < E; ++i) v[i] = 0.0;
+  if (valid) {
+    if constexpr (E == 2) {
+      const uint32_t r = *reinterpret_cast<const uint32_t*>(qp);
+      v[0] = bf16_to_f64(r & 0xFFFF);
+      v[1] = bf16_to_f64(r >> 16);
+    } else {
+#pragma unroll
+      for (int c = 0; c < E / 4; ++c) {
+        const uint2 r = *reinterpret_cast<const uint2*>(qp + 4 * c);
+        v[4 * c] = bf16_to_f64(r.x & 0xFFFF);
+        v[4 * c + 1] = bf16_to_f64(r.x >> 16);
+        v[4 * c + 2] = bf16_to_f64(r.y & 0xFFFF);
+        v[4 * c + 3] = bf16_to_f64(r.y >> 16);
+      }
     }
   }
-  fwht_wave<E, true>(v, lane);
+  fwht_wave<E, true, LPR>(v, lane);
   // codes of the float64 products, through float32 rounded to odd
   uint32_t w[(E + 3) / 4] = {};
 #pragma unroll
   for (int i = 0; i < E; i += 2)
     w[i / 4] |= e4m3_pair(to_f32_odd(v[i] * rot_scale<D>()), to_f32_odd(v[i + 1] * rot_scale<D>()))
                 << (8 * (i % 4));
-  uint8_t* dst = q8 + vec * D + E * lane;
+  if (!valid) return;
+  uint8_t* dst = q8 + vec * D + E * s;
   if constexpr (E == 2) {
     *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
   } else if constexpr (E == 4) {
     *reinterpret_cast<uint32_t*>(dst) = w[0];
-  } else {
+  } else if constexpr (E == 8) {
     *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < E / 16; ++k)
+      reinterpret_cast<uint4*>(dst)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
   }
 }
 
@@ -1006,13 +1020,25 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   if (p.D != 128 && p.D != 256 && p.D != 512) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
   if (stage_mask & 1) {
-    const dim3 g((unsigned)((vecs + 3) / 4));
-    if (p.D == 128)
-      hipLaunchKernelGGL(qprologue_kernel<128>, g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, a.qsb, a.qsh);
-    else if (p.D == 256)
-      hipLaunchKernelGGL(qprologue_kernel<256>, g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, a.qsb, a.qsh);
-    else
-      hipLaunchKernelGGL(qprologue_kernel<512>, g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, a.qsb, a.qsh);
+    // lanes per row: 16 from 4096 rows on (the mixed serving step's 8192
+    // rows: 6.00 -> 5.25 us), else 64 (3072 rows: 3.32 us against 3.63 with
+    // 16; 1024 rows: 2.35 us)
+    const int lpr = vecs <= 4096 ? 64 : 16;
+    const int64_t per_block = 4 * (64 / lpr);
+    const dim3 g((unsigned)((vecs + per_block - 1) / per_block));
+#define UQ_QPRO(DV)                                                                                     \
+    do {                                                                                                \
+      if (lpr == 64)                                                                                    \
+        hipLaunchKernelGGL((qprologue_kernel<DV, 64>), g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, \
+                           a.qsb, a.qsh);                                                               \
+      else                                                                                              \
+        hipLaunchKernelGGL((qprologue_kernel<DV, 16>), g, dim3(256), 0, stream, a.query, q8, p.B, p.Hq, \
+                           a.qsb, a.qsh);                                                               \
+    } while (0)
+    if (p.D == 128) UQ_QPRO(128);
+    else if (p.D == 256) UQ_QPRO(256);
+    else UQ_QPRO(512);
+#undef UQ_QPRO
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

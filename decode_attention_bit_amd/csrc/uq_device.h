@@ -104,10 +104,11 @@ __device__ __forceinline__ double negate_if(double x, uint32_t flip) {
   return __longlong_as_double(u);
 }
 
-template <int E, bool REG = false>
+template <int E, bool REG = false, int LPV = 64>
 __device__ __forceinline__ void fwht_wave(double v[E], int lane) {
-  // D-point butterfly, D = 64 E: index bits below log2(E) inside a lane, the
-  // rest are lane bits 0-5 (same exactness condition as below)
+  // D-point butterfly over LPV lanes (one vector per group of LPV lanes),
+  // D = LPV E: index bits below log2(E) inside a lane, the rest are lane
+  // bits 0 .. log2(LPV) - 1 (same exactness condition as below)
 #pragma unroll
   for (int m = 1; m < E; m <<= 1) {
 #pragma unroll
@@ -118,8 +119,9 @@ __device__ __forceinline__ void fwht_wave(double v[E], int lane) {
       v[i + m] = a - b;
     }
   }
+  static_assert(REG || LPV == 64, "LDS-pipe exchanges span the wave");
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
+  for (int m = 1; m < LPV; m <<= 1) {
     const uint32_t flip = (lane & m) ? 0x80000000u : 0u;   // upper lane: o - v = (-v) + o
 #pragma unroll
     for (int i = 0; i < E; ++i) {

@@ -377,3 +377,29 @@ def test_decode_paired_query_rows(d, qg):
         check_close(to_np(out), ref, f"paired rows d={d} qg={qg} splits={splits}")
         rep = uq.decode(q_dev, cache, tbl[rows_dev.long()].contiguous(), lens_dev, scale, splits)
         assert torch.equal(out, rep), f"splits={splits}: differs from the repeated-row decode"
+
+
+@pytest.mark.parametrize("rows", [1536, 8192])
+@pytest.mark.parametrize("d", [128, 256, 512])
+def test_query_prologue_codes_many_rows(d, rows):
+    """The query prologue of a large batch (64 lanes per row, or 16 lanes and
+    several rows per wave with a partly filled last wave) gives the oracle's codes bit
+    for bit: random rows, zero rows, tiny and huge rows, and rows of values
+    spread over 24 binades."""
+    say(f"prologue many rows d={d} rows={rows}")
+    rng = np.random.default_rng(d + rows)
+    hk, qg = 2, 8
+    B = rows // (hk * qg) + 1                 # one more sequence than needed: 16 extra rows
+    q = rng.standard_normal((B, hk * qg, d))
+    q[0, 0] = 0.0
+    q[1, 3] = rng.standard_normal(d) * 2.0 ** -20
+    q[2, 5] = rng.standard_normal(d) * 300.0
+    q[3, 7] = rng.choice([-1.0, 1.0], d) * (1 + rng.random(d)) * np.exp2(rng.integers(-12, 13, d))
+    qb = bf16(q)
+    cache = torch.zeros((1, 16, hk, slot(d)), dtype=torch.uint8, device=DEV)
+    ws = torch.full((uq.decode_workspace_bytes(B, hk * qg, hk, 1, 1, 16, d),), 0x55, dtype=torch.uint8, device=DEV)
+    uq.decode(qb.to(DEV), cache, torch.zeros((B, 1), dtype=torch.int32, device=DEV),
+              torch.ones(B, dtype=torch.int32, device=DEV), 1 / 16, 1, workspace=ws, stages=uq.STAGE_PROLOGUE)
+    got = ws[:B * hk * qg * d].cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy().reshape(B, hk * qg, d)
+    ref = O.query_haircut(bits(qb))
+    assert np.array_equal(got, ref), f"{(got != ref).sum()} codes differ"
