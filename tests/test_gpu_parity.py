@@ -497,6 +497,51 @@ def test_decode_multi_query_continuation_chunks():
     check_close(o[1:-1], ref[1:-1], "multi-query, valid rows")
 
 
+def test_decode_paired_rows_large_batch():
+    """Paired multi-query rows on a grid of many rounds (the two-slot ring of
+    stage 1): 256 sequences of 40 to 112 tokens, two query rows each (the
+    second one token longer, as in a two-token speculative step), against
+    the oracle on a sample of rows, and bit for bit like the same rows
+    through a repeated-row table with distinct row indices (the same
+    partials plan, no pairs)."""
+    say("decode paired rows, large batch")
+    rng = np.random.default_rng(61)
+    nseq, hk, qg, bs = 256, 4, 8, 16
+    full = rng.integers(40, 113, nseq)
+    width = int((full.max() + bs - 1) // bs)
+    nblk = [(int(L) + bs - 1) // bs for L in full]
+    nb = sum(nblk) + 5
+    perm = rng.permutation(nb)
+    table = np.zeros((nseq, width), dtype=np.int32)
+    cache = torch.zeros((nb, bs, hk, 272), dtype=torch.uint8, device=DEV)
+    ref_cache = np.zeros(tuple(cache.shape), dtype=np.uint8)
+    off = 0
+    kall = bf16(rng.standard_normal((int(full.sum()), hk, 256)))
+    vall = bf16(rng.standard_normal((int(full.sum()), hk, 256)))
+    slots = np.zeros(int(full.sum()), dtype=np.int64)
+    pos = 0
+    for b, L in enumerate(full):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+        t = np.arange(L)
+        slots[pos:pos + L] = table[b, t // bs].astype(np.int64) * bs + t % bs
+        pos += L
+    uq.store(kall.to(DEV), vall.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+    O.store(bits(kall), bits(vall), ref_cache, slots)
+    rows = np.repeat(np.arange(nseq), 2).astype(np.int32)
+    lens = (full[rows] - 1 + np.tile([0, 1], nseq)).astype(np.int32)
+    q = bf16(rng.standard_normal((len(rows), hk * qg, 256)))
+    q_dev, tbl = q.to(DEV), torch.from_numpy(table).to(DEV)
+    rows_dev, lens_dev = torch.from_numpy(rows).to(DEV), torch.from_numpy(lens).to(DEV)
+    out = uq.decode_ex(q_dev, cache, tbl, lens_dev, 1 / 16, 32, query_row=rows_dev)
+    pick = np.sort(rng.choice(len(rows), 24, replace=False))
+    ref = O.decode(bits(q[pick]), ref_cache, table[rows[pick]], lens[pick], 1 / 16)
+    check_close(to_np(out)[pick], ref, "paired rows, large batch")
+    own = torch.arange(len(rows), dtype=torch.int32, device=DEV)
+    rep = uq.decode_ex(q_dev, cache, tbl[rows_dev.long()].contiguous(), lens_dev, 1 / 16, 32, query_row=own)
+    assert torch.equal(out, rep), "paired rows differ from the same rows decoded one by one"
+
+
 @pytest.mark.parametrize("window", [0, 1, 15, 16, 17, 100, 333, 5000])
 def test_decode_sinks_and_sliding_window(window):
     """Per-head sink logits and a sliding window of the last W tokens against
