@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void qprologue_kernel(const uint16_t* __restri
       }
     }
   }
-  fwht_wave<E, true, LPR>(v, lane);
+  fwht_lanes<E, LPR>(v, lane);
   // codes of the float64 products, through float32 rounded to odd
   uint32_t w[(E + 3) / 4] = {};
 #pragma unroll

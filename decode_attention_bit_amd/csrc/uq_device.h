@@ -16,7 +16,6 @@ struct Fmt {
   static_assert(D == 128 || D == 256 || D == 512, "head dim");
   static constexpr int kSlot = D * 17 / 16;
   static constexpr int kKCode = 0, kVCode = D / 2, kKScale = D, kVScale = D + D / 32;
-  static constexpr int kPerLane = D / 64;          // elements per lane of a one-wave vector
 };
 
 // The float64 nearest 1/sqrt(D): sqrt(2) = 0x1.6a09e667f3bcdp+0 correctly
@@ -85,17 +84,6 @@ __device__ __forceinline__ double xor_lane(double v, int m, int lane) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-// 256-point Walsh-Hadamard butterfly (unnormalised) over one wave: lane l
-// holds x[4l .. 4l+3] in v[0..3]. Index bits 0-1 live inside a lane, bits 2-7
-// are lane bits 0-5. Each stage maps (a, b) -> (a + b, a - b). In float64 the
-// result is exact whenever every +-sum of the inputs fits 53 bits, which
-// holds for bf16 inputs whose non-zero magnitudes span at most 45 - log2(D)
-// binades (37 at D = 256).
-// REG: lane exchanges in registers (xor_lane), which shortens a wave's
-// latency (the query prologue: 2.81 -> 2.68 us); otherwise through the LDS
-// pipe (__shfl_xor), which runs beside the VALU when many waves are resident
-// (a one-vector-per-wave store of 16384 x 4 vectors took 51 us this way and
-// 60 us with register exchanges).
 // x with its sign bit XORed with flip (0 or the sign bit): -x or x, exactly;
 // IEEE subtraction o - x is by definition the sum (-x) + o, so a butterfly's
 // upper output needs no separate subtraction.
@@ -104,11 +92,20 @@ __device__ __forceinline__ double negate_if(double x, uint32_t flip) {
   return __longlong_as_double(u);
 }
 
-template <int E, bool REG = false, int LPV = 64>
-__device__ __forceinline__ void fwht_wave(double v[E], int lane) {
-  // D-point butterfly over LPV lanes (one vector per group of LPV lanes),
-  // D = LPV E: index bits below log2(E) inside a lane, the rest are lane
-  // bits 0 .. log2(LPV) - 1 (same exactness condition as below)
+// D-point Walsh-Hadamard butterfly (unnormalised), D = LPV E, over groups of
+// LPV lanes (one vector per group): lane s of a group holds x[E s .. E s +
+// E - 1] in v[0 .. E - 1], so index bits below log2(E) live inside a lane and
+// the rest are lane bits 0 .. log2(LPV) - 1. Each stage maps (a, b) ->
+// (a + b, a - b); the lane stages exchange through registers (xor_lane). In
+// float64 the result is exact whenever every +-sum of the inputs fits 53
+// bits, which holds for bf16 inputs whose non-zero magnitudes span at most
+// 45 - log2(D) binades (37 at D = 256). Fewer lanes per vector trade lane
+// exchanges for in-lane stages: better throughput with many vectors, longer
+// chains with few. (Lane stages through the LDS pipe instead, one vector per
+// wave, took 51 us for a store of 16384 x 4 vectors, and 60 us with register
+// exchanges; the query prologue's latency fell from 2.81 to 2.68 us with them.)
+template <int E, int LPV>
+__device__ __forceinline__ void fwht_lanes(double v[E], int lane) {
 #pragma unroll
   for (int m = 1; m < E; m <<= 1) {
 #pragma unroll
@@ -119,30 +116,12 @@ __device__ __forceinline__ void fwht_wave(double v[E], int lane) {
       v[i + m] = a - b;
     }
   }
-  static_assert(REG || LPV == 64, "LDS-pipe exchanges span the wave");
+  static_assert(LPV == 16 || LPV == 32 || LPV == 64, "lanes per vector");
 #pragma unroll
   for (int m = 1; m < LPV; m <<= 1) {
     const uint32_t flip = (lane & m) ? 0x80000000u : 0u;   // upper lane: o - v = (-v) + o
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const double o = REG ? xor_lane(v[i], m, lane) : __shfl_xor(v[i], m);
-      v[i] = negate_if(v[i], flip) + o;
-    }
-  }
-}
-
-__device__ __forceinline__ void fwht256_wave(double v[4], int lane) {
-  const double a0 = v[0] + v[1], a1 = v[0] - v[1];
-  const double a2 = v[2] + v[3], a3 = v[2] - v[3];
-  v[0] = a0 + a2; v[1] = a1 + a3; v[2] = a0 - a2; v[3] = a1 - a3;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint32_t flip = (lane & m) ? 0x80000000u : 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double o = __shfl_xor(v[i], m);
-      v[i] = negate_if(v[i], flip) + o;
-    }
+    for (int i = 0; i < E; ++i) v[i] = negate_if(v[i], flip) + xor_lane(v[i], m, lane);
   }
 }
 

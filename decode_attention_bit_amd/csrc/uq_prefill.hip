@@ -266,23 +266,27 @@ __device__ __forceinline__ void value_tile(const GatherArgs& a, int h, int64_t j
 
 // ---------------------------------------------------------------------------
 // Gather. With tiled values (the continuation prefill) the first Hk * vt_tiles
-// workgroups each build one value tile (value_tile). After them, one wave
-// per unit of work, the role chosen by the wave's index (wave-uniform):
-// first the prefix slots (token, KV head) to dequantise, then up to three
-// jobs over vectors of D bf16 (rotate or copy).
+// workgroups each build one value tile (value_tile). After them, waves with
+// a role chosen by the wave's index (wave-uniform): first one wave per prefix
+// slot (token, KV head) to dequantise, then up to three jobs over vectors of
+// D bf16 (rotate or copy), four vectors per wave.
 // Dequant: lanes 0-31 write K elements D/32 l .. D/32 l + D/32 - 1, lanes
 // 32-63 the same V elements (token-major values only); each reads the code
 // bytes and the one scale byte that cover them (D/32 <= 16 consecutive
 // elements never straddle a 32-element block).
-// Rotate: lane l holds x[D/64 l .. D/64 l + D/64 - 1] through the float64
-// butterfly, then the float64 nearest 1/sqrt(D) and one rounding to bf16.
+// Rotate: 16 lanes per vector; lane s of a vector holds x[D/16 s .. D/16 s +
+// D/16 - 1] through the float64 butterfly (its low stages inside the lane,
+// the four lane stages with register exchanges within the row of 16), then
+// the float64 nearest 1/sqrt(D) and one rounding to bf16. (One vector per
+// wave with the lane stages through the LDS pipe took 53 us for the gather
+// of the 4096 + 2048-token prefill at D = 256.)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
   using F = Fmt<D>;
   constexpr int EPL = D / 32;              // dequantised elements per lane
   constexpr int NCB = EPL / 2;             // code bytes per lane: 2, 4 or 8
-  constexpr int E = F::kPerLane;           // rotated elements per lane: 2, 4 or 8
+  constexpr int E = D / 16;                // vector-job elements per lane: 8, 16 or 32
   int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   {
@@ -336,48 +340,41 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
     return;
   }
   w -= n_slots;
+  const int s = lane & 15;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const VecJob& jb = a.job[j];
-    if (w >= jb.n) {
-      w -= jb.n;
+    const int64_t jw = (jb.n + 3) / 4;     // the job's waves
+    if (w >= jw) {
+      w -= jw;
       continue;
     }
-    const int64_t t = w / jb.H;
-    const int h = (int)(w - t * jb.H);
-    // E bf16 per lane in words of two: one 4-byte load at D = 128, else
-    // 8-byte loads (the rows are only 8-byte aligned)
-    const uint16_t* sp = jb.src + t * jb.ss_t + (int64_t)h * jb.ss_h + E * lane;
+    const int64_t vec = 4 * w + (lane >> 4);
+    const bool valid = vec < jb.n;         // lanes of a missing vector run the exchanges on zeros
+    const int64_t t = valid ? vec / jb.H : 0;
+    const int h = valid ? (int)(vec - t * jb.H) : 0;
+    // E bf16 per lane in 8-byte loads (the rows are only 8-byte aligned)
+    const uint16_t* sp = jb.src + t * jb.ss_t + (int64_t)h * jb.ss_h + E * s;
     uint32_t r[E / 2];
-    if constexpr (E == 2) {
-      r[0] = *reinterpret_cast<const uint32_t*>(sp);
-    } else {
 #pragma unroll
-      for (int i = 0; i < E / 4; ++i) {
-        const uint2 x = *reinterpret_cast<const uint2*>(sp + 4 * i);
-        r[2 * i] = x.x;
-        r[2 * i + 1] = x.y;
-      }
+    for (int i = 0; i < E / 4; ++i) {
+      const uint2 x = valid ? *reinterpret_cast<const uint2*>(sp + 4 * i) : make_uint2(0, 0);
+      r[2 * i] = x.x;
+      r[2 * i + 1] = x.y;
     }
     if (jb.rotate) {
       double v[E];
 #pragma unroll
       for (int i = 0; i < E; ++i) v[i] = bf16_to_f64((r[i >> 1] >> (16 * (i & 1))) & 0xFFFF);
-      if constexpr (D == kHeadDim)
-        fwht256_wave(v, lane);
-      else
-        fwht_wave<E>(v, lane);
+      fwht_lanes<E, 16>(v, lane);
 #pragma unroll
       for (int i = 0; i < E / 2; ++i)
         r[i] = bf16_bits_rne(v[2 * i] * rot_scale<D>()) | (bf16_bits_rne(v[2 * i + 1] * rot_scale<D>()) << 16);
     }
-    uint16_t* dp = jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + E * lane;
-    if constexpr (E == 2) {
-      *reinterpret_cast<uint32_t*>(dp) = r[0];
-    } else {
+    if (!valid) return;
+    uint16_t* dp = jb.dst + t * jb.ds_t + (int64_t)h * jb.ds_h + E * s;
 #pragma unroll
-      for (int i = 0; i < E / 4; ++i) *reinterpret_cast<uint2*>(dp + 4 * i) = make_uint2(r[2 * i], r[2 * i + 1]);
-    }
+    for (int i = 0; i < E / 4; ++i) *reinterpret_cast<uint2*>(dp + 4 * i) = make_uint2(r[2 * i], r[2 * i + 1]);
     return;
   }
 }
@@ -386,12 +383,14 @@ __global__ __launch_bounds__(256) void prefill_gather_kernel(GatherArgs a) {
 // Attention. Workgroup = (block of query positions, KV head); its 128 columns
 // are (position, query head) pairs of that KV head, column c -> position
 // p0 + c / QG, head hk * QG + c % QG, so the QG heads sharing a KV head share
-// every K/V tile. Wave w owns columns 32w .. 32w+31 as two 16-column blocks.
-// Keys stream in tiles of 32 through a kStages-deep LDS ring filled by
-// direct-to-LDS buffer loads (each wave moves 8 of the 32 rows of K and of V,
-// two rows per load); the rows are 512 bytes with their 16-byte chunks
-// permuted (chunk c of row r stored at c ^ f(r)) so that the reads below hit
-// distinct banks: f(r) = r & 15 for K, ((r >> 2) & 3) << 2 for V.
+// every K/V tile. Wave w owns columns 16 CB w .. 16 CB w + 16 CB - 1 as CB
+// 16-column blocks (CB = 1: eight waves, two per SIMD). Keys stream in tiles
+// of 32 through a kStages-deep LDS ring filled by direct-to-LDS buffer loads
+// (each wave moves its share of the 32 rows of K and of V, 1 KB per load);
+// the rows are 2 D bytes with their 16-byte chunks permuted (chunk c of row r
+// stored at c ^ f(r)) so that the reads below hit distinct banks: f(r) =
+// r & 15 for K, ((r >> 2) & 3) << 2 for token-major V (tiled values: by dim,
+// see vt_swizzle).
 //
 // V_MFMA_F32_16X16X32_BF16, lane l: row/col l%16, k-slots (l/16, 0..7);
 // result lane l: col l%16, rows 4*(l/16) + i. Which k a slot stands for is
@@ -1235,7 +1234,8 @@ __global__ __launch_bounds__(512) void prefill_attn512_kernel(
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
   const int64_t tile_waves = a.vt ? 4 * (int64_t)a.Hk * a.vt_tiles : 0;
-  const int64_t waves = tile_waves + (int64_t)a.n_tok * a.Hk + a.job[0].n + a.job[1].n + a.job[2].n;
+  const int64_t waves = tile_waves + (int64_t)a.n_tok * a.Hk + (a.job[0].n + 3) / 4 + (a.job[1].n + 3) / 4 +
+                        (a.job[2].n + 3) / 4;
   if (waves == 0) return hipSuccess;
   if (a.vt) {                                 // the value tiles' exponent shifts first
     const dim3 vgrid(kVexpParts, (unsigned)a.Hk);

@@ -74,22 +74,7 @@ __global__ __launch_bounds__(256) void store_kernel(
       v[0] = bf16_to_f32(vr & 0xFFFF); v[1] = bf16_to_f32(vr >> 16);
     }
   }
-#pragma unroll
-  for (int m = 1; m < E; m <<= 1) {
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      if (i & m) continue;
-      const double a = k[i], b = k[i + m];
-      k[i] = a + b;
-      k[i + m] = a - b;
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < LPS; m <<= 1) {
-    const uint32_t flip = (s & m) ? 0x80000000u : 0u;   // upper lane: o - v = (-v) + o
-#pragma unroll
-    for (int i = 0; i < E; ++i) k[i] = negate_if(k[i], flip) + xor_lane(k[i], m, lane);
-  }
+  fwht_lanes<E, LPS>(k, lane);
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     k[i] *= rot_scale<D>();            // 1/16 exact at D = 256; one rounding otherwise
