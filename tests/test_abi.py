@@ -147,6 +147,34 @@ def test_decode_ex_rejects(libuq, kw, code):
     assert _err(libuq)
 
 
+def _decode_ws(B, Hq, D, parts):
+    """Decode workspace bytes for `parts` partials per row: query codes, fp16
+    partial rows and three 4-byte statistics, each section 256-byte aligned."""
+    a = lambda x: (x + 255) // 256 * 256
+    rows = B * Hq
+    return a(rows * D) + a(rows * parts * D * 2) + 3 * a(rows * parts * 4)
+
+
+def test_workspace_covers_paired_rows(libuq):
+    """Multi-query rows that may pair plan partials for half the rows, so at
+    64 rows x 4 KV heads x 256 tiles the paired plan cuts 8 partials per row
+    where the plain decode cuts 4. The workspace size covers the larger one,
+    and uq_decode_ex with query_row rejects a workspace that only holds the
+    smaller one (checked before any HIP call)."""
+    B, Hq, Hk, D, S, mb, bs = 64, 32, 4, 256, 32, 256, 16
+    assert libuq.uq_decode_partials(B, Hq, Hk, D, S, mb, bs) == 4
+    n = libuq.uq_decode_workspace_bytes(B, Hq, Hk, D, S, mb, bs)
+    assert n == _decode_ws(B, Hq, D, 8)
+    small = _decode_ws(B, Hq, D, 4)
+    args = decode_ex_args(rows=B, B=B, Hq=Hq, Hk=Hk, D=D, splits=S, max_blocks=mb, block_size=bs,
+                          num_blocks=B * mb, ws_bytes=small)
+    assert libuq.uq_decode_ex(*args) == -3
+    assert "workspace" in _err(libuq)
+    # at a GQA group of 16 no rows pair: one plan
+    assert libuq.uq_decode_workspace_bytes(B, 64, Hk, D, S, mb, bs) == \
+        _decode_ws(B, 64, D, libuq.uq_decode_partials(B, 64, Hk, D, S, mb, bs))
+
+
 # ------------------------------------------------------ continuation prefill
 def rotate_args(**kw):
     a = dict(x=FAKE, out=FAKE, N=4, H=2, D=256, xsn=512, xsh=256, osn=512, osh=256, stream=None)
