@@ -1061,18 +1061,6 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   const int64_t n_wg = (int64_t)p.B * p.parts * hgroups;
   const dim3 grid1((unsigned)n_wg);
   const dim3 block1(64 * hpw);
-  // At head dim 256 a grid of several rounds of the chip (more than two waves
-  // per SIMD) streams through a two-slot ring (one tile in flight while one
-  // is computed): mixed 246.7 against 251.6 us, ragged 252.8 against 260.8
-  // with three slots; a grid of one round keeps three (decode 36.0 against
-  // 39.9 us with two).
-  const bool two_slots = p.D == 256 && n_wg * hpw > 2 * 1024;
-#define UQ_STAGE1S(DV, QGV, HPWV, NS, MD)                                                         \
-  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, NS, MD>), grid1, block1, 0, stream, q8, a.query,  \
-                     a.qsb, a.qsh, a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens,     \
-                     scale_log2, p.Hq, p.Hk, hgroups,                                             \
-                     cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,                   \
-                     a.num_blocks, a.window, p.B, part_o, part_m, part_l, part_e)
   // Stage 1 reads the query codes from the workspace, or (the two-launch
   // form, head dim 256) computes them itself.
   const bool fuse_q = p.D == 256 && (stage_mask & 8);
@@ -1080,6 +1068,21 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, int stage_mas
   // when the group leaves half the MFMA columns free and no window moves the
   // rows' ranges apart.
   const bool pair_rows = a.query_row != nullptr && a.window == 0 && p.QG <= 8 && !fuse_q;
+  // At head dim 256 a grid of two waves per SIMD or more (counting only the
+  // waves that stream: with paired rows half the grid exits at once) streams
+  // through a two-slot ring (one tile in flight while one is computed):
+  // mixed 246.7 against 251.6 us, ragged 252.8 against 260.8, long (2048
+  // waves) 208 against 216 us for stage 1, with three slots; a grid of one
+  // wave per SIMD keeps three (decode 36.0 against 39.9 us with two; two
+  // query rows per sequence 40.7 against 44.0).
+  const int64_t streaming_waves = pair_rows ? n_wg * hpw / 2 : n_wg * hpw;
+  const bool two_slots = p.D == 256 && streaming_waves >= 2 * 1024;
+#define UQ_STAGE1S(DV, QGV, HPWV, NS, MD)                                                         \
+  hipLaunchKernelGGL((stage1_kernel<DV, QGV, HPWV, NS, MD>), grid1, block1, 0, stream, q8, a.query,  \
+                     a.qsb, a.qsh, a.cache, a.block_table, a.query_row, a.n_rows, a.seq_lens,     \
+                     scale_log2, p.Hq, p.Hk, hgroups,                                             \
+                     cs, p.spw, p.nsub, p.parts, log2_bs, a.max_blocks_per_seq,                   \
+                     a.num_blocks, a.window, p.B, part_o, part_m, part_l, part_e)
 #define UQ_STAGE1F(DV, QGV, HPWV, NS)                                 \
   do {                                                                \
     if constexpr (QGV <= 8) {                                         \
